@@ -1,0 +1,330 @@
+/*
+ * CPU oracle for per-row RMSNorm fused with rotary position embedding.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load or call this library.  It shares no
+ * code with the HIP library.  Build: gcc -O2 -ffp-contract=off (no fast-math),
+ * so every operation below is one IEEE double operation in source order.
+ *
+ * Sources (web pages; cited by the short name in brackets):
+ *   [Ovis]   vllm-omni pull request "[Kernel][Ovis-Image] Fuse text/image QK
+ *            RMSNorm + cat + RoPE into one Triton launch"
+ *   [Vulkan] vllm.cpp pull request "perf(vulkan): decode RmsNorm ran on ONE
+ *            workgroup -- 7.85 -> 1.59 ms/token"
+ *   [IMROPE] llama.cpp fork pull request "hrx: the multi-section rotation of
+ *            Qwen3-VL runs on the device, not on the CPU"
+ *   [ViT]    vLLM API page "vllm.model_executor.layers.rotary_embedding.
+ *            mrope_vit_setup"
+ *   [VecRMS] vLLM pull request "Vectorize RMS norm variance using
+ *            vectorize_read_with_alignment"
+ *
+ * Readings taken where the pages leave a step open are listed with the
+ * function that takes them.  What pins each function against something other
+ * than itself is in tests/test_oracle_pins.py.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Rounding                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 keeps 8 significant bits and fp32's exponent range.  A normal value in
+ * [2^(e-1), 2^e) therefore sits on a grid of spacing 2^(e-8); below 2^-126 the
+ * spacing stays at 2^-133 (subnormals).  nearbyint() rounds half to even in
+ * the default rounding mode.  Results past the largest finite bf16
+ * (0x1.FEp127) become infinity. */
+double oracle_round_bf16(double v)
+{
+    if (v == 0.0 || !isfinite(v))
+        return v;
+    int e;
+    (void)frexp(v, &e);
+    int q = e - 8;
+    if (q < -133)
+        q = -133;
+    double r = ldexp(nearbyint(ldexp(v, -q)), q);
+    if (fabs(r) > 0x1.FEp127)
+        r = copysign(INFINITY, v);
+    return r;
+}
+
+static float round_out(double v, int32_t out_kind)
+{
+    if (out_kind == ORACLE_OUT_BF16)
+        return (float)oracle_round_bf16(v);   /* exact: a bf16 value fits a float */
+    return (float)v;                          /* round to nearest even fp32 */
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm of one row                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* u_i = x_i * rrms * w_i with rrms = 1 / sqrt(sum(x^2) / d + eps).
+ * The normalisation statistic is the mean of the squares and eps is added
+ * inside the square root ([Ovis] and [VecRMS]: RMSNorm with eps 1e-6; the
+ * weight multiplies the normalised value, [VecRMS] review thread quoting the
+ * output expression of rms_norm_kernel). */
+static void norm_row(const float* x, const float* w, int32_t d, float eps, double* u)
+{
+    double ss = 0.0;
+    for (int32_t i = 0; i < d; ++i)
+        ss += (double)x[i] * (double)x[i];
+    double rrms = 1.0 / sqrt(ss / (double)d + (double)eps);
+    for (int32_t i = 0; i < d; ++i)
+        u[i] = (double)x[i] * rrms * (double)w[i];
+}
+
+/* Plain row RMSNorm ([Vulkan] decode RmsNorm of width 5120; [VecRMS]).
+ * Reading: one rounding of x * rrms * w to the output type. */
+void oracle_rms_norm(const float* x, int64_t rows, int32_t width, const float* weight,
+                     float eps, int32_t out_kind, float* y)
+{
+    double* u = (double*)malloc(sizeof(double) * (size_t)width);
+    for (int64_t r = 0; r < rows; ++r) {
+        norm_row(x + r * width, weight, width, eps, u);
+        for (int32_t i = 0; i < width; ++i)
+            y[r * width + i] = round_out(u[i], out_kind);
+    }
+    free(u);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Which position axis a rotary pair reads                                   */
+/* ------------------------------------------------------------------------ */
+
+/* AXES / PLANES: the pairs are split into contiguous runs, sections[0] pairs
+ * on t, then sections[1] on h, then sections[2] on w ([ViT] setup kernel: the
+ * t, h and w column ranges of the planes follow one another).
+ * IMROPE: sector = p mod (s0+s1+s2+s3); sector mod 3 == 1 selects h while
+ * sector < 3*s1, == 2 selects w while sector < 3*s2, == 0 selects t while
+ * sector < 3*s0; every other pair reads the fourth component e ([IMROPE]
+ * "The change", and the review comment that sets the rule beside
+ * ggml_mrope_cache_init). */
+int32_t oracle_axis(const oracle_rope* rope, int32_t p)
+{
+    const int32_t* s = rope->sections;
+    switch (rope->mode) {
+    case ORACLE_POS_1D:
+        return ORACLE_AXIS_T;
+    case ORACLE_POS_AXES:
+    case ORACLE_POS_PLANES: {
+        int32_t end = 0;
+        for (int32_t a = 0; a < 3; ++a) {
+            end += s[a];
+            if (p < end)
+                return a;
+        }
+        return -1;   /* pair outside every section: invalid input */
+    }
+    case ORACLE_POS_IMROPE: {
+        int32_t sect_dims = s[0] + s[1] + s[2] + s[3];
+        int32_t sector = p % sect_dims;
+        if (sector % 3 == 1 && sector < 3 * s[1])
+            return ORACLE_AXIS_H;
+        if (sector % 3 == 2 && sector < 3 * s[2])
+            return ORACLE_AXIS_W;
+        if (sector % 3 == 0 && sector < 3 * s[0])
+            return ORACLE_AXIS_T;
+        return ORACLE_AXIS_E;
+    }
+    default:
+        return -1;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* cos and sin of one (token, pair)                                          */
+/* ------------------------------------------------------------------------ */
+
+/* The angle is the fp32 product of the fp32 position and the fp32 inverse
+ * frequency, rounded once ([ViT] setup kernel multiplies the float32 position
+ * by inv_freq).  Its cos and sin are then taken in double.  The position is
+ * read at plane * pos_stride + token_base + token: a launch over a token chunk
+ * keeps the whole-length planes and is told where its tokens start ([IMROPE]
+ * "The change" and "Proof", the chunk-offset bug).  PLANES mode reads the cos
+ * and sin that the setup wrote for the pair's axis ([ViT] the consumer reads
+ * only each axis's section columns). */
+static void pair_cos_sin(const oracle_rope* rope, int64_t tok, int32_t p, double* c, double* s)
+{
+    int32_t a = oracle_axis(rope, p);
+    int64_t t = rope->token_base + tok;
+    if (rope->mode == ORACLE_POS_PLANES) {
+        int64_t half = rope->rotary_dim / 2;
+        int64_t idx = ((int64_t)a * rope->planes_tokens + t) * half + p;
+        *c = (double)rope->cos_planes[idx];
+        *s = (double)rope->sin_planes[idx];
+        return;
+    }
+    int32_t pos = rope->positions[(int64_t)a * rope->pos_stride + t];
+    float theta = (float)((float)pos * rope->inv_freq[p]);
+    *c = cos((double)theta);
+    *s = sin((double)theta);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One (token, head) row: norm, contract rounding, rotation, final rounding  */
+/* ------------------------------------------------------------------------ */
+
+/* Rounding contract ([Ovis] kernel review): the normalised value (weight
+ * included) is rounded to bf16 once, the rotation runs on that value and the
+ * result is rounded once more.  For fp32 outputs there is no intermediate
+ * rounding.
+ *
+ * Pairing: NeoX pairs element p with p + R/2 ([IMROPE]: the sectioned mode
+ * keeps mode 2's pairing); the adjacent pairing pairs 2p with 2p+1 ([Ovis]
+ * interleaved=True path).  Rotation by +theta, the standard rotate-half
+ * convention a' = a cos - b sin, b' = b cos + a sin (the pages print no sign).
+ * Elements at or beyond R pass through. */
+static void norm_rope_row(const float* x, const float* w, int32_t d, float eps, int32_t out_kind,
+                          const oracle_rope* rope, int64_t tok, double* n, float* out)
+{
+    norm_row(x, w, d, eps, n);
+    if (out_kind == ORACLE_OUT_BF16)
+        for (int32_t i = 0; i < d; ++i)
+            n[i] = oracle_round_bf16(n[i]);
+
+    int32_t r = (rope != NULL) ? rope->rotary_dim : 0;
+    for (int32_t i = r; i < d; ++i)
+        out[i] = round_out(n[i], out_kind);
+    for (int32_t p = 0; p < r / 2; ++p) {
+        int32_t i, j;
+        if (rope->pairing == ORACLE_PAIR_NEOX) {
+            i = p;
+            j = p + r / 2;
+        } else {
+            i = 2 * p;
+            j = 2 * p + 1;
+        }
+        double c, s;
+        pair_cos_sin(rope, tok, p, &c, &s);
+        out[i] = round_out(n[i] * c - n[j] * s, out_kind);
+        out[j] = round_out(n[j] * c + n[i] * s, out_kind);
+    }
+}
+
+void oracle_qk_norm_rope(const float* x, int64_t tokens, int32_t heads, int32_t head_dim,
+                         const float* weight, float eps, int32_t out_kind,
+                         const oracle_rope* rope, float* out)
+{
+    double* n = (double*)malloc(sizeof(double) * (size_t)head_dim);
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int32_t h = 0; h < heads; ++h) {
+            int64_t row = (t * heads + h) * (int64_t)head_dim;
+            norm_rope_row(x + row, weight, head_dim, eps, out_kind, rope, t, n, out + row);
+        }
+    free(n);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Joint text/image op                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* [Ovis] "Purpose": four RMSNorms, three concatenations and the RoPE pass of
+ * a double block become one op whose outputs are the joint
+ * [B, S_txt + S_img, H, D] Q/K/V, text first.  Each stream keeps its own q and
+ * k norm weights; positions are indexed by the joint token; V is routed
+ * unchanged (the bitwise-candidate comment: routed V matches exactly). */
+void oracle_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim,
+                               const float* q_txt, const float* k_txt, const float* v_txt,
+                               int64_t tokens_txt, const float* qw_txt, const float* kw_txt,
+                               const float* q_img, const float* k_img, const float* v_img,
+                               int64_t tokens_img, const float* qw_img, const float* kw_img,
+                               float eps, int32_t out_kind, const oracle_rope* rope,
+                               float* q_out, float* k_out, float* v_out)
+{
+    int64_t joint = tokens_txt + tokens_img;
+    int64_t row_elems = (int64_t)heads * head_dim;
+    double* n = (double*)malloc(sizeof(double) * (size_t)head_dim);
+    for (int32_t b = 0; b < batch; ++b)
+        for (int64_t tau = 0; tau < joint; ++tau) {
+            const float *q, *k, *v, *qw, *kw;
+            if (tau < tokens_txt) {
+                int64_t src = ((int64_t)b * tokens_txt + tau) * row_elems;
+                q = q_txt + src; k = k_txt + src; v = v_txt + src;
+                qw = qw_txt; kw = kw_txt;
+            } else {
+                int64_t src = ((int64_t)b * tokens_img + (tau - tokens_txt)) * row_elems;
+                q = q_img + src; k = k_img + src; v = v_img + src;
+                qw = qw_img; kw = kw_img;
+            }
+            int64_t dst = ((int64_t)b * joint + tau) * row_elems;
+            for (int32_t h = 0; h < heads; ++h) {
+                int64_t o = (int64_t)h * head_dim;
+                norm_rope_row(q + o, qw, head_dim, eps, out_kind, rope, tau, n, q_out + dst + o);
+                norm_rope_row(k + o, kw, head_dim, eps, out_kind, rope, tau, n, k_out + dst + o);
+            }
+            memcpy(v_out + dst, v, sizeof(float) * (size_t)row_elems);
+        }
+    free(n);
+}
+
+/* ------------------------------------------------------------------------ */
+/* ViT positions and cos/sin planes                                          */
+/* ------------------------------------------------------------------------ */
+
+/* [ViT] setup kernel.  A token's grid is the number of grid ends it has
+ * reached; within its grid, local = token - start, the frame is
+ * local div (h*w), and inside a frame tokens run by spatial-merge block
+ * (block row bh, block column bw, then the m x m cells of the block):
+ *   bh = rem div (m*w), r = rem mod (m*w), bw = r div m^2, r2 = r mod m^2,
+ *   hpos = bh*m + r2 div m, wpos = bw*m + r2 mod m. */
+static void vit_token_position(const int32_t* grid_thw, int32_t num_grids, int32_t m,
+                               int64_t tok, int32_t* tpos, int32_t* hpos, int32_t* wpos)
+{
+    int64_t start = 0, end = 0;
+    int32_t g = 0;
+    for (int32_t k = 0; k < num_grids; ++k) {
+        end += (int64_t)grid_thw[3 * k] * grid_thw[3 * k + 1] * grid_thw[3 * k + 2];
+        if (tok >= end) {
+            g = k + 1;
+            start = end;
+        }
+    }
+    int64_t h = grid_thw[3 * g + 1], w = grid_thw[3 * g + 2];
+    int64_t local = tok - start;
+    int64_t rem = local % (h * w);
+    int64_t bh = rem / (m * w);
+    int64_t r = rem % (m * w);
+    int64_t bw = r / ((int64_t)m * m);
+    int64_t r2 = r % ((int64_t)m * m);
+    *tpos = (int32_t)(local / (h * w));
+    *hpos = (int32_t)(bh * m + r2 / m);
+    *wpos = (int32_t)(bw * m + r2 % m);
+}
+
+void oracle_vit_positions(const int32_t* grid_thw, int32_t num_grids, int32_t merge,
+                          int32_t* pos, int64_t n_tokens)
+{
+    for (int64_t n = 0; n < n_tokens; ++n)
+        vit_token_position(grid_thw, num_grids, merge, n, &pos[n], &pos[n_tokens + n],
+                           &pos[2 * n_tokens + n]);
+}
+
+/* Plane a, columns [off_a, off_a + half_a): cos and sin of
+ * fl32(fl32(pos_a) * inv_a[j]), each rounded once to fp32.  Other columns of
+ * plane a are not written ([ViT]: left uninitialized). */
+void oracle_vit_cos_sin(const float* inv_t, int32_t half_t, const float* inv_h, int32_t half_h,
+                        const float* inv_w, int32_t half_w, const int32_t* grid_thw,
+                        int32_t num_grids, int32_t merge, float* cos_out, float* sin_out,
+                        int64_t n_tokens)
+{
+    int64_t half_rot = (int64_t)half_t + half_h + half_w;
+    const float* inv[3] = {inv_t, inv_h, inv_w};
+    int32_t len[3] = {half_t, half_h, half_w};
+    int32_t off[3] = {0, half_t, half_t + half_h};
+    for (int64_t n = 0; n < n_tokens; ++n) {
+        int32_t pos[3];
+        vit_token_position(grid_thw, num_grids, merge, n, &pos[0], &pos[1], &pos[2]);
+        for (int32_t a = 0; a < 3; ++a)
+            for (int32_t j = 0; j < len[a]; ++j) {
+                float theta = (float)((float)pos[a] * inv[a][j]);
+                int64_t idx = ((int64_t)a * n_tokens + n) * half_rot + off[a] + j;
+                cos_out[idx] = (float)cos((double)theta);
+                sin_out[idx] = (float)sin((double)theta);
+            }
+    }
+}

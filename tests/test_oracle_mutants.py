@@ -1,0 +1,80 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each case below plants one mistake in a copy of oracle/oracle.c (a dropped
+term, a flipped sign, a swapped index, a missed offset, a wrong rounding),
+builds it into a scratch library and runs tests/test_oracle_pins.py against
+it.  The pins pass on the real oracle (that file's own run) and must fail on
+every mutant here.
+"""
+import concurrent.futures
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "sum_instead_of_mean": ("ss / (double)d + (double)eps", "ss + (double)eps"),
+    "eps_outside_sqrt": ("sqrt(ss / (double)d + (double)eps)", "(sqrt(ss / (double)d) + (double)eps)"),
+    "weight_dropped": ("rrms * (double)w[i]", "rrms"),
+    "rotation_sign_first": ("n[i] * c - n[j] * s", "n[i] * c + n[j] * s"),
+    "rotation_sign_second": ("n[j] * c + n[i] * s", "n[j] * c - n[i] * s"),
+    "neox_partner_swapped": ("i = p;\n            j = p + r / 2;", "i = p + r / 2;\n            j = p;"),
+    "adjacent_partner_swapped": ("i = 2 * p;\n            j = 2 * p + 1;", "i = 2 * p + 1;\n            j = 2 * p;"),
+    "token_base_ignored": ("int64_t t = rope->token_base + tok;", "int64_t t = tok;"),
+    "plane_stride_ignored": ("(int64_t)a * rope->pos_stride + t", "(int64_t)a + t"),
+    "angle_not_rounded_to_fp32": ("float theta = (float)((float)pos * rope->inv_freq[p]);",
+                                  "double theta = (double)pos * rope->inv_freq[p];"),
+    "imrope_h_limit_from_w": ("sector < 3 * s[1]", "sector < 3 * s[2]"),
+    "imrope_h_w_residues_swapped": ("sector % 3 == 1 && sector < 3 * s[1]", "sector % 3 == 2 && sector < 3 * s[1]"),
+    "imrope_t_limit_off": ("sector < 3 * s[0]", "sector < 3 * s[0] - 3"),
+    "axes_sections_shifted": ("if (p < end)", "if (p <= end)"),
+    "no_contract_rounding": ("n[i] = oracle_round_bf16(n[i]);", "n[i] = n[i];"),
+    "ties_away_from_zero": ("nearbyint(ldexp(v, -q))", "round(ldexp(v, -q))"),
+    "truncating_bf16": ("nearbyint(ldexp(v, -q))", "trunc(ldexp(v, -q))"),
+    "joint_weights_swapped": ("qw = qw_img; kw = kw_img;", "qw = qw_txt; kw = kw_txt;"),
+    "joint_local_token_positions": ("rope, tau, n, q_out", "rope, tau % (tau < tokens_txt ? tokens_txt : tokens_img), n, q_out"),
+    "joint_v_from_text_only": ("memcpy(v_out + dst, v,", "memcpy(v_out + dst, v_txt,"),
+    "vit_block_column_divisor": ("int64_t bw = r / ((int64_t)m * m);", "int64_t bw = r / m;"),
+    "vit_h_w_swapped": ("*hpos = (int32_t)(bh * m + r2 / m);\n    *wpos = (int32_t)(bw * m + r2 % m);",
+                        "*wpos = (int32_t)(bh * m + r2 / m);\n    *hpos = (int32_t)(bw * m + r2 % m);"),
+    "vit_frame_not_divided": ("*tpos = (int32_t)(local / (h * w));", "*tpos = (int32_t)(local / w);"),
+    "vit_plane_column_offset": ("idx = ((int64_t)a * n_tokens + n) * half_rot + off[a] + j;",
+                                "idx = ((int64_t)a * n_tokens + n) * half_rot + j;"),
+    "planes_read_wrong_plane": ("int64_t idx = ((int64_t)a * rope->planes_tokens + t) * half + p;",
+                                "int64_t idx = ((int64_t)0 * rope->planes_tokens + t) * half + p;"),
+    "passthrough_skipped": ("for (int32_t i = r; i < d; ++i)\n        out[i] = round_out(n[i], out_kind);",
+                            "for (int32_t i = r; i < d; ++i)\n        out[i] = 0.0f;"),
+}
+
+
+def _run_mutant(name, old, new, tmp):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutant {name}: pattern not found in oracle.c"
+    mutated = src.replace(old, new, 1)
+    c_path = os.path.join(tmp, f"{name}.c")
+    so_path = os.path.join(tmp, f"{name}.so")
+    with open(c_path, "w") as f:
+        f.write(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-I", os.path.join(ROOT, "oracle"), "-o", so_path, c_path, "-lm"],
+                   check=True)
+    env = dict(os.environ, ORACLE_LIB=so_path)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    return r.returncode
+
+
+def test_every_planted_mistake_fails_a_pin():
+    with tempfile.TemporaryDirectory() as tmp:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=6) as ex:
+            futs = {name: ex.submit(_run_mutant, name, old, new, tmp)
+                    for name, (old, new) in MUTANTS.items()}
+            codes = {name: f.result() for name, f in futs.items()}
+    survivors = [name for name, rc in codes.items() if rc == 0]
+    assert not survivors, f"mutants not caught by any pin: {survivors}"

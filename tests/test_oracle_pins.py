@@ -1,0 +1,460 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Every expected value here is fixed by something independent of the oracle's
+code: a closed form, an invariant of the mathematics, a library routine on a
+special case, or a fixture under tests/golden/ written out by hand from the
+pages.  Each test is chosen so that a plausible slip in the oracle (a dropped
+term, a wrong sign or index, a transposed operand, a missed offset) fails it.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import inv_freq_ladder
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(k):
+    return np.random.default_rng([7, k])
+
+
+# ----------------------------------------------------------------------------
+# bf16 rounding
+# ----------------------------------------------------------------------------
+
+def test_round_bf16_matches_torch_on_float32_values():
+    """torch's float32 -> bfloat16 cast rounds to nearest even.  For inputs that
+    are exactly float32, rounding the real value once to bf16 is the same
+    operation, so the two must agree bit for bit, ties included."""
+    rng = _rng(1)
+    normal = rng.normal(0.0, 1.0, 4000)
+    wide = rng.normal(0.0, 1.0, 2000) * np.exp2(rng.integers(-140, 126, 2000))
+    # exact ties: a bf16 value plus half its spacing
+    b = torch.from_numpy(rng.normal(0, 1, 2000).astype(np.float32)).to(torch.bfloat16)
+    b = b.float().numpy().astype(np.float64)
+    _, e = np.frexp(b)
+    ties = b + np.ldexp(0.5, e - 8)
+    edge = np.array([3.0e38, -3.3e38, np.float32(3.4028235e38), 1e-40, -1e-44, 0.0, -0.0])
+    x = np.concatenate([normal, wide, ties, edge]).astype(np.float32)
+    expect = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, expect, equal_nan=True)
+    assert np.array_equal(np.signbit(got), np.signbit(expect))
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("c", [0.5, -3.0, 1e-3, 7.25])
+def test_rms_norm_constant_row_closed_form(c):
+    """x_i = c for every i: mean(x^2) = c^2, so y_i = c / sqrt(c^2 + eps) * w_i."""
+    width = 96
+    eps = np.float32(1e-2)
+    w = _rng(2).normal(1.0, 0.1, width).astype(np.float32)
+    y = oracle.rms_norm(np.full((1, width), c, np.float32), w, float(eps), "f32")
+    expect = c / np.sqrt(c * c + np.float64(eps)) * w.astype(np.float64)
+    np.testing.assert_allclose(y[0], expect, rtol=1.5e-7, atol=0)
+
+
+@pytest.mark.parametrize("width", [1, 7, 64, 5120])
+def test_rms_norm_output_has_unit_rms_without_eps(width):
+    """With eps = 0 the weight-divided output has root mean square exactly 1,
+    whatever the row."""
+    rng = _rng(3)
+    x = rng.normal(0.0, 2.0, (5, width)).astype(np.float32)
+    w = rng.normal(1.0, 0.1, width).astype(np.float32)
+    y = oracle.rms_norm(x, w, 0.0, "f32")
+    r = np.sqrt(np.mean((y.astype(np.float64) / w) ** 2, axis=1))
+    np.testing.assert_allclose(r, 1.0, rtol=3e-7)
+
+
+def test_rms_norm_scale_invariant_without_eps():
+    """Scaling a row by a power of two changes no output bit when eps = 0."""
+    rng = _rng(4)
+    x = rng.normal(0.0, 1.0, (3, 256)).astype(np.float32)
+    w = rng.normal(1.0, 0.1, 256).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        a = oracle.rms_norm(x, w, 0.0, dt)
+        b = oracle.rms_norm(x * np.float32(8.0), w, 0.0, dt)
+        assert np.array_equal(a, b)
+
+
+def test_rms_norm_bf16_output_is_on_bf16_grid_and_close():
+    rng = _rng(5)
+    x = rng.normal(0.0, 1.0, (4, 5120)).astype(np.float32)
+    w = rng.normal(1.0, 0.1, 5120).astype(np.float32)
+    y32 = oracle.rms_norm(x, w, 1e-6, "f32")
+    y16 = oracle.rms_norm(x, w, 1e-6, "bf16")
+    grid = torch.from_numpy(y16).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(grid, y16)
+    assert np.max(np.abs(y16 - y32) / np.abs(y32)) <= 2.0 ** -8
+
+
+# ----------------------------------------------------------------------------
+# Rotation
+# ----------------------------------------------------------------------------
+
+def _rope_1d(positions, inv_freq, rotary_dim, pairing="neox", token_base=0):
+    return oracle.Rope("1d", rotary_dim, pairing, inv_freq=inv_freq,
+                       positions=np.asarray(positions, np.int32).reshape(1, -1),
+                       token_base=token_base)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("pairing", ["neox", "adjacent"])
+def test_position_zero_is_identity(out, pairing):
+    """At position 0 every angle is 0 (cos 1, sin 0): the output is the
+    norm-only output, bit for bit."""
+    rng = _rng(6)
+    x = rng.normal(0, 1, (3, 4, 64)).astype(np.float32)
+    w = rng.normal(1, 0.1, 64).astype(np.float32)
+    rope = _rope_1d(np.zeros(3), inv_freq_ladder(1e4, 64), 64, pairing)
+    assert np.array_equal(oracle.qk_norm_rope(x, w, 1e-6, rope, out),
+                          oracle.qk_norm_rope(x, w, 1e-6, None, out))
+
+
+@pytest.mark.parametrize("pairing", ["neox", "adjacent"])
+@pytest.mark.parametrize("rotary_dim", [64, 32])
+def test_rotation_is_complex_multiplication(pairing, rotary_dim):
+    """Rotating pair (a, b) by theta is multiplying a + ib by exp(i theta)
+    (numpy's complex exponential).  NeoX pairs element p with p + R/2, the
+    adjacent pairing 2p with 2p + 1; theta = fl32(fl32(pos) * inv_freq[p]);
+    elements at or past R pass through."""
+    rng = _rng(7)
+    tokens, heads, d = 5, 3, 64
+    x = rng.normal(0, 1, (tokens, heads, d)).astype(np.float32)
+    w = rng.normal(1, 0.1, d).astype(np.float32)
+    pos = rng.integers(0, 9000, tokens).astype(np.int32)
+    inv = inv_freq_ladder(1e4, rotary_dim)
+    out = oracle.qk_norm_rope(x, w, 1e-6, _rope_1d(pos, inv, rotary_dim, pairing), "f32")
+    n = oracle.qk_norm_rope(x, w, 1e-6, None, "f32").astype(np.float64)
+    theta = (pos.astype(np.float32)[:, None] * inv[None, :]).astype(np.float32)
+    rot = np.exp(1j * theta.astype(np.float64))[:, None, :]
+    half = rotary_dim // 2
+    if pairing == "neox":
+        i, j = np.arange(half), np.arange(half) + half
+    else:
+        i, j = 2 * np.arange(half), 2 * np.arange(half) + 1
+    z = (n[..., i] + 1j * n[..., j]) * rot
+    np.testing.assert_allclose(out[..., i], z.real, atol=2e-6, rtol=0)
+    np.testing.assert_allclose(out[..., j], z.imag, atol=2e-6, rtol=0)
+    np.testing.assert_allclose(out[..., rotary_dim:], n[..., rotary_dim:], atol=0, rtol=1e-7)
+
+
+def test_relative_position_property():
+    """<R(m) q, R(n) k> = <R(m - n) q, k>: the score depends only on the
+    position difference.  inv_freq and positions are chosen so that every fp32
+    angle product is exact."""
+    rng = _rng(8)
+    d = 64
+    p = np.arange(d // 2)
+    inv = ((1.0 + (p % 16) / 16.0) * np.exp2(-(p // 16))).astype(np.float32)
+    q = rng.normal(0, 1, (1, 1, d)).astype(np.float32)
+    k = rng.normal(0, 1, (1, 1, d)).astype(np.float32)
+    w = rng.normal(1, 0.1, d).astype(np.float32)
+    for pairing in ("neox", "adjacent"):
+        def rot(x, pos):
+            return oracle.qk_norm_rope(x, w, 1e-6, _rope_1d([pos], inv, d, pairing), "f32")[0, 0]
+        for m, n in [(5, 3), (300, 17), (2, 40), (511, 0)]:
+            a = np.dot(rot(q, m).astype(np.float64), rot(k, n))
+            b = np.dot(rot(q, m - n).astype(np.float64), rot(k, 0))
+            assert abs(a - b) <= 1e-5 * (1 + abs(a))
+
+
+# ----------------------------------------------------------------------------
+# Position axis maps
+# ----------------------------------------------------------------------------
+
+def _golden_imrope_cases():
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, "imrope_axes.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        tok = line.split()
+        if tok[0] == "case":
+            cur = {"sections": tuple(int(v) for v in tok[1:5]), "pairs": int(tok[6]), "axes": {}}
+            cases.append(cur)
+            continue
+        idx = []
+        for item in tok[1:]:
+            if ":" in item:
+                a, b, s = (int(v) for v in item.split(":"))
+                idx += list(range(a, b, s))
+            else:
+                idx.append(int(item))
+        cur["axes"]["thwe".index(tok[0])] = idx
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_imrope_cases(), ids=lambda c: str(c["sections"]))
+def test_imrope_axis_map_matches_hand_derived_table(case):
+    expect = np.full(case["pairs"], -1)
+    for axis, pairs in case["axes"].items():
+        expect[pairs] = axis
+    assert (expect >= 0).all(), "fixture must cover every pair"
+    rope = oracle.Rope("imrope", 2 * case["pairs"], sections=case["sections"])
+    assert np.array_equal(oracle.axis_map(rope, case["pairs"]), expect)
+
+
+def test_imrope_counts_for_24_20_20():
+    rope = oracle.Rope("imrope", 128, sections=(24, 20, 20, 0))
+    ax = oracle.axis_map(rope, 64)
+    assert np.bincount(ax, minlength=4).tolist() == [22, 20, 20, 2]
+    assert np.nonzero(ax == 3)[0].tolist() == [61, 62]
+
+
+def test_axes_map_is_contiguous_runs():
+    rope = oracle.Rope("axes", 128, sections=(8, 28, 28, 0))
+    assert np.array_equal(oracle.axis_map(rope, 64), np.repeat([0, 1, 2], [8, 28, 28]))
+
+
+def _imrope_setup(seed, tokens=37, heads=3, d=128):
+    rng = _rng(seed)
+    x = rng.normal(0, 1, (tokens, heads, d)).astype(np.float32)
+    w = rng.normal(1, 0.1, d).astype(np.float32)
+    pos = rng.integers(0, 8192, (4, tokens)).astype(np.int32)
+    return x, w, pos, inv_freq_ladder(1e6, d)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_imrope_collapses_to_plain_rope(out):
+    """All pairs on e ([0, 0, 0, R/2]) is plain RoPE over plane e; any sections
+    with four equal planes is plain RoPE over that plane."""
+    x, w, pos, inv = _imrope_setup(9)
+    all_e = oracle.Rope("imrope", 128, inv_freq=inv, sections=(0, 0, 0, 64), positions=pos)
+    assert np.array_equal(oracle.qk_norm_rope(x, w, 1e-6, all_e, out),
+                          oracle.qk_norm_rope(x, w, 1e-6, _rope_1d(pos[3], inv, 128), out))
+    same = np.repeat(pos[1:2], 4, axis=0)
+    sect = oracle.Rope("imrope", 128, inv_freq=inv, sections=(24, 20, 20, 0), positions=same)
+    assert np.array_equal(oracle.qk_norm_rope(x, w, 1e-6, sect, out),
+                          oracle.qk_norm_rope(x, w, 1e-6, _rope_1d(pos[1], inv, 128), out))
+
+
+def test_imrope_non_collapsing_differs_from_plain_rope():
+    """Sections that leave pairs on several axes, with independent planes, must
+    not reproduce plain RoPE over any single plane."""
+    x, w, pos, inv = _imrope_setup(10)
+    sect = oracle.Rope("imrope", 128, inv_freq=inv, sections=(24, 20, 20, 0), positions=pos)
+    got = oracle.qk_norm_rope(x, w, 1e-6, sect, "f32")
+    for plane in range(4):
+        plain = oracle.qk_norm_rope(x, w, 1e-6, _rope_1d(pos[plane], inv, 128), "f32")
+        assert np.max(np.abs(got - plain)) > 0.1
+
+
+def test_imrope_pair_reads_its_own_plane():
+    """Change only plane h at one token: exactly the pairs the fixture puts on
+    h change, at that token only."""
+    x, w, pos, inv = _imrope_setup(11)
+    rope = oracle.Rope("imrope", 128, inv_freq=inv, sections=(24, 20, 20, 0), positions=pos)
+    base = oracle.qk_norm_rope(x, w, 1e-6, rope, "f32")
+    pos2 = pos.copy()
+    pos2[1, 5] += 1
+    rope2 = oracle.Rope("imrope", 128, inv_freq=inv, sections=(24, 20, 20, 0), positions=pos2)
+    diff = oracle.qk_norm_rope(x, w, 1e-6, rope2, "f32") != base
+    tok, _, elem = np.nonzero(diff)
+    assert set(tok.tolist()) == {5}
+    pairs = sorted(set((elem % 64).tolist()))
+    assert pairs == list(range(1, 60, 3))
+
+
+def test_chunked_launch_equals_one_launch():
+    """A call over tokens [b, b + L) with token_base b, reading the whole-length
+    planes, reproduces those rows of the single call; reading the planes as if
+    they started at the chunk (the bug class the IMROPE page reports) does
+    not."""
+    x, w, pos, inv = _imrope_setup(12, tokens=64)
+    full = oracle.qk_norm_rope(
+        x, w, 1e-6, oracle.Rope("imrope", 128, inv_freq=inv, sections=(24, 20, 20, 0),
+                                positions=pos), "bf16")
+    for b in (0, 16, 32, 48):
+        rope = oracle.Rope("imrope", 128, inv_freq=inv, sections=(24, 20, 20, 0),
+                           positions=pos, token_base=b)
+        assert np.array_equal(oracle.qk_norm_rope(x[b:b + 16], w, 1e-6, rope, "bf16"),
+                              full[b:b + 16])
+    wrong = oracle.Rope("imrope", 128, inv_freq=inv, sections=(24, 20, 20, 0), positions=pos)
+    assert not np.array_equal(oracle.qk_norm_rope(x[16:32], w, 1e-6, wrong, "bf16"), full[16:32])
+
+
+# ----------------------------------------------------------------------------
+# Joint text/image op
+# ----------------------------------------------------------------------------
+
+def _joint_inputs(seed, batch=2, st=5, si=12, heads=3, d=64, grid=(3, 4)):
+    rng = _rng(seed)
+
+    def stream(n):
+        return {"q": rng.normal(0, 1, (batch, n, heads, d)).astype(np.float32),
+                "k": rng.normal(0, 1, (batch, n, heads, d)).astype(np.float32),
+                "v": rng.normal(0, 1, (batch, n, heads, d)).astype(np.float32),
+                "q_weight": rng.normal(1, 0.1, d).astype(np.float32),
+                "k_weight": rng.normal(1, 0.1, d).astype(np.float32)}
+
+    txt, img = stream(st), stream(si)
+    pos = np.zeros((3, st + si), np.int32)
+    k = np.arange(si)
+    pos[1, st:] = k // grid[1]
+    pos[2, st:] = k % grid[1]
+    inv = np.concatenate([inv_freq_ladder(1e4, 8), inv_freq_ladder(1e4, 28), inv_freq_ladder(1e4, 28)])
+    rope = oracle.Rope("axes", d, "adjacent", inv_freq=inv, sections=(4, 14, 14, 0), positions=pos)
+    return txt, img, rope, pos, inv
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_joint_is_text_first_concat_of_streams(out):
+    txt, img, rope, pos, inv = _joint_inputs(13)
+    st = txt["q"].shape[1]
+    q, k, v = oracle.joint_qk_norm_rope(txt, img, 1e-6, rope, out)
+    # V is routed unchanged, text first.
+    assert np.array_equal(v, np.concatenate([txt["v"], img["v"]], axis=1))
+    for b in range(q.shape[0]):
+        # text rows sit at position (0, 0, 0): norm-only with the text weights
+        assert np.array_equal(q[b, :st], oracle.qk_norm_rope(txt["q"][b], txt["q_weight"], 1e-6, None, out))
+        assert np.array_equal(k[b, :st], oracle.qk_norm_rope(txt["k"][b], txt["k_weight"], 1e-6, None, out))
+        # image rows: the image stream with its own weights at joint positions
+        r = oracle.Rope("axes", rope.rotary_dim, "adjacent", inv_freq=inv, sections=(4, 14, 14, 0),
+                        positions=pos, token_base=st)
+        assert np.array_equal(q[b, st:], oracle.qk_norm_rope(img["q"][b], img["q_weight"], 1e-6, r, out))
+        assert np.array_equal(k[b, st:], oracle.qk_norm_rope(img["k"][b], img["k_weight"], 1e-6, r, out))
+
+
+def test_joint_t_axis_pairs_of_image_rows_are_unrotated():
+    """Image positions are (0, row, col): the t-axis pairs see angle 0 and keep
+    their normalised values."""
+    txt, img, rope, pos, inv = _joint_inputs(14, batch=1)
+    st = txt["q"].shape[1]
+    q, _, _ = oracle.joint_qk_norm_rope(txt, img, 1e-6, rope, "f32")
+    n = oracle.qk_norm_rope(img["q"][0], img["q_weight"], 1e-6, None, "f32")
+    t_elems = np.arange(8)            # adjacent pairs 0..3 -> elements 0..7
+    assert np.array_equal(q[0, st:][..., t_elems], n[..., t_elems])
+    assert not np.array_equal(q[0, st:][..., 8:], n[..., 8:])
+
+
+# ----------------------------------------------------------------------------
+# ViT positions and planes
+# ----------------------------------------------------------------------------
+
+def test_vit_positions_match_hand_derived_fixture():
+    rows = np.loadtxt(os.path.join(GOLDEN, "vit_positions.txt"), dtype=np.int64)
+    pos = oracle.vit_positions([[1, 4, 6], [2, 2, 4]], 2)
+    assert pos.shape == (3, rows.shape[0])
+    assert np.array_equal(pos.T, rows[:, 1:])
+
+
+def test_vit_positions_merge_one_is_raster_order():
+    grids = [[2, 3, 5], [1, 4, 4]]
+    pos = oracle.vit_positions(grids, 1)
+    expect = []
+    for t, h, w in grids:
+        n = np.arange(t * h * w)
+        expect.append(np.stack([n // (h * w), (n % (h * w)) // w, n % w]))
+    assert np.array_equal(pos, np.concatenate(expect, axis=1))
+
+
+def _merge_permuted_ids(t, h, w, m):
+    """The ViT position-id permute written as array reshapes: lay (row, col) ids
+    on the h x w grid, cut it into m x m blocks, order blocks row-major and the
+    cells inside each block row-major."""
+    hh = np.broadcast_to(np.arange(h)[:, None], (h, w))
+    ww = np.broadcast_to(np.arange(w)[None, :], (h, w))
+
+    def permute(a):
+        return a.reshape(h // m, m, w // m, m).transpose(0, 2, 1, 3).reshape(-1)
+
+    frame = np.stack([permute(hh), permute(ww)])
+    tt = np.repeat(np.arange(t), h * w)
+    return np.concatenate([tt[None], np.tile(frame, (1, t))])
+
+
+def test_vit_positions_match_block_permute_on_workload_grids():
+    grids = [[1, 64, 64], [2, 32, 48], [1, 28, 28]]
+    pos = oracle.vit_positions(grids, 2)
+    expect = np.concatenate([_merge_permuted_ids(t, h, w, 2) for t, h, w in grids], axis=1)
+    assert np.array_equal(pos, expect)
+
+
+def test_vit_positions_are_a_bijection_per_frame():
+    grids = [[3, 6, 4], [1, 8, 10]]
+    pos = oracle.vit_positions(grids, 2)
+    start = 0
+    for t, h, w in grids:
+        for f in range(t):
+            sl = slice(start + f * h * w, start + (f + 1) * h * w)
+            assert (pos[0, sl] == f).all()
+            cells = set(zip(pos[1, sl].tolist(), pos[2, sl].tolist()))
+            assert cells == {(i, j) for i in range(h) for j in range(w)}
+        start += t * h * w
+
+
+def test_vit_planes_invariants():
+    grids = [[1, 8, 8], [2, 4, 6]]
+    inv_t, inv_h, inv_w = inv_freq_ladder(1e4, 16), inv_freq_ladder(1e4, 32), inv_freq_ladder(1e4, 32)
+    cos, sin = oracle.vit_cos_sin(inv_t, inv_h, inv_w, grids, 2)
+    own = [slice(0, 8), slice(8, 24), slice(24, 40)]
+    for a in range(3):
+        c, s = cos[a][:, own[a]].astype(np.float64), sin[a][:, own[a]].astype(np.float64)
+        np.testing.assert_allclose(c * c + s * s, 1.0, atol=3e-7)
+        rest = np.ones(40, bool)
+        rest[own[a]] = False
+        assert np.isnan(cos[a][:, rest]).all() and np.isnan(sin[a][:, rest]).all()
+    # frame 0 of grid 0 has t = 0: its t columns are exactly (1, 0)
+    assert (cos[0, :64, :8] == 1.0).all() and (sin[0, :64, :8] == 0.0).all()
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_vit_planes_apply_equals_axes_rope_from_positions(out):
+    """Rotating with the setup's planes is rotating with the ViT positions in
+    AXES mode over the concatenated per-axis inv_freq: the two routes differ
+    only by the planes' fp32 rounding of cos and sin."""
+    grids = [[1, 8, 8], [2, 4, 6]]
+    inv = [inv_freq_ladder(1e4, 16), inv_freq_ladder(1e4, 32), inv_freq_ladder(1e4, 32)]
+    cos, sin = oracle.vit_cos_sin(*inv, grids, 2)
+    pos = oracle.vit_positions(grids, 2)
+    rng = _rng(15)
+    n = pos.shape[1]
+    x = rng.normal(0, 1, (n, 4, 80)).astype(np.float32)
+    w = rng.normal(1, 0.1, 80).astype(np.float32)
+    planes = oracle.Rope("planes", 80, sections=(8, 16, 16, 0), cos_planes=cos, sin_planes=sin)
+    axes = oracle.Rope("axes", 80, inv_freq=np.concatenate(inv), sections=(8, 16, 16, 0),
+                       positions=pos)
+    a = oracle.qk_norm_rope(x, w, 1e-6, planes, out)
+    b = oracle.qk_norm_rope(x, w, 1e-6, axes, out)
+    if out == "f32":
+        np.testing.assert_allclose(a, b, atol=1e-6, rtol=0)
+    else:
+        # at most one bf16 step apart, measured against the pair's magnitude
+        assert np.max(np.abs(a - b)) <= 2.0 ** -7 * np.max(np.abs(b))
+        assert np.mean(a == b) > 0.99
+
+
+@pytest.mark.parametrize("pairing", ["neox", "adjacent"])
+def test_bf16_contract_rounds_normalised_value_then_result(pairing):
+    """bf16 contract: the rotation acts on the bf16-rounded normalised value
+    and its result is rounded once.  Rebuild that from the norm-only bf16
+    output with numpy's complex exponential and round with torch's cast; the
+    double-precision results agree except on exact ties."""
+    rng = _rng(16)
+    tokens, heads, d = 9, 4, 128
+    x = rng.normal(0, 1, (tokens, heads, d)).astype(np.float32)
+    w = rng.normal(1, 0.1, d).astype(np.float32)
+    pos = rng.integers(0, 8192, tokens).astype(np.int32)
+    inv = inv_freq_ladder(1e4, d)
+    got = oracle.qk_norm_rope(x, w, 1e-6, _rope_1d(pos, inv, d, pairing), "bf16")
+    n = oracle.qk_norm_rope(x, w, 1e-6, None, "bf16").astype(np.float64)
+    theta = (pos.astype(np.float32)[:, None] * inv[None, :]).astype(np.float32)
+    rot = np.exp(1j * theta.astype(np.float64))[:, None, :]
+    half = d // 2
+    i, j = ((np.arange(half), np.arange(half) + half) if pairing == "neox"
+            else (2 * np.arange(half), 2 * np.arange(half) + 1))
+    z = (n[..., i] + 1j * n[..., j]) * rot
+    expect = np.empty_like(n)
+    expect[..., i], expect[..., j] = z.real, z.imag
+    # float64 -> float32 -> bf16 could double-round; only ties of the float32
+    # step matter and they are vanishingly rare for these values.
+    expect = torch.from_numpy(expect.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.mean(got != expect) < 1e-3
