@@ -1,0 +1,401 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused QK RMSNorm + RoPE hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload joint|imrope|vit|rows1|rows32|rows4096|tiny]
+
+Prints one JSON line.  A step is one pass of the workload's hot path over one
+batch of synthetic input already resident in HBM (default workload: the joint
+text/image QK RMSNorm + concatenation + 3-axis RoPE, 512 text + 4096 image
+tokens, 24 heads x 128, bf16; one launch per step).  Consecutive steps rotate
+over several input/output buffer sets whose total exceeds the 256 MB
+last-level (Infinity) cache, so every step streams from HBM.
+
+value   = algorithmic bytes per step / time per step (GB/s), whole job.
+roofline.achieved = algorithmic bytes per launch of the dominant kernel /
+          its average launch duration, measured with HIP events recorded on
+          the stream the kernel runs on, around every launch of the timed
+          region.
+cpu_baseline: the CPU oracle on a bounded sample of the same workload, on
+          the host cores (single-threaded C).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20         # MI355X Infinity Cache
+METRIC = "fused QK-norm+RoPE µs/call and achieved HBM GB/s (% of peak), 1 MI355X"
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="joint",
+                    choices=["joint", "joint-neox", "imrope", "vit", "rows1", "rows32", "rows4096", "tiny"])
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
+    ap.add_argument("--variant", default=None, help="force a kernel variant (qkr_set_variant_override)")
+    return ap.parse_args()
+
+
+class Workload:
+    """name, description, bytes per step, dominant-kernel bytes per launch,
+    launches of it per step, make_set() -> state, step(state) launches the
+    path, cpu_step() runs the oracle on one step's input."""
+
+
+def build_joint(pairing):
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.joint()
+    H, D = case.heads, case.head_dim
+    st, si = case.text.qkv.shape[1], case.image.qkv.shape[1]
+    joint = st + si
+    dev = torch.device("cuda")
+    pos = torch.from_numpy(case.positions).to(dev)
+    inv = torch.from_numpy(case.inv_freq).to(dev)
+    rope = qkr.Rope("axes", D, pairing, inv_freq=inv, positions=pos, sections=case.sections)
+
+    def make_set():
+        g = {}
+        for nm, s in (("text", case.text), ("image", case.image)):
+            qkv = s.qkv.to(dev)
+            v = qkv.view(qkv.shape[0], qkv.shape[1], 3, H, D)
+            g[nm] = {"q": v[:, :, 0], "k": v[:, :, 1], "v": v[:, :, 2], "q_weight": s.q_weight.to(dev),
+                     "k_weight": s.k_weight.to(dev), "_qkv": qkv}
+        outs = [torch.empty((1, joint, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        return g, outs
+
+    def step(state):
+        g, outs = state
+        qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope, out=outs)
+
+    qkv_bytes = joint * 3 * H * D * 2
+    nbytes = 2 * qkv_bytes + case.positions.nbytes + 4 * D * 2 + case.inv_freq.nbytes
+
+    def cpu_step():
+        import oracle
+
+        def stream(s):
+            return {"q": W.as_f32(s.view(0, H, D)), "k": W.as_f32(s.view(1, H, D)), "v": W.as_f32(s.view(2, H, D)),
+                    "q_weight": W.as_f32(s.q_weight), "k_weight": W.as_f32(s.k_weight)}
+
+        tx, im = stream(case.text), stream(case.image)
+        orope = oracle.Rope("axes", D, pairing, inv_freq=case.inv_freq, sections=case.sections,
+                            positions=case.positions)
+
+        def run():
+            oracle.joint_qk_norm_rope(tx, im, case.eps, orope, "bf16")
+        return run
+
+    w = Workload()
+    w.name = f"joint text/image QK RMSNorm + cat + 3-axis RoPE ({pairing})"
+    w.config = {"workload": w.name, "text_tokens": st, "image_tokens": si, "heads": H, "head_dim": D,
+                "axes_pairs": list(case.sections[:3]), "theta": 1e4, "eps": case.eps, "batch": 1}
+    w.step_bytes = nbytes
+    w.launch_bytes = nbytes
+    w.launches = 1
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "bf16"
+    w.sample = "the full joint step (512 text + 4096 image tokens, Q/K/V)"
+    return w
+
+
+def build_imrope():
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.imrope()
+    dev = torch.device("cuda")
+    T, chunk = case.q.shape[0], case.chunk
+    pos = torch.from_numpy(case.positions).to(dev)
+    inv = torch.from_numpy(case.inv_freq).to(dev)
+    ropes = [qkr.Rope("imrope", 128, "neox", inv_freq=inv, positions=pos, sections=case.sections, token_base=b)
+             for b in range(0, T, chunk)]
+    qw, kw = case.q_weight.to(dev), case.k_weight.to(dev)
+
+    def make_set():
+        q, k = case.q.to(dev), case.k.to(dev)
+        return q, k, torch.empty_like(q), torch.empty_like(k)
+
+    def step(state):
+        q, k, qo, ko = state
+        for r in ropes:
+            b = r.token_base
+            qkr.qk_norm_rope(q[b:b + chunk], k[b:b + chunk], qw, kw, case.eps, r, q_out=qo[b:b + chunk],
+                             k_out=ko[b:b + chunk])
+
+    rows = case.q.shape[1] + case.k.shape[1]
+    chunk_bytes = 2 * chunk * rows * 128 * 2 + 4 * chunk * 4 + 2 * 128 * 2 + case.inv_freq.nbytes
+
+    def cpu_step():
+        import oracle
+        qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
+        orope = oracle.Rope("imrope", 128, "neox", inv_freq=case.inv_freq, sections=case.sections,
+                            positions=case.positions)
+
+        def run():
+            oracle.qk_norm_rope(qf, wq, case.eps, orope)
+            oracle.qk_norm_rope(kf, wk, case.eps, orope)
+        return run
+
+    w = Workload()
+    w.name = "IMROPE after per-head QK RMSNorm, 2048-token chunks"
+    w.config = {"workload": w.name, "tokens": T, "chunk": chunk, "q_heads": case.q.shape[1],
+                "k_heads": case.k.shape[1], "head_dim": 128, "sections": list(case.sections), "theta": 1e6}
+    w.step_bytes = chunk_bytes * (T // chunk)
+    w.launch_bytes = chunk_bytes
+    w.launches = T // chunk
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "bf16"
+    w.sample = "all 8192 tokens (4 chunks), Q and K"
+    return w
+
+
+def build_vit():
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.vit()
+    dev = torch.device("cuda")
+    n, half = case.n_tokens, case.half_rot
+    inv = [torch.from_numpy(a).to(dev) for a in (case.inv_t, case.inv_h, case.inv_w)]
+    secs = (case.inv_t.size, case.inv_h.size, case.inv_w.size, 0)
+    qw, kw = case.q_weight.to(dev), case.k_weight.to(dev)
+
+    def make_set():
+        q, k = case.q.to(dev), case.k.to(dev)
+        cos = torch.empty((3, n, half), device=dev)
+        sin = torch.empty((3, n, half), device=dev)
+        return q, k, torch.empty_like(q), torch.empty_like(k), cos, sin
+
+    def step(state):
+        q, k, qo, ko, cos, sin = state
+        qkr.mrope_cos_sin_setup(*inv, case.grid_thw, case.merge, out=(cos, sin))
+        rope = qkr.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=cos, sin_planes=sin)
+        qkr.qk_norm_rope(q, k, qw, kw, case.eps, rope, q_out=qo, k_out=ko)
+
+    heads = case.q.shape[1]
+    planes = 2 * n * half * 4
+    apply_bytes = 4 * n * heads * 2 * half * 2 + planes + 2 * 2 * half * 2
+
+    def cpu_step():
+        import oracle
+        qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
+
+        def run():
+            c, s = oracle.vit_cos_sin(case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
+            orope = oracle.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=c, sin_planes=s)
+            oracle.qk_norm_rope(qf, wq, case.eps, orope)
+            oracle.qk_norm_rope(kf, wk, case.eps, orope)
+        return run
+
+    w = Workload()
+    w.name = "ViT mrope cos/sin setup + apply after per-head QK RMSNorm"
+    w.config = {"workload": w.name, "grid_thw": case.grid_thw, "spatial_merge": case.merge, "tokens": n,
+                "heads": heads, "head_dim": 2 * half, "halves": list(secs[:3])}
+    w.step_bytes = planes + apply_bytes
+    w.launch_bytes = apply_bytes
+    w.launches = 1
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "bf16"
+    w.sample = "setup + apply over all 7952 tokens"
+    return w
+
+
+def build_rows(t):
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.rows(t)
+    dev = torch.device("cuda")
+    wgt = case.weight.to(dev)
+
+    def make_set():
+        x = case.x.to(dev)
+        return x, torch.empty_like(x)
+
+    def step(state):
+        x, y = state
+        qkr.rms_norm(x, wgt, case.eps, out=y)
+
+    width = case.x.shape[1]
+    nbytes = 2 * t * width * 2 + width * 2
+
+    def cpu_step():
+        import oracle
+        xf, wf = W.as_f32(case.x), W.as_f32(case.weight)
+
+        def run():
+            oracle.rms_norm(xf, wf, case.eps, "bf16")
+        return run
+
+    w = Workload()
+    w.name = f"plain row RMSNorm bf16 [{t}, {width}]"
+    w.config = {"workload": w.name, "rows": t, "width": width, "eps": case.eps}
+    w.step_bytes = w.launch_bytes = nbytes
+    w.launches = 1
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "bf16"
+    w.sample = f"the full [{t}, {width}] input"
+    return w
+
+
+def build_tiny():
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.tiny()
+    dev = torch.device("cuda")
+    rope = qkr.Rope("1d", 64, "neox", inv_freq=torch.from_numpy(case.inv_freq).to(dev),
+                    positions=torch.from_numpy(case.positions).to(dev))
+    ws = case.q_weight.to(dev), case.k_weight.to(dev)
+
+    def make_set():
+        q, k = case.q.to(dev), case.k.to(dev)
+        return q, k, torch.empty_like(q), torch.empty_like(k)
+
+    def step(state):
+        q, k, qo, ko = state
+        qkr.qk_norm_rope(q, k, ws[0], ws[1], case.eps, rope, q_out=qo, k_out=ko)
+
+    nbytes = 2 * 2 * q_numel(case) * 4 + 2 * 64 * 4 + 4 * 4 + 32 * 4
+
+    def cpu_step():
+        import oracle
+        orope = oracle.Rope("1d", 64, "neox", inv_freq=case.inv_freq, positions=case.positions)
+        qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
+
+        def run():
+            oracle.qk_norm_rope(qf, wq, case.eps, orope, "f32")
+            oracle.qk_norm_rope(kf, wk, case.eps, orope, "f32")
+        return run
+
+    w = Workload()
+    w.name = "tiny fp32 QK RMSNorm + NeoX RoPE [4, 2, 64]"
+    w.config = {"workload": w.name, "tokens": 4, "heads": 2, "head_dim": 64}
+    w.step_bytes = w.launch_bytes = nbytes
+    w.launches = 1
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "f32"
+    w.sample = "the full [4, 2, 64] input"
+    return w
+
+
+def q_numel(case):
+    return case.q.numel()
+
+
+def cpu_baseline(w, seconds):
+    run = w.cpu_step()
+    run()   # warm (page in, first-touch)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = w.step_bytes * reps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_step": round(el / reps * 1e6, 1),
+            "sample": f"{reps} x {w.sample}, single-threaded C oracle"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: every row of the path is per-row "
+                                   "independent and shards without communication; run with --gpus 1"}))
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: one process, one GPU; WORLD_SIZE > 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+
+    builders = {"joint": lambda: build_joint("adjacent"), "joint-neox": lambda: build_joint("neox"),
+                "imrope": build_imrope, "vit": build_vit, "rows1": lambda: build_rows(1),
+                "rows32": lambda: build_rows(32), "rows4096": lambda: build_rows(4096), "tiny": build_tiny}
+    w = builders[args.workload]()
+    nsets = args.sets or max(3, -(-2 * MALL_BYTES // max(w.step_bytes, 1)))
+    nsets = min(nsets, 64)
+    sets = [w.make_set() for _ in range(nsets)]
+    if args.variant:
+        qkr.set_variant_override(args.variant)
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        w.step(sets[i % nsets])
+    torch.cuda.synchronize()
+    variant = qkr.last_variant()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        starts[i].record(stream)
+        w.step(sets[i % nsets])
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_step = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    step_ms_med = per_step[len(per_step) // 2]
+    launch_us = sum(per_step) / K * 1e3 / w.launches
+    ms_per_step = total_ms / K
+
+    value = w.step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = w.launch_bytes / (launch_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(launch_us, 3),
+        "us_per_call_median_step": round(step_ms_med * 1e3 / w.launches, 3),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, workloads.py)",
+        "config": dict(w.config, buffer_sets=nsets, variant=variant, bytes_per_step=w.step_bytes),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": w.launch_bytes, "kernel": variant},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * qkrope: per-(token, head) RMSNorm fused with rotary position embedding on
+ * attention Q/K, for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operations come from these pages (cited by the short name in brackets):
+ *   [Ovis]   vllm-omni pull request "[Kernel][Ovis-Image] Fuse text/image QK
+ *            RMSNorm + cat + RoPE into one Triton launch"
+ *   [Vulkan] vllm.cpp pull request "perf(vulkan): decode RmsNorm ran on ONE
+ *            workgroup -- 7.85 -> 1.59 ms/token"
+ *   [IMROPE] llama.cpp fork pull request "hrx: the multi-section rotation of
+ *            Qwen3-VL runs on the device, not on the CPU"
+ *   [ViT]    vLLM API page "vllm.model_executor.layers.rotary_embedding.
+ *            mrope_vit_setup"
+ *   [VecRMS] vLLM pull request "Vectorize RMS norm variance using
+ *            vectorize_read_with_alignment"
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named *_dev are device (HBM) pointers; grid_thw is a host
+ *     pointer.  The caller owns every buffer, outputs included; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - Strides are in elements.  The last (head_dim / width) dimension is
+ *     contiguous.  Every base pointer must be 16-byte aligned and every stride
+ *     a multiple of 16 bytes (rows are moved as 128-bit vectors); otherwise
+ *     QKR_ERR_MISALIGNED.  Offsets are computed in 64 bits, so views deep
+ *     inside buffers larger than 4 GiB are fine ([Ovis] 64-bit row
+ *     addressing).
+ *   - Activations, weights and outputs share `dtype`.  Positions are int32,
+ *     inverse frequencies and cos/sin planes are fp32.
+ *   - `stream` is the caller's HIP stream (NULL: the null stream).  Work is
+ *     enqueued asynchronously; nothing synchronises the host.
+ *   - Arguments are validated on the host before any HIP call.  A refusal
+ *     returns a non-zero qkr_status, launches nothing and leaves a message for
+ *     qkr_last_error() (per calling thread).  There is no fallback path.
+ *   - Input and output rows may alias exactly (same pointer and strides: each
+ *     row is read whole before it is written); partial overlap is undefined.
+ *   - Results are deterministic: fixed launch shape, no atomics.
+ */
+#ifndef QKROPE_H
+#define QKROPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* qkr_stream_t; /* a hipStream_t */
+
+typedef enum {
+    QKR_OK = 0,
+    QKR_ERR_INVALID_ARGUMENT = 1, /* a size, pointer, mode or section is out of range */
+    QKR_ERR_UNSUPPORTED = 2,      /* valid, but a geometry this library does not run   */
+    QKR_ERR_MISALIGNED = 3,       /* a pointer or stride is not 16-byte aligned        */
+    QKR_ERR_HIP = 4               /* the HIP runtime refused the launch                */
+} qkr_status;
+
+typedef enum { QKR_F32 = 0, QKR_BF16 = 1 } qkr_dtype;
+
+/* Rotary pairing.  NEOX pairs element p with p + R/2 ([IMROPE]: the sectioned
+ * mode keeps the NeoX pairing); ADJACENT pairs 2p with 2p + 1 ([Ovis]:
+ * interleaved=True). */
+typedef enum { QKR_PAIR_NEOX = 0, QKR_PAIR_ADJACENT = 1 } qkr_pairing;
+
+/* Where pair p takes its position.
+ *   1D      one position plane.
+ *   AXES    sections[0..2] contiguous runs of pairs read planes t, h, w
+ *           ([Ovis] multi-axis image positions; [ViT] t/h/w column ranges).
+ *   IMROPE  interleaved multi-section rule of [IMROPE] ("The change"):
+ *           sector = p mod (s0+s1+s2+s3); sector mod 3 == 1 -> h while
+ *           sector < 3 s1, == 2 -> w while sector < 3 s2, == 0 -> t while
+ *           sector < 3 s0, else the fourth plane e.
+ *   PLANES  cos/sin come from (3, planes_tokens, R/2) fp32 planes written by
+ *           qkr_mrope_cos_sin_setup; pair p reads the plane of its axis, the
+ *           axes being contiguous runs of sections[0..2] pairs ([ViT]). */
+typedef enum { QKR_POS_1D = 0, QKR_POS_AXES = 1, QKR_POS_IMROPE = 2, QKR_POS_PLANES = 3 } qkr_pos_mode;
+
+/* Rotary embedding parameters.  The angle of pair p at token t is
+ * fl32(fl32(pos) * inv_freq[p]) with pos = positions[axis * pos_stride +
+ * token_base + t]; cos and sin are computed in registers, never read from a
+ * cache (except in PLANES mode).  A call over a chunk of a longer sequence
+ * passes the whole-length position planes and its first token in token_base
+ * ([IMROPE] "The change": chunked launches keep the whole positions buffer). */
+typedef struct {
+    int32_t mode;               /* qkr_pos_mode                                            */
+    int32_t pairing;            /* qkr_pairing                                             */
+    int32_t rotary_dim;         /* R: even, 0 <= R <= head_dim; 0 = norm only              */
+    int32_t sections[4];        /* AXES/PLANES: pairs on t, h, w (sum R/2, [3] = 0);
+                                   IMROPE: s0..s3 with R/2 <= sum <= R ([IMROPE] claim
+                                   window); unused otherwise                               */
+    const float* inv_freq_dev;  /* [R/2] fp32 (1D, AXES, IMROPE)                           */
+    const int32_t* positions_dev; /* [planes][pos_stride] int32: 1 plane (1D), 3 (AXES),
+                                     4 (IMROPE)                                            */
+    int64_t pos_stride;         /* elements between planes; >= token_base + tokens         */
+    int64_t token_base;         /* first token of this call inside every plane, >= 0       */
+    const float* cos_planes_dev; /* PLANES: [3][planes_tokens][R/2] fp32                   */
+    const float* sin_planes_dev;
+    int64_t planes_tokens;      /* PLANES: tokens per plane; >= token_base + tokens        */
+} qkr_rope;
+
+/* A [batch, tokens, heads, head_dim] tensor of rows. */
+typedef struct {
+    void* ptr_dev;        /* element (0, 0, 0, 0)                                          */
+    int64_t stride_batch; /* elements between batches (ignored when batch == 1)            */
+    int64_t stride_tok;   /* elements between tokens                                       */
+    int64_t stride_head;  /* elements between heads                                        */
+} qkr_view;
+
+/* Plain row RMSNorm ([Vulkan] decode RmsNorm; [VecRMS]):
+ *   y[r, i] = round(x[r, i] * rrms_r * weight[i]),
+ *   rrms_r = 1 / sqrt(mean_i(x[r, i]^2) + eps), sum of squares in fp32,
+ * one rounding to the output type.  x, y: [rows, width] with row strides in
+ * elements; weight: [width].  rows == 0 is a no-op.  A single row or a few
+ * rows are spread over many compute units (split-row variant). */
+qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, int64_t y_row_stride,
+                        const void* weight_dev, int64_t rows, int32_t width, float eps,
+                        int32_t dtype, qkr_stream_t stream);
+
+/* Per-(token, head) RMSNorm of Q and K followed by RoPE ([Ovis] single-stream
+ * fused_qk_norm_rope; [IMROPE] sectioned rotation after the per-head norm):
+ *   n = x * rrms * w over each head_dim row (fp32 sum of squares);
+ *   bf16: n is rounded to bf16, rotated in fp32, rounded once more ([Ovis]
+ *   kernel review: the documented rounding contract); fp32: no intermediate
+ *   rounding.  Elements at or past rotary_dim pass through normalised.
+ * q/q_out: q_heads rows per token with weight q_weight [head_dim]; likewise
+ * k.  Either tensor may be absent (heads == 0).  rope == NULL: norm only.
+ * Positions are indexed by token (shared across the batch). */
+qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int32_t dtype, float eps,
+                            const qkr_view* q, const qkr_view* q_out, int32_t q_heads,
+                            const void* q_weight_dev,
+                            const qkr_view* k, const qkr_view* k_out, int32_t k_heads,
+                            const void* k_weight_dev,
+                            const qkr_rope* rope, qkr_stream_t stream);
+
+/* One stream (text or image) of the joint op: Q, K, V views of `tokens`
+ * tokens (e.g. chunked views of one packed QKV projection) and the stream's
+ * own q/k norm weights [head_dim]. */
+typedef struct {
+    qkr_view q, k, v;
+    int64_t tokens;
+    const void* q_weight_dev;
+    const void* k_weight_dev;
+} qkr_stream;
+
+/* Joint text/image QK RMSNorm + concatenation + RoPE ([Ovis] "Purpose":
+ * fused_joint_qkv_norm_rope).  Each stream is normalised with its own
+ * weights; outputs are the joint [batch, text.tokens + image.tokens, heads,
+ * head_dim] Q, K and V, text first; the rotation reads positions by joint
+ * token; V rows are copied bit for bit. */
+qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype,
+                                  float eps, const qkr_stream* text, const qkr_stream* image,
+                                  const qkr_view* q_out, const qkr_view* k_out,
+                                  const qkr_view* v_out, const qkr_rope* rope,
+                                  qkr_stream_t stream);
+
+/* ViT multi-axis cos/sin setup ([ViT] VitMropeSetup / _vit_mrope_setup_kernel).
+ * For token n of the grids grid_thw[g] = (t, h, w) (host array, num_grids
+ * entries, tokens of grid g following those of grid g-1), the (t, h, w)
+ * position comes from the spatial-merge token order; plane a receives
+ * cos/sin of fl32(fl32(pos_a) * inv_freq_a[j]) in its own columns
+ * [off_a, off_a + half_a) of the (3, n_tokens, half_t + half_h + half_w) fp32
+ * outputs.  Other columns are not written.  n_tokens must equal sum t*h*w;
+ * h and w must be multiples of spatial_merge.  The grid table travels in
+ * kernel arguments (no host-to-device copy). */
+qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t,
+                                   const float* inv_freq_h_dev, int32_t half_h,
+                                   const float* inv_freq_w_dev, int32_t half_w,
+                                   const int32_t* grid_thw, int32_t num_grids,
+                                   int32_t spatial_merge, float* cos_out_dev, float* sin_out_dev,
+                                   int64_t n_tokens, qkr_stream_t stream);
+
+/* Text of a status code (static storage). */
+const char* qkr_status_string(qkr_status status);
+
+/* Detail of the last refusal on the calling thread ("" if none). */
+const char* qkr_last_error(void);
+
+/* ---- Introspection and test hooks (not for the hot path) ---------------- */
+
+/* Force a kernel variant by name for subsequent calls on any thread, or NULL
+ * for the automatic choice.  Names: "rms:rows", "rms:split", "rms:wide",
+ * "rope:np1", "rope:np2", "rope:np3", "rope:np4".  Unknown names are refused. */
+qkr_status qkr_set_variant_override(const char* name);
+
+/* Name of the kernel variant the last successful launch on the calling
+ * thread used ("" if none). */
+const char* qkr_last_variant(void);
+
+/* The position axis (0 t, 1 h, 2 w, 3 e) of each of n_pairs pairs under
+ * `rope`, computed by the same device function the kernels use, written to
+ * out_dev [n_pairs] int32. */
+qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* out_dev,
+                              qkr_stream_t stream);
+
+/* The (t, h, w) position of every ViT token, computed by the same device
+ * function the setup kernel uses, written to out_dev [3][n_tokens] int32. */
+qkr_status qkr_debug_vit_positions(const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
+                                   int32_t* out_dev, int64_t n_tokens, qkr_stream_t stream);
+
+/* Host builds of the same two index functions (no GPU needed): out_host
+ * [n_pairs] and [3][n_tokens] int32. */
+qkr_status qkr_axis_map_host(const qkr_rope* rope, int32_t n_pairs, int32_t* out_host);
+qkr_status qkr_vit_positions_host(const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
+                                  int32_t* out_host, int64_t n_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QKROPE_H */

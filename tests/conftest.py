@@ -25,3 +25,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # Name the case on the real stderr before it touches the GPU, so a run
+    # that ends the process still says which case it was in.
+    if "gpu" in request.keywords:
+        sys.__stderr__.write(f"[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

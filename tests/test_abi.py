@@ -1,0 +1,252 @@
+"""The C ABI on the host (CPU only, no compute calls).
+
+- libqkrope loads and exports every symbol include/qkrope.h declares;
+- every refusal returns its status code before any HIP call (the pointers
+  below are never dereferenced), so these run on a machine without a GPU;
+- the library's own index functions, compiled for the host from the same
+  source as the device build, agree exactly with the oracle.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import transformer_qk_rmsnorm_amd as qkr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkrope.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED = 0, 1, 2, 3
+FAKE = 0x7f0000000000          # 16-byte aligned stand-in for a device pointer
+ODD = FAKE + 8                 # 8-byte aligned only
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qkr_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    L = qkr.lib()
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in qkrope.h but not exported"
+    assert set(syms) == set(qkr._SIGNATURES), "binding signatures and header disagree"
+
+
+def test_status_strings():
+    for code, name in [(0, "QKR_OK"), (1, "QKR_ERR_INVALID_ARGUMENT"), (2, "QKR_ERR_UNSUPPORTED"),
+                       (3, "QKR_ERR_MISALIGNED"), (4, "QKR_ERR_HIP")]:
+        assert qkr.status_of(code) == name
+
+
+# ---------------------------------------------------------------------------
+# rms_norm refusals
+# ---------------------------------------------------------------------------
+
+def rms(x=FAKE, xs=5120, y=FAKE, ys=5120, w=FAKE, rows=4, width=5120, eps=1e-6, dtype=qkr.BF16):
+    return qkr.lib().qkr_rms_norm(x, xs, y, ys, w, rows, width, eps, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dtype=7), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(width=0), INVALID),
+    (dict(rows=-1), INVALID),
+    (dict(width=5121, xs=5121, ys=5121), MISALIGNED),
+    (dict(x=None), INVALID),
+    (dict(w=None), INVALID),
+    (dict(x=ODD), MISALIGNED),
+    (dict(xs=5000), INVALID),
+    (dict(ys=5128 + 4), MISALIGNED),
+    (dict(width=40960, xs=40960, ys=40960), UNSUPPORTED),
+])
+def test_rms_norm_refusals(kwargs, code):
+    assert rms(**kwargs) == code
+    assert qkr.last_error() != ""
+
+
+def test_rms_norm_zero_rows_is_a_noop():
+    assert rms(rows=0, x=None, y=None, w=None) == OK
+
+
+# ---------------------------------------------------------------------------
+# qk_norm_rope refusals
+# ---------------------------------------------------------------------------
+
+def view(ptr=FAKE, sb=0, st=24 * 128, sh=128):
+    return qkr._View(ptr, sb, st, sh)
+
+
+def rope_c(mode=2, pairing=0, rotary_dim=128, sections=(24, 20, 20, 0), inv=FAKE, pos=FAKE,
+           pos_stride=8192, token_base=0, cosp=None, sinp=None, planes_tokens=0):
+    return qkr._Rope(mode, pairing, rotary_dim, (ctypes.c_int32 * 4)(*sections), inv, pos, pos_stride,
+                     token_base, cosp, sinp, planes_tokens)
+
+
+def qknr(batch=1, tokens=2048, head_dim=128, dtype=qkr.BF16, eps=1e-6, q=None, qo=None, qh=16, qw=FAKE,
+         k=None, ko=None, kh=8, kw=FAKE, rope="default"):
+    q = q or view(st=16 * 128)
+    qo = qo or view(st=16 * 128)
+    k = k or view(st=8 * 128)
+    ko = ko or view(st=8 * 128)
+    r = rope_c() if rope == "default" else rope
+    return qkr.lib().qkr_qk_norm_rope(batch, tokens, head_dim, dtype, eps, ctypes.byref(q), ctypes.byref(qo), qh,
+                                      qw, ctypes.byref(k), ctypes.byref(ko), kh, kw,
+                                      ctypes.byref(r) if r is not None else None, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dtype=3), INVALID),
+    (dict(head_dim=0), INVALID),
+    (dict(head_dim=512), INVALID),
+    (dict(head_dim=100), MISALIGNED),                                 # 200 B rows
+    (dict(tokens=-1), INVALID),
+    (dict(qh=-2), INVALID),
+    (dict(q=view(ptr=None, st=2048)), INVALID),
+    (dict(q=view(ptr=ODD, st=2048)), MISALIGNED),
+    (dict(q=view(st=2048 + 4)), MISALIGNED),
+    (dict(k=view(st=-1024)), INVALID),
+    (dict(qw=None), INVALID),
+    (dict(kw=ODD), MISALIGNED),
+    (dict(rope=rope_c(rotary_dim=127)), INVALID),                      # odd
+    (dict(rope=rope_c(rotary_dim=130)), INVALID),                      # > head_dim
+    (dict(rope=rope_c(pairing=5)), INVALID),
+    (dict(rope=rope_c(mode=9)), INVALID),
+    (dict(rope=rope_c(rotary_dim=120, sections=(20, 20, 20, 0))), UNSUPPORTED),  # NeoX half 60 not 8-aligned
+    (dict(rope=rope_c(sections=(24, 20, 19, 0))), INVALID),            # sum 63 < R/2
+    (dict(rope=rope_c(sections=(60, 60, 10, 0))), INVALID),            # sum 130 > R
+    (dict(rope=rope_c(sections=(0, 0, 0, 0))), INVALID),               # missing sections refused
+    (dict(rope=rope_c(sections=(30, 20, 20, -6))), INVALID),
+    (dict(rope=rope_c(mode=1, sections=(8, 28, 27, 0))), INVALID),     # axes must sum to R/2
+    (dict(rope=rope_c(mode=1, sections=(8, 28, 24, 4))), INVALID),     # axes take three sections
+    (dict(rope=rope_c(inv=None)), INVALID),
+    (dict(rope=rope_c(pos=None)), INVALID),
+    (dict(rope=rope_c(pos_stride=2047)), INVALID),                     # positions shorter than the call
+    (dict(rope=rope_c(token_base=6145)), INVALID),                     # token_base + tokens > pos_stride
+    (dict(rope=rope_c(token_base=-1)), INVALID),
+    (dict(rope=rope_c(mode=3, sections=(16, 24, 24, 0))), INVALID),    # planes mode without planes
+    (dict(rope=rope_c(mode=3, sections=(16, 24, 24, 0), cosp=FAKE, sinp=FAKE, planes_tokens=100)), INVALID),
+    (dict(rope=rope_c(mode=3, sections=(16, 24, 24, 0), cosp=FAKE + 2, sinp=FAKE, planes_tokens=9000)),
+     MISALIGNED),
+])
+def test_qk_norm_rope_refusals(kwargs, code):
+    assert qknr(**kwargs) == code, qkr.last_error()
+    assert qkr.last_error() != ""
+
+
+def test_qk_norm_rope_empty_calls_are_noops():
+    assert qknr(tokens=0) == OK
+    assert qknr(batch=0) == OK
+    assert qknr(qh=0, kh=0, qw=None, kw=None) == OK
+    assert qkr.last_error() == ""
+
+
+def test_adjacent_pairing_takes_any_even_rotary_dim():
+    # a valid geometry gets past validation; with no tokens nothing launches
+    assert qknr(tokens=0, rope=rope_c(pairing=1, rotary_dim=122, sections=(61, 0, 0, 0), pos_stride=0)) == OK
+
+
+def test_joint_refusals():
+    L = qkr.lib()
+
+    def stream(tokens, ptr=FAKE, w=FAKE):
+        v = view(ptr=ptr, st=9216, sh=128)
+        return qkr._Stream(v, v, v, tokens, w, w)
+
+    out = view(st=24 * 128)
+    r = rope_c(mode=1, pairing=1, sections=(8, 28, 28, 0), pos_stride=4608)
+
+    def call(text, image, rope=r, heads=24, head_dim=128):
+        return L.qkr_joint_qk_norm_rope(1, heads, head_dim, qkr.BF16, 1e-6, ctypes.byref(text),
+                                        ctypes.byref(image), ctypes.byref(out), ctypes.byref(out),
+                                        ctypes.byref(out), ctypes.byref(rope), None)
+
+    assert call(stream(512), stream(4096, w=None)) == INVALID
+    assert call(stream(-1), stream(4096)) == INVALID
+    assert call(stream(512, ptr=ODD), stream(4096)) == MISALIGNED
+    short = rope_c(mode=1, pairing=1, sections=(8, 28, 28, 0), pos_stride=4607)
+    assert call(stream(512), stream(4096), rope=short) == INVALID     # positions cover joint tokens
+    assert L.qkr_joint_qk_norm_rope(1, 24, 128, qkr.BF16, 1e-6, None, None, None, None, None, None,
+                                    None) == INVALID
+    assert call(stream(0), stream(0)) == OK
+
+
+def test_mrope_setup_refusals():
+    L = qkr.lib()
+
+    def call(grids, merge=2, n=None, halves=(8, 16, 16), cos=FAKE, sin=FAKE, inv=FAKE):
+        flat = [v for g in grids for v in g]
+        arr = (ctypes.c_int32 * max(len(flat), 1))(*flat)
+        if n is None:
+            n = sum(t * h * w for t, h, w in grids)
+        return L.qkr_mrope_cos_sin_setup(inv, halves[0], inv, halves[1], inv, halves[2], arr, len(grids), merge,
+                                         cos, sin, n, None)
+
+    assert call([[1, 64, 63]]) == INVALID          # w not a multiple of merge
+    assert call([[1, 64, 64]], merge=0) == INVALID
+    assert call([[0, 64, 64]]) == INVALID
+    assert call([[1, 64, 64]], n=4095) == INVALID
+    assert call([]) == INVALID
+    assert call([[1, 64, 64]], cos=None) == INVALID
+    assert call([[1, 64, 64]], cos=FAKE + 2) == MISALIGNED
+    assert call([[1, 64, 64]], halves=(0, 0, 0)) == INVALID
+    assert call([[1, 64, 64]], inv=None) == INVALID
+
+
+def test_variant_override_names():
+    for name in ("rms:rows", "rms:split", "rms:wide", "rope:np1", "rope:np2", "rope:np3", "rope:np4"):
+        qkr.set_variant_override(name)
+    qkr.set_variant_override(None)
+    with pytest.raises(qkr.QkrError):
+        qkr.set_variant_override("rms:fastest")
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 5120, dtype=torch.bfloat16)
+    w = torch.ones(5120, dtype=torch.bfloat16)
+    with pytest.raises(qkr.QkrError, match="GPU tensor"):
+        qkr.rms_norm(x, w)
+    q = torch.zeros(4, 2, 64)
+    with pytest.raises(qkr.QkrError, match="GPU tensor"):
+        qkr.qk_norm_rope(q, q, w[:64].float(), w[:64].float())
+
+
+# ---------------------------------------------------------------------------
+# index maps: the library's host build vs the oracle (exact)
+# ---------------------------------------------------------------------------
+
+SECTION_CASES = [
+    ("imrope", (24, 20, 20, 0), 64), ("imrope", (16, 24, 24, 0), 64), ("imrope", (20, 24, 16, 4), 64),
+    ("imrope", (0, 0, 0, 64), 64), ("imrope", (11, 12, 13, 14), 40), ("imrope", (3, 3, 2, 0), 8),
+    ("imrope", (40, 40, 40, 8), 64), ("imrope", (1, 1, 1, 1), 2),
+    ("axes", (8, 28, 28, 0), 64), ("axes", (8, 16, 16, 0), 40), ("axes", (0, 32, 32, 0), 64),
+    ("planes", (8, 16, 16, 0), 40), ("1d", (0, 0, 0, 0), 64),
+]
+
+
+@pytest.mark.parametrize("mode,sections,pairs", SECTION_CASES)
+def test_axis_map_host_matches_oracle(mode, sections, pairs):
+    expect = oracle.axis_map(oracle.Rope(mode, 2 * pairs, sections=sections), pairs)
+    got = np.array(qkr.axis_map_host(mode, sections, pairs))
+    assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("grids,merge", [
+    ([[1, 64, 64], [2, 32, 48], [1, 28, 28]], 2),
+    ([[1, 4, 6], [2, 2, 4]], 2),
+    ([[3, 6, 9]], 3),
+    ([[2, 5, 7], [1, 1, 1], [4, 3, 2]], 1),
+    ([[1, 8, 8]] * 70, 2),                         # more grids than one launch carries
+])
+def test_vit_positions_host_matches_oracle(grids, merge):
+    expect = oracle.vit_positions(grids, merge)
+    got = np.array(qkr.vit_positions_host(grids, merge))
+    assert np.array_equal(got, expect)

@@ -1,0 +1,411 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every input is seeded and synthetic (workloads.py); the oracle receives the
+exact values the GPU reads.  Tolerances are in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_qk_rmsnorm_amd as qkr
+import workloads as W
+from parity import assert_bf16_close, assert_f32_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def gpu(t):
+    return t.to(DEV)
+
+
+def host(t):
+    return t.detach().float().cpu().numpy()
+
+
+def dt_name(t):
+    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+
+
+def check(got, ref, dtype, rotary_dim=0, pairing="neox", what=""):
+    if dtype == "f32":
+        return assert_f32_close(got, ref, what)
+    return assert_bf16_close(got, ref, rotary_dim, pairing, what)
+
+
+# ---------------------------------------------------------------------------
+# index maps (exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode,sections,pairs", [
+    ("imrope", (24, 20, 20, 0), 64), ("imrope", (20, 24, 16, 4), 64), ("imrope", (0, 0, 0, 64), 64),
+    ("imrope", (40, 40, 40, 8), 64), ("axes", (8, 28, 28, 0), 64), ("planes", (8, 16, 16, 0), 40),
+    ("1d", (0, 0, 0, 0), 128),
+])
+def test_device_axis_map_matches_oracle(mode, sections, pairs):
+    got = qkr.debug_axis_map(mode, sections, pairs).cpu().numpy()
+    expect = oracle.axis_map(oracle.Rope(mode, 2 * pairs, sections=sections), pairs)
+    assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("grids,merge", [
+    ([[1, 64, 64], [2, 32, 48], [1, 28, 28]], 2),
+    ([[1, 4, 6], [2, 2, 4]], 2),
+    ([[2, 6, 9]], 3),
+    ([[1, 8, 8]] * 70, 2),
+])
+def test_device_vit_positions_match_oracle(grids, merge):
+    got = qkr.debug_vit_positions(grids, merge).cpu().numpy()
+    assert np.array_equal(got, oracle.vit_positions(grids, merge))
+
+
+# ---------------------------------------------------------------------------
+# tiny: fp32 [4, 2, 64], NeoX 1-D RoPE (and bf16 / other head dims)
+# ---------------------------------------------------------------------------
+
+def run_1d(case, pairing="neox", rotary_dim=None, positions=None):
+    rd = case.rotary_dim if rotary_dim is None else rotary_dim
+    pos = case.positions if positions is None else positions
+    inv = W.inv_freq_ladder(1e4, rd) if rd else case.inv_freq
+    rope = qkr.Rope("1d", rd, pairing, inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    qo, ko = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+    orope = oracle.Rope("1d", rd, pairing, inv_freq=inv, positions=pos)
+    rq = oracle.qk_norm_rope(W.as_f32(case.q), W.as_f32(case.q_weight), case.eps, orope, case.dtype)
+    rk = oracle.qk_norm_rope(W.as_f32(case.k), W.as_f32(case.k_weight), case.eps, orope, case.dtype)
+    return host(qo), host(ko), rq, rk
+
+
+def test_tiny_fp32_neox():
+    case = W.tiny()
+    qo, ko, rq, rk = run_1d(case)
+    assert_f32_close(qo, rq, "q")
+    assert_f32_close(ko, rk, "k")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("head_dim", [16, 32, 64, 80, 128, 256])
+@pytest.mark.parametrize("pairing", ["neox", "adjacent"])
+def test_head_dims_and_pairings(dtype, head_dim, pairing):
+    case = W.tiny(tokens=37, heads=5, head_dim=head_dim, dtype=dtype, seed_stream=head_dim)
+    pos = np.random.default_rng(head_dim).integers(0, 9000, (1, 37)).astype(np.int32)
+    qo, ko, rq, rk = run_1d(case, pairing, positions=pos)
+    check(qo, rq, dtype, head_dim, pairing, "q")
+    check(ko, rk, dtype, head_dim, pairing, "k")
+
+
+@pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing", [
+    ("bf16", 128, 64, "neox"), ("bf16", 128, 32, "neox"), ("bf16", 256, 128, "neox"),
+    ("f32", 64, 24, "neox"), ("bf16", 128, 96, "adjacent"), ("bf16", 80, 34, "adjacent"),
+    ("f32", 128, 2, "adjacent"), ("bf16", 128, 0, "neox"),
+])
+def test_partial_rotary(dtype, head_dim, rotary_dim, pairing):
+    case = W.tiny(tokens=19, heads=3, head_dim=head_dim, dtype=dtype, seed_stream=rotary_dim + 1000)
+    pos = np.random.default_rng(rotary_dim).integers(0, 5000, (1, 19)).astype(np.int32)
+    qo, ko, rq, rk = run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos)
+    check(qo, rq, dtype, rotary_dim, pairing, "q")
+    check(ko, rk, dtype, rotary_dim, pairing, "k")
+
+
+def test_position_zero_equals_norm_only_bitwise():
+    case = W.tiny(tokens=64, heads=7, head_dim=128, dtype="bf16", seed_stream=5)
+    zeros = np.zeros((1, 64), np.int32)
+    for pairing in ("neox", "adjacent"):
+        rope = qkr.Rope("1d", 128, pairing, inv_freq=gpu(torch.from_numpy(W.inv_freq_ladder(1e4, 128))),
+                        positions=gpu(torch.from_numpy(zeros)))
+        a, b = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), 1e-6, rope)
+        c, d = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), 1e-6, None)
+        assert torch.equal(a, c) and torch.equal(b, d)
+
+
+def test_batch_and_strided_views():
+    """[batch, tokens, heads, D] views carved out of a wider buffer, positions
+    shared across the batch."""
+    rng = np.random.default_rng(11)
+    b, t, hq, hk, d = 3, 50, 6, 2, 128
+    big = torch.from_numpy(rng.normal(0, 1, (b, t, hq + hk + 3, d)).astype(np.float32)).to(torch.bfloat16)
+    q, k = big[:, :, :hq], big[:, :, hq + 1:hq + 1 + hk]
+    wq = torch.from_numpy(rng.normal(1, 0.1, d).astype(np.float32)).to(torch.bfloat16)
+    wk = torch.from_numpy(rng.normal(1, 0.1, d).astype(np.float32)).to(torch.bfloat16)
+    pos = rng.integers(0, 4096, (1, t)).astype(np.int32)
+    inv = W.inv_freq_ladder(1e4, d)
+    gbig = gpu(big)
+    rope = qkr.Rope("1d", d, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    qo, ko = qkr.qk_norm_rope(gbig[:, :, :hq], gbig[:, :, hq + 1:hq + 1 + hk], gpu(wq), gpu(wk), 1e-6, rope)
+    orope = oracle.Rope("1d", d, "neox", inv_freq=inv, positions=pos)
+    for bi in range(b):
+        assert_bf16_close(host(qo[bi]), oracle.qk_norm_rope(W.as_f32(q[bi]), W.as_f32(wq), 1e-6, orope), d)
+        assert_bf16_close(host(ko[bi]), oracle.qk_norm_rope(W.as_f32(k[bi]), W.as_f32(wk), 1e-6, orope), d)
+
+
+def test_in_place():
+    case = W.tiny(tokens=40, heads=4, head_dim=128, dtype="bf16", seed_stream=9)
+    pos = np.arange(40, dtype=np.int32)[None] * 7
+    inv = W.inv_freq_ladder(1e4, 128)
+    rope = qkr.Rope("1d", 128, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    q, k = gpu(case.q), gpu(case.k)
+    ref_q, ref_k = qkr.qk_norm_rope(q, k, gpu(case.q_weight), gpu(case.k_weight), 1e-6, rope)
+    qkr.qk_norm_rope(q, k, gpu(case.q_weight), gpu(case.k_weight), 1e-6, rope, q_out=q, k_out=k)
+    assert torch.equal(q, ref_q) and torch.equal(k, ref_k)
+
+
+def test_q_only_and_k_only():
+    case = W.tiny(tokens=21, heads=3, head_dim=64, dtype="bf16", seed_stream=3)
+    pos = np.arange(21, dtype=np.int32)[None]
+    inv = W.inv_freq_ladder(1e4, 64)
+    rope = qkr.Rope("1d", 64, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    orope = oracle.Rope("1d", 64, "neox", inv_freq=inv, positions=pos)
+    qo, ko = qkr.qk_norm_rope(gpu(case.q), None, gpu(case.q_weight), None, 1e-6, rope)
+    assert ko is None
+    assert_bf16_close(host(qo), oracle.qk_norm_rope(W.as_f32(case.q), W.as_f32(case.q_weight), 1e-6, orope), 64)
+    qo, ko = qkr.qk_norm_rope(None, gpu(case.k), None, gpu(case.k_weight), 1e-6, rope)
+    assert qo is None
+    assert_bf16_close(host(ko), oracle.qk_norm_rope(W.as_f32(case.k), W.as_f32(case.k_weight), 1e-6, orope), 64)
+
+
+# ---------------------------------------------------------------------------
+# rows: plain RMSNorm, bf16 [t, 5120], t in {1, 32, 4096}; every variant
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t", [1, 32, 4096])
+@pytest.mark.parametrize("variant", [None, "rms:rows", "rms:split", "rms:wide"])
+def test_rms_norm_rows(t, variant):
+    case = W.rows(t)
+    qkr.set_variant_override(variant)
+    try:
+        y = qkr.rms_norm(gpu(case.x), gpu(case.weight), case.eps)
+        name = qkr.last_variant()
+    finally:
+        qkr.set_variant_override(None)
+    if variant is not None:
+        assert name.startswith(variant + ":"), name
+    elif t < 256:
+        assert name.startswith("rms:split"), name
+    ref = oracle.rms_norm(W.as_f32(case.x), W.as_f32(case.weight), case.eps, "bf16")
+    assert_bf16_close(host(y), ref, what=f"rms t={t} {name}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("width", [8, 64, 1000, 2048, 4104, 8192, 12800, 16384])
+def test_rms_norm_widths(dtype, width):
+    if dtype == "f32" and width % 4:
+        pytest.skip("fp32 rows must be 16-byte multiples")
+    case = W.rows(7, width=width, dtype=dtype, seed_stream=width)
+    for variant in (None, "rms:rows", "rms:split", "rms:wide"):
+        qkr.set_variant_override(variant)
+        try:
+            y = qkr.rms_norm(gpu(case.x), gpu(case.weight), case.eps)
+        finally:
+            qkr.set_variant_override(None)
+        ref = oracle.rms_norm(W.as_f32(case.x), W.as_f32(case.weight), case.eps, dtype)
+        check(host(y), ref, dtype, what=f"width {width} {variant}")
+
+
+def test_rms_norm_strided_rows():
+    case = W.rows(33, width=5120, seed_stream=77)
+    buf = torch.zeros(33, 5120 + 64, dtype=torch.bfloat16)
+    buf[:, 32:32 + 5120] = case.x
+    g = gpu(buf)
+    x = g[:, 32:32 + 5120]
+    out = torch.zeros(33, 5120 + 128, dtype=torch.bfloat16, device=DEV)
+    y = qkr.rms_norm(x, gpu(case.weight), case.eps, out=out[:, 64:64 + 5120])
+    ref = oracle.rms_norm(W.as_f32(case.x), W.as_f32(case.weight), case.eps, "bf16")
+    assert_bf16_close(host(y), ref)
+    assert (out[:, :64] == 0).all() and (out[:, 64 + 5120:] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# joint text/image op (512 + 4096 tokens, 24 x 128, 3-axis RoPE)
+# ---------------------------------------------------------------------------
+
+def joint_gpu(case, pairing, rope_tokens=None):
+    hd = case.head_dim
+    g = {}
+    for nm, s in (("text", case.text), ("image", case.image)):
+        qkv = gpu(s.qkv)
+        v = qkv.view(qkv.shape[0], qkv.shape[1], 3, case.heads, hd)
+        g[nm] = {"q": v[:, :, 0], "k": v[:, :, 1], "v": v[:, :, 2], "q_weight": gpu(s.q_weight),
+                 "k_weight": gpu(s.k_weight)}
+    rope = qkr.Rope("axes", hd, pairing, inv_freq=gpu(torch.from_numpy(case.inv_freq)),
+                    positions=gpu(torch.from_numpy(case.positions)), sections=case.sections)
+    return g, rope
+
+
+def joint_oracle(case, pairing):
+    hd = case.head_dim
+
+    def stream(s):
+        return {"q": W.as_f32(s.view(0, case.heads, hd)), "k": W.as_f32(s.view(1, case.heads, hd)),
+                "v": W.as_f32(s.view(2, case.heads, hd)), "q_weight": W.as_f32(s.q_weight),
+                "k_weight": W.as_f32(s.k_weight)}
+
+    rope = oracle.Rope("axes", hd, pairing, inv_freq=case.inv_freq, sections=case.sections,
+                       positions=case.positions)
+    return oracle.joint_qk_norm_rope(stream(case.text), stream(case.image), case.eps, rope, "bf16")
+
+
+@pytest.mark.parametrize("pairing", ["adjacent", "neox"])
+def test_joint_full_size(pairing):
+    case = W.joint()
+    g, rope = joint_gpu(case, pairing)
+    q, k, v = qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope)
+    rq, rk, rv = joint_oracle(case, pairing)
+    assert_bf16_close(host(q), rq, 128, pairing, "joint q")
+    assert_bf16_close(host(k), rk, 128, pairing, "joint k")
+    assert np.array_equal(host(v), rv)
+
+
+def test_joint_equals_per_stream_bitwise():
+    """joint == cat(text, image) of per-stream qk_norm_rope calls reading the
+    joint positions at token_base 0 and S_txt."""
+    case = W.joint(tokens_txt=77, grid=(12, 20), heads=5, batch=2, seed_stream=3)
+    g, rope = joint_gpu(case, "adjacent")
+    q, k, v = qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope)
+    st = 77
+    for nm, base, sl in (("text", 0, slice(0, st)), ("image", st, slice(st, None))):
+        r = qkr.Rope("axes", 128, "adjacent", inv_freq=rope.inv_freq, positions=rope.positions,
+                     sections=case.sections, token_base=base)
+        s = g[nm]
+        qs, ks = qkr.qk_norm_rope(s["q"], s["k"], s["q_weight"], s["k_weight"], case.eps, r)
+        assert torch.equal(q[:, sl], qs) and torch.equal(k[:, sl], ks)
+        assert torch.equal(v[:, sl], s["v"])
+
+
+def test_joint_ragged_and_empty_streams():
+    for st, grid in ((0, (8, 8)), (13, (1, 1)), (5, (3, 7))):
+        case = W.joint(tokens_txt=st, grid=grid, heads=3, seed_stream=st)
+        g, rope = joint_gpu(case, "adjacent")
+        q, k, v = qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope)
+        rq, rk, rv = joint_oracle(case, "adjacent")
+        assert_bf16_close(host(q), rq, 128, "adjacent")
+        assert_bf16_close(host(k), rk, 128, "adjacent")
+        assert np.array_equal(host(v), rv)
+
+
+# ---------------------------------------------------------------------------
+# IMROPE (8192 tokens, 16 + 8 heads, sections [24, 20, 20, 0], 2048-token chunks)
+# ---------------------------------------------------------------------------
+
+def imrope_call(case, q, k, pos, inv, token_base, tokens=None):
+    rope = qkr.Rope("imrope", 128, "neox", inv_freq=inv, positions=pos, sections=case.sections,
+                    token_base=token_base)
+    return qkr.qk_norm_rope(q, k, gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+
+
+def test_imrope_full_size_chunked():
+    case = W.imrope()
+    pos, inv = gpu(torch.from_numpy(case.positions)), gpu(torch.from_numpy(case.inv_freq))
+    q, k = gpu(case.q), gpu(case.k)
+    outs = [imrope_call(case, q[b:b + case.chunk], k[b:b + case.chunk], pos, inv, b)
+            for b in range(0, 8192, case.chunk)]
+    qo = torch.cat([o[0] for o in outs])
+    ko = torch.cat([o[1] for o in outs])
+    orope = oracle.Rope("imrope", 128, "neox", inv_freq=case.inv_freq, sections=case.sections,
+                        positions=case.positions)
+    assert_bf16_close(host(qo), oracle.qk_norm_rope(W.as_f32(case.q), W.as_f32(case.q_weight), case.eps, orope),
+                      128, "neox", "imrope q")
+    assert_bf16_close(host(ko), oracle.qk_norm_rope(W.as_f32(case.k), W.as_f32(case.k_weight), case.eps, orope),
+                      128, "neox", "imrope k")
+    # chunked == one launch, bitwise
+    q1, k1 = imrope_call(case, q, k, pos, inv, 0)
+    assert torch.equal(q1, qo) and torch.equal(k1, ko)
+
+
+@pytest.mark.parametrize("tokens", [2, 300, 2457])
+def test_imrope_test_sizes(tokens):
+    """Token counts the IMROPE page tests (2, 300, 2,457), with ragged chunks."""
+    case = W.imrope(tokens=tokens, seed_stream=tokens)
+    pos, inv = gpu(torch.from_numpy(case.positions)), gpu(torch.from_numpy(case.inv_freq))
+    q, k = gpu(case.q), gpu(case.k)
+    full = imrope_call(case, q, k, pos, inv, 0)
+    orope = oracle.Rope("imrope", 128, "neox", inv_freq=case.inv_freq, sections=case.sections,
+                        positions=case.positions)
+    assert_bf16_close(host(full[0]), oracle.qk_norm_rope(W.as_f32(case.q), W.as_f32(case.q_weight), case.eps,
+                                                         orope), 128)
+    assert_bf16_close(host(full[1]), oracle.qk_norm_rope(W.as_f32(case.k), W.as_f32(case.k_weight), case.eps,
+                                                         orope), 128)
+    step = 1000
+    for b in range(0, tokens, step):
+        part = imrope_call(case, q[b:b + step], k[b:b + step], pos, inv, b)
+        assert torch.equal(part[0], full[0][b:b + step]) and torch.equal(part[1], full[1][b:b + step])
+
+
+def test_imrope_differs_from_plain_and_collapses():
+    case = W.imrope(tokens=64, seed_stream=8)
+    pos, inv = gpu(torch.from_numpy(case.positions)), gpu(torch.from_numpy(case.inv_freq))
+    q, k = gpu(case.q), gpu(case.k)
+    sect = imrope_call(case, q, k, pos, inv, 0)
+    plain = qkr.qk_norm_rope(q, k, gpu(case.q_weight), gpu(case.k_weight), case.eps,
+                             qkr.Rope("1d", 128, "neox", inv_freq=inv, positions=pos[0:1]))
+    assert (sect[0] - plain[0]).abs().max().item() > 0.1
+    # all pairs on e == plain over plane e
+    all_e = qkr.Rope("imrope", 128, "neox", inv_freq=inv, positions=pos, sections=(0, 0, 0, 64))
+    plain_e = qkr.Rope("1d", 128, "neox", inv_freq=inv, positions=pos[3:4].contiguous())
+    a = qkr.qk_norm_rope(q, k, gpu(case.q_weight), gpu(case.k_weight), case.eps, all_e)
+    b = qkr.qk_norm_rope(q, k, gpu(case.q_weight), gpu(case.k_weight), case.eps, plain_e)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# ViT setup + apply (grids [[1,64,64],[2,32,48],[1,28,28]], merge 2, 16 x 80)
+# ---------------------------------------------------------------------------
+
+def test_vit_setup_planes_and_sentinel():
+    case = W.vit()
+    n, half = case.n_tokens, case.half_rot
+    inv = [gpu(torch.from_numpy(a)) for a in (case.inv_t, case.inv_h, case.inv_w)]
+    cos = torch.full((3, n, half), float("nan"), device=DEV)
+    sin = torch.full((3, n, half), float("nan"), device=DEV)
+    qkr.mrope_cos_sin_setup(*inv, case.grid_thw, case.merge, out=(cos, sin))
+    rc, rs = oracle.vit_cos_sin(case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
+    gc, gs = cos.cpu().numpy(), sin.cpu().numpy()
+    written = ~np.isnan(rc)
+    assert np.array_equal(np.isnan(gc), ~written) and np.array_equal(np.isnan(gs), ~written)
+    assert_f32_close(gc[written], rc[written], "cos")
+    assert_f32_close(gs[written], rs[written], "sin")
+
+
+def test_vit_apply_chain():
+    """setup -> planes -> apply on the GPU against the oracle's own chain
+    (oracle planes, oracle apply); the apply never reads an unwritten column
+    (those are NaN)."""
+    case = W.vit()
+    n, half = case.n_tokens, case.half_rot
+    inv = [gpu(torch.from_numpy(a)) for a in (case.inv_t, case.inv_h, case.inv_w)]
+    cos = torch.full((3, n, half), float("nan"), device=DEV)
+    sin = torch.full((3, n, half), float("nan"), device=DEV)
+    qkr.mrope_cos_sin_setup(*inv, case.grid_thw, case.merge, out=(cos, sin))
+    secs = (case.inv_t.size, case.inv_h.size, case.inv_w.size, 0)
+    rope = qkr.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=cos, sin_planes=sin)
+    qo, ko = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+    rc, rs = oracle.vit_cos_sin(case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
+    orope = oracle.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=rc, sin_planes=rs)
+    rq = oracle.qk_norm_rope(W.as_f32(case.q), W.as_f32(case.q_weight), case.eps, orope)
+    rk = oracle.qk_norm_rope(W.as_f32(case.k), W.as_f32(case.k_weight), case.eps, orope)
+    assert not torch.isnan(qo.float()).any() and not torch.isnan(ko.float()).any()
+    assert_bf16_close(host(qo), rq, 2 * half, "neox", "vit q")
+    assert_bf16_close(host(ko), rk, 2 * half, "neox", "vit k")
+
+
+# ---------------------------------------------------------------------------
+# 64-bit addressing: a view more than 2^31 elements into a > 4 GiB buffer
+# ---------------------------------------------------------------------------
+
+def test_large_storage_offset():
+    case = W.tiny(tokens=16, heads=8, head_dim=128, dtype="bf16", seed_stream=21)
+    off = (1 << 31) + 4096                     # elements
+    total = off + 16 * 8 * 128 + 4096
+    buf = torch.empty(total, dtype=torch.bfloat16, device=DEV)
+    x = buf[off:off + 16 * 8 * 128].view(16, 8, 128)
+    x.copy_(gpu(case.q))
+    pos = np.arange(16, dtype=np.int32)[None] * 31
+    inv = W.inv_freq_ladder(1e4, 128)
+    rope = qkr.Rope("1d", 128, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    out = buf[off - 16 * 8 * 128 - 2048:off - 2048].view(16, 8, 128)
+    qkr.qk_norm_rope(x, None, gpu(case.q_weight), None, 1e-6, rope, q_out=out)
+    ref = oracle.qk_norm_rope(W.as_f32(case.q), W.as_f32(case.q_weight), 1e-6,
+                              oracle.Rope("1d", 128, "neox", inv_freq=inv, positions=pos))
+    assert_bf16_close(host(out), ref, 128)
+    del buf
+    torch.cuda.empty_cache()

@@ -1,0 +1,607 @@
+// C-ABI entry points of libqkrope: argument validation (pure host code, run
+// before any HIP call), translation of element strides into the byte strides
+// the kernels take, variant choice and launch on the caller's stream.
+//
+// Page names used in comments:
+//   [Ovis]   vllm-omni pull request "[Kernel][Ovis-Image] Fuse text/image QK
+//            RMSNorm + cat + RoPE into one Triton launch"
+//   [IMROPE] llama.cpp fork pull request "hrx: the multi-section rotation of
+//            Qwen3-VL runs on the device, not on the CPU"
+//   [ViT]    vLLM API page "vllm.model_executor.layers.rotary_embedding.
+//            mrope_vit_setup"
+#include "qkrope.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "qkr_internal.hpp"
+
+namespace {
+
+using namespace qkr;
+
+thread_local char g_error[512] = "";
+thread_local char g_variant[96] = "";
+
+// Test hook: forced variants (-1 / 0 = automatic).
+std::atomic<int> g_rms_kind{-1};
+std::atomic<int> g_rope_np{0};
+
+qkr_status fail(qkr_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof(g_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qkr_status ok()
+{
+    g_error[0] = '\0';
+    return QKR_OK;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+qkr_status hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess)
+        return fail(QKR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+qkr_status check_dtype(int32_t dtype, int& esize)
+{
+    if (dtype == QKR_F32) {
+        esize = 4;
+        return QKR_OK;
+    }
+    if (dtype == QKR_BF16) {
+        esize = 2;
+        return QKR_OK;
+    }
+    return fail(QKR_ERR_INVALID_ARGUMENT, "dtype %d is neither QKR_F32 nor QKR_BF16", dtype);
+}
+
+qkr_status check_eps(float eps)
+{
+    if (!std::isfinite(eps) || eps < 0.0f)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    return QKR_OK;
+}
+
+// Rows of head_dim elements move as 16-byte vectors.
+qkr_status check_head_dim(int32_t head_dim, int esize)
+{
+    if (head_dim <= 0 || head_dim > 256)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "head_dim %d outside [1, 256]", head_dim);
+    if ((head_dim * esize) % 16 != 0)
+        return fail(QKR_ERR_MISALIGNED, "head_dim %d is not a whole number of 16-byte vectors", head_dim);
+    return QKR_OK;
+}
+
+// A [batch, tokens, heads, head_dim] view that the kernels will touch.
+qkr_status check_view(const char* name, const qkr_view* v, int esize, int32_t batch, int64_t tokens,
+                      int32_t heads)
+{
+    if (batch == 0 || tokens == 0 || heads == 0)
+        return QKR_OK;
+    if (v == nullptr || v->ptr_dev == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "%s: null view or pointer", name);
+    if (!aligned(v->ptr_dev, 16))
+        return fail(QKR_ERR_MISALIGNED, "%s: pointer is not 16-byte aligned", name);
+    const int64_t st[3] = {v->stride_batch, v->stride_tok, v->stride_head};
+    const bool used[3] = {batch > 1, tokens > 1, heads > 1};
+    static const char* what[3] = {"stride_batch", "stride_tok", "stride_head"};
+    for (int i = 0; i < 3; ++i) {
+        if (!used[i])
+            continue;
+        if (st[i] < 0)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "%s: negative %s", name, what[i]);
+        if ((st[i] * esize) % 16 != 0)
+            return fail(QKR_ERR_MISALIGNED, "%s: %s %lld is not a multiple of 16 bytes", name, what[i],
+                        (long long)st[i]);
+    }
+    return QKR_OK;
+}
+
+qkr_status check_weight(const char* name, const void* w)
+{
+    if (w == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "%s: null weight", name);
+    if (!aligned(w, 16))
+        return fail(QKR_ERR_MISALIGNED, "%s: weight is not 16-byte aligned", name);
+    return QKR_OK;
+}
+
+// The one predicate for the rotation: what it refuses is exactly what no
+// kernel variant takes, and what it accepts fixes the variant ([IMROPE]: the
+// claim and the matcher share one predicate).  `tokens` is the number of
+// tokens the call indexes positions with.
+qkr_status check_rope(const qkr_rope* r, int32_t head_dim, int esize, int64_t tokens, RopeArgs& out,
+                      int32_t& pairing, int32_t& rotary_dim)
+{
+    std::memset(&out, 0, sizeof(out));
+    out.mode = kPosNone;
+    pairing = kNeox;
+    rotary_dim = 0;
+    if (r == nullptr || r->rotary_dim == 0)
+        return QKR_OK;
+    const int32_t R = r->rotary_dim;
+    if (R < 0 || R % 2 != 0 || R > head_dim)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "rotary_dim %d must be even and in [0, head_dim=%d]", R, head_dim);
+    if (r->pairing != QKR_PAIR_NEOX && r->pairing != QKR_PAIR_ADJACENT)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown pairing %d", r->pairing);
+    if (r->mode < QKR_POS_1D || r->mode > QKR_POS_PLANES)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown position mode %d", r->mode);
+    const int ve = 16 / esize;
+    if (r->pairing == QKR_PAIR_NEOX && (R / 2) % ve != 0)
+        return fail(QKR_ERR_UNSUPPORTED,
+                    "NeoX pairing needs rotary_dim/2 (%d) to be a multiple of %d elements (whole 16-byte "
+                    "vectors per half)", R / 2, ve);
+    if (r->token_base < 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "token_base %lld < 0", (long long)r->token_base);
+    const int32_t* s = r->sections;
+    const int32_t half = R / 2;
+    if (r->mode == QKR_POS_AXES || r->mode == QKR_POS_PLANES) {
+        if (s[0] < 0 || s[1] < 0 || s[2] < 0 || s[3] != 0 || s[0] + s[1] + s[2] != half)
+            return fail(QKR_ERR_INVALID_ARGUMENT,
+                        "axis sections (%d, %d, %d, %d) must be >= 0, end with 0 and sum to rotary_dim/2 = %d",
+                        s[0], s[1], s[2], s[3], half);
+    }
+    if (r->mode == QKR_POS_IMROPE) {
+        // [IMROPE] follow-up commit: claim only n_dims/2 <= sum <= n_dims, and
+        // refuse a sectioned rotation without sections rather than default.
+        const int64_t sum = (int64_t)s[0] + s[1] + s[2] + s[3];
+        if (s[0] < 0 || s[1] < 0 || s[2] < 0 || s[3] < 0 || sum < half || sum > R)
+            return fail(QKR_ERR_INVALID_ARGUMENT,
+                        "IMROPE sections (%d, %d, %d, %d) must be >= 0 with rotary_dim/2 <= sum <= rotary_dim",
+                        s[0], s[1], s[2], s[3]);
+    }
+    if (r->mode == QKR_POS_PLANES) {
+        if (r->cos_planes_dev == nullptr || r->sin_planes_dev == nullptr)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "PLANES mode needs cos and sin planes");
+        if (!aligned(r->cos_planes_dev, 4) || !aligned(r->sin_planes_dev, 4))
+            return fail(QKR_ERR_MISALIGNED, "cos/sin planes are not 4-byte aligned");
+        if (tokens > 0 && r->planes_tokens < r->token_base + tokens)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "planes hold %lld tokens, the call reads up to %lld",
+                        (long long)r->planes_tokens, (long long)(r->token_base + tokens));
+    } else {
+        if (r->inv_freq_dev == nullptr || r->positions_dev == nullptr)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "position mode %d needs inv_freq and positions", r->mode);
+        if (!aligned(r->inv_freq_dev, 4) || !aligned(r->positions_dev, 4))
+            return fail(QKR_ERR_MISALIGNED, "inv_freq/positions are not 4-byte aligned");
+        if (tokens > 0 && r->pos_stride < r->token_base + tokens)
+            return fail(QKR_ERR_INVALID_ARGUMENT,
+                        "position planes hold %lld tokens (pos_stride), the call reads up to %lld",
+                        (long long)r->pos_stride, (long long)(r->token_base + tokens));
+    }
+    out.mode = r->mode;
+    out.half = half;
+    for (int i = 0; i < 4; ++i)
+        out.sec[i] = s[i];
+    out.inv_freq = r->inv_freq_dev;
+    out.positions = r->positions_dev;
+    out.pos_stride = r->pos_stride;
+    out.token_base = r->token_base;
+    out.cos_planes = r->cos_planes_dev;
+    out.sin_planes = r->sin_planes_dev;
+    out.planes_tokens = r->planes_tokens;
+    pairing = r->pairing;
+    rotary_dim = R;
+    return QKR_OK;
+}
+
+void fill_in(TensorArgs& t, int s, const qkr_view* v, int esize)
+{
+    t.in[s] = v ? static_cast<const char*>(v->ptr_dev) : nullptr;
+    t.in_sb[s] = v ? v->stride_batch * esize : 0;
+    t.in_st[s] = v ? v->stride_tok * esize : 0;
+    t.in_sh[s] = v ? v->stride_head * esize : 0;
+}
+
+void fill_out(TensorArgs& t, const qkr_view* v, int esize)
+{
+    t.out = v ? static_cast<char*>(v->ptr_dev) : nullptr;
+    t.out_sb = v ? v->stride_batch * esize : 0;
+    t.out_st = v ? v->stride_tok * esize : 0;
+    t.out_sh = v ? v->stride_head * esize : 0;
+}
+
+qkr_status launch(NormRopeArgs& a, int32_t dtype, int32_t pairing, hipStream_t stream)
+{
+    (void)hipGetLastError();   // clear a stale error so the launch reports its own
+    const char* variant = "";
+    hipError_t e = launch_norm_rope(a, dtype, pairing, g_rope_np.load(), stream, &variant);
+    if (e != hipSuccess)
+        return fail(QKR_ERR_HIP, "norm_rope launch: %s", hipGetErrorString(e));
+    std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
+    return ok();
+}
+
+// Shared set-up of the ViT grid table; validates and returns the total.
+qkr_status check_grids(const int32_t* grid_thw, int32_t num_grids, int32_t merge, int64_t& total)
+{
+    if (grid_thw == nullptr || num_grids <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "grid_thw must hold at least one grid");
+    if (merge <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "spatial_merge %d must be >= 1", merge);
+    total = 0;
+    for (int32_t g = 0; g < num_grids; ++g) {
+        const int32_t t = grid_thw[3 * g], h = grid_thw[3 * g + 1], w = grid_thw[3 * g + 2];
+        if (t <= 0 || h <= 0 || w <= 0)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "grid %d (%d, %d, %d) must have t, h, w >= 1", g, t, h, w);
+        if (h % merge != 0 || w % merge != 0)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "grid %d: h %d and w %d must be multiples of spatial_merge %d",
+                        g, h, w, merge);
+        total += (int64_t)t * h * w;
+    }
+    return QKR_OK;
+}
+
+// Grid groups of at most kMaxGrids per launch; token offsets stay absolute.
+template <class F>
+hipError_t for_grid_groups(const int32_t* grid_thw, int32_t num_grids, int32_t merge, VitArgs base, F&& fn)
+{
+    int64_t start = 0;
+    for (int32_t g0 = 0; g0 < num_grids; g0 += kMaxGrids) {
+        const int32_t n = num_grids - g0 < kMaxGrids ? num_grids - g0 : kMaxGrids;
+        VitArgs a = base;
+        a.merge = merge;
+        a.num_grids = n;
+        a.tok_begin = start;
+        int64_t cu = start;
+        for (int32_t k = 0; k < n; ++k) {
+            const int32_t* g = grid_thw + 3 * (g0 + k);
+            a.cu[k] = cu;
+            a.hw[k][0] = g[1];
+            a.hw[k][1] = g[2];
+            cu += (int64_t)g[0] * g[1] * g[2];
+        }
+        a.cu[n] = cu;
+        a.tok_count = cu - start;
+        const hipError_t e = fn(a);
+        if (e != hipSuccess)
+            return e;
+        start = cu;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qkr_status_string(qkr_status status)
+{
+    switch (status) {
+    case QKR_OK: return "QKR_OK";
+    case QKR_ERR_INVALID_ARGUMENT: return "QKR_ERR_INVALID_ARGUMENT";
+    case QKR_ERR_UNSUPPORTED: return "QKR_ERR_UNSUPPORTED";
+    case QKR_ERR_MISALIGNED: return "QKR_ERR_MISALIGNED";
+    case QKR_ERR_HIP: return "QKR_ERR_HIP";
+    }
+    return "unknown qkr_status";
+}
+
+const char* qkr_last_error(void) { return g_error; }
+
+const char* qkr_last_variant(void) { return g_variant; }
+
+qkr_status qkr_set_variant_override(const char* name)
+{
+    if (name == nullptr) {
+        g_rms_kind = -1;
+        g_rope_np = 0;
+        return ok();
+    }
+    static const char* rms[3] = {"rms:rows", "rms:split", "rms:wide"};
+    for (int i = 0; i < 3; ++i)
+        if (std::strcmp(name, rms[i]) == 0) {
+            g_rms_kind = i;
+            return ok();
+        }
+    static const char* np[4] = {"rope:np1", "rope:np2", "rope:np3", "rope:np4"};
+    for (int i = 0; i < 4; ++i)
+        if (std::strcmp(name, np[i]) == 0) {
+            g_rope_np = i + 1;
+            return ok();
+        }
+    return fail(QKR_ERR_INVALID_ARGUMENT, "unknown variant '%s'", name);
+}
+
+qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, int64_t y_row_stride,
+                        const void* weight_dev, int64_t rows, int32_t width, float eps, int32_t dtype,
+                        qkr_stream_t stream)
+{
+    int esize = 0;
+    qkr_status st;
+    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)))
+        return st;
+    if (rows < 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "rows %lld < 0", (long long)rows);
+    if (width <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "width %d must be > 0", width);
+    if (((int64_t)width * esize) % 16 != 0)
+        return fail(QKR_ERR_MISALIGNED, "width %d is not a whole number of 16-byte vectors", width);
+    const int64_t nvec = (int64_t)width * esize / 16;
+    if (nvec > 16 * kThreads)
+        return fail(QKR_ERR_UNSUPPORTED, "width %d exceeds %d elements", width, 16 * kThreads * 16 / esize);
+    if (rows == 0)
+        return ok();
+    if (x_dev == nullptr || y_dev == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "null x or y");
+    if ((st = check_weight("weight", weight_dev)))
+        return st;
+    if (!aligned(x_dev, 16) || !aligned(y_dev, 16))
+        return fail(QKR_ERR_MISALIGNED, "x or y is not 16-byte aligned");
+    if (rows > 1) {
+        if (x_row_stride < width || y_row_stride < width)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "row strides must be >= width");
+        if ((x_row_stride * esize) % 16 != 0 || (y_row_stride * esize) % 16 != 0)
+            return fail(QKR_ERR_MISALIGNED, "row strides are not multiples of 16 bytes");
+    }
+    if (rows > (int64_t)1 << 33)
+        return fail(QKR_ERR_UNSUPPORTED, "rows %lld exceed the launch grid", (long long)rows);
+
+    RmsArgs a{};
+    a.x = static_cast<const char*>(x_dev);
+    a.y = static_cast<char*>(y_dev);
+    a.w = static_cast<const char*>(weight_dev);
+    a.x_stride = x_row_stride * esize;
+    a.y_stride = y_row_stride * esize;
+    a.rows = rows;
+    a.nvec = (int32_t)nvec;
+    a.eps = eps;
+    a.inv_width = 1.0f / (float)width;
+    (void)hipGetLastError();
+    const char* variant = "";
+    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), reinterpret_cast<hipStream_t>(stream), &variant);
+    if (e != hipSuccess)
+        return fail(QKR_ERR_HIP, "rms_norm launch: %s", hipGetErrorString(e));
+    std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
+    return ok();
+}
+
+qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int32_t dtype, float eps,
+                            const qkr_view* q, const qkr_view* q_out, int32_t q_heads, const void* q_weight_dev,
+                            const qkr_view* k, const qkr_view* k_out, int32_t k_heads, const void* k_weight_dev,
+                            const qkr_rope* rope, qkr_stream_t stream)
+{
+    int esize = 0;
+    qkr_status st;
+    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+        return st;
+    if (batch < 0 || tokens < 0 || q_heads < 0 || k_heads < 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "negative batch, tokens or heads");
+    if ((int64_t)q_heads + k_heads > (1 << 20))
+        return fail(QKR_ERR_UNSUPPORTED, "too many heads");
+    if ((st = check_view("q", q, esize, batch, tokens, q_heads)) ||
+        (st = check_view("q_out", q_out, esize, batch, tokens, q_heads)) ||
+        (st = check_view("k", k, esize, batch, tokens, k_heads)) ||
+        (st = check_view("k_out", k_out, esize, batch, tokens, k_heads)))
+        return st;
+    if (q_heads > 0 && (st = check_weight("q_weight", q_weight_dev)))
+        return st;
+    if (k_heads > 0 && (st = check_weight("k_weight", k_weight_dev)))
+        return st;
+    NormRopeArgs a{};
+    int32_t pairing = 0, rotary_dim = 0;
+    if ((st = check_rope(rope, head_dim, esize, tokens, a.rope, pairing, rotary_dim)))
+        return st;
+    if (batch == 0 || tokens == 0 || q_heads + k_heads == 0)
+        return ok();
+
+    fill_in(a.t[0], 0, q_heads ? q : nullptr, esize);
+    fill_out(a.t[0], q_heads ? q_out : nullptr, esize);
+    a.t[0].weight[0] = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
+    a.t[0].heads = q_heads;
+    fill_in(a.t[1], 0, k_heads ? k : nullptr, esize);
+    fill_out(a.t[1], k_heads ? k_out : nullptr, esize);
+    a.t[1].weight[0] = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
+    a.t[1].heads = k_heads;
+    a.t[2].heads = 0;
+    a.ntensors = 2;
+    a.rows_per_token = q_heads + k_heads;
+    a.rope_rows = q_heads + k_heads;
+    a.batch = batch;
+    a.tokens = tokens;
+    a.tokens0 = tokens;
+    a.head_dim = head_dim;
+    a.rotary_dim = rotary_dim;
+    a.eps = eps;
+    a.inv_d = 1.0f / (float)head_dim;
+    return launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream));
+}
+
+qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, float eps,
+                                  const qkr_stream* text, const qkr_stream* image, const qkr_view* q_out,
+                                  const qkr_view* k_out, const qkr_view* v_out, const qkr_rope* rope,
+                                  qkr_stream_t stream)
+{
+    int esize = 0;
+    qkr_status st;
+    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+        return st;
+    if (text == nullptr || image == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "null text or image stream");
+    if (batch < 0 || heads < 0 || text->tokens < 0 || image->tokens < 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "negative batch, heads or tokens");
+    if (heads > (1 << 18))
+        return fail(QKR_ERR_UNSUPPORTED, "too many heads");
+    const int64_t joint = text->tokens + image->tokens;
+    const qkr_stream* streams[2] = {text, image};
+    static const char* names[2][3] = {{"text.q", "text.k", "text.v"}, {"image.q", "image.k", "image.v"}};
+    for (int s = 0; s < 2; ++s) {
+        const qkr_stream* x = streams[s];
+        if ((st = check_view(names[s][0], &x->q, esize, batch, x->tokens, heads)) ||
+            (st = check_view(names[s][1], &x->k, esize, batch, x->tokens, heads)) ||
+            (st = check_view(names[s][2], &x->v, esize, batch, x->tokens, heads)))
+            return st;
+        if (x->tokens > 0 && heads > 0 &&
+            ((st = check_weight(s ? "image.q_weight" : "text.q_weight", x->q_weight_dev)) ||
+             (st = check_weight(s ? "image.k_weight" : "text.k_weight", x->k_weight_dev))))
+            return st;
+    }
+    if ((st = check_view("q_out", q_out, esize, batch, joint, heads)) ||
+        (st = check_view("k_out", k_out, esize, batch, joint, heads)) ||
+        (st = check_view("v_out", v_out, esize, batch, joint, heads)))
+        return st;
+    NormRopeArgs a{};
+    int32_t pairing = 0, rotary_dim = 0;
+    if ((st = check_rope(rope, head_dim, esize, joint, a.rope, pairing, rotary_dim)))
+        return st;
+    if (batch == 0 || joint == 0 || heads == 0)
+        return ok();
+
+    const qkr_view* outs[3] = {q_out, k_out, v_out};
+    for (int ti = 0; ti < 3; ++ti) {
+        for (int s = 0; s < 2; ++s) {
+            const qkr_stream* x = streams[s];
+            const qkr_view* v = ti == 0 ? &x->q : (ti == 1 ? &x->k : &x->v);
+            fill_in(a.t[ti], s, x->tokens > 0 ? v : nullptr, esize);
+            a.t[ti].weight[s] = ti == 2 || x->tokens == 0
+                                    ? nullptr
+                                    : static_cast<const char*>(ti == 0 ? x->q_weight_dev : x->k_weight_dev);
+        }
+        fill_out(a.t[ti], outs[ti], esize);
+        a.t[ti].heads = heads;
+    }
+    a.ntensors = 3;
+    a.rows_per_token = 3 * heads;
+    a.rope_rows = 2 * heads;
+    a.batch = batch;
+    a.tokens = joint;
+    a.tokens0 = text->tokens;
+    a.head_dim = head_dim;
+    a.rotary_dim = rotary_dim;
+    a.eps = eps;
+    a.inv_d = 1.0f / (float)head_dim;
+    return launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream));
+}
+
+qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t, const float* inv_freq_h_dev,
+                                   int32_t half_h, const float* inv_freq_w_dev, int32_t half_w,
+                                   const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
+                                   float* cos_out_dev, float* sin_out_dev, int64_t n_tokens, qkr_stream_t stream)
+{
+    if (half_t < 0 || half_h < 0 || half_w < 0 || half_t + half_h + half_w <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "axis halves (%d, %d, %d) must be >= 0 with a positive sum",
+                    half_t, half_h, half_w);
+    const float* inv[3] = {inv_freq_t_dev, inv_freq_h_dev, inv_freq_w_dev};
+    const int32_t half[3] = {half_t, half_h, half_w};
+    for (int i = 0; i < 3; ++i) {
+        if (half[i] > 0 && inv[i] == nullptr)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "axis %d has %d frequencies but a null inv_freq", i, half[i]);
+        if (!aligned(inv[i], 4))
+            return fail(QKR_ERR_MISALIGNED, "inv_freq of axis %d is not 4-byte aligned", i);
+    }
+    int64_t total = 0;
+    qkr_status st;
+    if ((st = check_grids(grid_thw, num_grids, spatial_merge, total)))
+        return st;
+    if (n_tokens != total)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "n_tokens %lld != sum of t*h*w = %lld", (long long)n_tokens,
+                    (long long)total);
+    if (cos_out_dev == nullptr || sin_out_dev == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "null cos or sin output");
+    if (!aligned(cos_out_dev, 4) || !aligned(sin_out_dev, 4))
+        return fail(QKR_ERR_MISALIGNED, "cos/sin outputs are not 4-byte aligned");
+
+    VitArgs base{};
+    for (int i = 0; i < 3; ++i) {
+        base.inv[i] = inv[i];
+        base.half[i] = half[i];
+    }
+    base.off[0] = 0;
+    base.off[1] = half_t;
+    base.off[2] = half_t + half_h;
+    base.half_rot = half_t + half_h + half_w;
+    base.cos_out = cos_out_dev;
+    base.sin_out = sin_out_dev;
+    base.n_tokens = n_tokens;
+    (void)hipGetLastError();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = for_grid_groups(grid_thw, num_grids, spatial_merge, base,
+                                         [&](const VitArgs& a) { return launch_vit_setup(a, s); });
+    if (e == hipSuccess)
+        std::snprintf(g_variant, sizeof(g_variant), "vit_setup");
+    return hip_status(e, "mrope_cos_sin_setup launch");
+}
+
+qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* out_dev, qkr_stream_t stream)
+{
+    if (rope == nullptr || n_pairs < 0 || (n_pairs > 0 && out_dev == nullptr))
+        return fail(QKR_ERR_INVALID_ARGUMENT, "debug_axis_map: null rope/output or negative n_pairs");
+    if (rope->mode < QKR_POS_1D || rope->mode > QKR_POS_PLANES)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown position mode %d", rope->mode);
+    if (rope->mode == QKR_POS_IMROPE && rope->sections[0] + rope->sections[1] + rope->sections[2] +
+                                                rope->sections[3] <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "IMROPE needs a positive section sum");
+    (void)hipGetLastError();
+    return hip_status(launch_debug_axis_map(rope->mode, rope->sections, n_pairs, out_dev,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                      "debug_axis_map launch");
+}
+
+qkr_status qkr_axis_map_host(const qkr_rope* rope, int32_t n_pairs, int32_t* out_host)
+{
+    if (rope == nullptr || n_pairs < 0 || (n_pairs > 0 && out_host == nullptr))
+        return fail(QKR_ERR_INVALID_ARGUMENT, "axis_map_host: null rope/output or negative n_pairs");
+    if (rope->mode < QKR_POS_1D || rope->mode > QKR_POS_PLANES)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown position mode %d", rope->mode);
+    if (rope->mode == QKR_POS_IMROPE && rope->sections[0] + rope->sections[1] + rope->sections[2] +
+                                                rope->sections[3] <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "IMROPE needs a positive section sum");
+    for (int32_t p = 0; p < n_pairs; ++p)
+        out_host[p] = pair_axis(rope->mode, rope->sections, p);
+    return ok();
+}
+
+qkr_status qkr_debug_vit_positions(const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
+                                   int32_t* out_dev, int64_t n_tokens, qkr_stream_t stream)
+{
+    int64_t total = 0;
+    qkr_status st;
+    if ((st = check_grids(grid_thw, num_grids, spatial_merge, total)))
+        return st;
+    if (n_tokens != total || out_dev == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "n_tokens must equal sum t*h*w and out must be non-null");
+    VitArgs base{};
+    base.n_tokens = n_tokens;
+    (void)hipGetLastError();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return hip_status(for_grid_groups(grid_thw, num_grids, spatial_merge, base,
+                                      [&](const VitArgs& a) { return launch_debug_vit_positions(a, out_dev, s); }),
+                      "debug_vit_positions launch");
+}
+
+qkr_status qkr_vit_positions_host(const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
+                                  int32_t* out_host, int64_t n_tokens)
+{
+    int64_t total = 0;
+    qkr_status st;
+    if ((st = check_grids(grid_thw, num_grids, spatial_merge, total)))
+        return st;
+    if (n_tokens != total || out_host == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "n_tokens must equal sum t*h*w and out must be non-null");
+    std::vector<int64_t> cu(num_grids + 1, 0);
+    std::vector<int32_t> hw(2 * (size_t)num_grids);
+    for (int32_t g = 0; g < num_grids; ++g) {
+        cu[g + 1] = cu[g] + (int64_t)grid_thw[3 * g] * grid_thw[3 * g + 1] * grid_thw[3 * g + 2];
+        hw[2 * g] = grid_thw[3 * g + 1];
+        hw[2 * g + 1] = grid_thw[3 * g + 2];
+    }
+    const int32_t(*hwp)[2] = reinterpret_cast<const int32_t(*)[2]>(hw.data());
+    for (int64_t n = 0; n < n_tokens; ++n)
+        vit_position(cu.data(), hwp, num_grids, spatial_merge, n, &out_host[n], &out_host[n_tokens + n],
+                     &out_host[2 * n_tokens + n]);
+    return ok();
+}
+
+}  // extern "C"

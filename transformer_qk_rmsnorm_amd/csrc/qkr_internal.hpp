@@ -1,0 +1,153 @@
+// Internal interface between the C-ABI host layer (qkr_api.cpp) and the
+// gfx950 kernels (qkr_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkr {
+
+constexpr int kMaxGrids = 64;     // ViT grids per launch (metadata rides in kernel arguments)
+constexpr int kThreads = 256;     // threads per workgroup of the row kernels (4 waves)
+
+enum PosMode : int32_t { kPos1D = 0, kPosAxes = 1, kPosImrope = 2, kPosPlanes = 3, kPosNone = 4 };
+enum Pairing : int32_t { kNeox = 0, kAdjacent = 1 };
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
+
+// Rotation parameters as the kernels read them.
+struct RopeArgs {
+    int32_t mode;        // PosMode
+    int32_t half;        // R / 2
+    int32_t sec[4];      // raw sections (AXES/PLANES: pairs per axis; IMROPE: s0..s3)
+    const float* inv_freq;
+    const int32_t* positions;
+    int64_t pos_stride;
+    int64_t token_base;
+    const float* cos_planes;
+    const float* sin_planes;
+    int64_t planes_tokens;
+};
+
+// One of Q, K, V.  Input views exist per stream (stream 1 only for the joint
+// op); strides are in bytes.  weight == nullptr marks a copied tensor (V).
+struct TensorArgs {
+    const char* in[2];
+    int64_t in_sb[2], in_st[2], in_sh[2];
+    const char* weight[2];
+    char* out;
+    int64_t out_sb, out_st, out_sh;
+    int32_t heads;
+};
+
+struct NormRopeArgs {
+    TensorArgs t[3];
+    int32_t ntensors;
+    int32_t rows_per_token;     // sum of heads over the tensors
+    int32_t rope_rows;          // rows [0, rope_rows) are normalised (Q, K); the rest copied
+    int32_t batch;
+    int64_t tokens;             // tokens per batch (joint count for the joint op)
+    int64_t tokens0;            // tokens of stream 0; tokens at or past it belong to stream 1
+    int32_t head_dim;
+    int32_t rotary_dim;
+    int32_t blocks_per_token;   // tiles per (batch, token)
+    float eps;
+    float inv_d;                // 1 / head_dim
+    RopeArgs rope;
+};
+
+struct RmsArgs {
+    const char* x;
+    char* y;
+    const char* w;
+    int64_t x_stride;           // bytes
+    int64_t y_stride;           // bytes
+    int64_t rows;
+    int32_t nvec;               // 16-byte vectors per row
+    int32_t splits;             // workgroups per row (split variant)
+    int32_t split_len;          // vectors stored by one split
+    float eps;
+    float inv_width;
+};
+
+struct VitArgs {
+    const float* inv[3];
+    float* cos_out;
+    float* sin_out;
+    int64_t n_tokens;           // tokens in the whole output planes
+    int64_t tok_begin;          // first token this launch covers
+    int64_t tok_count;          // tokens this launch covers
+    int32_t half[3];
+    int32_t off[3];
+    int32_t half_rot;
+    int32_t merge;
+    int32_t num_grids;          // grids in this launch
+    int64_t cu[kMaxGrids + 1];  // token offsets of this launch's grids (absolute)
+    int32_t hw[kMaxGrids][2];   // h, w of each grid
+};
+
+// Axis of pair p (0 t, 1 h, 2 w, 3 e).  Host and device share this one
+// definition so the host can be checked without a GPU.
+__host__ __device__ inline int32_t pair_axis(int32_t mode, const int32_t* sec, int32_t p)
+{
+    if (mode == kPosImrope) {
+        // interleaved multi-section sector rule
+        const int32_t sect_dims = sec[0] + sec[1] + sec[2] + sec[3];
+        const int32_t sector = p % sect_dims;
+        const int32_t m3 = sector % 3;
+        if (m3 == 1 && sector < 3 * sec[1]) return 1;
+        if (m3 == 2 && sector < 3 * sec[2]) return 2;
+        if (m3 == 0 && sector < 3 * sec[0]) return 0;
+        return 3;
+    }
+    if (mode == kPosAxes || mode == kPosPlanes) {
+        // contiguous runs: [0, s0) t, [s0, s0+s1) h, the rest w
+        if (p < sec[0]) return 0;
+        if (p < sec[0] + sec[1]) return 1;
+        return 2;
+    }
+    return 0;
+}
+
+// (t, h, w) of ViT token `tok`: its grid is the last one whose first token
+// it has reached (grids are non-empty, so this is the number of grid ends
+// reached), then frame, spatial-merge block and cell inside the block.  The
+// grid is picked by a select loop, not an index, so the device build never
+// indexes kernel arguments with a per-lane value.
+__host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*hw)[2], int32_t num_grids,
+                                             int32_t merge, int64_t tok, int32_t* tpos, int32_t* hpos,
+                                             int32_t* wpos)
+{
+    int64_t start = cu[0], h = hw[0][0], w = hw[0][1];
+    for (int32_t k = 1; k < num_grids; ++k) {
+        const bool in_k = tok >= cu[k];
+        start = in_k ? cu[k] : start;
+        h = in_k ? hw[k][0] : h;
+        w = in_k ? hw[k][1] : w;
+    }
+    const int64_t local = tok - start;
+    const int64_t area = h * w;
+    const int64_t rem = local % area;
+    const int64_t mw = (int64_t)merge * w;
+    const int64_t bh = rem / mw;
+    const int64_t r = rem - bh * mw;
+    const int64_t mm = (int64_t)merge * merge;
+    const int64_t bw = r / mm;
+    const int64_t r2 = r - bw * mm;
+    *tpos = (int32_t)(local / area);
+    *hpos = (int32_t)(bh * merge + r2 / merge);
+    *wpos = (int32_t)(bw * merge + r2 % merge);
+}
+
+// Kernel launchers (qkr_kernels.hip).  Each returns the variant name it
+// launched through *variant; launch errors surface through hipGetLastError.
+// norm_rope: np = passes (row groups) per wave; 0 = automatic.
+hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, int np,
+                            hipStream_t stream, const char** variant);
+// rms: kind 0 rows, 1 split, 2 wide; -1 = automatic.
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, hipStream_t stream, const char** variant);
+hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream);
+hipError_t launch_debug_axis_map(int32_t mode, const int32_t* sec, int32_t n_pairs, int32_t* out,
+                                 hipStream_t stream);
+hipError_t launch_debug_vit_positions(const VitArgs& a, int32_t* out, hipStream_t stream);
+
+}  // namespace qkr

@@ -1,0 +1,694 @@
+// gfx950 kernels: per-head QK RMSNorm + RoPE, plain row RMSNorm, ViT cos/sin
+// setup.  All of them are HBM-bound streams: rows move as 128-bit vectors,
+// reductions stay inside a wavefront (DPP), cos/sin are computed in registers
+// once per (token, pair) and shared by every head of the token.  No LDS tree,
+// no atomics, no MFMA (there is no dense contraction in this path).
+//
+// Page names used in comments:
+//   [Ovis]   vllm-omni pull request "[Kernel][Ovis-Image] Fuse text/image QK
+//            RMSNorm + cat + RoPE into one Triton launch"
+//   [Vulkan] vllm.cpp pull request "perf(vulkan): decode RmsNorm ran on ONE
+//            workgroup -- 7.85 -> 1.59 ms/token"
+//   [IMROPE] llama.cpp fork pull request "hrx: the multi-section rotation of
+//            Qwen3-VL runs on the device, not on the CPU"
+//   [ViT]    vLLM API page "vllm.model_executor.layers.rotary_embedding.
+//            mrope_vit_setup"
+//   [VecRMS] vLLM pull request "Vectorize RMS norm variance using
+//            vectorize_read_with_alignment"
+#include "qkr_internal.hpp"
+
+namespace qkr {
+namespace {
+
+constexpr int kWaves = kThreads / 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Element formats.  A 16-byte vector holds VE elements.
+// ---------------------------------------------------------------------------
+struct F32 {
+    static constexpr int VE = 4;
+    __device__ __forceinline__ static void unpack(const uint4& v, float* x)
+    {
+        x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+        x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float* x)
+    {
+        return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                          __float_as_uint(x[2]), __float_as_uint(x[3]));
+    }
+    // fp32 outputs keep the normalised value unrounded.
+    __device__ __forceinline__ static void round_trip(float*) {}
+};
+
+struct BF16 {
+    static constexpr int VE = 8;
+    __device__ __forceinline__ static void unpack(const uint4& v, float* x)
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    // Round to nearest even (v_cvt_pk_bf16_f32), two values per instruction.
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi)
+    {
+        const float2_t f = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    }
+    __device__ __forceinline__ static uint4 pack(const float* x)
+    {
+        return make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+    }
+    // Contract rounding: the normalised value is rounded to bf16 before the
+    // rotation ([Ovis] kernel review: one documented rounding contract).
+    __device__ __forceinline__ static void round_trip(float* x)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = pack2(x[2 * i], x[2 * i + 1]);
+            x[2 * i] = __uint_as_float(w << 16);
+            x[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+    }
+};
+
+__device__ __forceinline__ uint4 load16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store16(char* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions without LDS.  DPP moves inside rows of 16 lanes:
+// quad_perm xor 1 and xor 2, then row_half_mirror (lane i <- 7 - i within 8
+// lanes) and row_mirror (lane i <- 15 - i within 16 lanes); each step adds a
+// disjoint partner group, so after log2(L) steps every lane of an L-lane
+// group holds the group's sum.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+    if constexpr (L >= 16) v += dpp_f32<0x140>(v); // row_mirror
+    if constexpr (L >= 32) v += __shfl_xor(v, 16);
+    if constexpr (L >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Whole-wave sum, returned wave-uniform: 16-lane DPP sums, then the four
+// row totals read with v_readlane.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    const int iv = __float_as_int(group_sum<16>(v));
+    return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
+}
+
+__device__ __forceinline__ float bperm(int src_lane, float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+// ---------------------------------------------------------------------------
+// cos/sin of pair p at absolute token t (token_base already added).
+// The angle is the fp32 product of the fp32 position and inv_freq[p]
+// ([ViT] setup kernel); sincosf is the accurate device-library routine
+// (argument reduction good far past the 8191 rad these workloads reach).
+// ---------------------------------------------------------------------------
+template <bool PLANES>
+__device__ __forceinline__ void pair_cos_sin(const RopeArgs& r, int64_t t, int32_t p, float& c, float& s)
+{
+    const int32_t axis = pair_axis(r.mode, r.sec, p);
+    if constexpr (PLANES) {
+        const int64_t idx = ((int64_t)axis * r.planes_tokens + t) * r.half + p;
+        c = r.cos_planes[idx];
+        s = r.sin_planes[idx];
+    } else {
+        const int32_t pos = r.positions[(int64_t)axis * r.pos_stride + t];
+        const float theta = (float)pos * r.inv_freq[p];
+        sincosf(theta, &s, &c);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-(token, head) RMSNorm + RoPE.
+//
+// Work unit (tile): one wavefront takes NP passes over RPP = 64 / LPR rows of
+// one token; LPR lanes share a row and every lane owns two 16-byte vectors of
+// it.  With the NeoX pairing a lane owns vectors j and j + R/(2 VE), so every
+// rotated pair (p, p + R/2) is lane-local; with the adjacent pairing the pairs
+// sit inside one vector.  All loads of a tile are issued before the first use,
+// the token's cos/sin are computed once (lane i: pair i) and handed to the
+// lanes that need them with ds_bpermute, then each row is reduced over its LPR
+// lanes with DPP, normalised, rounded per the contract, rotated and stored.
+//
+// ROPE: 0 norm only, 1 positions + inv_freq (1D / AXES / IMROPE chosen at run
+// time), 2 cos/sin planes.
+// ---------------------------------------------------------------------------
+template <class E, int LPR, int NP, int ROPE, int PAIRING>
+__global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs a)
+{
+    constexpr int VE = E::VE;
+    constexpr int RPP = 64 / LPR;
+    constexpr int RPW = RPP * NP;
+    constexpr bool ROT = ROPE != 0;
+
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t ntiles = (int64_t)a.batch * a.tokens * a.blocks_per_token;
+    if (tile >= ntiles)
+        return;   // wave-uniform
+    const int32_t blk = (int32_t)(tile % a.blocks_per_token);
+    const int64_t bt = tile / a.blocks_per_token;
+    const int64_t tok = bt % a.tokens;
+    const int64_t b = bt / a.tokens;
+    const int s = tok >= a.tokens0 ? 1 : 0;
+    const int64_t ltok = s ? tok - a.tokens0 : tok;
+
+    const int g = lane / LPR;
+    const int j = lane % LPR;
+    const int nv = a.head_dim / VE;
+
+    // The two vectors this lane owns in every row.
+    int v0, v1;
+    bool rot_lane = false;
+    if (PAIRING == kNeox && ROT) {
+        const int nr = a.rotary_dim / (2 * VE);   // vector pairs that rotate
+        if (j < nr) {
+            v0 = j;
+            v1 = j + nr;
+            rot_lane = true;
+        } else {                                  // pass-through vectors past R
+            v0 = 2 * nr + 2 * (j - nr);
+            v1 = v0 + 1;
+        }
+    } else {
+        const int hv = (nv + 1) >> 1;
+        v0 = j < hv ? j : nv;
+        v1 = j < hv ? j + hv : nv;
+    }
+    const bool own0 = v0 < nv, own1 = v1 < nv;
+    const int64_t off0 = (int64_t)v0 * 16, off1 = (int64_t)v1 * 16;
+
+    // Row r of the token -> (tensor, head).
+    auto locate = [&](int r, int& ti, int& h) {
+        const int h0 = a.t[0].heads, h1 = a.t[1].heads;
+        ti = r < h0 ? 0 : (r < h0 + h1 ? 1 : 2);
+        h = r - (ti == 0 ? 0 : (ti == 1 ? h0 : h0 + h1));
+    };
+    auto in_row = [&](int ti, int h) -> const char* {
+        const TensorArgs& t0 = a.t[0];
+        const TensorArgs& t1 = a.t[1];
+        const TensorArgs& t2 = a.t[2];
+        const char* base = ti == 0 ? t0.in[s] : (ti == 1 ? t1.in[s] : t2.in[s]);
+        const int64_t sb = ti == 0 ? t0.in_sb[s] : (ti == 1 ? t1.in_sb[s] : t2.in_sb[s]);
+        const int64_t st = ti == 0 ? t0.in_st[s] : (ti == 1 ? t1.in_st[s] : t2.in_st[s]);
+        const int64_t sh = ti == 0 ? t0.in_sh[s] : (ti == 1 ? t1.in_sh[s] : t2.in_sh[s]);
+        return base + b * sb + ltok * st + (int64_t)h * sh;
+    };
+    auto out_row = [&](int ti, int h) -> char* {
+        const TensorArgs& t0 = a.t[0];
+        const TensorArgs& t1 = a.t[1];
+        const TensorArgs& t2 = a.t[2];
+        char* base = ti == 0 ? t0.out : (ti == 1 ? t1.out : t2.out);
+        const int64_t sb = ti == 0 ? t0.out_sb : (ti == 1 ? t1.out_sb : t2.out_sb);
+        const int64_t st = ti == 0 ? t0.out_st : (ti == 1 ? t1.out_st : t2.out_st);
+        const int64_t sh = ti == 0 ? t0.out_sh : (ti == 1 ? t1.out_sh : t2.out_sh);
+        return base + b * sb + tok * st + (int64_t)h * sh;
+    };
+
+    // 1) Issue every load of the tile.
+    uint4 d[NP][2];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int r = blk * RPW + p * RPP + g;
+        d[p][0] = make_uint4(0, 0, 0, 0);
+        d[p][1] = make_uint4(0, 0, 0, 0);
+        if (r < a.rows_per_token) {
+            int ti, h;
+            locate(r, ti, h);
+            const char* row = in_row(ti, h);
+            if (own0) d[p][0] = load16(row + off0);
+            if (own1) d[p][1] = load16(row + off1);
+        }
+    }
+    // Weights of Q and K for this stream (tiny, cached).
+    uint4 wq0 = make_uint4(0, 0, 0, 0), wq1 = wq0, wk0 = wq0, wk1 = wq0;
+    const bool tile_norms = blk * RPW < a.rope_rows;   // wave-uniform
+    if (tile_norms) {
+        const char* wq = a.t[0].weight[s];
+        const char* wk = a.t[1].weight[s];
+        if (wq != nullptr) {
+            if (own0) wq0 = load16(wq + off0);
+            if (own1) wq1 = load16(wq + off1);
+        }
+        if (wk != nullptr) {
+            if (own0) wk0 = load16(wk + off0);
+            if (own1) wk1 = load16(wk + off1);
+        }
+    }
+
+    // 2) cos/sin of the lane's VE pairs, computed once per token.
+    float cs_c[VE], cs_s[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        cs_c[e] = 1.0f;
+        cs_s[e] = 0.0f;
+    }
+    if constexpr (ROT) {
+        if (tile_norms) {
+            const RopeArgs& rp = a.rope;
+            const int64_t tabs = rp.token_base + tok;
+            const int half = rp.half;
+            float c0, s0, c1 = 1.0f, s1 = 0.0f;
+            pair_cos_sin<ROPE == 2>(rp, tabs, lane < half ? lane : half - 1, c0, s0);
+            const bool wide = half > 64;   // wave-uniform
+            if (wide)
+                pair_cos_sin<ROPE == 2>(rp, tabs, lane + 64 < half ? lane + 64 : half - 1, c1, s1);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                int p;
+                if constexpr (PAIRING == kNeox)
+                    p = j * VE + e;
+                else
+                    p = (e < VE / 2 ? v0 : v1) * (VE / 2) + (e % (VE / 2));
+                p = p < half ? p : half - 1;
+                const int src = p & 63;
+                float c = bperm(src, c0), sn = bperm(src, s0);
+                if (wide) {
+                    const float c_hi = bperm(src, c1), s_hi = bperm(src, s1);
+                    c = p >= 64 ? c_hi : c;
+                    sn = p >= 64 ? s_hi : sn;
+                }
+                cs_c[e] = c;
+                cs_s[e] = sn;
+            }
+        }
+    }
+
+    // 3) Row sums of squares; every lane takes part in every DPP step.
+    float ssq[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        float x0[VE], x1[VE];
+        E::unpack(d[p][0], x0);
+        E::unpack(d[p][1], x1);
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+            ss += x0[e] * x0[e] + x1[e] * x1[e];
+        ssq[p] = group_sum<LPR>(ss);
+    }
+
+    // 4) Per row: normalise, round, rotate, store.
+    const float eps = a.eps, inv_d = a.inv_d;
+    const int half = a.rope.half;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int r = blk * RPW + p * RPP + g;
+        if (r >= a.rows_per_token)
+            continue;
+        float x0[VE], x1[VE];
+        E::unpack(d[p][0], x0);
+        E::unpack(d[p][1], x1);
+        int ti, h;
+        locate(r, ti, h);
+        char* orow = out_row(ti, h);
+        if (r >= a.rope_rows) {   // routed tensor (V): bit copy
+            if (own0) store16(orow + off0, d[p][0]);
+            if (own1) store16(orow + off1, d[p][1]);
+            continue;
+        }
+        const float rrms = rsqrtf(ssq[p] * inv_d + eps);
+        float w0[VE], w1[VE];
+        E::unpack(ti == 0 ? wq0 : wk0, w0);
+        E::unpack(ti == 0 ? wq1 : wk1, w1);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            x0[e] = x0[e] * rrms * w0[e];
+            x1[e] = x1[e] * rrms * w1[e];
+        }
+        E::round_trip(x0);
+        E::round_trip(x1);
+        if constexpr (ROT) {
+            if constexpr (PAIRING == kNeox) {
+                if (rot_lane) {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) {
+                        const float xa = x0[e], xb = x1[e];
+                        x0[e] = xa * cs_c[e] - xb * cs_s[e];
+                        x1[e] = xb * cs_c[e] + xa * cs_s[e];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < VE / 2; ++k) {
+                    if (v0 * (VE / 2) + k < half) {
+                        const float xa = x0[2 * k], xb = x0[2 * k + 1];
+                        x0[2 * k] = xa * cs_c[k] - xb * cs_s[k];
+                        x0[2 * k + 1] = xb * cs_c[k] + xa * cs_s[k];
+                    }
+                    if (v1 * (VE / 2) + k < half) {
+                        const float xa = x1[2 * k], xb = x1[2 * k + 1];
+                        x1[2 * k] = xa * cs_c[VE / 2 + k] - xb * cs_s[VE / 2 + k];
+                        x1[2 * k + 1] = xb * cs_c[VE / 2 + k] + xa * cs_s[VE / 2 + k];
+                    }
+                }
+            }
+        }
+        if (own0) store16(orow + off0, E::pack(x0));
+        if (own1) store16(orow + off1, E::pack(x1));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Plain row RMSNorm.
+//   KIND 0 rows : one wavefront per row, 4 rows per workgroup.
+//   KIND 1 split: `splits` wavefronts per row, each on its own workgroup (so
+//                 on different compute units); each reads the whole row for
+//                 the sum of squares (the repeats come from L2) and writes
+//                 only its slice: one launch, no atomics, no cross-workgroup
+//                 hand-off.  For the few-row decode case ([Vulkan]: one row
+//                 on one workgroup leaves the GPU idle).
+//   KIND 2 wide : one workgroup of 4 wavefronts per row, one LDS exchange.
+// Every lane holds VPL 16-byte vectors of the row, all loaded up front
+// ([VecRMS]: 16-byte vectorized reads of the row).
+// ---------------------------------------------------------------------------
+template <class E, int VPL, int KIND>
+__global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
+{
+    constexpr int VE = E::VE;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int64_t row;
+    int split = 0;
+    int first, step;   // vector index of the lane's slot 0, distance between slots
+    if constexpr (KIND == 0) {
+        row = (int64_t)blockIdx.x * kWaves + wave;
+        first = lane;
+        step = 64;
+    } else if constexpr (KIND == 1) {
+        const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
+        row = item / a.splits;
+        split = (int)(item % a.splits);
+        first = lane;
+        step = 64;
+    } else {
+        row = blockIdx.x;
+        first = threadIdx.x;
+        step = kThreads;
+    }
+    if (row >= a.rows)
+        return;   // wave-uniform (workgroup-uniform for KIND 2)
+
+    const char* x = a.x + row * a.x_stride;
+    uint4 d[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int v = first + k * step;
+        d[k] = v < a.nvec ? load16(x + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        float xv[VE];
+        E::unpack(d[k], xv);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+            ss += xv[e] * xv[e];
+    }
+    ss = wave_sum(ss);
+    if constexpr (KIND == 2) {
+        __shared__ float part[kWaves];
+        if (lane == 0)
+            part[wave] = ss;
+        __syncthreads();
+        ss = part[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            ss += part[w];
+    }
+    const float rrms = rsqrtf(ss * a.inv_width + a.eps);
+
+    int lo = 0, hi = a.nvec;
+    if constexpr (KIND == 1) {
+        lo = split * a.split_len;
+        hi = min(a.nvec, lo + a.split_len);
+    }
+    char* y = a.y + row * a.y_stride;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int v = first + k * step;
+        if (v >= lo && v < hi) {
+            float xv[VE], wv[VE];
+            E::unpack(d[k], xv);
+            E::unpack(load16(a.w + (int64_t)v * 16), wv);
+#pragma unroll
+            for (int e = 0; e < VE; ++e)
+                xv[e] = xv[e] * rrms * wv[e];
+            store16(y + (int64_t)v * 16, E::pack(xv));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ViT cos/sin planes ([ViT] setup kernel): one thread per (token, column).
+// Column c belongs to axis a (t, h, w contiguous); plane a receives
+// cos/sin(fl32(pos_a) * inv_a[c - off_a]) at [a][token][c].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void vit_setup_kernel(const VitArgs a)
+{
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= a.tok_count * a.half_rot)
+        return;
+    const int64_t tok = a.tok_begin + idx / a.half_rot;
+    const int32_t col = (int32_t)(idx % a.half_rot);
+    int32_t pos[3];
+    vit_position(a.cu, a.hw, a.num_grids, a.merge, tok, &pos[0], &pos[1], &pos[2]);
+    const int axis = col < a.off[1] ? 0 : (col < a.off[2] ? 1 : 2);
+    const float* inv = axis == 0 ? a.inv[0] : (axis == 1 ? a.inv[1] : a.inv[2]);
+    const int32_t off = axis == 0 ? a.off[0] : (axis == 1 ? a.off[1] : a.off[2]);
+    const int32_t p = axis == 0 ? pos[0] : (axis == 1 ? pos[1] : pos[2]);
+    const float theta = (float)p * inv[col - off];
+    float s, c;
+    sincosf(theta, &s, &c);
+    const int64_t o = ((int64_t)axis * a.n_tokens + tok) * a.half_rot + col;
+    a.cos_out[o] = c;
+    a.sin_out[o] = s;
+}
+
+__global__ void debug_axis_kernel(int32_t mode, int32_t s0, int32_t s1, int32_t s2, int32_t s3,
+                                  int32_t n_pairs, int32_t* out)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n_pairs)
+        return;
+    const int32_t sec[4] = {s0, s1, s2, s3};
+    out[p] = pair_axis(mode, sec, p);
+}
+
+__global__ __launch_bounds__(kThreads) void debug_vit_kernel(const VitArgs a, int32_t* out)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= a.tok_count)
+        return;
+    const int64_t tok = a.tok_begin + i;
+    int32_t t, h, w;
+    vit_position(a.cu, a.hw, a.num_grids, a.merge, tok, &t, &h, &w);
+    out[tok] = t;
+    out[a.n_tokens + tok] = h;
+    out[2 * a.n_tokens + tok] = w;
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch tables
+// ---------------------------------------------------------------------------
+using NormRopeFn = void (*)(NormRopeArgs);
+
+template <class E, int LPR, int ROPE, int PAIRING>
+NormRopeFn pick_np(int np)
+{
+    switch (np) {
+    case 1: return norm_rope_kernel<E, LPR, 1, ROPE, PAIRING>;
+    case 2: return norm_rope_kernel<E, LPR, 2, ROPE, PAIRING>;
+    case 3: return norm_rope_kernel<E, LPR, 3, ROPE, PAIRING>;
+    default: return norm_rope_kernel<E, LPR, 4, ROPE, PAIRING>;
+    }
+}
+
+template <class E, int LPR, int ROPE>
+NormRopeFn pick_pairing(int pairing, int np)
+{
+    return pairing == kNeox ? pick_np<E, LPR, ROPE, kNeox>(np) : pick_np<E, LPR, ROPE, kAdjacent>(np);
+}
+
+template <class E, int LPR>
+NormRopeFn pick_rope(int rope, int pairing, int np)
+{
+    switch (rope) {
+    case 0: return pick_pairing<E, LPR, 0>(pairing, np);
+    case 1: return pick_pairing<E, LPR, 1>(pairing, np);
+    default: return pick_pairing<E, LPR, 2>(pairing, np);
+    }
+}
+
+template <class E>
+NormRopeFn pick_lpr(int lpr, int rope, int pairing, int np)
+{
+    switch (lpr) {
+    case 1: return pick_rope<E, 1>(rope, pairing, np);
+    case 2: return pick_rope<E, 2>(rope, pairing, np);
+    case 4: return pick_rope<E, 4>(rope, pairing, np);
+    case 8: return pick_rope<E, 8>(rope, pairing, np);
+    case 16: return pick_rope<E, 16>(rope, pairing, np);
+    default: return pick_rope<E, 32>(rope, pairing, np);
+    }
+}
+
+using RmsFn = void (*)(RmsArgs);
+
+template <class E, int KIND>
+RmsFn pick_vpl(int vpl)
+{
+    switch (vpl) {
+    case 1: return rms_kernel<E, 1, KIND>;
+    case 2: return rms_kernel<E, 2, KIND>;
+    case 3: return rms_kernel<E, 3, KIND>;
+    case 4: return rms_kernel<E, 4, KIND>;
+    case 5: return rms_kernel<E, 5, KIND>;
+    case 6: return rms_kernel<E, 6, KIND>;
+    case 8: return rms_kernel<E, 8, KIND>;
+    case 10: return rms_kernel<E, 10, KIND>;
+    case 12: return rms_kernel<E, 12, KIND>;
+    default: return rms_kernel<E, 16, KIND>;
+    }
+}
+
+int round_vpl(int need)
+{
+    static const int sizes[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
+    for (int s : sizes)
+        if (need <= s)
+            return s;
+    return -1;
+}
+
+thread_local char g_variant[96];
+
+}  // namespace
+
+hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, int np,
+                            hipStream_t stream, const char** variant)
+{
+    NormRopeArgs a = a_in;
+    const int ve = dtype == kBF16 ? 8 : 4;
+    const int nv = a.head_dim / ve;
+    // Lanes per row: enough for two vectors per lane, a power of two.
+    int lpr = 1;
+    while (2 * lpr < nv)
+        lpr *= 2;
+    const int rpp = 64 / lpr;
+    if (np <= 0) {
+        // Cover a token's rows with as few waves as possible, at most 4 passes.
+        const int passes = (a.rows_per_token + rpp - 1) / rpp;
+        np = passes <= 4 ? passes : (passes % 3 == 0 ? 3 : 4);
+        if (np < 1) np = 1;
+    }
+    const int rope = a.rope.mode == kPosNone ? 0 : (a.rope.mode == kPosPlanes ? 2 : 1);
+    const int rpw = rpp * np;
+    a.blocks_per_token = (a.rows_per_token + rpw - 1) / rpw;
+    const int64_t tiles = (int64_t)a.batch * a.tokens * a.blocks_per_token;
+    if (tiles == 0)
+        return hipSuccess;
+    const int64_t blocks = (tiles + kWaves - 1) / kWaves;
+    NormRopeFn fn = dtype == kBF16 ? pick_lpr<BF16>(lpr, rope, pairing, np)
+                                   : pick_lpr<F32>(lpr, rope, pairing, np);
+    hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
+    snprintf(g_variant, sizeof(g_variant), "rope:np%d:lpr%d:%s:%s:%s", np, lpr,
+             dtype == kBF16 ? "bf16" : "f32", rope == 0 ? "none" : (rope == 1 ? "pos" : "planes"),
+             pairing == kNeox ? "neox" : "adjacent");
+    *variant = g_variant;
+    return hipGetLastError();
+}
+
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, hipStream_t stream, const char** variant)
+{
+    if (a.rows == 0)
+        return hipSuccess;
+    if (kind < 0) {
+        // Few rows: spread each row over several compute units.
+        kind = a.rows < 256 ? 1 : 0;
+    }
+    int vpl = round_vpl(kind == 2 ? (a.nvec + kThreads - 1) / kThreads : (a.nvec + 63) / 64);
+    if (vpl < 0 && kind != 2) {
+        kind = 2;
+        vpl = round_vpl((a.nvec + kThreads - 1) / kThreads);
+    }
+    if (vpl < 0)
+        return hipErrorInvalidValue;
+    int64_t blocks;
+    if (kind == 0) {
+        blocks = (a.rows + kWaves - 1) / kWaves;
+    } else if (kind == 1) {
+        // one slice of 64 vectors per wave (each lane stores one vector)
+        a.split_len = 64;
+        a.splits = (a.nvec + a.split_len - 1) / a.split_len;
+        blocks = (a.rows * a.splits + kWaves - 1) / kWaves;
+    } else {
+        blocks = a.rows;
+    }
+    RmsFn fn;
+    if (dtype == kBF16)
+        fn = kind == 0 ? pick_vpl<BF16, 0>(vpl) : (kind == 1 ? pick_vpl<BF16, 1>(vpl) : pick_vpl<BF16, 2>(vpl));
+    else
+        fn = kind == 0 ? pick_vpl<F32, 0>(vpl) : (kind == 1 ? pick_vpl<F32, 1>(vpl) : pick_vpl<F32, 2>(vpl));
+    hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
+    snprintf(g_variant, sizeof(g_variant), "rms:%s:vpl%d:%s", kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"),
+             vpl, dtype == kBF16 ? "bf16" : "f32");
+    *variant = g_variant;
+    return hipGetLastError();
+}
+
+hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream)
+{
+    const int64_t n = a.tok_count * a.half_rot;
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(vit_setup_kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_axis_map(int32_t mode, const int32_t* sec, int32_t n_pairs, int32_t* out,
+                                 hipStream_t stream)
+{
+    if (n_pairs == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(debug_axis_kernel, dim3((n_pairs + 63) / 64), dim3(64), 0, stream, mode, sec[0], sec[1],
+                       sec[2], sec[3], n_pairs, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_vit_positions(const VitArgs& a, int32_t* out, hipStream_t stream)
+{
+    if (a.tok_count == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(debug_vit_kernel, dim3((uint32_t)((a.tok_count + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, a, out);
+    return hipGetLastError();
+}
+
+}  // namespace qkr
