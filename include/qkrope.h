@@ -179,7 +179,9 @@ const char* qkr_last_error(void);
 
 /* Force a kernel variant by name for subsequent calls on any thread, or NULL
  * for the automatic choice.  Names: "rms:rows", "rms:split", "rms:wide",
- * "rope:np1", "rope:np2", "rope:np3", "rope:np4".  Unknown names are refused. */
+ * "rope:np1", "rope:np2", "rope:np3", "rope:np4" (rows per wavefront), "nt:0" /
+ * "nt:1" (plain / nontemporal row accesses).  Overrides accumulate until NULL
+ * resets all of them.  Unknown names are refused. */
 qkr_status qkr_set_variant_override(const char* name);
 
 /* Name of the kernel variant the last successful launch on the calling

@@ -409,3 +409,34 @@ def test_large_storage_offset():
     assert_bf16_close(host(out), ref, 128)
     del buf
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: replays match eager calls, every replay
+# ---------------------------------------------------------------------------
+
+def test_graph_capture_replays_match_eager():
+    case = W.joint(tokens_txt=40, grid=(8, 12), heads=6, seed_stream=31)
+    g, rope = joint_gpu(case, "adjacent")
+    eager = qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope)
+    rows = W.rows(3, seed_stream=31)
+    x, wgt = gpu(rows.x), gpu(rows.weight)
+    y_eager = qkr.rms_norm(x, wgt, rows.eps)
+    outs = [torch.empty_like(t) for t in eager]
+    y = torch.empty_like(y_eager)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope, out=outs)
+        qkr.rms_norm(x, wgt, rows.eps, out=y)
+    for _ in range(3):
+        for t in outs + [y]:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b)
+        assert torch.equal(y, y_eager)
+        # eager work between replays
+        qkr.rms_norm(x, wgt, rows.eps)
+        torch.cuda.synchronize()

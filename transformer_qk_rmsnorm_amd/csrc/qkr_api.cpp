@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <vector>
 
@@ -30,6 +31,7 @@ thread_local char g_variant[96] = "";
 // Test hook: forced variants (-1 / 0 = automatic).
 std::atomic<int> g_rms_kind{-1};
 std::atomic<int> g_rope_np{0};
+std::atomic<int> g_nt{1};
 
 qkr_status fail(qkr_status st, const char* fmt, ...)
 {
@@ -217,7 +219,7 @@ qkr_status launch(NormRopeArgs& a, int32_t dtype, int32_t pairing, hipStream_t s
 {
     (void)hipGetLastError();   // clear a stale error so the launch reports its own
     const char* variant = "";
-    hipError_t e = launch_norm_rope(a, dtype, pairing, g_rope_np.load(), stream, &variant);
+    hipError_t e = launch_norm_rope(a, dtype, pairing, g_rope_np.load(), g_nt.load(), stream, &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "norm_rope launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
@@ -298,6 +300,11 @@ qkr_status qkr_set_variant_override(const char* name)
     if (name == nullptr) {
         g_rms_kind = -1;
         g_rope_np = 0;
+        g_nt = 1;
+        return ok();
+    }
+    if (std::strcmp(name, "nt:0") == 0 || std::strcmp(name, "nt:1") == 0) {
+        g_nt = name[3] - '0';
         return ok();
     }
     static const char* rms[3] = {"rms:rows", "rms:split", "rms:wide"};
@@ -346,7 +353,7 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
         if ((x_row_stride * esize) % 16 != 0 || (y_row_stride * esize) % 16 != 0)
             return fail(QKR_ERR_MISALIGNED, "row strides are not multiples of 16 bytes");
     }
-    if (rows > (int64_t)1 << 33)
+    if (rows * ((nvec + 63) / 64) >= ((int64_t)1 << 31))
         return fail(QKR_ERR_UNSUPPORTED, "rows %lld exceed the launch grid", (long long)rows);
 
     RmsArgs a{};
@@ -361,7 +368,8 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
     a.inv_width = 1.0f / (float)width;
     (void)hipGetLastError();
     const char* variant = "";
-    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), reinterpret_cast<hipStream_t>(stream), &variant);
+    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), g_nt.load(), reinterpret_cast<hipStream_t>(stream),
+                                   &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "rms_norm launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
@@ -379,6 +387,8 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
         return st;
     if (batch < 0 || tokens < 0 || q_heads < 0 || k_heads < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative batch, tokens or heads");
+    if (tokens > INT32_MAX || (int64_t)batch * tokens * (q_heads + k_heads) >= ((int64_t)1 << 31))
+        return fail(QKR_ERR_UNSUPPORTED, "batch * tokens * heads must stay below 2^31 rows per call");
     if ((int64_t)q_heads + k_heads > (1 << 20))
         return fail(QKR_ERR_UNSUPPORTED, "too many heads");
     if ((st = check_view("q", q, esize, batch, tokens, q_heads)) ||
@@ -410,8 +420,8 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
     a.rows_per_token = q_heads + k_heads;
     a.rope_rows = q_heads + k_heads;
     a.batch = batch;
-    a.tokens = tokens;
-    a.tokens0 = tokens;
+    a.tokens = (int32_t)tokens;
+    a.tokens0 = (int32_t)tokens;
     a.head_dim = head_dim;
     a.rotary_dim = rotary_dim;
     a.eps = eps;
@@ -435,6 +445,8 @@ qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim
     if (heads > (1 << 18))
         return fail(QKR_ERR_UNSUPPORTED, "too many heads");
     const int64_t joint = text->tokens + image->tokens;
+    if (joint > INT32_MAX || (int64_t)batch * joint * 3 * heads >= ((int64_t)1 << 31))
+        return fail(QKR_ERR_UNSUPPORTED, "batch * tokens * 3 heads must stay below 2^31 rows per call");
     const qkr_stream* streams[2] = {text, image};
     static const char* names[2][3] = {{"text.q", "text.k", "text.v"}, {"image.q", "image.k", "image.v"}};
     for (int s = 0; s < 2; ++s) {
@@ -476,8 +488,8 @@ qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim
     a.rows_per_token = 3 * heads;
     a.rope_rows = 2 * heads;
     a.batch = batch;
-    a.tokens = joint;
-    a.tokens0 = text->tokens;
+    a.tokens = (int32_t)joint;
+    a.tokens0 = (int32_t)text->tokens;
     a.head_dim = head_dim;
     a.rotary_dim = rotary_dim;
     a.eps = eps;

@@ -1,0 +1,48 @@
+// Division of 32-bit unsigned integers by a run-time invariant divisor with
+// one multiply-high, a subtract, an add and two shifts (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", PLDI
+// 1994, the round-up method for N-bit dividends).  The host computes the
+// multiplier once per launch; the kernels split their flat tile index into
+// (batch, token, block) without a hardware divide.
+//
+// Plain C++ so that the host test can compile it with g++.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__) || defined(__HIP__)
+#define QKR_HD __host__ __device__
+#else
+#define QKR_HD
+#endif
+
+namespace qkr {
+
+struct FastDiv {
+    uint32_t d;   // divisor (>= 1)
+    uint32_t m;   // multiplier
+    uint32_t l;   // ceil(log2(d))
+};
+
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f{d, 0u, 0u};
+    while (((uint64_t)1 << f.l) < d)
+        ++f.l;
+    f.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << f.l) - d)) / d + 1);
+    return f;
+}
+
+QKR_HD inline uint32_t mulhi32(uint32_t a, uint32_t b) { return (uint32_t)(((uint64_t)a * b) >> 32); }
+
+// n / f.d for every 32-bit n:  t = mulhi(m, n);  q = (t + ((n - t) >> 1)) >> (l - 1).
+QKR_HD inline uint32_t fast_div(uint32_t n, const FastDiv& f)
+{
+    if (f.d == 1)
+        return n;
+    const uint32_t t = mulhi32(f.m, n);
+    return (t + ((n - t) >> 1)) >> (f.l - 1);
+}
+
+}  // namespace qkr

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qkr_fastdiv.hpp"
+
 namespace qkr {
 
 constexpr int kMaxGrids = 64;     // ViT grids per launch (metadata rides in kernel arguments)
@@ -45,11 +47,13 @@ struct NormRopeArgs {
     int32_t rows_per_token;     // sum of heads over the tensors
     int32_t rope_rows;          // rows [0, rope_rows) are normalised (Q, K); the rest copied
     int32_t batch;
-    int64_t tokens;             // tokens per batch (joint count for the joint op)
-    int64_t tokens0;            // tokens of stream 0; tokens at or past it belong to stream 1
+    int32_t tokens;             // tokens per batch (joint count for the joint op)
+    int32_t tokens0;            // tokens of stream 0; tokens at or past it belong to stream 1
     int32_t head_dim;
     int32_t rotary_dim;
-    int32_t blocks_per_token;   // tiles per (batch, token)
+    uint32_t ntiles;            // batch * tokens * blocks_per_token (< 2^31), set by the launcher
+    FastDiv div_bpt;            // blocks (tiles) per token
+    FastDiv div_tokens;         // tokens per batch
     float eps;
     float inv_d;                // 1 / head_dim
     RopeArgs rope;
@@ -65,6 +69,7 @@ struct RmsArgs {
     int32_t nvec;               // 16-byte vectors per row
     int32_t splits;             // workgroups per row (split variant)
     int32_t split_len;          // vectors stored by one split
+    FastDiv div_splits;
     float eps;
     float inv_width;
 };
@@ -140,11 +145,12 @@ __host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*
 
 // Kernel launchers (qkr_kernels.hip).  Each returns the variant name it
 // launched through *variant; launch errors surface through hipGetLastError.
-// norm_rope: np = passes (row groups) per wave; 0 = automatic.
-hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, int np,
+// norm_rope: np = passes (row groups) per wave, 0 = automatic; nt = 1
+// nontemporal row accesses, 0 plain.
+hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, int np, int nt,
                             hipStream_t stream, const char** variant);
 // rms: kind 0 rows, 1 split, 2 wide; -1 = automatic.
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, hipStream_t stream, const char** variant);
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, hipStream_t stream, const char** variant);
 hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream);
 hipError_t launch_debug_axis_map(int32_t mode, const int32_t* sec, int32_t n_pairs, int32_t* out,
                                  hipStream_t stream);

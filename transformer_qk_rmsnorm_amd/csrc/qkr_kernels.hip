@@ -42,6 +42,13 @@ struct F32 {
     }
     // fp32 outputs keep the normalised value unrounded.
     __device__ __forceinline__ static void round_trip(float*) {}
+    __device__ __forceinline__ static float sumsq(const uint4& v, float acc)
+    {
+        acc = fmaf(__uint_as_float(v.x), __uint_as_float(v.x), acc);
+        acc = fmaf(__uint_as_float(v.y), __uint_as_float(v.y), acc);
+        acc = fmaf(__uint_as_float(v.z), __uint_as_float(v.z), acc);
+        return fmaf(__uint_as_float(v.w), __uint_as_float(v.w), acc);
+    }
 };
 
 struct BF16 {
@@ -76,10 +83,48 @@ struct BF16 {
             x[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
         }
     }
+    // Sum of squares straight from the packed pairs (v_dot2c_f32_bf16: the
+    // bf16 products are exact in fp32, accumulation in fp32), so no unpacked
+    // copy of the row has to stay live until it is normalised.
+    __device__ __forceinline__ static float sumsq(const uint4& v, float acc)
+    {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(v.z), acc, false);
+        return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(v.w), acc, false);
+    }
+    __device__ __forceinline__ static bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 };
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void store16(char* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Row data is read once and written once: with NT the accesses carry the
+// nontemporal hint (streaming, evict-first) so they do not displace the
+// small reused operands (weights, positions, planes) from the caches.
+template <bool NT>
+__device__ __forceinline__ uint4 load_row16(const char* p)
+{
+    if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return load16(p);
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_row16(char* p, const uint4& v)
+{
+    if constexpr (NT) {
+        const u32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    } else {
+        store16(p, v);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Wavefront reductions without LDS.  DPP moves inside rows of 16 lanes:
@@ -123,24 +168,75 @@ __device__ __forceinline__ float bperm(int src_lane, float v)
 }
 
 // ---------------------------------------------------------------------------
-// cos/sin of pair p at absolute token t (token_base already added).
-// The angle is the fp32 product of the fp32 position and inv_freq[p]
-// ([ViT] setup kernel); sincosf is the accurate device-library routine
-// (argument reduction good far past the 8191 rad these workloads reach).
+// Rotation operands of one (token, pair), fetched before the row data so that
+// cos/sin are ready while the rows are still in flight.
+//   ROPE 1: the token's positions, one per plane (wave-uniform scalar loads,
+//           counted apart from the vector loads), and inv_freq[p].
+//   ROPE 2: the cos/sin the setup wrote for the pair's axis.
 // ---------------------------------------------------------------------------
-template <bool PLANES>
-__device__ __forceinline__ void pair_cos_sin(const RopeArgs& r, int64_t t, int32_t p, float& c, float& s)
+struct PairOperand {
+    float inv_or_c;   // inv_freq[p] (ROPE 1) or cos (ROPE 2)
+    float s;          // sin (ROPE 2)
+    int32_t axis;
+};
+
+template <int ROPE>
+__device__ __forceinline__ PairOperand fetch_pair(const RopeArgs& r, int64_t t, int32_t p)
 {
-    const int32_t axis = pair_axis(r.mode, r.sec, p);
-    if constexpr (PLANES) {
-        const int64_t idx = ((int64_t)axis * r.planes_tokens + t) * r.half + p;
-        c = r.cos_planes[idx];
-        s = r.sin_planes[idx];
+    PairOperand o;
+    o.axis = pair_axis(r.mode, r.sec, p);
+    if constexpr (ROPE == 2) {
+        const int64_t idx = ((int64_t)o.axis * r.planes_tokens + t) * r.half + p;
+        o.inv_or_c = r.cos_planes[idx];
+        o.s = r.sin_planes[idx];
     } else {
-        const int32_t pos = r.positions[(int64_t)axis * r.pos_stride + t];
-        const float theta = (float)pos * r.inv_freq[p];
+        o.inv_or_c = r.inv_freq[p];
+        o.s = 0.0f;
+    }
+    return o;
+}
+
+// The angle is the fp32 product of the fp32 position and inv_freq[p] ([ViT]
+// setup kernel); sincosf is the accurate device-library routine (its argument
+// reduction holds far past the 8191 rad these workloads reach).
+// The token's position on each plane (wave-uniform).
+struct TokenPositions {
+    int32_t t, h, w, e;
+};
+
+template <int ROPE>
+__device__ __forceinline__ void pair_cos_sin(const PairOperand& o, const TokenPositions& pos, float& c, float& s)
+{
+    if constexpr (ROPE == 2) {
+        c = o.inv_or_c;
+        s = o.s;
+    } else {
+        const int32_t q = o.axis == 0 ? pos.t : (o.axis == 1 ? pos.h : (o.axis == 2 ? pos.w : pos.e));
+        const float theta = (float)q * o.inv_or_c;
         sincosf(theta, &s, &c);
     }
+}
+
+// Row addressing of one tensor at one (batch, token): address of head 0 and
+// the head stride, for the input view of the token's stream and for the
+// joint output.  Pointers stay derived from the kernel-argument pointers so
+// the accesses are global (not flat) memory operations.
+struct TensorRows {
+    const char* in;
+    char* out;
+    int64_t in_sh, out_sh;
+};
+
+__device__ __forceinline__ TensorRows tensor_rows(const TensorArgs& t, bool s1, int32_t b, int32_t tok,
+                                                  int32_t ltok)
+{
+    TensorRows r;
+    const char* in = s1 ? t.in[1] : t.in[0];
+    r.in = in + (int64_t)b * (s1 ? t.in_sb[1] : t.in_sb[0]) + (int64_t)ltok * (s1 ? t.in_st[1] : t.in_st[0]);
+    r.in_sh = s1 ? t.in_sh[1] : t.in_sh[0];
+    r.out = t.out + (int64_t)b * t.out_sb + (int64_t)tok * t.out_st;
+    r.out_sh = t.out_sh;
+    return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -150,15 +246,23 @@ __device__ __forceinline__ void pair_cos_sin(const RopeArgs& r, int64_t t, int32
 // one token; LPR lanes share a row and every lane owns two 16-byte vectors of
 // it.  With the NeoX pairing a lane owns vectors j and j + R/(2 VE), so every
 // rotated pair (p, p + R/2) is lane-local; with the adjacent pairing the pairs
-// sit inside one vector.  All loads of a tile are issued before the first use,
-// the token's cos/sin are computed once (lane i: pair i) and handed to the
-// lanes that need them with ds_bpermute, then each row is reduced over its LPR
-// lanes with DPP, normalised, rounded per the contract, rotated and stored.
+// sit inside one vector.
+//
+// Order of work in a wave:
+//   1. the rotation operands (the token's positions by scalar loads, the
+//      lane's inv_freq or planes entry), then the weights, then every row
+//      load of the tile.  All vector loads are unconditional (lanes without
+//      a vector of their own re-read one of their row, a cache hit), so the
+//      compiler can count them and wait only for the operands;
+//   2. cos/sin of the token's pairs (lane i: pair i) while the rows are in
+//      flight, handed to the lanes that need them with ds_bpermute;
+//   3. per row: DPP sum of squares over the row's LPR lanes, normalise, round
+//      per the contract, rotate, store (stores only for owned vectors).
 //
 // ROPE: 0 norm only, 1 positions + inv_freq (1D / AXES / IMROPE chosen at run
 // time), 2 cos/sin planes.
 // ---------------------------------------------------------------------------
-template <class E, int LPR, int NP, int ROPE, int PAIRING>
+template <class E, int LPR, int NP, int ROPE, int PAIRING, bool NT>
 __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs a)
 {
     constexpr int VE = E::VE;
@@ -167,16 +271,26 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     constexpr bool ROT = ROPE != 0;
 
     const int lane = threadIdx.x & 63;
-    const int64_t tile = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t ntiles = (int64_t)a.batch * a.tokens * a.blocks_per_token;
-    if (tile >= ntiles)
+    // Tile coordinates are wave-uniform and stay in scalar registers:
+    // tile = ((batch * tokens) + token) * blocks_per_token + block.
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t tile = blockIdx.x * kWaves + wave;
+    if (tile >= a.ntiles)
         return;   // wave-uniform
-    const int32_t blk = (int32_t)(tile % a.blocks_per_token);
-    const int64_t bt = tile / a.blocks_per_token;
-    const int64_t tok = bt % a.tokens;
-    const int64_t b = bt / a.tokens;
-    const int s = tok >= a.tokens0 ? 1 : 0;
-    const int64_t ltok = s ? tok - a.tokens0 : tok;
+    const uint32_t bt = fast_div(tile, a.div_bpt);
+    const int32_t blk = (int32_t)(tile - bt * a.div_bpt.d);
+    const uint32_t bq = fast_div(bt, a.div_tokens);
+    const int32_t tok = (int32_t)(bt - bq * a.div_tokens.d);
+    const int32_t b = (int32_t)bq;
+    const bool s1 = tok >= a.tokens0;              // token of stream 1 (image)
+    const int32_t ltok = s1 ? tok - a.tokens0 : tok;
+
+    // Named per-tensor values, not arrays: a per-lane choice among them must
+    // stay a select, never an indexed memory access.
+    const TensorRows R0 = tensor_rows(a.t[0], s1, b, tok, ltok);
+    const TensorRows R1 = tensor_rows(a.t[1], s1, b, tok, ltok);
+    const TensorRows R2 = tensor_rows(a.t[2], s1, b, tok, ltok);
+    const int h0 = a.t[0].heads, h01 = a.t[0].heads + a.t[1].heads;
 
     const int g = lane / LPR;
     const int j = lane % LPR;
@@ -201,67 +315,68 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         v1 = j < hv ? j + hv : nv;
     }
     const bool own0 = v0 < nv, own1 = v1 < nv;
-    const int64_t off0 = (int64_t)v0 * 16, off1 = (int64_t)v1 * 16;
+    const int64_t off0 = (int64_t)(own0 ? v0 : 0) * 16, off1 = (int64_t)(own1 ? v1 : 0) * 16;
 
-    // Row r of the token -> (tensor, head).
+    // Row r of the token (clamped to a real row for the load) -> tensor, head.
     auto locate = [&](int r, int& ti, int& h) {
-        const int h0 = a.t[0].heads, h1 = a.t[1].heads;
-        ti = r < h0 ? 0 : (r < h0 + h1 ? 1 : 2);
-        h = r - (ti == 0 ? 0 : (ti == 1 ? h0 : h0 + h1));
-    };
-    auto in_row = [&](int ti, int h) -> const char* {
-        const TensorArgs& t0 = a.t[0];
-        const TensorArgs& t1 = a.t[1];
-        const TensorArgs& t2 = a.t[2];
-        const char* base = ti == 0 ? t0.in[s] : (ti == 1 ? t1.in[s] : t2.in[s]);
-        const int64_t sb = ti == 0 ? t0.in_sb[s] : (ti == 1 ? t1.in_sb[s] : t2.in_sb[s]);
-        const int64_t st = ti == 0 ? t0.in_st[s] : (ti == 1 ? t1.in_st[s] : t2.in_st[s]);
-        const int64_t sh = ti == 0 ? t0.in_sh[s] : (ti == 1 ? t1.in_sh[s] : t2.in_sh[s]);
-        return base + b * sb + ltok * st + (int64_t)h * sh;
-    };
-    auto out_row = [&](int ti, int h) -> char* {
-        const TensorArgs& t0 = a.t[0];
-        const TensorArgs& t1 = a.t[1];
-        const TensorArgs& t2 = a.t[2];
-        char* base = ti == 0 ? t0.out : (ti == 1 ? t1.out : t2.out);
-        const int64_t sb = ti == 0 ? t0.out_sb : (ti == 1 ? t1.out_sb : t2.out_sb);
-        const int64_t st = ti == 0 ? t0.out_st : (ti == 1 ? t1.out_st : t2.out_st);
-        const int64_t sh = ti == 0 ? t0.out_sh : (ti == 1 ? t1.out_sh : t2.out_sh);
-        return base + b * sb + tok * st + (int64_t)h * sh;
+        ti = r < h0 ? 0 : (r < h01 ? 1 : 2);
+        h = r - (ti == 0 ? 0 : (ti == 1 ? h0 : h01));
     };
 
-    // 1) Issue every load of the tile.
+    const bool tile_norms = blk * RPW < a.rope_rows;   // wave-uniform
+    const RopeArgs& rp = a.rope;
+    const int half = rp.half;
+    const int64_t tabs = rp.token_base + tok;          // token inside the position planes
+
+    // 1a) Rotation operands: positions (scalar), then the lane's pair operands.
+    TokenPositions pos{0, 0, 0, 0};
+    PairOperand op0{}, op1{};
+    if constexpr (ROT) {
+        if constexpr (ROPE == 1) {
+            const int nplanes = rp.mode == kPosImrope ? 4 : (rp.mode == kPos1D ? 1 : 3);
+            pos.t = rp.positions[tabs];
+            if (nplanes > 1) {
+                pos.h = rp.positions[rp.pos_stride + tabs];
+                pos.w = rp.positions[2 * rp.pos_stride + tabs];
+            }
+            if (nplanes > 3)
+                pos.e = rp.positions[3 * rp.pos_stride + tabs];
+        }
+        op0 = fetch_pair<ROPE>(rp, tabs, lane < half ? lane : half - 1);
+        op1 = fetch_pair<ROPE>(rp, tabs, lane + 64 < half ? lane + 64 : half - 1);
+    }
+
+    // 1b) Weights of Q and K for this stream (tiny, cached).  A tensor without
+    //     heads has no weight; the other one's stands in (never used).
+    const char* wq = s1 ? a.t[0].weight[1] : a.t[0].weight[0];
+    const char* wk = s1 ? a.t[1].weight[1] : a.t[1].weight[0];
+    wq = wq != nullptr ? wq : wk;
+    wk = wk != nullptr ? wk : wq;
+    uint4 wq0 = make_uint4(0, 0, 0, 0), wq1 = wq0, wk0 = wq0, wk1 = wq0;
+    if (wq != nullptr) {   // wave-uniform; null only for a copy-only call
+        wq0 = load16(wq + off0);
+        wq1 = load16(wq + off1);
+        wk0 = load16(wk + off0);
+        wk1 = load16(wk + off1);
+    }
+
+    // 1c) Every row load of the tile.
     uint4 d[NP][2];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const int r = blk * RPW + p * RPP + g;
-        d[p][0] = make_uint4(0, 0, 0, 0);
-        d[p][1] = make_uint4(0, 0, 0, 0);
-        if (r < a.rows_per_token) {
-            int ti, h;
-            locate(r, ti, h);
-            const char* row = in_row(ti, h);
-            if (own0) d[p][0] = load16(row + off0);
-            if (own1) d[p][1] = load16(row + off1);
-        }
-    }
-    // Weights of Q and K for this stream (tiny, cached).
-    uint4 wq0 = make_uint4(0, 0, 0, 0), wq1 = wq0, wk0 = wq0, wk1 = wq0;
-    const bool tile_norms = blk * RPW < a.rope_rows;   // wave-uniform
-    if (tile_norms) {
-        const char* wq = a.t[0].weight[s];
-        const char* wk = a.t[1].weight[s];
-        if (wq != nullptr) {
-            if (own0) wq0 = load16(wq + off0);
-            if (own1) wq1 = load16(wq + off1);
-        }
-        if (wk != nullptr) {
-            if (own0) wk0 = load16(wk + off0);
-            if (own1) wk1 = load16(wk + off1);
-        }
+        int r = blk * RPW + p * RPP + g;
+        r = r < a.rows_per_token ? r : a.rows_per_token - 1;
+        int ti, h;
+        locate(r, ti, h);
+        const char* base = ti == 0 ? R0.in : (ti == 1 ? R1.in : R2.in);
+        const int64_t sh = ti == 0 ? R0.in_sh : (ti == 1 ? R1.in_sh : R2.in_sh);
+        const char* row = base + (int64_t)h * sh;
+        d[p][0] = load_row16<NT>(row + off0);
+        d[p][1] = load_row16<NT>(row + off1);
     }
 
-    // 2) cos/sin of the lane's VE pairs, computed once per token.
+    // 2) cos/sin of the lane's VE pairs, computed once per token while the
+    //    rows are in flight.
     float cs_c[VE], cs_s[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
@@ -270,14 +385,11 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     }
     if constexpr (ROT) {
         if (tile_norms) {
-            const RopeArgs& rp = a.rope;
-            const int64_t tabs = rp.token_base + tok;
-            const int half = rp.half;
-            float c0, s0, c1 = 1.0f, s1 = 0.0f;
-            pair_cos_sin<ROPE == 2>(rp, tabs, lane < half ? lane : half - 1, c0, s0);
             const bool wide = half > 64;   // wave-uniform
+            float c0, s0, c1 = 1.0f, s1v = 0.0f;
+            pair_cos_sin<ROPE>(op0, pos, c0, s0);
             if (wide)
-                pair_cos_sin<ROPE == 2>(rp, tabs, lane + 64 < half ? lane + 64 : half - 1, c1, s1);
+                pair_cos_sin<ROPE>(op1, pos, c1, s1v);
 #pragma unroll
             for (int e = 0; e < VE; ++e) {
                 int p;
@@ -289,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
                 const int src = p & 63;
                 float c = bperm(src, c0), sn = bperm(src, s0);
                 if (wide) {
-                    const float c_hi = bperm(src, c1), s_hi = bperm(src, s1);
+                    const float c_hi = bperm(src, c1), s_hi = bperm(src, s1v);
                     c = p >= 64 ? c_hi : c;
                     sn = p >= 64 ? s_hi : sn;
                 }
@@ -303,35 +415,30 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     float ssq[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        float x0[VE], x1[VE];
-        E::unpack(d[p][0], x0);
-        E::unpack(d[p][1], x1);
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-            ss += x0[e] * x0[e] + x1[e] * x1[e];
-        ssq[p] = group_sum<LPR>(ss);
+        const float part = E::sumsq(d[p][1], E::sumsq(d[p][0], 0.0f));
+        ssq[p] = group_sum<LPR>((own0 || own1) ? part : 0.0f);
     }
 
     // 4) Per row: normalise, round, rotate, store.
     const float eps = a.eps, inv_d = a.inv_d;
-    const int half = a.rope.half;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int r = blk * RPW + p * RPP + g;
         if (r >= a.rows_per_token)
             continue;
+        int ti, h;
+        locate(r, ti, h);
+        char* obase = ti == 0 ? R0.out : (ti == 1 ? R1.out : R2.out);
+        const int64_t osh = ti == 0 ? R0.out_sh : (ti == 1 ? R1.out_sh : R2.out_sh);
+        char* orow = obase + (int64_t)h * osh;
+        if (r >= a.rope_rows) {   // routed tensor (V): bit copy
+            if (own0) store_row16<NT>(orow + off0, d[p][0]);
+            if (own1) store_row16<NT>(orow + off1, d[p][1]);
+            continue;
+        }
         float x0[VE], x1[VE];
         E::unpack(d[p][0], x0);
         E::unpack(d[p][1], x1);
-        int ti, h;
-        locate(r, ti, h);
-        char* orow = out_row(ti, h);
-        if (r >= a.rope_rows) {   // routed tensor (V): bit copy
-            if (own0) store16(orow + off0, d[p][0]);
-            if (own1) store16(orow + off1, d[p][1]);
-            continue;
-        }
         const float rrms = rsqrtf(ssq[p] * inv_d + eps);
         float w0[VE], w1[VE];
         E::unpack(ti == 0 ? wq0 : wk0, w0);
@@ -369,8 +476,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
                 }
             }
         }
-        if (own0) store16(orow + off0, E::pack(x0));
-        if (own1) store16(orow + off1, E::pack(x1));
+        if (own0) store_row16<NT>(orow + off0, E::pack(x0));
+        if (own1) store_row16<NT>(orow + off1, E::pack(x1));
     }
 }
 
@@ -387,23 +494,24 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
 // Every lane holds VPL 16-byte vectors of the row, all loaded up front
 // ([VecRMS]: 16-byte vectorized reads of the row).
 // ---------------------------------------------------------------------------
-template <class E, int VPL, int KIND>
+template <class E, int VPL, int KIND, bool NT>
 __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
 {
     constexpr int VE = E::VE;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t row;
     int split = 0;
     int first, step;   // vector index of the lane's slot 0, distance between slots
     if constexpr (KIND == 0) {
-        row = (int64_t)blockIdx.x * kWaves + wave;
+        row = blockIdx.x * kWaves + wave;
         first = lane;
         step = 64;
     } else if constexpr (KIND == 1) {
-        const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-        row = item / a.splits;
-        split = (int)(item % a.splits);
+        const uint32_t item = blockIdx.x * kWaves + wave;
+        const uint32_t r = fast_div(item, a.div_splits);
+        row = r;
+        split = (int)(item - r * a.div_splits.d);
         first = lane;
         step = 64;
     } else {
@@ -419,17 +527,12 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
         const int v = first + k * step;
-        d[k] = v < a.nvec ? load16(x + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
+        d[k] = v < a.nvec ? load_row16<NT>(x + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
     }
     float ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        float xv[VE];
-        E::unpack(d[k], xv);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-            ss += xv[e] * xv[e];
-    }
+    for (int k = 0; k < VPL; ++k)
+        ss = E::sumsq(d[k], ss);
     ss = wave_sum(ss);
     if constexpr (KIND == 2) {
         __shared__ float part[kWaves];
@@ -459,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
 #pragma unroll
             for (int e = 0; e < VE; ++e)
                 xv[e] = xv[e] * rrms * wv[e];
-            store16(y + (int64_t)v * 16, E::pack(xv));
+            store_row16<NT>(y + (int64_t)v * 16, E::pack(xv));
         }
     }
 }
@@ -518,63 +621,75 @@ __global__ __launch_bounds__(kThreads) void debug_vit_kernel(const VitArgs a, in
 // ---------------------------------------------------------------------------
 using NormRopeFn = void (*)(NormRopeArgs);
 
-template <class E, int LPR, int ROPE, int PAIRING>
+template <class E, int LPR, int ROPE, int PAIRING, bool NT>
 NormRopeFn pick_np(int np)
 {
     switch (np) {
-    case 1: return norm_rope_kernel<E, LPR, 1, ROPE, PAIRING>;
-    case 2: return norm_rope_kernel<E, LPR, 2, ROPE, PAIRING>;
-    case 3: return norm_rope_kernel<E, LPR, 3, ROPE, PAIRING>;
-    default: return norm_rope_kernel<E, LPR, 4, ROPE, PAIRING>;
+    case 1: return norm_rope_kernel<E, LPR, 1, ROPE, PAIRING, NT>;
+    case 2: return norm_rope_kernel<E, LPR, 2, ROPE, PAIRING, NT>;
+    case 3: return norm_rope_kernel<E, LPR, 3, ROPE, PAIRING, NT>;
+    default: return norm_rope_kernel<E, LPR, 4, ROPE, PAIRING, NT>;
     }
 }
 
-template <class E, int LPR, int ROPE>
-NormRopeFn pick_pairing(int pairing, int np)
+template <class E, int LPR, int ROPE, int PAIRING>
+NormRopeFn pick_nt(bool nt, int np)
 {
-    return pairing == kNeox ? pick_np<E, LPR, ROPE, kNeox>(np) : pick_np<E, LPR, ROPE, kAdjacent>(np);
+    return nt ? pick_np<E, LPR, ROPE, PAIRING, true>(np) : pick_np<E, LPR, ROPE, PAIRING, false>(np);
+}
+
+template <class E, int LPR, int ROPE>
+NormRopeFn pick_pairing(int pairing, bool nt, int np)
+{
+    return pairing == kNeox ? pick_nt<E, LPR, ROPE, kNeox>(nt, np) : pick_nt<E, LPR, ROPE, kAdjacent>(nt, np);
 }
 
 template <class E, int LPR>
-NormRopeFn pick_rope(int rope, int pairing, int np)
+NormRopeFn pick_rope(int rope, int pairing, bool nt, int np)
 {
     switch (rope) {
-    case 0: return pick_pairing<E, LPR, 0>(pairing, np);
-    case 1: return pick_pairing<E, LPR, 1>(pairing, np);
-    default: return pick_pairing<E, LPR, 2>(pairing, np);
+    case 0: return pick_pairing<E, LPR, 0>(pairing, nt, np);
+    case 1: return pick_pairing<E, LPR, 1>(pairing, nt, np);
+    default: return pick_pairing<E, LPR, 2>(pairing, nt, np);
     }
 }
 
 template <class E>
-NormRopeFn pick_lpr(int lpr, int rope, int pairing, int np)
+NormRopeFn pick_lpr(int lpr, int rope, int pairing, bool nt, int np)
 {
     switch (lpr) {
-    case 1: return pick_rope<E, 1>(rope, pairing, np);
-    case 2: return pick_rope<E, 2>(rope, pairing, np);
-    case 4: return pick_rope<E, 4>(rope, pairing, np);
-    case 8: return pick_rope<E, 8>(rope, pairing, np);
-    case 16: return pick_rope<E, 16>(rope, pairing, np);
-    default: return pick_rope<E, 32>(rope, pairing, np);
+    case 1: return pick_rope<E, 1>(rope, pairing, nt, np);
+    case 2: return pick_rope<E, 2>(rope, pairing, nt, np);
+    case 4: return pick_rope<E, 4>(rope, pairing, nt, np);
+    case 8: return pick_rope<E, 8>(rope, pairing, nt, np);
+    case 16: return pick_rope<E, 16>(rope, pairing, nt, np);
+    default: return pick_rope<E, 32>(rope, pairing, nt, np);
     }
 }
 
 using RmsFn = void (*)(RmsArgs);
 
-template <class E, int KIND>
+template <class E, int KIND, bool NT>
 RmsFn pick_vpl(int vpl)
 {
     switch (vpl) {
-    case 1: return rms_kernel<E, 1, KIND>;
-    case 2: return rms_kernel<E, 2, KIND>;
-    case 3: return rms_kernel<E, 3, KIND>;
-    case 4: return rms_kernel<E, 4, KIND>;
-    case 5: return rms_kernel<E, 5, KIND>;
-    case 6: return rms_kernel<E, 6, KIND>;
-    case 8: return rms_kernel<E, 8, KIND>;
-    case 10: return rms_kernel<E, 10, KIND>;
-    case 12: return rms_kernel<E, 12, KIND>;
-    default: return rms_kernel<E, 16, KIND>;
+    case 1: return rms_kernel<E, 1, KIND, NT>;
+    case 2: return rms_kernel<E, 2, KIND, NT>;
+    case 3: return rms_kernel<E, 3, KIND, NT>;
+    case 4: return rms_kernel<E, 4, KIND, NT>;
+    case 5: return rms_kernel<E, 5, KIND, NT>;
+    case 6: return rms_kernel<E, 6, KIND, NT>;
+    case 8: return rms_kernel<E, 8, KIND, NT>;
+    case 10: return rms_kernel<E, 10, KIND, NT>;
+    case 12: return rms_kernel<E, 12, KIND, NT>;
+    default: return rms_kernel<E, 16, KIND, NT>;
     }
+}
+
+template <class E, int KIND>
+RmsFn pick_rms_nt(bool nt, int vpl)
+{
+    return nt ? pick_vpl<E, KIND, true>(vpl) : pick_vpl<E, KIND, false>(vpl);
 }
 
 int round_vpl(int need)
@@ -590,7 +705,7 @@ thread_local char g_variant[96];
 
 }  // namespace
 
-hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, int np,
+hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, int np, int nt,
                             hipStream_t stream, const char** variant)
 {
     NormRopeArgs a = a_in;
@@ -602,29 +717,38 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
         lpr *= 2;
     const int rpp = 64 / lpr;
     if (np <= 0) {
-        // Cover a token's rows with as few waves as possible, at most 4 passes.
+        // A token of up to three passes goes to one wavefront (its cos/sin
+        // computed once); longer tokens are cut into two-pass tiles, which
+        // keeps registers low enough for 5-7 waves per SIMD.  Measured on
+        // MI355X: 24 rows/token (16 Q + 8 K) fastest at 3 passes, 72 rows
+        // (joint Q, K, V of 24 heads) and 32 rows (16 + 16) at 2 passes.
         const int passes = (a.rows_per_token + rpp - 1) / rpp;
-        np = passes <= 4 ? passes : (passes % 3 == 0 ? 3 : 4);
-        if (np < 1) np = 1;
+        np = passes <= 3 ? (passes < 1 ? 1 : passes) : 2;
     }
     const int rope = a.rope.mode == kPosNone ? 0 : (a.rope.mode == kPosPlanes ? 2 : 1);
     const int rpw = rpp * np;
-    a.blocks_per_token = (a.rows_per_token + rpw - 1) / rpw;
-    const int64_t tiles = (int64_t)a.batch * a.tokens * a.blocks_per_token;
+    const uint32_t bpt = (uint32_t)((a.rows_per_token + rpw - 1) / rpw);
+    const int64_t tiles = (int64_t)a.batch * a.tokens * bpt;
     if (tiles == 0)
         return hipSuccess;
+    if (tiles >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;   // the host layer refuses such calls first
+    a.ntiles = (uint32_t)tiles;
+    a.div_bpt = make_fastdiv(bpt);
+    a.div_tokens = make_fastdiv((uint32_t)a.tokens);
     const int64_t blocks = (tiles + kWaves - 1) / kWaves;
-    NormRopeFn fn = dtype == kBF16 ? pick_lpr<BF16>(lpr, rope, pairing, np)
-                                   : pick_lpr<F32>(lpr, rope, pairing, np);
+    const bool use_nt = nt != 0;
+    NormRopeFn fn = dtype == kBF16 ? pick_lpr<BF16>(lpr, rope, pairing, use_nt, np)
+                                   : pick_lpr<F32>(lpr, rope, pairing, use_nt, np);
     hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
-    snprintf(g_variant, sizeof(g_variant), "rope:np%d:lpr%d:%s:%s:%s", np, lpr,
+    snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s", np, (int)use_nt, lpr,
              dtype == kBF16 ? "bf16" : "f32", rope == 0 ? "none" : (rope == 1 ? "pos" : "planes"),
              pairing == kNeox ? "neox" : "adjacent");
     *variant = g_variant;
     return hipGetLastError();
 }
 
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, hipStream_t stream, const char** variant)
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, hipStream_t stream, const char** variant)
 {
     if (a.rows == 0)
         return hipSuccess;
@@ -646,18 +770,22 @@ hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, hipStream_t strea
         // one slice of 64 vectors per wave (each lane stores one vector)
         a.split_len = 64;
         a.splits = (a.nvec + a.split_len - 1) / a.split_len;
+        a.div_splits = make_fastdiv((uint32_t)a.splits);
         blocks = (a.rows * a.splits + kWaves - 1) / kWaves;
     } else {
         blocks = a.rows;
     }
+    const bool use_nt = nt != 0;
     RmsFn fn;
     if (dtype == kBF16)
-        fn = kind == 0 ? pick_vpl<BF16, 0>(vpl) : (kind == 1 ? pick_vpl<BF16, 1>(vpl) : pick_vpl<BF16, 2>(vpl));
+        fn = kind == 0 ? pick_rms_nt<BF16, 0>(use_nt, vpl)
+                       : (kind == 1 ? pick_rms_nt<BF16, 1>(use_nt, vpl) : pick_rms_nt<BF16, 2>(use_nt, vpl));
     else
-        fn = kind == 0 ? pick_vpl<F32, 0>(vpl) : (kind == 1 ? pick_vpl<F32, 1>(vpl) : pick_vpl<F32, 2>(vpl));
+        fn = kind == 0 ? pick_rms_nt<F32, 0>(use_nt, vpl)
+                       : (kind == 1 ? pick_rms_nt<F32, 1>(use_nt, vpl) : pick_rms_nt<F32, 2>(use_nt, vpl));
     hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
-    snprintf(g_variant, sizeof(g_variant), "rms:%s:vpl%d:%s", kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"),
-             vpl, dtype == kBF16 ? "bf16" : "f32");
+    snprintf(g_variant, sizeof(g_variant), "rms:%s:nt%d:vpl%d:%s",
+             kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"), (int)use_nt, vpl, dtype == kBF16 ? "bf16" : "f32");
     *variant = g_variant;
     return hipGetLastError();
 }
