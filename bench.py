@@ -38,7 +38,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint",
-                    choices=["joint", "joint-neox", "imrope", "vit", "rows1", "rows32", "rows4096", "tiny"])
+                    choices=["joint", "joint-neox", "imrope", "vit", "rows1", "rows32", "rows4096", "tiny", "copy"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--variant", default=None,
@@ -307,6 +307,71 @@ def q_numel(case):
     return case.q.numel()
 
 
+def build_copy():
+    """Calibration only: a plain device copy of 256 MiB (read + write), the
+    reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    nbytes = 256 << 20
+    dev = torch.device("cuda")
+
+    def make_set():
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        return src, torch.empty_like(src)
+
+    def step(state):
+        src, dst = state
+        dst.copy_(src)
+
+    w = Workload()
+    w.name = "plain device copy, 256 MiB (counter calibration)"
+    w.config = {"workload": w.name, "bytes_copied": nbytes}
+    w.step_bytes = w.launch_bytes = 2 * nbytes
+    w.launches = 1
+    w.make_set, w.step = make_set, step
+    w.cpu_step = None
+    w.dtype = "f32"
+    w.sample = "none"
+    return w
+
+
+KERNEL_SOURCES = ["transformer_qk_rmsnorm_amd/csrc/qkr_kernels.hip",
+                  "transformer_qk_rmsnorm_amd/csrc/qkr_internal.hpp",
+                  "transformer_qk_rmsnorm_amd/csrc/qkr_fastdiv.hpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by
+    what the counter reads for a plain copy of known size), or None when no
+    summary exists or the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["write_scale"])
+        return round(fetch + write)
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, seconds):
     run = w.cpu_step()
     run()   # warm (page in, first-touch)
@@ -339,7 +404,8 @@ def main():
 
     builders = {"joint": lambda: build_joint("adjacent"), "joint-neox": lambda: build_joint("neox"),
                 "imrope": build_imrope, "vit": build_vit, "rows1": lambda: build_rows(1),
-                "rows32": lambda: build_rows(32), "rows4096": lambda: build_rows(4096), "tiny": build_tiny}
+                "rows32": lambda: build_rows(32), "rows4096": lambda: build_rows(4096), "tiny": build_tiny,
+                "copy": build_copy}
     w = builders[args.workload]()
     nsets = args.sets or max(3, -(-2 * MALL_BYTES // max(w.step_bytes, 1)))
     nsets = min(nsets, 64)
@@ -403,10 +469,10 @@ def main():
         "config": dict(w.config, buffer_sets=nsets, variant=variant, bytes_per_step=w.step_bytes,
                        launch="eager" if args.eager else "hipGraph replay"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
                      "bytes_per_launch": w.launch_bytes, "kernel": variant},
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and w.cpu_step is not None:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
