@@ -80,6 +80,11 @@ def _load():
         lib.oracle_vit_positions.restype = None
         lib.oracle_vit_positions.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, _i32p,
                                              ctypes.c_int64]
+        lib.oracle_vit_qk_norm_rope.restype = None
+        lib.oracle_vit_qk_norm_rope.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _f32p,
+                                                ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                                _f32p, ctypes.c_int32, _f32p, ctypes.c_int32, _f32p,
+                                                ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _f32p]
         lib.oracle_vit_cos_sin.restype = None
         lib.oracle_vit_cos_sin.argtypes = [_f32p, ctypes.c_int32, _f32p, ctypes.c_int32,
                                            _f32p, ctypes.c_int32, _i32p, ctypes.c_int32,
@@ -236,3 +241,20 @@ def vit_cos_sin(inv_t, inv_h, inv_w, grid_thw, merge, fill=np.nan):
     lib.oracle_vit_cos_sin(itp, it.size, ihp, ih.size, iwp, iw.size, gp, g.shape[0], merge,
                            cos.ctypes.data_as(_f32p), sin.ctypes.data_as(_f32p), n)
     return cos, sin
+
+
+def vit_qk_norm_rope(x, weight, eps, inv_t, inv_h, inv_w, grid_thw, merge, pairing="neox", out_dtype="bf16"):
+    """Per-head RMSNorm + RoPE of x [N, heads, head_dim] with (t, h, w)
+    positions computed from the ViT grids (no cos/sin planes)."""
+    lib = _load()
+    x, xp = _f32(x)
+    w, wp = _f32(weight)
+    it, itp = _f32(inv_t)
+    ih, ihp = _f32(inv_h)
+    iw, iwp = _f32(inv_w)
+    g, gp = _i32(np.asarray(grid_thw).reshape(-1, 3))
+    n, heads, d = x.shape
+    out = np.empty_like(x)
+    lib.oracle_vit_qk_norm_rope(xp, n, heads, d, wp, eps, _OUT[out_dtype], _PAIRS[pairing], itp, it.size, ihp,
+                                ih.size, iwp, iw.size, gp, g.shape[0], merge, out.ctypes.data_as(_f32p))
+    return out

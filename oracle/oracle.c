@@ -328,3 +328,47 @@ void oracle_vit_cos_sin(const float* inv_t, int32_t half_t, const float* inv_h, 
             }
     }
 }
+
+/* Setup and rotation in one step ([ViT] positions computed arithmetically
+ * from the grids, applied as the contiguous t/h/w sections of the rotary
+ * pairs): each token's (t, h, w) become a one-token, three-plane position
+ * buffer and the per-axis inv_freq a single [R/2] ladder, then the row goes
+ * through the same norm and rotation as every other mode. */
+void oracle_vit_qk_norm_rope(const float* x, int64_t n_tokens, int32_t heads, int32_t head_dim,
+                             const float* weight, float eps, int32_t out_kind, int32_t pairing,
+                             const float* inv_t, int32_t half_t, const float* inv_h, int32_t half_h,
+                             const float* inv_w, int32_t half_w, const int32_t* grid_thw,
+                             int32_t num_grids, int32_t merge, float* out)
+{
+    int32_t half = half_t + half_h + half_w;
+    float* inv = (float*)malloc(sizeof(float) * (size_t)(half > 0 ? half : 1));
+    for (int32_t j = 0; j < half_t; ++j)
+        inv[j] = inv_t[j];
+    for (int32_t j = 0; j < half_h; ++j)
+        inv[half_t + j] = inv_h[j];
+    for (int32_t j = 0; j < half_w; ++j)
+        inv[half_t + half_h + j] = inv_w[j];
+    double* n = (double*)malloc(sizeof(double) * (size_t)head_dim);
+    for (int64_t tok = 0; tok < n_tokens; ++tok) {
+        int32_t pos[3];
+        vit_token_position(grid_thw, num_grids, merge, tok, &pos[0], &pos[1], &pos[2]);
+        oracle_rope rope;
+        memset(&rope, 0, sizeof(rope));
+        rope.mode = ORACLE_POS_AXES;
+        rope.pairing = pairing;
+        rope.rotary_dim = 2 * half;
+        rope.inv_freq = inv;
+        rope.sections[0] = half_t;
+        rope.sections[1] = half_h;
+        rope.sections[2] = half_w;
+        rope.positions = pos;
+        rope.pos_stride = 1;
+        rope.token_base = 0;
+        for (int32_t h = 0; h < heads; ++h) {
+            int64_t row = (tok * heads + h) * (int64_t)head_dim;
+            norm_rope_row(x + row, weight, head_dim, eps, out_kind, &rope, 0, n, out + row);
+        }
+    }
+    free(n);
+    free(inv);
+}

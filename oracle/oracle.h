@@ -83,6 +83,17 @@ void oracle_vit_cos_sin(const float* inv_t, int32_t half_t, const float* inv_h, 
                         int32_t num_grids, int32_t merge, float* cos_out, float* sin_out,
                         int64_t n_tokens);
 
+/* ViT QK RMSNorm + RoPE with positions taken from the patch grids (the setup
+ * and the rotation in one step, no cos/sin planes): pair p of token n reads
+ * axis a by contiguous sections (half_t, half_h, half_w) and rotates by
+ * fl32(fl32(pos_a(n)) * inv_a[p - off_a]).  x, out: [n_tokens][heads][head_dim];
+ * rotary_dim = 2 * (half_t + half_h + half_w). */
+void oracle_vit_qk_norm_rope(const float* x, int64_t n_tokens, int32_t heads, int32_t head_dim,
+                             const float* weight, float eps, int32_t out_kind, int32_t pairing,
+                             const float* inv_t, int32_t half_t, const float* inv_h, int32_t half_h,
+                             const float* inv_w, int32_t half_w, const int32_t* grid_thw,
+                             int32_t num_grids, int32_t merge, float* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,9 @@ MUTANTS = {
                                 "idx = ((int64_t)a * n_tokens + n) * half_rot + j;"),
     "planes_read_wrong_plane": ("int64_t idx = ((int64_t)a * rope->planes_tokens + t) * half + p;",
                                 "int64_t idx = ((int64_t)0 * rope->planes_tokens + t) * half + p;"),
+    "vit_fused_h_w_ladders_swapped": ("inv[half_t + j] = inv_h[j];", "inv[half_t + j] = inv_w[j];"),
+    "vit_fused_axes_misordered": ("rope.sections[0] = half_t;\n        rope.sections[1] = half_h;",
+                                  "rope.sections[0] = half_h;\n        rope.sections[1] = half_t;"),
     "passthrough_skipped": ("for (int32_t i = r; i < d; ++i)\n        out[i] = round_out(n[i], out_kind);",
                             "for (int32_t i = r; i < d; ++i)\n        out[i] = 0.0f;"),
 }

@@ -458,3 +458,32 @@ def test_bf16_contract_rounds_normalised_value_then_result(pairing):
     # step matter and they are vanishingly rare for these values.
     expect = torch.from_numpy(expect.astype(np.float32)).to(torch.bfloat16).float().numpy()
     assert np.mean(got != expect) < 1e-3
+
+
+# ----------------------------------------------------------------------------
+# ViT setup and rotation in one step
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pairing", ["neox", "adjacent"])
+def test_vit_fused_equals_setup_then_planes_apply(pairing):
+    """Computing each token's positions from the grids inside the rotation
+    equals writing the cos/sin planes and rotating with them, up to the
+    planes' fp32 rounding of cos and sin."""
+    grids = [[1, 8, 8], [2, 4, 6], [1, 2, 2]]
+    # distinct h and w ladders, so a mix-up of the two axes shows
+    inv = [inv_freq_ladder(1e4, 16), inv_freq_ladder(1e4, 32), inv_freq_ladder(2e3, 32)]
+    cos, sin = oracle.vit_cos_sin(*inv, grids, 2)
+    rng = _rng(17)
+    n = cos.shape[1]
+    x = rng.normal(0, 1, (n, 3, 96)).astype(np.float32)      # 80 rotary dims + 16 pass-through
+    w = rng.normal(1, 0.1, 96).astype(np.float32)
+    planes = oracle.Rope("planes", 80, pairing, sections=(8, 16, 16, 0), cos_planes=cos, sin_planes=sin)
+    a = oracle.qk_norm_rope(x, w, 1e-6, planes, "f32")
+    b = oracle.vit_qk_norm_rope(x, w, 1e-6, *inv, grids, 2, pairing, "f32")
+    np.testing.assert_allclose(b, a, atol=1e-6, rtol=0)
+    # frame 0 of grid 0 has t = 0: its t pairs keep their normalised values
+    nrm = oracle.qk_norm_rope(x, w, 1e-6, None, "f32")
+    # elements of the 8 t pairs: NeoX p and p + 40, adjacent 2p and 2p + 1
+    t_elems = np.concatenate([np.arange(8), 40 + np.arange(8)]) if pairing == "neox" else np.arange(16)
+    assert np.array_equal(b[:64][..., t_elems], nrm[:64][..., t_elems])
+    assert np.array_equal(b[..., 80:], nrm[..., 80:])
