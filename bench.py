@@ -38,7 +38,8 @@ def _parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint",
-                    choices=["joint", "joint-neox", "imrope", "vit", "rows1", "rows32", "rows4096", "tiny", "copy"])
+                    choices=["joint", "joint-neox", "imrope", "vit", "vit-fused", "rows1", "rows32", "rows4096",
+                             "tiny", "copy"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--variant", default=None,
@@ -217,6 +218,51 @@ def build_vit():
     w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
     w.dtype = "bf16"
     w.sample = "setup + apply over all 7952 tokens"
+    return w
+
+
+def build_vit_fused():
+    """ViT workload with the setup folded into the rotation (no planes)."""
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.vit()
+    dev = torch.device("cuda")
+    n, half = case.n_tokens, case.half_rot
+    inv = [torch.from_numpy(a).to(dev) for a in (case.inv_t, case.inv_h, case.inv_w)]
+    qw, kw = case.q_weight.to(dev), case.k_weight.to(dev)
+
+    def make_set():
+        q, k = case.q.to(dev), case.k.to(dev)
+        return q, k, torch.empty_like(q), torch.empty_like(k)
+
+    def step(state):
+        q, k, qo, ko = state
+        qkr.vit_qk_norm_rope(q, k, qw, kw, case.eps, *inv, case.grid_thw, case.merge, q_out=qo, k_out=ko)
+
+    heads = case.q.shape[1]
+    nbytes = 4 * n * heads * 2 * half * 2 + 2 * 2 * half * 2 + 4 * half
+
+    def cpu_step():
+        import oracle
+        qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
+
+        def run():
+            oracle.vit_qk_norm_rope(qf, wq, case.eps, case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
+            oracle.vit_qk_norm_rope(kf, wk, case.eps, case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
+        return run
+
+    w = Workload()
+    w.name = "ViT QK RMSNorm + mrope with positions from the grids (setup folded in)"
+    w.config = {"workload": w.name, "grid_thw": case.grid_thw, "spatial_merge": case.merge, "tokens": n,
+                "heads": heads, "head_dim": 2 * half, "halves": [case.inv_t.size, case.inv_h.size, case.inv_w.size]}
+    w.step_bytes = w.launch_bytes = nbytes
+    w.launches = 1
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "bf16"
+    w.sample = "all 7952 tokens, Q and K"
     return w
 
 
@@ -403,7 +449,7 @@ def main():
     import transformer_qk_rmsnorm_amd as qkr
 
     builders = {"joint": lambda: build_joint("adjacent"), "joint-neox": lambda: build_joint("neox"),
-                "imrope": build_imrope, "vit": build_vit, "rows1": lambda: build_rows(1),
+                "imrope": build_imrope, "vit": build_vit, "vit-fused": build_vit_fused, "rows1": lambda: build_rows(1),
                 "rows32": lambda: build_rows(32), "rows4096": lambda: build_rows(4096), "tiny": build_tiny,
                 "copy": build_copy}
     w = builders[args.workload]()

@@ -169,6 +169,28 @@ qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t,
                                    int32_t spatial_merge, float* cos_out_dev, float* sin_out_dev,
                                    int64_t n_tokens, qkr_stream_t stream);
 
+/* ViT per-head QK RMSNorm + RoPE with the cos/sin setup folded in: the
+ * (t, h, w) position of every token comes from the patch grids (host array
+ * grid_thw[num_grids][3], spatial merge order, as in qkr_mrope_cos_sin_setup)
+ * and pair p rotates by fl32(fl32(pos_a) * inv_freq_a[p - off_a]) for the
+ * contiguous t/h/w sections (half_t, half_h, half_w pairs), cos and sin
+ * computed in registers: no planes are written or read and there is no setup
+ * launch ([ViT]: positions computed arithmetically from the grids, no cos/sin
+ * cache).  rotary_dim = 2 (half_t + half_h + half_w) <= head_dim.  Q and K are
+ * [tokens, heads, head_dim] views with tokens = sum t*h*w; the rounding
+ * contract is that of qkr_qk_norm_rope.  More than 32 grids take several
+ * launches. */
+qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype, float eps,
+                                const qkr_view* q, const qkr_view* q_out, int32_t q_heads,
+                                const void* q_weight_dev,
+                                const qkr_view* k, const qkr_view* k_out, int32_t k_heads,
+                                const void* k_weight_dev, int32_t pairing,
+                                const float* inv_freq_t_dev, int32_t half_t,
+                                const float* inv_freq_h_dev, int32_t half_h,
+                                const float* inv_freq_w_dev, int32_t half_w,
+                                const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
+                                qkr_stream_t stream);
+
 /* Text of a status code (static storage). */
 const char* qkr_status_string(qkr_status status);
 

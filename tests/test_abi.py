@@ -3,6 +3,8 @@
 - libqkrope loads and exports every symbol include/qkrope.h declares;
 - every refusal returns its status code before any HIP call (the pointers
   below are never dereferenced), so these run on a machine without a GPU;
+  no test here makes a call that would pass validation with a stand-in
+  pointer (it would launch);
 - the library's own index functions, compiled for the host from the same
   source as the device build, agree exactly with the oracle.
 """
@@ -250,3 +252,26 @@ def test_vit_positions_host_matches_oracle(grids, merge):
     expect = oracle.vit_positions(grids, merge)
     got = np.array(qkr.vit_positions_host(grids, merge))
     assert np.array_equal(got, expect)
+
+
+def test_vit_fused_refusals():
+    L = qkr.lib()
+
+    def call(grids, merge=2, tokens=None, halves=(8, 16, 16), head_dim=80, pairing=0, inv=FAKE, qw=FAKE):
+        flat = [v for g in grids for v in g]
+        arr = (ctypes.c_int32 * max(len(flat), 1))(*flat)
+        if tokens is None:
+            tokens = sum(t * h * w for t, h, w in grids)
+        v = view(st=16 * head_dim, sh=head_dim)
+        return L.qkr_vit_qk_norm_rope(tokens, head_dim, qkr.BF16, 1e-6, ctypes.byref(v), ctypes.byref(v), 16, qw,
+                                      ctypes.byref(v), ctypes.byref(v), 16, FAKE, pairing, inv, halves[0], inv,
+                                      halves[1], inv, halves[2], arr, len(grids), merge, None)
+
+    assert call([[1, 64, 63]]) == INVALID                 # w not a multiple of merge
+    assert call([[1, 64, 64]], tokens=4095) == INVALID    # tokens != sum t*h*w
+    assert call([[1, 64, 64]], halves=(8, 16, 24)) == INVALID   # 2 * 48 > head_dim 80
+    assert call([[1, 64, 64]], halves=(4, 16, 16)) == UNSUPPORTED  # NeoX half 36 not whole vectors
+    assert call([[1, 64, 64]], inv=None) == INVALID
+    assert call([[1, 64, 64]], qw=None) == INVALID
+    assert call([[1, 64, 64]], pairing=7) == INVALID
+    assert call([]) == INVALID

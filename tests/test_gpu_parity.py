@@ -440,3 +440,82 @@ def test_graph_capture_replays_match_eager():
         # eager work between replays
         qkr.rms_norm(x, wgt, rows.eps)
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# ViT setup folded into the rotation (positions from the grids in the kernel)
+# ---------------------------------------------------------------------------
+
+def vit_fused_case(case, pairing="neox"):
+    inv = [gpu(torch.from_numpy(a)) for a in (case.inv_t, case.inv_h, case.inv_w)]
+    qo, ko = qkr.vit_qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps,
+                                  *inv, case.grid_thw, case.merge, pairing)
+    rq = oracle.vit_qk_norm_rope(W.as_f32(case.q), W.as_f32(case.q_weight), case.eps, case.inv_t, case.inv_h,
+                                 case.inv_w, case.grid_thw, case.merge, pairing)
+    rk = oracle.vit_qk_norm_rope(W.as_f32(case.k), W.as_f32(case.k_weight), case.eps, case.inv_t, case.inv_h,
+                                 case.inv_w, case.grid_thw, case.merge, pairing)
+    return qo, ko, rq, rk
+
+
+@pytest.mark.parametrize("pairing", ["neox", "adjacent"])
+def test_vit_fused_full_size(pairing):
+    case = W.vit()
+    qo, ko, rq, rk = vit_fused_case(case, pairing)
+    assert "vit" in qkr.last_variant()
+    assert_bf16_close(host(qo), rq, 2 * case.half_rot, pairing, "vit fused q")
+    assert_bf16_close(host(ko), rk, 2 * case.half_rot, pairing, "vit fused k")
+
+
+def test_vit_fused_many_grids_and_partial_rotary():
+    """More grids than one launch carries (several launches over token
+    ranges), head_dim 96 with 80 rotary dims, merge 2."""
+    rng = np.random.default_rng(41)
+    grids = [[int(t), 2 * int(h), 2 * int(w)] for t, h, w in rng.integers(1, 4, (45, 3))]
+    case = W.vit(grid_thw=grids, heads=3, head_dim=96, seed_stream=41)
+    qo, ko, rq, rk = vit_fused_case(case)
+    assert_bf16_close(host(qo), rq, 80, "neox", "q")
+    assert_bf16_close(host(ko), rk, 80, "neox", "k")
+
+
+def test_vit_fused_equals_axes_mode_bitwise():
+    """The same rotation through the AXES mode, fed the device-computed ViT
+    positions and the concatenated ladders, is the same arithmetic: equal
+    bit for bit."""
+    case = W.vit(grid_thw=[[1, 16, 16], [2, 8, 12], [1, 6, 6]], seed_stream=42)
+    qo, ko, _, _ = vit_fused_case(case)
+    pos = qkr.debug_vit_positions(case.grid_thw, case.merge)
+    inv = gpu(torch.from_numpy(np.concatenate([case.inv_t, case.inv_h, case.inv_w])))
+    secs = (case.inv_t.size, case.inv_h.size, case.inv_w.size, 0)
+    rope = qkr.Rope("axes", 2 * case.half_rot, "neox", inv_freq=inv, positions=pos, sections=secs)
+    qa, ka = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+    assert torch.equal(qo, qa) and torch.equal(ko, ka)
+
+
+def test_vit_fused_close_to_setup_and_planes():
+    case = W.vit(grid_thw=[[1, 16, 16], [2, 8, 12]], seed_stream=43)
+    qo, ko, _, _ = vit_fused_case(case)
+    n, half = case.n_tokens, case.half_rot
+    inv = [gpu(torch.from_numpy(a)) for a in (case.inv_t, case.inv_h, case.inv_w)]
+    cos, sin = qkr.mrope_cos_sin_setup(*inv, case.grid_thw, case.merge)
+    secs = (case.inv_t.size, case.inv_h.size, case.inv_w.size, 0)
+    rope = qkr.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=cos, sin_planes=sin)
+    qp, kp = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+    assert_bf16_close(host(qo), host(qp), 2 * half)
+    assert_bf16_close(host(ko), host(kp), 2 * half)
+
+
+@pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing,lpr", [
+    ("f32", 40, 40, "neox", 5), ("bf16", 72, 72, "adjacent", 5), ("bf16", 80, 64, "neox", 5),
+    ("bf16", 80, 48, "adjacent", 5), ("bf16", 72, 0, "neox", 5), ("f32", 40, 24, "adjacent", 5),
+    ("f32", 36, 36, "adjacent", 5), ("bf16", 104, 104, "adjacent", 8), ("bf16", 120, 64, "neox", 8),
+    ("f32", 60, 60, "adjacent", 8), ("bf16", 24, 24, "adjacent", 2),
+])
+def test_odd_and_five_lane_rows(dtype, head_dim, rotary_dim, pairing, lpr):
+    """Rows of five 16-byte vector pairs run 12 rows per pass on 60 lanes;
+    rows with an odd number of vectors leave one lane a single vector."""
+    case = W.tiny(tokens=29, heads=13, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + rotary_dim)
+    pos = np.random.default_rng(head_dim).integers(0, 7000, (1, 29)).astype(np.int32)
+    qo, ko, rq, rk = run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos)
+    assert f":lpr{lpr}:" in qkr.last_variant()
+    check(qo, rq, dtype, rotary_dim, pairing, "q")
+    check(ko, rk, dtype, rotary_dim, pairing, "k")

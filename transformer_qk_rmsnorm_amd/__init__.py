@@ -12,6 +12,8 @@ the prefixed spellings are aliases):
     qk_norm_rope(q, k, q_weight, k_weight, eps, rope) -> (q_out, k_out)
     joint_qk_norm_rope(text, image, eps, rope)        -> (q, k, v)
     mrope_cos_sin_setup(inv_t, inv_h, inv_w, grid_thw, spatial_merge) -> (cos, sin)
+    vit_qk_norm_rope(q, k, q_weight, k_weight, eps, inv_t, inv_h, inv_w, grid_thw, spatial_merge)
+                                                      -> (q_out, k_out)
 """
 import ctypes
 import os
@@ -70,6 +72,12 @@ _SIGNATURES = {
                                                ctypes.c_void_p, ctypes.c_int32, _P(ctypes.c_int32),
                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_int64, ctypes.c_void_p]),
+    "qkr_vit_qk_norm_rope": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                            _P(_View), _P(_View), ctypes.c_int32, ctypes.c_void_p,
+                                            _P(_View), _P(_View), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_int32, _P(ctypes.c_int32), ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_void_p]),
     "qkr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qkr_last_error": (ctypes.c_char_p, []),
     "qkr_set_variant_override": (ctypes.c_int, [ctypes.c_char_p]),
@@ -383,6 +391,61 @@ def mrope_cos_sin_setup(inv_t: torch.Tensor, inv_h: torch.Tensor, inv_w: torch.T
     return cos, sin
 
 
+def vit_qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_weight: Optional[torch.Tensor],
+                     k_weight: Optional[torch.Tensor], eps: float, inv_t: torch.Tensor, inv_h: torch.Tensor,
+                     inv_w: torch.Tensor, grid_thw, spatial_merge: int, pairing: str = "neox",
+                     q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None):
+    """ViT per-head RMSNorm + RoPE of q, k [N, heads, head_dim] with (t, h, w)
+    positions computed from the patch grids in the kernel (no cos/sin planes)."""
+    ref = q if q is not None else k
+    if ref is None:
+        raise QkrError("need q or k")
+    dev = ref.device
+    for nm, t in (("inv_t", inv_t), ("inv_h", inv_h), ("inv_w", inv_w)):
+        _on_gpu(nm, t, dev)
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 1:
+            raise QkrError(f"{nm} must be contiguous float32 [half]")
+    if pairing not in PAIRINGS:
+        raise QkrError(f"unknown pairing {pairing!r}")
+    outs, views = [], []
+    for nm, t, w, o in (("q", q, q_weight, q_out), ("k", k, k_weight, k_out)):
+        if t is None:
+            outs.append(None)
+            views.append((None, None, 0, None))
+            continue
+        if t.dim() != 3 or (t.shape[-1] > 1 and t.stride(-1) != 1):
+            raise QkrError(f"{nm} must be [tokens, heads, head_dim] with a contiguous last dimension")
+        _on_gpu(nm, t, dev)
+        if t.dtype != ref.dtype or t.shape[0] != ref.shape[0] or t.shape[2] != ref.shape[2]:
+            raise QkrError(f"{nm} does not match the other tensor's tokens/head_dim/dtype")
+        if w is None:
+            raise QkrError(f"{nm}_weight is required")
+        _on_gpu(f"{nm}_weight", w, dev)
+        if w.dtype != t.dtype or not w.is_contiguous() or w.numel() != t.shape[2]:
+            raise QkrError(f"{nm}_weight must be contiguous [head_dim] of the activation dtype")
+        oo = torch.empty(t.shape, dtype=t.dtype, device=dev) if o is None else o
+        if oo.shape != t.shape or oo.dtype != t.dtype:
+            raise QkrError(f"{nm}_out must match {nm}")
+        _on_gpu(f"{nm}_out", oo, dev)
+        outs.append(oo)
+        views.append((t, oo, t.shape[1], w))
+
+    def view3(x):
+        return _View(None, 0, 0, 0) if x is None else _View(x.data_ptr(), 0, x.stride(0), x.stride(1))
+
+    arr, g, n = _grid_array(grid_thw)
+    (qi, qo, qh, qw), (ki, ko, kh, kw) = views
+    st = lib().qkr_vit_qk_norm_rope(ref.shape[0], ref.shape[2], _dtype_code(ref), float(eps),
+                                    ctypes.byref(view3(qi)), ctypes.byref(view3(qo)), qh,
+                                    qw.data_ptr() if qw is not None else None,
+                                    ctypes.byref(view3(ki)), ctypes.byref(view3(ko)), kh,
+                                    kw.data_ptr() if kw is not None else None, PAIRINGS[pairing],
+                                    inv_t.data_ptr(), inv_t.numel(), inv_h.data_ptr(), inv_h.numel(),
+                                    inv_w.data_ptr(), inv_w.numel(), arr, g, int(spatial_merge), _stream(dev))
+    _check(st, "vit_qk_norm_rope")
+    return outs[0], outs[1]
+
+
 # ----------------------------------------------------------------------------
 # index-map introspection
 # ----------------------------------------------------------------------------
@@ -427,3 +490,4 @@ qkr_rms_norm = rms_norm
 qkr_qk_norm_rope = qk_norm_rope
 qkr_joint_qk_norm_rope = joint_qk_norm_rope
 qkr_mrope_cos_sin_setup = mrope_cos_sin_setup
+qkr_vit_qk_norm_rope = vit_qk_norm_rope

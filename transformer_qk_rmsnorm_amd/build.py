@@ -19,6 +19,10 @@ LIB = os.path.join(PKG, "libqkrope.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["qkr_kernels.hip", "qkr_api.cpp"]
+# Kernels must not use private (scratch) memory: a stray dynamic index into a
+# by-value kernel argument or a local array silently costs a per-lane copy in
+# scratch.  The compiler's resource remarks are checked on every build.
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -29,16 +33,33 @@ FLAGS = [
 ]
 
 
+def _scratch_users(lines):
+    """Kernels whose resource remark reports a non-zero scratch size."""
+    users, name = [], None
+    for ln in lines:
+        if "Function Name:" in ln:
+            name = ln.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in ln:
+            size = int(ln.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size and name:
+                users.append((name, size))
+    return users
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", *FLAGS, *RESOURCE_REMARKS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln]
+    lines = (r.stdout + r.stderr).splitlines()
+    msgs = [ln for ln in lines if noise not in ln and "remark:" not in ln]
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+    users = _scratch_users(lines)
+    if users:
+        raise RuntimeError(f"{src}: kernels using scratch memory: {users[:5]}")
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
     return obj

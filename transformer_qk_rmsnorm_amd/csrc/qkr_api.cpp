@@ -546,6 +546,125 @@ qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t, 
     return hip_status(e, "mrope_cos_sin_setup launch");
 }
 
+qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype, float eps, const qkr_view* q,
+                                const qkr_view* q_out, int32_t q_heads, const void* q_weight_dev,
+                                const qkr_view* k, const qkr_view* k_out, int32_t k_heads,
+                                const void* k_weight_dev, int32_t pairing, const float* inv_freq_t_dev,
+                                int32_t half_t, const float* inv_freq_h_dev, int32_t half_h,
+                                const float* inv_freq_w_dev, int32_t half_w, const int32_t* grid_thw,
+                                int32_t num_grids, int32_t spatial_merge, qkr_stream_t stream)
+{
+    int esize = 0;
+    qkr_status st;
+    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+        return st;
+    if (tokens < 0 || q_heads < 0 || k_heads < 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "negative tokens or heads");
+    if (tokens > INT32_MAX || tokens * (q_heads + k_heads) >= ((int64_t)1 << 31))
+        return fail(QKR_ERR_UNSUPPORTED, "tokens * heads must stay below 2^31 rows per call");
+    if ((st = check_view("q", q, esize, 1, tokens, q_heads)) ||
+        (st = check_view("q_out", q_out, esize, 1, tokens, q_heads)) ||
+        (st = check_view("k", k, esize, 1, tokens, k_heads)) ||
+        (st = check_view("k_out", k_out, esize, 1, tokens, k_heads)))
+        return st;
+    if (q_heads > 0 && (st = check_weight("q_weight", q_weight_dev)))
+        return st;
+    if (k_heads > 0 && (st = check_weight("k_weight", k_weight_dev)))
+        return st;
+    if (pairing != QKR_PAIR_NEOX && pairing != QKR_PAIR_ADJACENT)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown pairing %d", pairing);
+    if (half_t < 0 || half_h < 0 || half_w < 0 || half_t + half_h + half_w <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "axis halves (%d, %d, %d) must be >= 0 with a positive sum",
+                    half_t, half_h, half_w);
+    const int32_t half = half_t + half_h + half_w;
+    if (2 * half > head_dim)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "rotary dims 2 * %d exceed head_dim %d", half, head_dim);
+    if (pairing == QKR_PAIR_NEOX && half % (16 / esize) != 0)
+        return fail(QKR_ERR_UNSUPPORTED, "NeoX pairing needs rotary_dim/2 (%d) to be a multiple of %d elements",
+                    half, 16 / esize);
+    const float* inv[3] = {inv_freq_t_dev, inv_freq_h_dev, inv_freq_w_dev};
+    const int32_t halves[3] = {half_t, half_h, half_w};
+    for (int i = 0; i < 3; ++i) {
+        if (halves[i] > 0 && inv[i] == nullptr)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "axis %d has %d frequencies but a null inv_freq", i, halves[i]);
+        if (!aligned(inv[i], 4))
+            return fail(QKR_ERR_MISALIGNED, "inv_freq of axis %d is not 4-byte aligned", i);
+    }
+    int64_t total = 0;
+    if ((st = check_grids(grid_thw, num_grids, spatial_merge, total)))
+        return st;
+    if (tokens != total)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "tokens %lld != sum of t*h*w = %lld", (long long)tokens,
+                    (long long)total);
+    if (tokens == 0 || q_heads + k_heads == 0)
+        return ok();
+
+    NormRopeArgs base{};
+    base.t[0].heads = q_heads;
+    base.t[0].weight[0] = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
+    base.t[1].heads = k_heads;
+    base.t[1].weight[0] = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
+    base.t[2].heads = 0;
+    base.ntensors = 2;
+    base.rows_per_token = q_heads + k_heads;
+    base.rope_rows = q_heads + k_heads;
+    base.batch = 1;
+    base.head_dim = head_dim;
+    base.rotary_dim = 2 * half;
+    base.eps = eps;
+    base.inv_d = 1.0f / (float)head_dim;
+    base.rope.mode = kPosVit;
+    base.rope.half = half;
+    base.rope.sec[0] = half_t;
+    base.rope.sec[1] = half_h;
+    base.rope.sec[2] = half_w;
+    base.rope.sec[3] = 0;
+    for (int i = 0; i < 3; ++i)
+        base.vit.inv[i] = inv[i];
+    base.vit.merge = spatial_merge;
+    base.vit.div_m = make_fastdiv((uint32_t)spatial_merge);
+    base.vit.div_mm = make_fastdiv((uint32_t)(spatial_merge * spatial_merge));
+
+    // One launch per group of grids; views start at the group's first token,
+    // positions use absolute token indices (token_base).
+    (void)hipGetLastError();
+    int64_t start = 0;
+    for (int32_t g0 = 0; g0 < num_grids; g0 += kMaxFusedGrids) {
+        const int32_t n = num_grids - g0 < kMaxFusedGrids ? num_grids - g0 : kMaxFusedGrids;
+        NormRopeArgs a = base;
+        a.vit.num_grids = n;
+        int64_t cu = start;
+        for (int32_t k2 = 0; k2 < n; ++k2) {
+            const int32_t* g = grid_thw + 3 * (g0 + k2);
+            a.vit.cu[k2] = cu;
+            a.vit.div_area[k2] = make_fastdiv((uint32_t)(g[1] * g[2]));
+            a.vit.div_mw[k2] = make_fastdiv((uint32_t)(spatial_merge * g[2]));
+            cu += (int64_t)g[0] * g[1] * g[2];
+        }
+        a.vit.cu[n] = cu;
+        const int64_t count = cu - start;
+        const qkr_view* ins[2] = {q, k};
+        const qkr_view* outs[2] = {q_out, k_out};
+        const int32_t heads[2] = {q_heads, k_heads};
+        for (int ti = 0; ti < 2; ++ti) {
+            if (heads[ti] == 0)
+                continue;
+            qkr_view vi = *ins[ti], vo = *outs[ti];
+            vi.ptr_dev = static_cast<char*>(vi.ptr_dev) + start * vi.stride_tok * esize;
+            vo.ptr_dev = static_cast<char*>(vo.ptr_dev) + start * vo.stride_tok * esize;
+            fill_in(a.t[ti], 0, &vi, esize);
+            fill_out(a.t[ti], &vo, esize);
+        }
+        a.tokens = (int32_t)count;
+        a.tokens0 = (int32_t)count;
+        a.rope.token_base = start;
+        if ((st = launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream))))
+            return st;
+        start = cu;
+    }
+    return ok();
+}
+
 qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* out_dev, qkr_stream_t stream)
 {
     if (rope == nullptr || n_pairs < 0 || (n_pairs > 0 && out_dev == nullptr))

@@ -9,10 +9,11 @@
 
 namespace qkr {
 
-constexpr int kMaxGrids = 64;     // ViT grids per launch (metadata rides in kernel arguments)
+constexpr int kMaxGrids = 64;     // ViT grids per setup launch (metadata rides in kernel arguments)
+constexpr int kMaxFusedGrids = 32; // ViT grids per fused norm + rotation launch
 constexpr int kThreads = 256;     // threads per workgroup of the row kernels (4 waves)
 
-enum PosMode : int32_t { kPos1D = 0, kPosAxes = 1, kPosImrope = 2, kPosPlanes = 3, kPosNone = 4 };
+enum PosMode : int32_t { kPos1D = 0, kPosAxes = 1, kPosImrope = 2, kPosPlanes = 3, kPosNone = 4, kPosVit = 5 };
 enum Pairing : int32_t { kNeox = 0, kAdjacent = 1 };
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 
@@ -28,6 +29,19 @@ struct RopeArgs {
     const float* cos_planes;
     const float* sin_planes;
     int64_t planes_tokens;
+};
+
+// ViT patch grids for the fused mode: positions are computed per token from
+// the grid table (absolute token offsets) with host-computed divisors.
+struct VitGridArgs {
+    int32_t num_grids;
+    int32_t merge;
+    FastDiv div_m;                       // merge
+    FastDiv div_mm;                      // merge * merge
+    int64_t cu[kMaxFusedGrids + 1];      // first token of each grid, then the end
+    FastDiv div_area[kMaxFusedGrids];    // h * w of each grid
+    FastDiv div_mw[kMaxFusedGrids];      // merge * w of each grid
+    const float* inv[3];                 // per-axis inverse frequencies
 };
 
 // One of Q, K, V.  Input views exist per stream (stream 1 only for the joint
@@ -57,6 +71,7 @@ struct NormRopeArgs {
     float eps;
     float inv_d;                // 1 / head_dim
     RopeArgs rope;
+    VitGridArgs vit;            // kPosVit only
 };
 
 struct RmsArgs {

@@ -139,9 +139,23 @@ __device__ __forceinline__ float dpp_f32(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ float bperm(int src_lane, float v);
+
 template <int L>
 __device__ __forceinline__ float group_sum(float v)
 {
+    if constexpr ((L & (L - 1)) != 0) {
+        // Groups of L consecutive lanes, L not a power of two (rows that are
+        // not a power-of-two number of vector pairs, e.g. head_dim 80 bf16):
+        // every lane adds the group's values in the same lane order, so all
+        // lanes of a group hold the identical sum.
+        const int base = ((int)(threadIdx.x & 63) / L) * L;
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < L; ++k)
+            s += bperm(base + k, v);
+        return s;
+    }
     if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
     if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
     if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
@@ -174,6 +188,11 @@ __device__ __forceinline__ float bperm(int src_lane, float v)
 //           counted apart from the vector loads), and inv_freq[p].
 //   ROPE 2: the cos/sin the setup wrote for the pair's axis.
 // ---------------------------------------------------------------------------
+// The token's position on each plane (wave-uniform).
+struct TokenPositions {
+    int32_t t, h, w, e;
+};
+
 struct PairOperand {
     float inv_or_c;   // inv_freq[p] (ROPE 1) or cos (ROPE 2)
     float s;          // sin (ROPE 2)
@@ -181,9 +200,19 @@ struct PairOperand {
 };
 
 template <int ROPE>
-__device__ __forceinline__ PairOperand fetch_pair(const RopeArgs& r, int64_t t, int32_t p)
+__device__ __forceinline__ PairOperand fetch_pair(const RopeArgs& r, const VitGridArgs& v, int64_t t, int32_t p)
 {
     PairOperand o;
+    if constexpr (ROPE == 3) {
+        // ViT: contiguous t/h/w sections of the pairs, one inverse-frequency
+        // ladder per axis.
+        o.axis = pair_axis(kPosAxes, r.sec, p);
+        const float* inv = o.axis == 0 ? v.inv[0] : (o.axis == 1 ? v.inv[1] : v.inv[2]);
+        const int32_t off = o.axis == 0 ? 0 : (o.axis == 1 ? r.sec[0] : r.sec[0] + r.sec[1]);
+        o.inv_or_c = inv[p - off];
+        o.s = 0.0f;
+        return o;
+    }
     o.axis = pair_axis(r.mode, r.sec, p);
     if constexpr (ROPE == 2) {
         const int64_t idx = ((int64_t)o.axis * r.planes_tokens + t) * r.half + p;
@@ -196,14 +225,47 @@ __device__ __forceinline__ PairOperand fetch_pair(const RopeArgs& r, int64_t t, 
     return o;
 }
 
+// (t, h, w) of ViT token `tok` for the fused mode, wave-uniform: the grid is
+// the last one whose first token has been reached (a select loop, scalar),
+// then frame, spatial-merge block and cell ([ViT] setup kernel's token
+// order), with the host's divisors instead of hardware divides.
+__device__ __forceinline__ TokenPositions vit_token_positions(const VitGridArgs& v, uint32_t tok)
+{
+    // Scalar fields only: selecting whole structs out of the kernel-argument
+    // table would make the compiler copy the table to private memory.
+    uint32_t start = (uint32_t)v.cu[0];
+    uint32_t a_d = v.div_area[0].d, a_m = v.div_area[0].m, a_l = v.div_area[0].l;
+    uint32_t w_d = v.div_mw[0].d, w_m = v.div_mw[0].m, w_l = v.div_mw[0].l;
+    for (int k = 1; k < v.num_grids; ++k) {
+        const bool in_k = tok >= (uint32_t)v.cu[k];
+        start = in_k ? (uint32_t)v.cu[k] : start;
+        a_d = in_k ? v.div_area[k].d : a_d;
+        a_m = in_k ? v.div_area[k].m : a_m;
+        a_l = in_k ? v.div_area[k].l : a_l;
+        w_d = in_k ? v.div_mw[k].d : w_d;
+        w_m = in_k ? v.div_mw[k].m : w_m;
+        w_l = in_k ? v.div_mw[k].l : w_l;
+    }
+    const FastDiv da{a_d, a_m, a_l}, dmw{w_d, w_m, w_l};
+    const uint32_t local = tok - start;
+    const uint32_t t = fast_div(local, da);
+    const uint32_t rem = local - t * da.d;
+    const uint32_t bh = fast_div(rem, dmw);
+    const uint32_t r = rem - bh * dmw.d;
+    const uint32_t bw = fast_div(r, v.div_mm);
+    const uint32_t r2 = r - bw * v.div_mm.d;
+    const uint32_t mh = fast_div(r2, v.div_m);
+    TokenPositions p;
+    p.t = (int32_t)t;
+    p.h = (int32_t)(bh * v.div_m.d + mh);
+    p.w = (int32_t)(bw * v.div_m.d + (r2 - mh * v.div_m.d));
+    p.e = 0;
+    return p;
+}
+
 // The angle is the fp32 product of the fp32 position and inv_freq[p] ([ViT]
 // setup kernel); sincosf is the accurate device-library routine (its argument
 // reduction holds far past the 8191 rad these workloads reach).
-// The token's position on each plane (wave-uniform).
-struct TokenPositions {
-    int32_t t, h, w, e;
-};
-
 template <int ROPE>
 __device__ __forceinline__ void pair_cos_sin(const PairOperand& o, const TokenPositions& pos, float& c, float& s)
 {
@@ -260,7 +322,7 @@ __device__ __forceinline__ TensorRows tensor_rows(const TensorArgs& t, bool s1, 
 //      per the contract, rotate, store (stores only for owned vectors).
 //
 // ROPE: 0 norm only, 1 positions + inv_freq (1D / AXES / IMROPE chosen at run
-// time), 2 cos/sin planes.
+// time), 2 cos/sin planes, 3 ViT positions computed from the grid table.
 // ---------------------------------------------------------------------------
 template <class E, int LPR, int NP, int ROPE, int PAIRING, bool NT>
 __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs a)
@@ -292,8 +354,11 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const TensorRows R2 = tensor_rows(a.t[2], s1, b, tok, ltok);
     const int h0 = a.t[0].heads, h01 = a.t[0].heads + a.t[1].heads;
 
-    const int g = lane / LPR;
-    const int j = lane % LPR;
+    // Lanes past RPP * LPR (64 is not a multiple of a non-power-of-two LPR)
+    // own nothing.
+    const bool lane_ok = lane < RPP * LPR;
+    const int g = lane_ok ? lane / LPR : 0;
+    const int j = lane_ok ? lane % LPR : LPR;
     const int nv = a.head_dim / VE;
 
     // The two vectors this lane owns in every row.
@@ -313,6 +378,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         const int hv = (nv + 1) >> 1;
         v0 = j < hv ? j : nv;
         v1 = j < hv ? j + hv : nv;
+    }
+    if (!lane_ok) {
+        v0 = v1 = nv;
+        rot_lane = false;
     }
     const bool own0 = v0 < nv, own1 = v1 < nv;
     const int64_t off0 = (int64_t)(own0 ? v0 : 0) * 16, off1 = (int64_t)(own1 ? v1 : 0) * 16;
@@ -342,8 +411,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
             if (nplanes > 3)
                 pos.e = rp.positions[3 * rp.pos_stride + tabs];
         }
-        op0 = fetch_pair<ROPE>(rp, tabs, lane < half ? lane : half - 1);
-        op1 = fetch_pair<ROPE>(rp, tabs, lane + 64 < half ? lane + 64 : half - 1);
+        if constexpr (ROPE == 3)
+            pos = vit_token_positions(a.vit, (uint32_t)tabs);
+        op0 = fetch_pair<ROPE>(rp, a.vit, tabs, lane < half ? lane : half - 1);
+        op1 = fetch_pair<ROPE>(rp, a.vit, tabs, lane + 64 < half ? lane + 64 : half - 1);
     }
 
     // 1b) Weights of Q and K for this stream (tiny, cached).  A tensor without
@@ -415,8 +486,11 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     float ssq[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const float part = E::sumsq(d[p][1], E::sumsq(d[p][0], 0.0f));
-        ssq[p] = group_sum<LPR>((own0 || own1) ? part : 0.0f);
+        // A slot the lane does not own holds a re-read of another vector
+        // (the loads are unconditional): it must not count.
+        const float s0 = E::sumsq(d[p][0], 0.0f);
+        const float part = (own0 ? s0 : 0.0f) + (own1 ? E::sumsq(d[p][1], 0.0f) : 0.0f);
+        ssq[p] = group_sum<LPR>(part);
     }
 
     // 4) Per row: normalise, round, rotate, store.
@@ -650,7 +724,8 @@ NormRopeFn pick_rope(int rope, int pairing, bool nt, int np)
     switch (rope) {
     case 0: return pick_pairing<E, LPR, 0>(pairing, nt, np);
     case 1: return pick_pairing<E, LPR, 1>(pairing, nt, np);
-    default: return pick_pairing<E, LPR, 2>(pairing, nt, np);
+    case 2: return pick_pairing<E, LPR, 2>(pairing, nt, np);
+    default: return pick_pairing<E, LPR, 3>(pairing, nt, np);
     }
 }
 
@@ -661,6 +736,7 @@ NormRopeFn pick_lpr(int lpr, int rope, int pairing, bool nt, int np)
     case 1: return pick_rope<E, 1>(rope, pairing, nt, np);
     case 2: return pick_rope<E, 2>(rope, pairing, nt, np);
     case 4: return pick_rope<E, 4>(rope, pairing, nt, np);
+    case 5: return pick_rope<E, 5>(rope, pairing, nt, np);
     case 8: return pick_rope<E, 8>(rope, pairing, nt, np);
     case 16: return pick_rope<E, 16>(rope, pairing, nt, np);
     default: return pick_rope<E, 32>(rope, pairing, nt, np);
@@ -711,10 +787,14 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     NormRopeArgs a = a_in;
     const int ve = dtype == kBF16 ? 8 : 4;
     const int nv = a.head_dim / ve;
-    // Lanes per row: enough for two vectors per lane, a power of two.
+    // Lanes per row: enough for two vectors per lane; a power of two, or 5
+    // (rows of 5 vector pairs, e.g. head_dim 80 bf16: 12 rows per pass in 60
+    // lanes instead of 8 rows in 64 lanes of which 24 idle).
     int lpr = 1;
     while (2 * lpr < nv)
         lpr *= 2;
+    if ((nv + 1) / 2 == 5)
+        lpr = 5;
     const int rpp = 64 / lpr;
     if (np <= 0) {
         // A token of up to three passes goes to one wavefront (its cos/sin
@@ -725,7 +805,8 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
         const int passes = (a.rows_per_token + rpp - 1) / rpp;
         np = passes <= 3 ? (passes < 1 ? 1 : passes) : 2;
     }
-    const int rope = a.rope.mode == kPosNone ? 0 : (a.rope.mode == kPosPlanes ? 2 : 1);
+    const int rope = a.rope.mode == kPosNone ? 0
+                     : (a.rope.mode == kPosPlanes ? 2 : (a.rope.mode == kPosVit ? 3 : 1));
     const int rpw = rpp * np;
     const uint32_t bpt = (uint32_t)((a.rows_per_token + rpw - 1) / rpw);
     const int64_t tiles = (int64_t)a.batch * a.tokens * bpt;
@@ -742,7 +823,8 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
                                    : pick_lpr<F32>(lpr, rope, pairing, use_nt, np);
     hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
     snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s", np, (int)use_nt, lpr,
-             dtype == kBF16 ? "bf16" : "f32", rope == 0 ? "none" : (rope == 1 ? "pos" : "planes"),
+             dtype == kBF16 ? "bf16" : "f32",
+             rope == 0 ? "none" : (rope == 1 ? "pos" : (rope == 2 ? "planes" : "vit")),
              pairing == kNeox ? "neox" : "adjacent");
     *variant = g_variant;
     return hipGetLastError();
