@@ -381,9 +381,9 @@ def build_copy():
     return w
 
 
-KERNEL_SOURCES = ["transformer_qk_rmsnorm_amd/csrc/qkr_kernels.hip",
-                  "transformer_qk_rmsnorm_amd/csrc/qkr_internal.hpp",
-                  "transformer_qk_rmsnorm_amd/csrc/qkr_fastdiv.hpp"]
+KERNEL_SOURCES = ["transformer_qk_rmsnorm_amd/csrc/" + f for f in
+                  ("qkr_kernels.hip", "qkr_rope_part.hip", "qkr_rope_kernel.hpp", "qkr_device.hpp",
+                   "qkr_internal.hpp", "qkr_fastdiv.hpp")]
 
 
 def kernel_source_hash():

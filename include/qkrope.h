@@ -201,8 +201,11 @@ const char* qkr_last_error(void);
 
 /* Force a kernel variant by name for subsequent calls on any thread, or NULL
  * for the automatic choice.  Names: "rms:rows", "rms:split", "rms:wide",
- * "rope:np1", "rope:np2", "rope:np3", "rope:np4" (rows per wavefront), "nt:0" /
- * "nt:1" (plain / nontemporal row accesses).  Overrides accumulate until NULL
+ * "rope:np1", "rope:np2", "rope:np3", "rope:np4" (passes of rows per wavefront),
+ * "rope:lpr4", "rope:lpr5", "rope:lpr8", "rope:lpr16", "rope:lpr32" (lanes per
+ * row; ignored where the row needs more lanes), "rope:stage0" / "rope:stage1"
+ * (QK stores straight from registers / through LDS in contiguous runs),
+ * "nt:0" / "nt:1" (plain / nontemporal row accesses).  Overrides accumulate until NULL
  * resets all of them.  Unknown names are refused. */
 qkr_status qkr_set_variant_override(const char* name);
 

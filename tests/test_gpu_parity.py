@@ -119,11 +119,12 @@ def test_position_zero_equals_norm_only_bitwise():
         assert torch.equal(a, c) and torch.equal(b, d)
 
 
-def test_batch_and_strided_views():
+@pytest.mark.parametrize("d", [128, 80])
+def test_batch_and_strided_views(d):
     """[batch, tokens, heads, D] views carved out of a wider buffer, positions
     shared across the batch."""
-    rng = np.random.default_rng(11)
-    b, t, hq, hk, d = 3, 50, 6, 2, 128
+    rng = np.random.default_rng(11 + d)
+    b, t, hq, hk = 3, 50, 6, 2
     big = torch.from_numpy(rng.normal(0, 1, (b, t, hq + hk + 3, d)).astype(np.float32)).to(torch.bfloat16)
     q, k = big[:, :, :hq], big[:, :, hq + 1:hq + 1 + hk]
     wq = torch.from_numpy(rng.normal(1, 0.1, d).astype(np.float32)).to(torch.bfloat16)
@@ -519,3 +520,59 @@ def test_odd_and_five_lane_rows(dtype, head_dim, rotary_dim, pairing, lpr):
     assert f":lpr{lpr}:" in qkr.last_variant()
     check(qo, rq, dtype, rotary_dim, pairing, "q")
     check(ko, rk, dtype, rotary_dim, pairing, "k")
+
+
+# ---------------------------------------------------------------------------
+# staged stores (through LDS, contiguous runs) against direct stores
+# ---------------------------------------------------------------------------
+
+def _with_variants(names, fn):
+    for nm in names:
+        qkr.set_variant_override(nm)
+    try:
+        out = fn()
+        return out, qkr.last_variant()
+    finally:
+        qkr.set_variant_override(None)
+
+
+@pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing", [
+    ("bf16", 80, 80, "neox"), ("bf16", 64, 64, "adjacent"), ("bf16", 96, 64, "neox"),
+    ("f32", 40, 40, "adjacent"), ("bf16", 72, 48, "neox"), ("f32", 32, 16, "neox"),
+    ("bf16", 128, 128, "neox"), ("bf16", 24, 0, "adjacent"),
+])
+def test_staged_stores_equal_direct_bitwise(dtype, head_dim, rotary_dim, pairing):
+    """Staging changes where results are stored from, never their values."""
+    case = W.tiny(tokens=45, heads=11, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 7)
+    pos = np.random.default_rng(head_dim).integers(0, 6000, (1, 45)).astype(np.int32)
+    ref = None
+    for np_ in ("rope:np1", "rope:np3"):
+        for st in ("rope:stage0", "rope:stage1"):
+            (qo, ko, rq, rk), name = _with_variants(
+                [np_, st], lambda: run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos))
+            assert f":stage{st[-1]}" in name, name
+            if ref is None:
+                ref = (qo, ko)
+                check(qo, rq, dtype, rotary_dim, pairing, "q")
+                check(ko, rk, dtype, rotary_dim, pairing, "k")
+            else:
+                assert np.array_equal(qo, ref[0]) and np.array_equal(ko, ref[1]), (np_, st)
+
+
+def test_joint_head_dim_80_staged():
+    """Q, K and copied V rows all leave through the staged path."""
+    case = W.joint(tokens_txt=33, grid=(6, 10), heads=5, head_dim=80, axes_pairs=(8, 16, 16), batch=2,
+                   seed_stream=8)
+    g, rope = joint_gpu(case, "neox")
+    outs = {}
+    for st in ("rope:stage0", "rope:stage1"):
+        (q, k, v), name = _with_variants([st], lambda: qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope))
+        assert f":stage{st[-1]}" in name, name
+        outs[st] = (q, k, v)
+    for a, b in zip(outs["rope:stage0"], outs["rope:stage1"]):
+        assert torch.equal(a, b)
+    rq, rk, rv = joint_oracle(case, "neox")
+    q, k, v = outs["rope:stage1"]
+    assert_bf16_close(host(q), rq, 80, "neox", "joint q")
+    assert_bf16_close(host(k), rk, 80, "neox", "joint k")
+    assert np.array_equal(host(v), rv)

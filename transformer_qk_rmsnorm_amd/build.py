@@ -2,7 +2,7 @@
 
     python -m transformer_qk_rmsnorm_amd.build [-v]
 
-Both translation units are compiled as HIP for gfx950 only.  Packed fp32
+Every translation unit is compiled as HIP for gfx950 only.  Packed fp32
 VALU instructions are disabled (-packed-fp32-ops); hipcc's host pass warns
 that it does not know that feature, which is harmless.
 """
@@ -18,7 +18,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqkrope.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["qkr_kernels.hip", "qkr_api.cpp"]
+# (source, extra flags, object name): the QK RMSNorm + RoPE kernels are
+# instantiated once per lanes-per-row value, in parallel compilations.
+LANES_PER_ROW = (1, 2, 4, 5, 8, 16, 32)
+UNITS = ([("qkr_kernels.hip", [], "qkr_kernels"), ("qkr_api.cpp", [], "qkr_api")] +
+         [("qkr_rope_part.hip", [f"-DQKR_LPR={n}"], f"qkr_rope_lpr{n}") for n in LANES_PER_ROW])
 # Kernels must not use private (scratch) memory: a stray dynamic index into a
 # by-value kernel argument or a local array silently costs a per-lane copy in
 # scratch.  The compiler's resource remarks are checked on every build.
@@ -46,9 +50,10 @@ def _scratch_users(lines):
     return users
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, *RESOURCE_REMARKS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit, verbose: bool) -> str:
+    src, extra, name = unit
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    cmd = ["hipcc", *FLAGS, *extra, *RESOURCE_REMARKS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,10 +61,10 @@ def _compile(src: str, verbose: bool) -> str:
     lines = (r.stdout + r.stderr).splitlines()
     msgs = [ln for ln in lines if noise not in ln and "remark:" not in ln]
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+        raise RuntimeError(f"hipcc failed on {name}:\n" + "\n".join(msgs))
     users = _scratch_users(lines)
     if users:
-        raise RuntimeError(f"{src}: kernels using scratch memory: {users[:5]}")
+        raise RuntimeError(f"{name}: kernels using scratch memory: {users[:5]}")
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
     return obj
@@ -67,8 +72,9 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    workers = max(1, min(len(UNITS), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

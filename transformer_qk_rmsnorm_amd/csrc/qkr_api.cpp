@@ -32,6 +32,8 @@ thread_local char g_variant[96] = "";
 std::atomic<int> g_rms_kind{-1};
 std::atomic<int> g_rope_np{0};
 std::atomic<int> g_nt{1};
+std::atomic<int> g_rope_lpr{0};
+std::atomic<int> g_rope_stage{-1};
 
 qkr_status fail(qkr_status st, const char* fmt, ...)
 {
@@ -219,7 +221,8 @@ qkr_status launch(NormRopeArgs& a, int32_t dtype, int32_t pairing, hipStream_t s
 {
     (void)hipGetLastError();   // clear a stale error so the launch reports its own
     const char* variant = "";
-    hipError_t e = launch_norm_rope(a, dtype, pairing, g_rope_np.load(), g_nt.load(), stream, &variant);
+    hipError_t e = launch_norm_rope(a, dtype, pairing, g_rope_np.load(), g_rope_lpr.load(), g_rope_stage.load(), g_nt.load(),
+                                    stream, &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "norm_rope launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
@@ -300,6 +303,8 @@ qkr_status qkr_set_variant_override(const char* name)
     if (name == nullptr) {
         g_rms_kind = -1;
         g_rope_np = 0;
+        g_rope_lpr = 0;
+        g_rope_stage = -1;
         g_nt = 1;
         return ok();
     }
@@ -317,6 +322,17 @@ qkr_status qkr_set_variant_override(const char* name)
     for (int i = 0; i < 4; ++i)
         if (std::strcmp(name, np[i]) == 0) {
             g_rope_np = i + 1;
+            return ok();
+        }
+    if (std::strcmp(name, "rope:stage0") == 0 || std::strcmp(name, "rope:stage1") == 0) {
+        g_rope_stage = name[10] - '0';
+        return ok();
+    }
+    static const char* lpr[5] = {"rope:lpr4", "rope:lpr5", "rope:lpr8", "rope:lpr16", "rope:lpr32"};
+    static const int lpr_val[5] = {4, 5, 8, 16, 32};
+    for (int i = 0; i < 5; ++i)
+        if (std::strcmp(name, lpr[i]) == 0) {
+            g_rope_lpr = lpr_val[i];
             return ok();
         }
     return fail(QKR_ERR_INVALID_ARGUMENT, "unknown variant '%s'", name);

@@ -1,0 +1,187 @@
+// Device building blocks shared by the gfx950 kernels: 16-byte element
+// formats (fp32, bf16 with round-to-nearest-even packing), row loads and
+// stores (optionally nontemporal) and wavefront reductions without LDS.
+//
+// Page names used in comments:
+//   [Ovis]   vllm-omni pull request "[Kernel][Ovis-Image] Fuse text/image QK
+//            RMSNorm + cat + RoPE into one Triton launch"
+#pragma once
+
+#include "qkr_internal.hpp"
+
+namespace qkr {
+namespace {
+
+constexpr int kWaves = kThreads / 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Element formats.  A 16-byte vector holds VE elements.
+// ---------------------------------------------------------------------------
+struct F32 {
+    static constexpr int VE = 4;
+    __device__ __forceinline__ static void unpack(const uint4& v, float* x)
+    {
+        x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+        x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float* x)
+    {
+        return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                          __float_as_uint(x[2]), __float_as_uint(x[3]));
+    }
+    // fp32 outputs keep the normalised value unrounded.
+    __device__ __forceinline__ static void round_trip(float*) {}
+    __device__ __forceinline__ static float sumsq(const uint4& v, float acc)
+    {
+        acc = fmaf(__uint_as_float(v.x), __uint_as_float(v.x), acc);
+        acc = fmaf(__uint_as_float(v.y), __uint_as_float(v.y), acc);
+        acc = fmaf(__uint_as_float(v.z), __uint_as_float(v.z), acc);
+        return fmaf(__uint_as_float(v.w), __uint_as_float(v.w), acc);
+    }
+};
+
+struct BF16 {
+    static constexpr int VE = 8;
+    __device__ __forceinline__ static void unpack(const uint4& v, float* x)
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    // Round to nearest even (v_cvt_pk_bf16_f32), two values per instruction.
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi)
+    {
+        const float2_t f = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    }
+    __device__ __forceinline__ static uint4 pack(const float* x)
+    {
+        return make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+    }
+    // Contract rounding: the normalised value is rounded to bf16 before the
+    // rotation ([Ovis] kernel review: one documented rounding contract).
+    __device__ __forceinline__ static void round_trip(float* x)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = pack2(x[2 * i], x[2 * i + 1]);
+            x[2 * i] = __uint_as_float(w << 16);
+            x[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+    }
+    // Sum of squares straight from the packed pairs (v_dot2c_f32_bf16: the
+    // bf16 products are exact in fp32, accumulation in fp32), so no unpacked
+    // copy of the row has to stay live until it is normalised.
+    __device__ __forceinline__ static float sumsq(const uint4& v, float acc)
+    {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(v.z), acc, false);
+        return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(v.w), acc, false);
+    }
+    __device__ __forceinline__ static bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store16(char* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Row data is read once and written once: with NT the accesses carry the
+// nontemporal hint (streaming, evict-first) so they do not displace the
+// small reused operands (weights, positions, planes) from the caches.
+template <bool NT>
+__device__ __forceinline__ uint4 load_row16(const char* p)
+{
+    if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return load16(p);
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_row16(char* p, const uint4& v)
+{
+    if constexpr (NT) {
+        const u32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    } else {
+        store16(p, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions without LDS.  DPP moves inside rows of 16 lanes:
+// quad_perm xor 1 and xor 2, then row_half_mirror (lane i <- 7 - i within 8
+// lanes) and row_mirror (lane i <- 15 - i within 16 lanes); each step adds a
+// disjoint partner group, so after log2(L) steps every lane of an L-lane
+// group holds the group's sum.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float bperm(int src_lane, float v);
+
+template <int L>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if constexpr ((L & (L - 1)) != 0) {
+        // Groups of L consecutive lanes, L not a power of two (rows that are
+        // not a power-of-two number of vector pairs, e.g. head_dim 80 bf16):
+        // every lane adds the group's values in the same lane order, so all
+        // lanes of a group hold the identical sum.
+        const int base = ((int)(threadIdx.x & 63) / L) * L;
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < L; ++k)
+            s += bperm(base + k, v);
+        return s;
+    }
+    if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+    if constexpr (L >= 16) v += dpp_f32<0x140>(v); // row_mirror
+    if constexpr (L >= 32) v += __shfl_xor(v, 16);
+    if constexpr (L >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Whole-wave sum, returned wave-uniform: 16-lane DPP sums, then the four
+// row totals read with v_readlane.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    const int iv = __float_as_int(group_sum<16>(v));
+    return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
+}
+
+__device__ __forceinline__ float bperm(int src_lane, float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+// Orders one wave's LDS writes before its later LDS reads of other lanes'
+// data (and those reads before the next writes).  LDS executes a wave's
+// operations in order, so this only keeps the compiler from moving them.
+__device__ __forceinline__ void wave_lds_order()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace
+}  // namespace qkr

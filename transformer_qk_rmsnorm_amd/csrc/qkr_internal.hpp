@@ -70,6 +70,7 @@ struct NormRopeArgs {
     FastDiv div_tokens;         // tokens per batch
     float eps;
     float inv_d;                // 1 / head_dim
+    uint32_t nv_recip;          // ceil(2^16 / vectors per row): row of a staged vector
     RopeArgs rope;
     VitGridArgs vit;            // kPosVit only
 };
@@ -158,12 +159,22 @@ __host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*
     *wpos = (int32_t)(bw * merge + r2 % merge);
 }
 
+// QK RMSNorm + RoPE kernel for one lanes-per-row value (LPR in 1, 2, 4, 5, 8,
+// 16, 32), chosen by element type, rotation source (0 none, 1 positions, 2
+// planes, 3 ViT grids), pairing, nontemporal accesses, staged stores and
+// passes per wave.  Each LPR is defined in its own build of qkr_rope_part.hip.
+using NormRopeFn = void (*)(NormRopeArgs);
+template <int LPR>
+NormRopeFn pick_norm_rope(int32_t dtype, int rope, int32_t pairing, bool nt, bool stage, int np);
+
 // Kernel launchers (qkr_kernels.hip).  Each returns the variant name it
 // launched through *variant; launch errors surface through hipGetLastError.
-// norm_rope: np = passes (row groups) per wave, 0 = automatic; nt = 1
+// norm_rope: np = passes (row groups) per wave and lpr = lanes per row, 0 =
+// automatic (an lpr too small for the row is ignored); stage = 1 stores
+// through LDS in contiguous runs, 0 directly, -1 automatic; nt = 1
 // nontemporal row accesses, 0 plain.
-hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, int np, int nt,
-                            hipStream_t stream, const char** variant);
+hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, int np, int lpr, int stage,
+                            int nt, hipStream_t stream, const char** variant);
 // rms: kind 0 rows, 1 split, 2 wide; -1 = automatic.
 hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, hipStream_t stream, const char** variant);
 hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream);
