@@ -202,7 +202,7 @@ const char* qkr_last_error(void);
 /* Force a kernel variant by name for subsequent calls on any thread, or NULL
  * for the automatic choice.  Names: "rms:rows", "rms:split", "rms:wide",
  * "rope:np1", "rope:np2", "rope:np3", "rope:np4" (passes of rows per wavefront),
- * "rope:lpr4", "rope:lpr5", "rope:lpr8", "rope:lpr16", "rope:lpr32" (lanes per
+ * "rope:lpr4", "rope:lpr8", "rope:lpr16", "rope:lpr32" (lanes per
  * row; ignored where the row needs more lanes), "rope:stage0" / "rope:stage1"
  * (QK stores straight from registers / through LDS in contiguous runs),
  * "nt:0" / "nt:1" (plain / nontemporal row accesses).  Overrides accumulate until NULL
@@ -213,9 +213,9 @@ qkr_status qkr_set_variant_override(const char* name);
  * thread used ("" if none). */
 const char* qkr_last_variant(void);
 
-/* The position axis (0 t, 1 h, 2 w, 3 e) of each of n_pairs pairs under
- * `rope`, computed by the same device function the kernels use, written to
- * out_dev [n_pairs] int32. */
+/* The position axis (0 t, 1 h, 2 w, 3 e) of each of n_pairs (<= 128) pairs
+ * under `rope`, as the kernels see it: the host-built axis table they receive,
+ * decoded by the same device function, written to out_dev [n_pairs] int32. */
 qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* out_dev,
                               qkr_stream_t stream);
 

@@ -506,14 +506,14 @@ def test_vit_fused_close_to_setup_and_planes():
 
 
 @pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing,lpr", [
-    ("f32", 40, 40, "neox", 5), ("bf16", 72, 72, "adjacent", 5), ("bf16", 80, 64, "neox", 5),
-    ("bf16", 80, 48, "adjacent", 5), ("bf16", 72, 0, "neox", 5), ("f32", 40, 24, "adjacent", 5),
-    ("f32", 36, 36, "adjacent", 5), ("bf16", 104, 104, "adjacent", 8), ("bf16", 120, 64, "neox", 8),
-    ("f32", 60, 60, "adjacent", 8), ("bf16", 24, 24, "adjacent", 2),
+    ("f32", 40, 40, "neox", 8), ("bf16", 72, 72, "adjacent", 8), ("bf16", 80, 64, "neox", 8),
+    ("bf16", 80, 48, "adjacent", 8), ("bf16", 72, 0, "neox", 8), ("f32", 40, 24, "adjacent", 8),
+    ("f32", 36, 36, "adjacent", 8), ("bf16", 104, 104, "adjacent", 8), ("bf16", 120, 64, "neox", 8),
+    ("f32", 60, 60, "adjacent", 8), ("bf16", 24, 24, "adjacent", 2), ("f32", 20, 20, "adjacent", 4),
 ])
-def test_odd_and_five_lane_rows(dtype, head_dim, rotary_dim, pairing, lpr):
-    """Rows of five 16-byte vector pairs run 12 rows per pass on 60 lanes;
-    rows with an odd number of vectors leave one lane a single vector."""
+def test_odd_vector_counts(dtype, head_dim, rotary_dim, pairing, lpr):
+    """Rows whose vector count is not a power of two leave lanes without a
+    vector of their own, and an odd count leaves one lane a single vector."""
     case = W.tiny(tokens=29, heads=13, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + rotary_dim)
     pos = np.random.default_rng(head_dim).integers(0, 7000, (1, 29)).astype(np.int32)
     qo, ko, rq, rk = run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos)

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 # (source, extra flags, object name): the QK RMSNorm + RoPE kernels are
 # instantiated once per lanes-per-row value, in parallel compilations.
-LANES_PER_ROW = (1, 2, 4, 5, 8, 16, 32)
+LANES_PER_ROW = (1, 2, 4, 8, 16, 32)
 UNITS = ([("qkr_kernels.hip", [], "qkr_kernels"), ("qkr_api.cpp", [], "qkr_api")] +
          [("qkr_rope_part.hip", [f"-DQKR_LPR={n}"], f"qkr_rope_lpr{n}") for n in LANES_PER_ROW])
 # Kernels must not use private (scratch) memory: a stray dynamic index into a

@@ -192,6 +192,12 @@ qkr_status check_rope(const qkr_rope* r, int32_t head_dim, int esize, int64_t to
     out.inv_freq = r->inv_freq_dev;
     out.positions = r->positions_dev;
     out.pos_stride = r->pos_stride;
+    // Position planes the mode reads (t; t, h, w; t, h, w, e); the others
+    // alias plane t and are never used.
+    const int planes = r->mode == QKR_POS_IMROPE ? 4 : (r->mode == QKR_POS_AXES ? 3 : 1);
+    for (int i = 0; i < 4; ++i)
+        out.plane_off[i] = r->mode == QKR_POS_PLANES || i >= planes ? 0 : (int64_t)i * r->pos_stride;
+    build_axis_bits(r->mode, s, half, out.axis_bits);
     out.token_base = r->token_base;
     out.cos_planes = r->cos_planes_dev;
     out.sin_planes = r->sin_planes_dev;
@@ -328,9 +334,9 @@ qkr_status qkr_set_variant_override(const char* name)
         g_rope_stage = name[10] - '0';
         return ok();
     }
-    static const char* lpr[5] = {"rope:lpr4", "rope:lpr5", "rope:lpr8", "rope:lpr16", "rope:lpr32"};
-    static const int lpr_val[5] = {4, 5, 8, 16, 32};
-    for (int i = 0; i < 5; ++i)
+    static const char* lpr[4] = {"rope:lpr4", "rope:lpr8", "rope:lpr16", "rope:lpr32"};
+    static const int lpr_val[4] = {4, 8, 16, 32};
+    for (int i = 0; i < 4; ++i)
         if (std::strcmp(name, lpr[i]) == 0) {
             g_rope_lpr = lpr_val[i];
             return ok();
@@ -432,9 +438,6 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
     a.t[1].weight[0] = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
     a.t[1].heads = k_heads;
     a.t[2].heads = 0;
-    a.ntensors = 2;
-    a.rows_per_token = q_heads + k_heads;
-    a.rope_rows = q_heads + k_heads;
     a.batch = batch;
     a.tokens = (int32_t)tokens;
     a.tokens0 = (int32_t)tokens;
@@ -500,9 +503,6 @@ qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim
         fill_out(a.t[ti], outs[ti], esize);
         a.t[ti].heads = heads;
     }
-    a.ntensors = 3;
-    a.rows_per_token = 3 * heads;
-    a.rope_rows = 2 * heads;
     a.batch = batch;
     a.tokens = (int32_t)joint;
     a.tokens0 = (int32_t)text->tokens;
@@ -621,9 +621,6 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
     base.t[1].heads = k_heads;
     base.t[1].weight[0] = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
     base.t[2].heads = 0;
-    base.ntensors = 2;
-    base.rows_per_token = q_heads + k_heads;
-    base.rope_rows = q_heads + k_heads;
     base.batch = 1;
     base.head_dim = head_dim;
     base.rotary_dim = 2 * half;
@@ -635,6 +632,7 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
     base.rope.sec[1] = half_h;
     base.rope.sec[2] = half_w;
     base.rope.sec[3] = 0;
+    build_axis_bits(kPosAxes, base.rope.sec, half, base.rope.axis_bits);
     for (int i = 0; i < 3; ++i)
         base.vit.inv[i] = inv[i];
     base.vit.merge = spatial_merge;
@@ -690,9 +688,12 @@ qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* ou
     if (rope->mode == QKR_POS_IMROPE && rope->sections[0] + rope->sections[1] + rope->sections[2] +
                                                 rope->sections[3] <= 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "IMROPE needs a positive section sum");
+    if (n_pairs > kMaxPairs)
+        return fail(QKR_ERR_UNSUPPORTED, "debug_axis_map: at most %d pairs", kMaxPairs);
+    RopeArgs r{};
+    build_axis_bits(rope->mode, rope->sections, n_pairs, r.axis_bits);
     (void)hipGetLastError();
-    return hip_status(launch_debug_axis_map(rope->mode, rope->sections, n_pairs, out_dev,
-                                            reinterpret_cast<hipStream_t>(stream)),
+    return hip_status(launch_debug_axis_map(r, n_pairs, out_dev, reinterpret_cast<hipStream_t>(stream)),
                       "debug_axis_map launch");
 }
 

@@ -131,23 +131,10 @@ __device__ __forceinline__ float dpp_f32(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float bperm(int src_lane, float v);
-
 template <int L>
 __device__ __forceinline__ float group_sum(float v)
 {
-    if constexpr ((L & (L - 1)) != 0) {
-        // Groups of L consecutive lanes, L not a power of two (rows that are
-        // not a power-of-two number of vector pairs, e.g. head_dim 80 bf16):
-        // every lane adds the group's values in the same lane order, so all
-        // lanes of a group hold the identical sum.
-        const int base = ((int)(threadIdx.x & 63) / L) * L;
-        float s = 0.0f;
-#pragma unroll
-        for (int k = 0; k < L; ++k)
-            s += bperm(base + k, v);
-        return s;
-    }
+    static_assert((L & (L - 1)) == 0, "groups of a power-of-two number of lanes");
     if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
     if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
     if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
@@ -171,6 +158,34 @@ __device__ __forceinline__ float wave_sum(float v)
 __device__ __forceinline__ float bperm(int src_lane, float v)
 {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+// A wave-uniform value held in a scalar register.  Selecting among such
+// values per lane stays a chain of selects: the compiler cannot turn it back
+// into a per-lane indexed load from the kernel arguments (a vector memory
+// access that would queue behind the row loads).
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <class T>
+__device__ __forceinline__ const T* uniform(const T* ptr)
+{
+    // readfirstlane yields a signed int: widen each half through uint32_t,
+    // or a low word with bit 31 set would sign-extend into the high word.
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const T*>((uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+// Axis of pair p (p < kMaxPairs) from the host-built table of 2-bit fields.
+__device__ __forceinline__ int32_t axis_of(const uint32_t (&bits)[kMaxPairs / 16], int32_t p)
+{
+    const int32_t w = p >> 4;
+    uint32_t v = uniform(bits[0]);
+#pragma unroll
+    for (int k = 1; k < kMaxPairs / 16; ++k)
+        v = w == k ? uniform(bits[k]) : v;
+    return (int32_t)((v >> ((p & 15) << 1)) & 3u);
 }
 
 // Orders one wave's LDS writes before its later LDS reads of other lanes'

@@ -17,14 +17,18 @@ enum PosMode : int32_t { kPos1D = 0, kPosAxes = 1, kPosImrope = 2, kPosPlanes = 
 enum Pairing : int32_t { kNeox = 0, kAdjacent = 1 };
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 
+constexpr int kMaxPairs = 128;    // rotary_dim / 2 <= head_dim / 2 <= 128
+
 // Rotation parameters as the kernels read them.
 struct RopeArgs {
     int32_t mode;        // PosMode
     int32_t half;        // R / 2
     int32_t sec[4];      // raw sections (AXES/PLANES: pairs per axis; IMROPE: s0..s3)
+    uint32_t axis_bits[kMaxPairs / 16];   // axis of pair p: bits 2(p%16).. of word p/16 (host-built)
     const float* inv_freq;
     const int32_t* positions;
     int64_t pos_stride;
+    int64_t plane_off[4];                 // element offset of the t, h, w, e position planes
     int64_t token_base;
     const float* cos_planes;
     const float* sin_planes;
@@ -45,7 +49,8 @@ struct VitGridArgs {
 };
 
 // One of Q, K, V.  Input views exist per stream (stream 1 only for the joint
-// op); strides are in bytes.  weight == nullptr marks a copied tensor (V).
+// op); strides are in bytes.  weight == nullptr marks a copied tensor (V); a
+// tensor with heads == 0 takes no work.
 struct TensorArgs {
     const char* in[2];
     int64_t in_sb[2], in_st[2], in_sh[2];
@@ -55,18 +60,18 @@ struct TensorArgs {
     int32_t heads;
 };
 
+// A tile is one wavefront's work: up to rows_per_tile heads of one tensor of
+// one token.  Tiles of a token are numbered tensor by tensor.
 struct NormRopeArgs {
     TensorArgs t[3];
-    int32_t ntensors;
-    int32_t rows_per_token;     // sum of heads over the tensors
-    int32_t rope_rows;          // rows [0, rope_rows) are normalised (Q, K); the rest copied
     int32_t batch;
     int32_t tokens;             // tokens per batch (joint count for the joint op)
     int32_t tokens0;            // tokens of stream 0; tokens at or past it belong to stream 1
     int32_t head_dim;
     int32_t rotary_dim;
-    uint32_t ntiles;            // batch * tokens * blocks_per_token (< 2^31), set by the launcher
-    FastDiv div_bpt;            // blocks (tiles) per token
+    uint32_t ntiles;            // batch * tokens * tiles per token (< 2^31), set by the launcher
+    int32_t tile_first[3];      // first tile of tensors 0, 1, 2 within a token (set by the launcher)
+    FastDiv div_tpt;            // tiles per token
     FastDiv div_tokens;         // tokens per batch
     float eps;
     float inv_d;                // 1 / head_dim
@@ -129,6 +134,16 @@ __host__ __device__ inline int32_t pair_axis(int32_t mode, const int32_t* sec, i
     return 0;
 }
 
+// The axis table of the rotation kernels: 2 bits per pair, pair p in bits
+// 2 (p % 16) and up of word p / 16.  Pairs past n_pairs read axis 0.
+inline void build_axis_bits(int32_t mode, const int32_t* sec, int32_t n_pairs, uint32_t* bits)
+{
+    for (int i = 0; i < kMaxPairs / 16; ++i)
+        bits[i] = 0;
+    for (int32_t p = 0; p < n_pairs && p < kMaxPairs; ++p)
+        bits[p >> 4] |= (uint32_t)pair_axis(mode, sec, p) << ((p & 15) * 2);
+}
+
 // (t, h, w) of ViT token `tok`: its grid is the last one whose first token
 // it has reached (grids are non-empty, so this is the number of grid ends
 // reached), then frame, spatial-merge block and cell inside the block.  The
@@ -178,8 +193,7 @@ hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairin
 // rms: kind 0 rows, 1 split, 2 wide; -1 = automatic.
 hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, hipStream_t stream, const char** variant);
 hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream);
-hipError_t launch_debug_axis_map(int32_t mode, const int32_t* sec, int32_t n_pairs, int32_t* out,
-                                 hipStream_t stream);
+hipError_t launch_debug_axis_map(const RopeArgs& r, int32_t n_pairs, int32_t* out, hipStream_t stream);
 hipError_t launch_debug_vit_positions(const VitArgs& a, int32_t* out, hipStream_t stream);
 
 }  // namespace qkr

@@ -132,14 +132,13 @@ __global__ __launch_bounds__(kThreads) void vit_setup_kernel(const VitArgs a)
     a.sin_out[o] = s;
 }
 
-__global__ void debug_axis_kernel(int32_t mode, int32_t s0, int32_t s1, int32_t s2, int32_t s3,
-                                  int32_t n_pairs, int32_t* out)
+// The axis of every pair as the rotation kernels decode it from the table.
+__global__ void debug_axis_kernel(const RopeArgs r, int32_t n_pairs, int32_t* out)
 {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= n_pairs)
         return;
-    const int32_t sec[4] = {s0, s1, s2, s3};
-    out[p] = pair_axis(mode, sec, p);
+    out[p] = axis_of(r.axis_bits, p);
 }
 
 __global__ __launch_bounds__(kThreads) void debug_vit_kernel(const VitArgs a, int32_t* out)
@@ -202,37 +201,42 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     NormRopeArgs a = a_in;
     const int ve = dtype == kBF16 ? 8 : 4;
     const int nv = a.head_dim / ve;
-    // Lanes per row: enough for two vectors per lane; a power of two, or 5
-    // (rows of 5 vector pairs, e.g. head_dim 80 bf16: 12 rows per pass in 60
-    // lanes instead of 8 rows in 64 lanes of which 24 idle).
+    // Lanes per row: the smallest power of two that gives every lane at most
+    // two vectors of the row.
     int lpr = 1;
     while (2 * lpr < nv)
         lpr *= 2;
-    if ((nv + 1) / 2 == 5)
-        lpr = 5;
-    if (lpr_req > 0 && 2 * lpr_req >= nv)
+    if (lpr_req > 0 && (lpr_req & (lpr_req - 1)) == 0 && lpr_req <= 32 && 2 * lpr_req >= nv)
         lpr = lpr_req;
     const int rpp = 64 / lpr;
+    int max_heads = 0;
+    for (int i = 0; i < 3; ++i)
+        max_heads = a.t[i].heads > max_heads ? a.t[i].heads : max_heads;
     if (np <= 0) {
-        // A token of up to three passes goes to one wavefront (its cos/sin
-        // computed once); longer tokens are cut into two-pass tiles, which
-        // keeps registers low enough for 5-7 waves per SIMD.  Measured on
-        // MI355X: 24 rows/token (16 Q + 8 K) fastest at 3 passes, 72 rows
-        // (joint Q, K, V of 24 heads) and 32 rows (16 + 16) at 2 passes.
-        const int passes = (a.rows_per_token + rpp - 1) / rpp;
-        np = passes <= 3 ? (passes < 1 ? 1 : passes) : 2;
+        // Two passes per tile where the tensor has two or more passes of
+        // heads.  Measured on MI355X: the joint op (24 heads of 128) runs at
+        // 31.7 us with two and 32.8 us with three; ViT (16 heads of 80) at
+        // 22.5 / 24.1 us (one pass: 30.4 us); 16 + 8 heads of 128 at 7.8-8.0
+        // us either way.
+        const int passes = (max_heads + rpp - 1) / rpp;
+        np = passes >= 2 ? 2 : 1;
     }
+    np = np < 1 ? 1 : (np > 4 ? 4 : np);
     const int rope = a.rope.mode == kPosNone ? 0
                      : (a.rope.mode == kPosPlanes ? 2 : (a.rope.mode == kPosVit ? 3 : 1));
     const int rpw = rpp * np;
-    const uint32_t bpt = (uint32_t)((a.rows_per_token + rpw - 1) / rpw);
-    const int64_t tiles = (int64_t)a.batch * a.tokens * bpt;
+    int32_t tpt = 0;
+    for (int i = 0; i < 3; ++i) {
+        a.tile_first[i] = tpt;
+        tpt += (a.t[i].heads + rpw - 1) / rpw;
+    }
+    const int64_t tiles = (int64_t)a.batch * a.tokens * tpt;
     if (tiles == 0)
         return hipSuccess;
     if (tiles >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;   // the host layer refuses such calls first
     a.ntiles = (uint32_t)tiles;
-    a.div_bpt = make_fastdiv(bpt);
+    a.div_tpt = make_fastdiv((uint32_t)tpt);
     a.div_tokens = make_fastdiv((uint32_t)a.tokens);
     const int64_t blocks = (tiles + kWaves - 1) / kWaves;
     const bool use_nt = nt != 0;
@@ -245,7 +249,6 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     case 1: fn = pick_norm_rope<1>(dtype, rope, pairing, use_nt, stage, np); break;
     case 2: fn = pick_norm_rope<2>(dtype, rope, pairing, use_nt, stage, np); break;
     case 4: fn = pick_norm_rope<4>(dtype, rope, pairing, use_nt, stage, np); break;
-    case 5: fn = pick_norm_rope<5>(dtype, rope, pairing, use_nt, stage, np); break;
     case 8: fn = pick_norm_rope<8>(dtype, rope, pairing, use_nt, stage, np); break;
     case 16: fn = pick_norm_rope<16>(dtype, rope, pairing, use_nt, stage, np); break;
     default: fn = pick_norm_rope<32>(dtype, rope, pairing, use_nt, stage, np); break;
@@ -311,13 +314,11 @@ hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_debug_axis_map(int32_t mode, const int32_t* sec, int32_t n_pairs, int32_t* out,
-                                 hipStream_t stream)
+hipError_t launch_debug_axis_map(const RopeArgs& r, int32_t n_pairs, int32_t* out, hipStream_t stream)
 {
     if (n_pairs == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(debug_axis_kernel, dim3((n_pairs + 63) / 64), dim3(64), 0, stream, mode, sec[0], sec[1],
-                       sec[2], sec[3], n_pairs, out);
+    hipLaunchKernelGGL(debug_axis_kernel, dim3((n_pairs + 63) / 64), dim3(64), 0, stream, r, n_pairs, out);
     return hipGetLastError();
 }
 
