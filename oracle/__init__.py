@@ -65,6 +65,14 @@ def _load():
         lib.oracle_rms_norm.restype = None
         lib.oracle_rms_norm.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, _f32p,
                                         ctypes.c_float, ctypes.c_int32, _f32p]
+        lib.oracle_fp8_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_add_rms_norm.restype = None
+        lib.oracle_add_rms_norm.argtypes = [_f32p, _f32p, ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_float,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _f32p, _f32p,
+                                            ctypes.POINTER(ctypes.c_uint8)]
         lib.oracle_axis.restype = ctypes.c_int32
         lib.oracle_axis.argtypes = [ctypes.POINTER(_Rope), ctypes.c_int32]
         lib.oracle_qk_norm_rope.restype = None
@@ -161,6 +169,44 @@ def rms_norm(x, weight, eps, out_dtype="bf16"):
     y = np.empty_like(x)
     lib.oracle_rms_norm(xp, rows, width, wp, eps, _OUT[out_dtype], y.ctypes.data_as(_f32p))
     return y
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (uint8 array)."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_fp8_e4m3_decode(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def fp8_e4m3_encode(values) -> np.ndarray:
+    """OCP FP8 E4M3 codes of finite reals (round half to even, saturating)."""
+    lib = _load()
+    v = np.asarray(values, dtype=np.float64)
+    return np.array([lib.oracle_fp8_e4m3_encode(float(a)) for a in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def add_rms_norm(x, weight, eps, residual=None, act_dtype="bf16", out_dtype="bf16", scale=1.0):
+    """Residual add + RMSNorm of x [rows, width]: returns (s, y) where s is the
+    new residual stream and y the output (float array, or uint8 FP8 E4M3
+    codes for out_dtype "fp8_e4m3")."""
+    lib = _load()
+    x, xp = _f32(x)
+    w, wp = _f32(weight)
+    rows, width = x.shape
+    if residual is not None:
+        r, rp = _f32(residual)
+        if r.shape != x.shape:
+            raise ValueError("residual must match x")
+    else:
+        r, rp = None, None
+    s = np.empty_like(x)
+    fp8 = out_dtype == "fp8_e4m3"
+    y = np.empty(x.shape, np.uint8 if fp8 else np.float32)
+    out_kind = 2 if fp8 else _OUT[out_dtype]
+    lib.oracle_add_rms_norm(xp, rp, rows, width, wp, eps, _OUT[act_dtype], out_kind, scale,
+                            s.ctypes.data_as(_f32p), None if fp8 else y.ctypes.data_as(_f32p),
+                            y.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)) if fp8 else None)
+    return s, y
 
 
 def axis_map(rope: Rope, n_pairs: int) -> np.ndarray:

@@ -93,6 +93,89 @@ void oracle_rms_norm(const float* x, int64_t rows, int32_t width, const float* w
 }
 
 /* ------------------------------------------------------------------------ */
+/* Residual add + RMSNorm, optionally with a static FP8 E4M3 output          */
+/* ------------------------------------------------------------------------ */
+
+/* OCP FP8 E4M3 (the variant without infinities): sign, a 4-bit exponent with
+ * bias 7 and a 3-bit mantissa.  Exponent field e > 0: 2^(e-7) * (1 + m/8);
+ * e == 0: 2^-6 * m/8; e == 15 with m == 7 is NaN, so the largest finite
+ * magnitude is 2^8 * 1.75 = 448.  ([VecRMS] names the static FP8 RMSNorm
+ * kernel; the format is the one gfx950 converts to natively.) */
+double oracle_fp8_e4m3_decode(uint8_t code)
+{
+    const int e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(8.0 + (double)m, e - 10);
+    return (code & 0x80) ? -v : v;
+}
+
+/* Reading: a static quantiser saturates at the largest finite magnitude and
+ * rounds half to even on the E4M3 grid: spacing 2^-9 below 2^-6 (subnormals,
+ * whose top step lands on 2^-6 itself), spacing 2^(k-3) in [2^k, 2^(k+1)).
+ * Finite inputs only; the sign of zero is kept. */
+uint8_t oracle_fp8_e4m3_encode(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs(v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < 0x1p-6)
+        return sign | (uint8_t)nearbyint(ldexp(a, 9));   /* 0..8; 8 is the code of 2^-6 */
+    int k;
+    (void)frexp(a, &k);
+    k -= 1;                                   /* a in [2^k, 2^(k+1)), -6 <= k <= 8 */
+    double q = nearbyint(ldexp(a, 3 - k));    /* 8..16 */
+    if (q == 16.0) {
+        q = 8.0;
+        k += 1;
+    }
+    return sign | (uint8_t)(((k + 7) << 3) | ((int)q - 8));
+}
+
+/* [Vulkan] decode RmsNorm: the calls carry the residual add and the weight
+ * multiply, and the residual stream is held bit-exactly by rounding the sum
+ * in registers.  Reading: s = x + r rounded once to the activation type is
+ * both the stored residual stream and the norm's input; the norm then follows
+ * norm_row.  For the FP8 output the quantised code is decided in fp32, as a
+ * kernel holding y in a register decides it: fl32(y), then the correctly
+ * rounded fp32 quotient by the scale (a double quotient of two floats rounded
+ * to float is the correctly rounded float quotient), then the encoding. */
+void oracle_add_rms_norm(const float* x, const float* r, int64_t rows, int32_t width, const float* weight,
+                         float eps, int32_t act_kind, int32_t out_kind, float scale, float* s_out,
+                         float* y_out, uint8_t* code_out)
+{
+    float* s = (float*)malloc(sizeof(float) * (size_t)width);
+    double* u = (double*)malloc(sizeof(double) * (size_t)width);
+    for (int64_t row = 0; row < rows; ++row) {
+        const float* xr = x + row * width;
+        for (int32_t i = 0; i < width; ++i) {
+            const double sum = r ? (double)xr[i] + (double)r[row * width + i] : (double)xr[i];
+            s[i] = round_out(sum, act_kind);
+        }
+        if (s_out)
+            memcpy(s_out + row * width, s, sizeof(float) * (size_t)width);
+        norm_row(s, weight, width, eps, u);
+        for (int32_t i = 0; i < width; ++i) {
+            if (out_kind == ORACLE_OUT_FP8_E4M3) {
+                const float y32 = (float)u[i];
+                const float q = (float)((double)y32 / (double)scale);
+                if (code_out)
+                    code_out[row * width + i] = oracle_fp8_e4m3_encode((double)q);
+            } else if (y_out) {
+                y_out[row * width + i] = round_out(u[i], out_kind);
+            }
+        }
+    }
+    free(u);
+    free(s);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Which position axis a rotary pair reads                                   */
 /* ------------------------------------------------------------------------ */
 

@@ -21,7 +21,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_OUT_F32 = 0, ORACLE_OUT_BF16 = 1 };
+enum { ORACLE_OUT_F32 = 0, ORACLE_OUT_BF16 = 1, ORACLE_OUT_FP8_E4M3 = 2 };
 enum { ORACLE_POS_1D = 0, ORACLE_POS_AXES = 1, ORACLE_POS_IMROPE = 2, ORACLE_POS_PLANES = 3 };
 enum { ORACLE_PAIR_NEOX = 0, ORACLE_PAIR_ADJACENT = 1 };
 enum { ORACLE_AXIS_T = 0, ORACLE_AXIS_H = 1, ORACLE_AXIS_W = 2, ORACLE_AXIS_E = 3 };
@@ -47,6 +47,20 @@ double oracle_round_bf16(double v);
 /* Plain row RMSNorm: y = round(x * rrms * w), rrms = 1/sqrt(mean(x^2) + eps). */
 void oracle_rms_norm(const float* x, int64_t rows, int32_t width, const float* weight,
                      float eps, int32_t out_kind, float* y);
+
+/* OCP FP8 E4M3 ("fn": no infinities, NaN = S.1111.111): value of a code, and
+ * the code of a finite real (round half to even, saturating at +-448). */
+double oracle_fp8_e4m3_decode(uint8_t code);
+uint8_t oracle_fp8_e4m3_encode(double v);
+
+/* Residual add + RMSNorm.  s = x + r rounded once to act_kind (F32 or BF16)
+ * is the new residual stream (s_out) and the norm's input; y = s * rrms(s) * w.
+ * out_kind F32 / BF16: y rounded once into y_out.  FP8_E4M3: code_out =
+ * encode(fl32(fl32(y) / scale)) (a static per-tensor scale).  r == NULL means
+ * no residual (s = x).  Unused outputs may be NULL. */
+void oracle_add_rms_norm(const float* x, const float* r, int64_t rows, int32_t width, const float* weight,
+                         float eps, int32_t act_kind, int32_t out_kind, float scale, float* s_out,
+                         float* y_out, uint8_t* code_out);
 
 /* Position axis that pair p reads (ORACLE_AXIS_*). */
 int32_t oracle_axis(const oracle_rope* rope, int32_t p);

@@ -50,6 +50,14 @@ MUTANTS = {
     "vit_fused_h_w_ladders_swapped": ("inv[half_t + j] = inv_h[j];", "inv[half_t + j] = inv_w[j];"),
     "vit_fused_axes_misordered": ("rope.sections[0] = half_t;\n        rope.sections[1] = half_h;",
                                   "rope.sections[0] = half_h;\n        rope.sections[1] = half_t;"),
+    "fp8_ties_away": ("double q = nearbyint(ldexp(a, 3 - k));", "double q = round(ldexp(a, 3 - k));"),
+    "fp8_no_saturation": ("if (a >= 448.0)\n        return sign | 0x7E;", "if (a >= 1e300)\n        return sign | 0x7E;"),
+    "fp8_subnormals_flushed": ("return sign | (uint8_t)nearbyint(ldexp(a, 9));", "return sign;"),
+    "fp8_exponent_bias_off": ("(((k + 7) << 3) | ((int)q - 8))", "(((k + 8) << 3) | ((int)q - 8))"),
+    "fp8_scale_multiplied": ("(float)((double)y32 / (double)scale)", "(float)((double)y32 * (double)scale)"),
+    "add_norm_sum_unrounded": ("s[i] = round_out(sum, act_kind);", "s[i] = (float)sum;"),
+    "add_norm_residual_ignored": ("? (double)xr[i] + (double)r[row * width + i] : (double)xr[i]",
+                                  "? (double)xr[i] : (double)xr[i]"),
     "passthrough_skipped": ("for (int32_t i = r; i < d; ++i)\n        out[i] = round_out(n[i], out_kind);",
                             "for (int32_t i = r; i < d; ++i)\n        out[i] = 0.0f;"),
 }

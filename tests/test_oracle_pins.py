@@ -487,3 +487,101 @@ def test_vit_fused_equals_setup_then_planes_apply(pairing):
     t_elems = np.concatenate([np.arange(8), 40 + np.arange(8)]) if pairing == "neox" else np.arange(16)
     assert np.array_equal(b[:64][..., t_elems], nrm[:64][..., t_elems])
     assert np.array_equal(b[..., 80:], nrm[..., 80:])
+
+
+# ---------------------------------------------------------------------------
+# residual add + RMSNorm, static FP8 E4M3 output
+# ---------------------------------------------------------------------------
+
+def _fp8_torch(values):
+    """torch's float -> float8_e4m3fn conversion (round half to even) of
+    values inside the finite range."""
+    t = torch.tensor(np.asarray(values, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_every_code_round_trips():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.fp8_e4m3_decode(codes)
+    assert np.array_equal(oracle.fp8_e4m3_encode(vals), codes)
+    assert np.isnan(oracle.fp8_e4m3_decode([0x7F, 0xFF])).all()
+    pos = np.sort(vals[vals > 0])
+    assert pos[0] == 2.0 ** -9 and pos[-1] == 448.0 and len(pos) == 126
+
+
+def test_fp8_matches_torch_on_grid_midpoints_and_random_values():
+    codes = np.arange(0, 0x7F, dtype=np.uint8)              # 0 .. 448, increasing
+    vals = oracle.fp8_e4m3_decode(codes)
+    mids = (vals[:-1] + vals[1:]) / 2                         # exact ties: must go to the even code
+    near = np.concatenate([np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9))])
+    rng = np.random.default_rng(7)
+    rand = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-2 ** -5, 2 ** -5, 4000),
+                           np.exp2(rng.uniform(-12, 8.8, 4000)) * rng.choice([-1, 1], 4000)])
+    for v in (mids, -mids, near, rand.astype(np.float32)):
+        v = np.asarray(v, dtype=np.float32)
+        v = v[np.abs(v) < 448]
+        assert np.array_equal(oracle.fp8_e4m3_encode(v), _fp8_torch(v))
+    # every exact tie went to the code with an even mantissa
+    assert (oracle.fp8_e4m3_encode(mids.astype(np.float32)) & 1 == 0).all()
+
+
+def test_fp8_saturates_at_448():
+    big = np.array([448.0, 448.5, 463.9, 464.0, 1e4, 3.4e38])
+    assert (oracle.fp8_e4m3_encode(big) == 0x7E).all()
+    assert (oracle.fp8_e4m3_encode(-big) == 0xFE).all()
+    assert oracle.fp8_e4m3_encode([-0.0])[0] == 0x80 and oracle.fp8_e4m3_encode([0.0])[0] == 0x00
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_add_rms_norm_without_residual_is_rms_norm(act):
+    x = _act(np.random.default_rng(3).normal(0, 2, (5, 96)), act)
+    w = _act(np.random.default_rng(4).normal(1, 0.1, 96), act)
+    for out in ("bf16", "f32"):
+        s, y = oracle.add_rms_norm(x, w, 1e-6, None, act, out)
+        assert np.array_equal(s, x)
+        assert np.array_equal(y, oracle.rms_norm(x, w, 1e-6, out))
+        s0, y0 = oracle.add_rms_norm(x, w, 1e-6, np.zeros_like(x), act, out)
+        assert np.array_equal(s0, x) and np.array_equal(y0, y)
+
+
+def _act(a, act):
+    a = np.asarray(a, dtype=np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16).float().numpy() if act == "bf16" else a
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_add_rms_norm_residual_stream_and_norm_input(act):
+    """s is the sum rounded once to the activation type (torch: fp32 sum of
+    the two operands, then its bf16 cast), and y is the norm of that s."""
+    rng = np.random.default_rng(5)
+    x = _act(rng.normal(0, 1, (7, 128)) * np.exp2(rng.integers(-20, 20, (7, 128))), act)
+    r = _act(rng.normal(0, 1, (7, 128)) * np.exp2(rng.integers(-20, 20, (7, 128))), act)
+    w = _act(rng.normal(1, 0.1, 128), act)
+    s, y = oracle.add_rms_norm(x, w, 1e-6, r, act, act)
+    ref = torch.from_numpy(x) + torch.from_numpy(r)
+    if act == "bf16":
+        ref = ref.to(torch.bfloat16).float()
+    assert np.array_equal(s, ref.numpy())
+    assert np.array_equal(y, oracle.rms_norm(ref.numpy(), w, 1e-6, act))
+    s2, y2 = oracle.add_rms_norm(r, w, 1e-6, x, act, act)     # the add commutes
+    assert np.array_equal(s2, s) and np.array_equal(y2, y)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.005, 3.5])
+def test_add_rms_norm_fp8_codes(scale):
+    """code = e4m3(fl32(fl32(y) / scale)): y from the fp32-output norm of the
+    rounded sum, the fp32 quotient by numpy, the encoding by torch where it is
+    in range, saturation at +-448 otherwise."""
+    rng = np.random.default_rng(int(scale * 1000))
+    x = _act(rng.normal(0, 1, (6, 64)), "bf16")
+    r = _act(rng.normal(0, 1, (6, 64)), "bf16")
+    w = _act(rng.normal(1, 0.3, 64), "bf16")
+    s, q = oracle.add_rms_norm(x, w, 1e-6, r, "bf16", "fp8_e4m3", scale)
+    y32 = oracle.rms_norm(s, w, 1e-6, "f32")
+    quo = (y32 / np.float32(scale)).astype(np.float32)
+    inside = np.abs(quo) < 448
+    assert np.array_equal(q[inside], _fp8_torch(quo[inside]))
+    assert (q[~inside] == np.where(quo[~inside] > 0, 0x7E, 0xFE)).all()
+    if scale == 0.005:
+        assert (~inside).any() and inside.any()
