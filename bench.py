@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the fused QK RMSNorm + RoPE hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload joint|imrope|vit|rows1|rows32|rows4096|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload joint|joint-neox|imrope|vit|vit-fused|rows1|rows32|
+                                                 rows4096|addrms4096|addrms4096-fp8|addrms1|tiny|copy]
 
 Prints one JSON line.  A step is one pass of the workload's hot path over one
 batch of synthetic input already resident in HBM (default workload: the joint
@@ -39,7 +40,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint",
                     choices=["joint", "joint-neox", "imrope", "vit", "vit-fused", "rows1", "rows32", "rows4096",
-                             "tiny", "copy"])
+                             "addrms4096", "addrms4096-fp8", "addrms1", "tiny", "copy"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--variant", default=None,
@@ -306,6 +307,51 @@ def build_rows(t):
     return w
 
 
+def build_addrms(t, fp8):
+    """Residual add + RMSNorm of bf16 [t, 5120] rows, bf16 or static FP8 E4M3 output."""
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.rows(t)
+    res = W.rows(t, seed_stream=1).x
+    dev = torch.device("cuda")
+    wgt = case.weight.to(dev)
+    scale = torch.tensor([0.02], dtype=torch.float32, device=dev)
+
+    def make_set():
+        x, r = case.x.to(dev), res.to(dev)
+        y = torch.empty(x.shape, dtype=torch.float8_e4m3fn if fp8 else x.dtype, device=dev)
+        return x, r, torch.empty_like(x), y
+
+    def step(state):
+        x, r, s_out, y = state
+        qkr.add_rms_norm(x, wgt, case.eps, residual=r, residual_out=s_out, out_dtype="fp8_e4m3" if fp8 else None,
+                         scale=scale, out=y)
+
+    width = case.x.shape[1]
+    nbytes = t * width * (2 + 2 + 2 + (1 if fp8 else 2)) + width * 2 + (4 if fp8 else 0)
+
+    def cpu_step():
+        import oracle
+        xf, rf, wf = W.as_f32(case.x), W.as_f32(res), W.as_f32(case.weight)
+
+        def run():
+            oracle.add_rms_norm(xf, wf, case.eps, rf, "bf16", "fp8_e4m3" if fp8 else "bf16", 0.02)
+        return run
+
+    w = Workload()
+    w.name = f"residual add + RMSNorm bf16 [{t}, {width}] -> {'FP8 E4M3 (static scale)' if fp8 else 'bf16'}"
+    w.config = {"workload": w.name, "rows": t, "width": width, "eps": case.eps, "out": "fp8_e4m3" if fp8 else "bf16"}
+    w.step_bytes = w.launch_bytes = nbytes
+    w.launches = 1
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "bf16"
+    w.sample = f"the full [{t}, {width}] input"
+    return w
+
+
 def build_tiny():
     import torch
 
@@ -451,6 +497,8 @@ def main():
     builders = {"joint": lambda: build_joint("adjacent"), "joint-neox": lambda: build_joint("neox"),
                 "imrope": build_imrope, "vit": build_vit, "vit-fused": build_vit_fused, "rows1": lambda: build_rows(1),
                 "rows32": lambda: build_rows(32), "rows4096": lambda: build_rows(4096), "tiny": build_tiny,
+                "addrms4096": lambda: build_addrms(4096, False), "addrms4096-fp8": lambda: build_addrms(4096, True),
+                "addrms1": lambda: build_addrms(1, False),
                 "copy": build_copy}
     w = builders[args.workload]()
     nsets = args.sets or max(3, -(-2 * MALL_BYTES // max(w.step_bytes, 1)))

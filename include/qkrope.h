@@ -116,6 +116,32 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
                         const void* weight_dev, int64_t rows, int32_t width, float eps,
                         int32_t dtype, qkr_stream_t stream);
 
+/* Output kinds of qkr_add_rms_norm. */
+typedef enum { QKR_OUT_ACT = 0, QKR_OUT_FP8_E4M3 = 1 } qkr_out_kind;
+
+/* Residual add + RMSNorm, with the output in the activation type or as static
+ * FP8 codes ([Vulkan] decode RmsNorm: its calls carry the residual add and the
+ * weight multiply, and the residual stream is held bit-exactly by rounding the
+ * sum in registers; [VecRMS]: the static FP8 RMSNorm kernel):
+ *   s[r, i] = round(x[r, i] + res[r, i])          the new residual stream -> s_dev
+ *   y[r, i] = s[r, i] * rrms_r * weight[i],  rrms_r = 1 / sqrt(mean_i(s[r, i]^2) + eps)
+ *   y_kind QKR_OUT_ACT:      y rounded once to the activation type
+ *   y_kind QKR_OUT_FP8_E4M3: one byte per element, the OCP E4M3 code of the
+ *                            correctly rounded fp32 quotient y / *scale_dev
+ *                            (round half to even, saturating at +-448)
+ * x, res, s: [rows, width] of dtype with row strides in elements; y: row
+ * stride in elements of its own type (bytes for FP8).  res_dev == NULL means
+ * no add (s_dev must then be NULL too: plain RMSNorm with the chosen output).
+ * s may be res or x itself (same pointer and stride: in-place update of the
+ * residual stream); no other overlap of s or y with the inputs is accepted.
+ * scale_dev: device fp32 scalar, read by the kernel (FP8 only); the caller
+ * keeps it finite and positive.  Inputs are finite.  FP8 rows need y aligned
+ * to 16 / sizeof(dtype) bytes.  Refusals as for qkr_rms_norm. */
+qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void* res_dev, int64_t res_row_stride,
+                            void* s_dev, int64_t s_row_stride, void* y_dev, int64_t y_row_stride, int32_t y_kind,
+                            const float* scale_dev, const void* weight_dev, int64_t rows, int32_t width, float eps,
+                            int32_t dtype, qkr_stream_t stream);
+
 /* Per-(token, head) RMSNorm of Q and K followed by RoPE ([Ovis] single-stream
  * fused_qk_norm_rope; [IMROPE] sectioned rotation after the per-head norm):
  *   n = x * rrms * w over each head_dim row (fp32 sum of squares);
@@ -223,6 +249,12 @@ qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* ou
  * function the setup kernel uses, written to out_dev [3][n_tokens] int32. */
 qkr_status qkr_debug_vit_positions(const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
                                    int32_t* out_dev, int64_t n_tokens, qkr_stream_t stream);
+
+/* The FP8 E4M3 quantiser of qkr_add_rms_norm applied to x_dev [n] fp32:
+ * out_dev [n] uint8 = code(x / *scale_dev) with the kernel's quotient, or
+ * code(x) when scale_dev is NULL. */
+qkr_status qkr_debug_fp8_e4m3(const float* x_dev, int64_t n, const float* scale_dev, uint8_t* out_dev,
+                              qkr_stream_t stream);
 
 /* Host builds of the same two index functions (no GPU needed): out_host
  * [n_pairs] and [3][n_tokens] int32. */

@@ -79,6 +79,40 @@ def test_rms_norm_zero_rows_is_a_noop():
 
 
 # ---------------------------------------------------------------------------
+# add_rms_norm refusals (every call below fails validation before any device
+# access: the pointers are stand-ins)
+# ---------------------------------------------------------------------------
+
+XA, RA, YA = FAKE, FAKE + (1 << 30), FAKE + (1 << 31)
+
+
+def addrms(x=XA, xs=5120, r=RA, rs=5120, s=RA, ss=5120, y=YA, ys=5120, kind=0, scale=None, w=FAKE, rows=4,
+           width=5120, eps=1e-6, dtype=qkr.BF16):
+    return qkr.lib().qkr_add_rms_norm(x, xs, r, rs, s, ss, y, ys, kind, scale, w, rows, width, eps, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dtype=7), INVALID), (dict(kind=5), INVALID), (dict(eps=-1.0), INVALID), (dict(width=0), INVALID),
+    (dict(width=5121), MISALIGNED), (dict(rows=-1), INVALID), (dict(s=None), INVALID), (dict(r=None), INVALID),
+    (dict(kind=1), INVALID), (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(w=ODD), MISALIGNED),
+    (dict(x=ODD), MISALIGNED), (dict(r=ODD, s=ODD), MISALIGNED), (dict(y=XA), INVALID),
+    (dict(y=RA + 64), INVALID), (dict(s=XA + 16), INVALID), (dict(s=RA + 32), INVALID),
+    (dict(s=RA, ss=6144), INVALID), (dict(ys=5000), MISALIGNED), (dict(xs=5124), MISALIGNED),
+    (dict(kind=1, scale=FAKE, y=YA + 4), MISALIGNED), (dict(kind=1, scale=FAKE + 2), MISALIGNED),
+    (dict(kind=1, scale=FAKE, ys=5124), MISALIGNED), (dict(width=16 * 256 * 8 + 8), UNSUPPORTED),
+])
+def test_add_rms_norm_refusals(kwargs, code):
+    assert addrms(**kwargs) == code
+    assert qkr.last_error() != ""
+
+
+def test_add_rms_norm_zero_rows_is_a_noop():
+    assert addrms(rows=0, x=None, r=None, s=None, y=None, w=None) == OK
+    assert qkr.lib().qkr_debug_fp8_e4m3(None, 0, None, None, None) == OK
+    assert qkr.lib().qkr_debug_fp8_e4m3(None, 5, None, None, None) == INVALID
+
+
+# ---------------------------------------------------------------------------
 # qk_norm_rope refusals
 # ---------------------------------------------------------------------------
 

@@ -10,7 +10,7 @@ import torch
 import oracle
 import transformer_qk_rmsnorm_amd as qkr
 import workloads as W
-from parity import assert_bf16_close, assert_f32_close
+from parity import assert_bf16_close, assert_f32_close, assert_fp8_close
 
 pytestmark = pytest.mark.gpu
 
@@ -576,3 +576,112 @@ def test_joint_head_dim_80_staged():
     assert_bf16_close(host(q), rq, 80, "neox", "joint q")
     assert_bf16_close(host(k), rk, 80, "neox", "joint k")
     assert np.array_equal(host(v), rv)
+
+
+# ---------------------------------------------------------------------------
+# residual add + RMSNorm, static FP8 output
+# ---------------------------------------------------------------------------
+
+def _fp8_codes(t):
+    return t.view(torch.uint8).cpu().numpy()
+
+
+def test_fp8_encoder_matches_oracle_bitwise():
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    vals = oracle.fp8_e4m3_decode(codes).astype(np.float32)
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)   # exact in fp32
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([vals, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                         rng.uniform(-500, 500, 20000), rng.uniform(-2 ** -5, 2 ** -5, 20000),
+                         np.exp2(rng.uniform(-140, 12, 20000)), [0.0, 448.0, 464.0, 1e30, 3.4e38]]).astype(np.float32)
+    xs = np.concatenate([xs, -xs])
+    got = qkr.debug_fp8_e4m3(gpu(torch.from_numpy(xs))).cpu().numpy()
+    assert np.array_equal(got, oracle.fp8_e4m3_encode(xs))
+
+
+@pytest.mark.parametrize("scale", [0.02, 1.0 / 3.0, 3.7, 0.1, 1e-3, 65.5])
+def test_fp8_codes_of_the_kernel_quotient(scale):
+    """Codes of the kernel's y / scale (reciprocal, one FMA remainder, one FMA
+    correction) equal the codes of the correctly rounded fp32 quotient, on
+    values across the range the quotient can take."""
+    rng = np.random.default_rng(int(scale * 1e4))
+    ys = np.concatenate([rng.normal(0, 3, 200000), np.exp2(rng.uniform(-30, 8, 200000)),
+                         rng.uniform(-448 * scale, 448 * scale, 200000)]).astype(np.float32)
+    sc = np.float32(scale)
+    quo = (ys / sc).astype(np.float32)                       # numpy: correctly rounded fp32 division
+    got = qkr.debug_fp8_e4m3(gpu(torch.from_numpy(ys)), gpu(torch.tensor([scale], dtype=torch.float32)))
+    ref = oracle.fp8_e4m3_encode(quo)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def _addrms_case(rows, width, act, seed):
+    x = W.to_dtype(W.normal((rows, width), 0.0, 1.0, 41, seed, 0), act)
+    r = W.to_dtype(W.normal((rows, width), 0.0, 1.0, 41, seed, 1), act)
+    w = W.to_dtype(W.normal((width,), 1.0, 0.1, 41, seed, 2), act)
+    return x, r, w
+
+
+@pytest.mark.parametrize("rows", [1, 7, 300, 4096])
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("out", ["act", "fp8_e4m3"])
+def test_add_rms_norm(rows, act, out):
+    width = 5120
+    x, r, w = _addrms_case(rows, width, act, rows)
+    scale = torch.tensor([0.02], dtype=torch.float32)
+    gr = gpu(r)
+    y, s = qkr.add_rms_norm(gpu(x), gpu(w), 1e-6, residual=gr, out_dtype=None if out == "act" else out,
+                            scale=gpu(scale))
+    assert s.data_ptr() == gr.data_ptr()                     # updated in place
+    name = qkr.last_variant()
+    assert ":add" in name and (":fp8" in name) == (out != "act"), name
+    rs, ry = oracle.add_rms_norm(W.as_f32(x), W.as_f32(w), 1e-6, W.as_f32(r), act,
+                                 act if out == "act" else out, float(scale[0]))
+    assert np.array_equal(host(s), rs), "the residual stream must be bit-exact"
+    if out == "act":
+        check(host(y), ry, act, what=f"add_rms_norm y {name}")
+    else:
+        assert_fp8_close(_fp8_codes(y), ry, what=f"add_rms_norm fp8 {name}")
+
+
+@pytest.mark.parametrize("variant", ["rms:rows", "rms:wide", "rms:split"])
+def test_add_rms_norm_variants_and_in_place_on_x(variant):
+    """Every row variant (the split one is replaced by the workgroup-wide one
+    for the add), with the residual output written over x."""
+    x, r, w = _addrms_case(9, 2048, "bf16", 5)
+    gx = gpu(x)
+    qkr.set_variant_override(variant)
+    try:
+        y, s = qkr.add_rms_norm(gx, gpu(w), 1e-6, residual=gpu(r), residual_out=gx)
+        name = qkr.last_variant()
+    finally:
+        qkr.set_variant_override(None)
+    assert name.startswith("rms:wide" if variant == "rms:split" else variant), name
+    rs, ry = oracle.add_rms_norm(W.as_f32(x), W.as_f32(w), 1e-6, W.as_f32(r), "bf16", "bf16")
+    assert np.array_equal(host(s), rs) and s.data_ptr() == gx.data_ptr()
+    assert_bf16_close(host(y), ry, what=name)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_rms_norm_fp8_without_residual(act):
+    x, _, w = _addrms_case(33, 4096, act, 9)
+    scale = gpu(torch.tensor([0.05], dtype=torch.float32))
+    y, s = qkr.add_rms_norm(gpu(x), gpu(w), 1e-6, out_dtype="fp8_e4m3", scale=scale)
+    assert s is None
+    _, ry = oracle.add_rms_norm(W.as_f32(x), W.as_f32(w), 1e-6, None, act, "fp8_e4m3", 0.05)
+    assert_fp8_close(_fp8_codes(y), ry, what="rms fp8")
+    # plain output without residual equals rms_norm bitwise
+    y2, _ = qkr.add_rms_norm(gpu(x), gpu(w), 1e-6)
+    assert torch.equal(y2, qkr.rms_norm(gpu(x), gpu(w), 1e-6))
+
+
+def test_add_rms_norm_strided_rows_and_separate_output():
+    big = W.to_dtype(W.normal((6, 3 * 1024), 0.0, 1.0, 43), "bf16")
+    x, r = big[:, :1024], big[:, 1024:2048]
+    w = W.to_dtype(W.normal((1024,), 1.0, 0.1, 44), "bf16")
+    gbig = gpu(big)
+    sout = torch.empty((6, 1024), dtype=torch.bfloat16, device=DEV)
+    y, s = qkr.add_rms_norm(gbig[:, :1024], gpu(w), 1e-6, residual=gbig[:, 1024:2048], residual_out=sout)
+    rs, ry = oracle.add_rms_norm(W.as_f32(x), W.as_f32(w), 1e-6, W.as_f32(r), "bf16", "bf16")
+    assert np.array_equal(host(s), rs)
+    assert_bf16_close(host(y), ry)
+    assert torch.equal(gbig[:, 1024:2048].cpu(), r)            # the residual input is untouched

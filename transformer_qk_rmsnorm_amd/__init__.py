@@ -61,6 +61,12 @@ _SIGNATURES = {
     "qkr_rms_norm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
                                     ctypes.c_int32, ctypes.c_void_p]),
+    "qkr_add_rms_norm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]),
+    "qkr_debug_fp8_e4m3": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]),
     "qkr_qk_norm_rope": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_float, _P(_View), _P(_View), ctypes.c_int32, ctypes.c_void_p,
                                         _P(_View), _P(_View), ctypes.c_int32, ctypes.c_void_p, _P(_Rope),
@@ -257,6 +263,78 @@ def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
                             x.shape[0], x.shape[1], float(eps), _dtype_code(x), _stream(dev))
     _check(st, "rms_norm")
     return y
+
+
+def add_rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
+                 residual: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
+                 out_dtype: Optional[str] = None, scale: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None):
+    """Residual add + RMSNorm of x [rows, width] (qkr_add_rms_norm).
+
+    With `residual`, s = x + residual rounded to x's dtype is written to
+    `residual_out` (default: `residual` itself, updated in place) and
+    normalised.  out_dtype None: y in x's dtype; "fp8_e4m3": y as OCP E4M3
+    codes (torch.float8_e4m3fn) of y / scale, `scale` a one-element float32
+    device tensor.  Returns (y, residual_out)."""
+    dev = x.device
+    _on_gpu("x", x, dev)
+    _on_gpu("weight", weight, dev)
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise QkrError("x must be [rows, width] with contiguous rows")
+    if weight.dtype != x.dtype or not weight.is_contiguous() or weight.numel() != x.shape[1]:
+        raise QkrError("weight must be contiguous [width] of x's dtype")
+
+    def rows_like(name, t):
+        _on_gpu(name, t, dev)
+        if t.shape != x.shape or t.dtype != x.dtype or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise QkrError(f"{name} must match x")
+
+    if residual is not None:
+        rows_like("residual", residual)
+        residual_out = residual if residual_out is None else residual_out
+        rows_like("residual_out", residual_out)
+    elif residual_out is not None:
+        raise QkrError("residual_out needs a residual")
+    fp8 = out_dtype == "fp8_e4m3"
+    if out_dtype not in (None, "fp8_e4m3"):
+        raise QkrError(f"unknown out_dtype {out_dtype!r}")
+    ydt = torch.float8_e4m3fn if fp8 else x.dtype
+    y = torch.empty(x.shape, dtype=ydt, device=dev) if out is None else out
+    if y.shape != x.shape or y.dtype != ydt or (y.shape[1] > 1 and y.stride(1) != 1):
+        raise QkrError(f"out must be {tuple(x.shape)} of {ydt}")
+    _on_gpu("out", y, dev)
+    if fp8:
+        if scale is None:
+            raise QkrError("FP8 output needs scale")
+        _on_gpu("scale", scale, dev)
+        if scale.dtype != torch.float32 or scale.numel() != 1:
+            raise QkrError("scale must be a one-element float32 tensor")
+    st = lib().qkr_add_rms_norm(x.data_ptr(), x.stride(0),
+                                residual.data_ptr() if residual is not None else None,
+                                residual.stride(0) if residual is not None else 0,
+                                residual_out.data_ptr() if residual is not None else None,
+                                residual_out.stride(0) if residual is not None else 0,
+                                y.data_ptr(), y.stride(0), 1 if fp8 else 0,
+                                scale.data_ptr() if fp8 else None, weight.data_ptr(),
+                                x.shape[0], x.shape[1], float(eps), _dtype_code(x), _stream(dev))
+    _check(st, "add_rms_norm")
+    return y, residual_out
+
+
+def debug_fp8_e4m3(x: torch.Tensor, scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The row kernel's FP8 E4M3 quantiser applied to a float32 device tensor:
+    uint8 codes of x / scale (or of x when scale is None)."""
+    _on_gpu("x", x, x.device)
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise QkrError("x must be contiguous float32")
+    if scale is not None:
+        _on_gpu("scale", scale, x.device)
+        if scale.dtype != torch.float32 or scale.numel() != 1:
+            raise QkrError("scale must be a one-element float32 tensor")
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().qkr_debug_fp8_e4m3(x.data_ptr(), x.numel(), scale.data_ptr() if scale is not None else None,
+                                    out.data_ptr(), _stream(x.device)), "debug_fp8_e4m3")
+    return out
 
 
 def qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_weight: Optional[torch.Tensor],
@@ -487,6 +565,7 @@ def vit_positions_host(grid_thw, spatial_merge: int):
 
 
 qkr_rms_norm = rms_norm
+qkr_add_rms_norm = add_rms_norm
 qkr_qk_norm_rope = qk_norm_rope
 qkr_joint_qk_norm_rope = joint_qk_norm_rope
 qkr_mrope_cos_sin_setup = mrope_cos_sin_setup

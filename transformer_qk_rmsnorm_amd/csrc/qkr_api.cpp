@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <climits>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "qkr_internal.hpp"
@@ -390,12 +391,120 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
     a.inv_width = 1.0f / (float)width;
     (void)hipGetLastError();
     const char* variant = "";
-    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), g_nt.load(), reinterpret_cast<hipStream_t>(stream),
-                                   &variant);
+    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), g_nt.load(), 0,
+                                   reinterpret_cast<hipStream_t>(stream), &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "rms_norm launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
     return ok();
+}
+
+qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void* r_dev, int64_t r_row_stride,
+                            void* s_dev, int64_t s_row_stride, void* y_dev, int64_t y_row_stride, int32_t y_kind,
+                            const float* scale_dev, const void* weight_dev, int64_t rows, int32_t width, float eps,
+                            int32_t dtype, qkr_stream_t stream)
+{
+    int esize = 0;
+    qkr_status st;
+    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)))
+        return st;
+    if (y_kind != QKR_OUT_ACT && y_kind != QKR_OUT_FP8_E4M3)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown output kind %d", y_kind);
+    const bool fp8 = y_kind == QKR_OUT_FP8_E4M3;
+    const bool add = r_dev != nullptr;
+    if (rows < 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "rows %lld < 0", (long long)rows);
+    if (width <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "width %d must be > 0", width);
+    if (((int64_t)width * esize) % 16 != 0)
+        return fail(QKR_ERR_MISALIGNED, "width %d is not a whole number of 16-byte vectors", width);
+    const int64_t nvec = (int64_t)width * esize / 16;
+    if (nvec > 16 * kThreads)
+        return fail(QKR_ERR_UNSUPPORTED, "width %d exceeds %d elements", width, 16 * kThreads * 16 / esize);
+    if (add != (s_dev != nullptr))
+        return fail(QKR_ERR_INVALID_ARGUMENT, "the residual and the residual output come together (both or neither)");
+    if (fp8 && scale_dev == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "FP8 output needs a device scale");
+    if (rows == 0)
+        return ok();
+    if (x_dev == nullptr || y_dev == nullptr)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "null x or y");
+    if ((st = check_weight("weight", weight_dev)))
+        return st;
+    const int ve = 16 / esize;                     // elements per 16-byte vector = FP8 bytes per store
+    const int64_t y_esize = fp8 ? 1 : esize;
+    if (!aligned(x_dev, 16) || (add && (!aligned(r_dev, 16) || !aligned(s_dev, 16))))
+        return fail(QKR_ERR_MISALIGNED, "x, residual or residual output is not 16-byte aligned");
+    if (!aligned(y_dev, fp8 ? ve : 16) || (fp8 && !aligned(scale_dev, 4)))
+        return fail(QKR_ERR_MISALIGNED, "y or scale is not aligned");
+    if (rows > 1) {
+        const int64_t strides[3] = {x_row_stride, add ? r_row_stride : width, add ? s_row_stride : width};
+        for (int i = 0; i < 3; ++i)
+            if (strides[i] < width || (strides[i] * esize) % 16 != 0)
+                return fail(QKR_ERR_MISALIGNED, "row strides must be >= width and multiples of 16 bytes");
+        if (y_row_stride < width || (y_row_stride * y_esize) % (fp8 ? ve : 16) != 0)
+            return fail(QKR_ERR_MISALIGNED, "y row stride must be >= width and keep rows aligned");
+    }
+    // The residual output may overwrite the residual or x in place (same
+    // rows); any other overlap of the outputs with the inputs is refused.
+    auto span = [&](const void* p, int64_t stride, int64_t es) {
+        const char* b = static_cast<const char*>(p);
+        return std::make_pair(b, b + ((rows - 1) * stride + width) * es);
+    };
+    auto overlap = [](std::pair<const char*, const char*> u, std::pair<const char*, const char*> v) {
+        return u.first < v.second && v.first < u.second;
+    };
+    const auto sx = span(x_dev, x_row_stride, esize), sy = span(y_dev, y_row_stride, y_esize);
+    if (overlap(sy, sx))
+        return fail(QKR_ERR_INVALID_ARGUMENT, "y overlaps x");
+    if (add) {
+        const auto sr = span(r_dev, r_row_stride, esize), so = span(s_dev, s_row_stride, esize);
+        if (overlap(sy, sr) || overlap(sy, so))
+            return fail(QKR_ERR_INVALID_ARGUMENT, "y overlaps the residual");
+        const bool same_r = s_dev == r_dev && s_row_stride == r_row_stride;
+        const bool same_x = s_dev == x_dev && s_row_stride == x_row_stride;
+        if ((overlap(so, sr) && !same_r) || (overlap(so, sx) && !same_x))
+            return fail(QKR_ERR_INVALID_ARGUMENT, "the residual output overlaps an input other than in place");
+    }
+    if (rows * ((nvec + 63) / 64) >= ((int64_t)1 << 31))
+        return fail(QKR_ERR_UNSUPPORTED, "rows %lld exceed the launch grid", (long long)rows);
+
+    RmsArgs a{};
+    a.x = static_cast<const char*>(x_dev);
+    a.y = static_cast<char*>(y_dev);
+    a.w = static_cast<const char*>(weight_dev);
+    a.r = static_cast<const char*>(r_dev);
+    a.s = static_cast<char*>(s_dev);
+    a.scale = scale_dev;
+    a.x_stride = x_row_stride * esize;
+    a.y_stride = y_row_stride * y_esize;
+    a.r_stride = add ? r_row_stride * esize : 0;
+    a.s_stride = add ? s_row_stride * esize : 0;
+    a.rows = rows;
+    a.nvec = (int32_t)nvec;
+    a.eps = eps;
+    a.inv_width = 1.0f / (float)width;
+    (void)hipGetLastError();
+    const char* variant = "";
+    const int mode = (add ? 1 : 0) | (fp8 ? 2 : 0);
+    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), g_nt.load(), mode,
+                                   reinterpret_cast<hipStream_t>(stream), &variant);
+    if (e != hipSuccess)
+        return fail(QKR_ERR_HIP, "add_rms_norm launch: %s", hipGetErrorString(e));
+    std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
+    return ok();
+}
+
+qkr_status qkr_debug_fp8_e4m3(const float* x_dev, int64_t n, const float* scale_dev, uint8_t* out_dev,
+                              qkr_stream_t stream)
+{
+    if (n < 0 || (n > 0 && (x_dev == nullptr || out_dev == nullptr)))
+        return fail(QKR_ERR_INVALID_ARGUMENT, "debug_fp8_e4m3: null pointers or negative n");
+    if (n >= ((int64_t)1 << 38))
+        return fail(QKR_ERR_UNSUPPORTED, "debug_fp8_e4m3: n too large");
+    (void)hipGetLastError();
+    return hip_status(launch_debug_fp8(x_dev, n, scale_dev, out_dev, reinterpret_cast<hipStream_t>(stream)),
+                      "debug_fp8_e4m3 launch");
 }
 
 qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int32_t dtype, float eps,

@@ -22,6 +22,13 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 struct F32 {
     static constexpr int VE = 4;
+    __device__ __forceinline__ static uint4 add(const uint4& x, const uint4& r)
+    {
+        return make_uint4(__float_as_uint(__uint_as_float(x.x) + __uint_as_float(r.x)),
+                          __float_as_uint(__uint_as_float(x.y) + __uint_as_float(r.y)),
+                          __float_as_uint(__uint_as_float(x.z) + __uint_as_float(r.z)),
+                          __float_as_uint(__uint_as_float(x.w) + __uint_as_float(r.w)));
+    }
     __device__ __forceinline__ static void unpack(const uint4& v, float* x)
     {
         x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
@@ -45,6 +52,10 @@ struct F32 {
 
 struct BF16 {
     static constexpr int VE = 8;
+    // The sum of two bf16 vectors rounded once to bf16 (the fp32 sum of two
+    // bf16 values is exact unless their exponents differ by more than 15, and
+    // then the smaller one is far below half a bf16 step: one rounding either way).
+    __device__ __forceinline__ static uint4 add(const uint4& x, const uint4& r);
     __device__ __forceinline__ static void unpack(const uint4& v, float* x)
     {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -87,6 +98,41 @@ struct BF16 {
     }
     __device__ __forceinline__ static bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 };
+
+__device__ __forceinline__ uint4 BF16::add(const uint4& x, const uint4& r)
+{
+    float a[8], b[8];
+    unpack(x, a);
+    unpack(r, b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        a[i] += b[i];
+    return pack(a);
+}
+
+// y / scale rounded to nearest fp32 from the reciprocal inv = 1 / scale
+// (computed once, correctly rounded): q = y * inv, the remainder y - scale * q
+// exactly by one FMA, and one correction q + r * inv (a reciprocal-based
+// division with one Newton-style correction step; the tests compare it with
+// the correctly rounded quotient bit for bit).  |y / scale| must stay below
+// the fp32 overflow threshold.
+__device__ __forceinline__ float div_by_scale(float y, float scale, float inv)
+{
+    const float q = y * inv;
+    const float r = fmaf(-scale, q, y);
+    return fmaf(r, inv, q);
+}
+
+// Four OCP FP8 E4M3 codes (lowest byte first) of finite fp32 values: clamp to
+// +-448 (saturation), then gfx950's packed conversion, which rounds half to
+// even on the E4M3 grid and keeps subnormals (checked against the oracle's
+// encoder on every tie and its neighbours).
+__device__ __forceinline__ uint32_t fp8_e4m3_pack4(float a, float b, float c, float d)
+{
+    const auto clamp = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(a), clamp(b), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp(c), clamp(d), lo, true);
+}
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 

@@ -84,8 +84,13 @@ struct RmsArgs {
     const char* x;
     char* y;
     const char* w;
+    const char* r;              // residual (add modes)
+    char* s;                    // new residual stream (add modes)
+    const float* scale;         // static FP8 scale (FP8 mode)
     int64_t x_stride;           // bytes
     int64_t y_stride;           // bytes
+    int64_t r_stride;           // bytes
+    int64_t s_stride;           // bytes
     int64_t rows;
     int32_t nvec;               // 16-byte vectors per row
     int32_t splits;             // workgroups per row (split variant)
@@ -190,8 +195,12 @@ NormRopeFn pick_norm_rope(int32_t dtype, int rope, int32_t pairing, bool nt, boo
 // nontemporal row accesses, 0 plain.
 hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, int np, int lpr, int stage,
                             int nt, hipStream_t stream, const char** variant);
-// rms: kind 0 rows, 1 split, 2 wide; -1 = automatic.
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, hipStream_t stream, const char** variant);
+// rms: kind 0 rows, 1 split, 2 wide; -1 = automatic.  mode: bit 0 residual
+// add, bit 1 FP8 E4M3 output (add modes never take the split variant: its
+// workgroups read the whole row while others write the residual).
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, int mode, hipStream_t stream,
+                           const char** variant);
+hipError_t launch_debug_fp8(const float* x, int64_t n, const float* scale, uint8_t* out, hipStream_t stream);
 hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream);
 hipError_t launch_debug_axis_map(const RopeArgs& r, int32_t n_pairs, int32_t* out, hipStream_t stream);
 hipError_t launch_debug_vit_positions(const VitArgs& a, int32_t* out, hipStream_t stream);

@@ -33,10 +33,12 @@ namespace {
 // Every lane holds VPL 16-byte vectors of the row, all loaded up front
 // ([VecRMS]: 16-byte vectorized reads of the row).
 // ---------------------------------------------------------------------------
-template <class E, int VPL, int KIND, bool NT>
+template <class E, int VPL, int KIND, bool NT, int MODE>
 __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
 {
     constexpr int VE = E::VE;
+    constexpr bool ADD = (MODE & 1) != 0, FP8 = (MODE & 2) != 0;
+    static_assert(!(ADD && KIND == 1), "the split variant cannot update the residual in place");
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t row;
@@ -68,6 +70,28 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
         const int v = first + k * step;
         d[k] = v < a.nvec ? load_row16<NT>(x + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
     }
+    if constexpr (ADD) {
+        // Residual add ([Vulkan] decode RmsNorm: the residual stream is held
+        // bit-exactly by rounding the sum in registers): s = x + r rounded once
+        // to the activation type is stored as the new residual and normalised.
+        // Every lane has read all of its vectors of x and r before it writes,
+        // and no other lane touches them, so s may overwrite r or x in place.
+        const char* r = a.r + row * a.r_stride;
+        uint4 rv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = first + k * step;
+            rv[k] = v < a.nvec ? load_row16<NT>(r + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
+        }
+        char* sres = a.s + row * a.s_stride;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = first + k * step;
+            d[k] = E::add(d[k], rv[k]);   // zero + zero on lanes past the row
+            if (v < a.nvec)
+                store_row16<NT>(sres + (int64_t)v * 16, d[k]);
+        }
+    }
     float ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
@@ -84,6 +108,11 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
             ss += part[w];
     }
     const float rrms = rsqrtf(ss * a.inv_width + a.eps);
+    float scale = 1.0f, inv_scale = 1.0f;
+    if constexpr (FP8) {
+        scale = *a.scale;   // wave-uniform
+        inv_scale = 1.0f / scale;
+    }
 
     int lo = 0, hi = a.nvec;
     if constexpr (KIND == 1) {
@@ -101,9 +130,52 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
 #pragma unroll
             for (int e = 0; e < VE; ++e)
                 xv[e] = xv[e] * rrms * wv[e];
-            store_row16<NT>(y + (int64_t)v * 16, E::pack(xv));
+            if constexpr (FP8) {
+                // One E4M3 code per element (VE bytes per vector): the code of
+                // the fp32 quotient y / scale.
+                uint32_t c[VE / 4];
+#pragma unroll
+                for (int q = 0; q < VE / 4; ++q)
+                    c[q] = fp8_e4m3_pack4(div_by_scale(xv[4 * q], scale, inv_scale),
+                                          div_by_scale(xv[4 * q + 1], scale, inv_scale),
+                                          div_by_scale(xv[4 * q + 2], scale, inv_scale),
+                                          div_by_scale(xv[4 * q + 3], scale, inv_scale));
+                char* dst = y + (int64_t)v * VE;
+                if constexpr (VE == 8) {
+                    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+                    const u32x2_t pk = {c[0], c[1]};
+                    if constexpr (NT)
+                        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_t*>(dst));
+                    else
+                        *reinterpret_cast<u32x2_t*>(dst) = pk;
+                } else {
+                    if constexpr (NT)
+                        __builtin_nontemporal_store(c[0], reinterpret_cast<uint32_t*>(dst));
+                    else
+                        *reinterpret_cast<uint32_t*>(dst) = c[0];
+                }
+            } else {
+                store_row16<NT>(y + (int64_t)v * 16, E::pack(xv));
+            }
         }
     }
+}
+
+// The row kernel's quotient and E4M3 encoding, element by element (tests
+// compare them with the correctly rounded quotient and the oracle's encoder
+// bit for bit).  scale == nullptr: the values are encoded as they are.
+__global__ __launch_bounds__(kThreads) void debug_fp8_kernel(const float* x, int64_t n, const float* scale,
+                                                             uint8_t* out)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n)
+        return;
+    float v = x[i];
+    if (scale != nullptr) {
+        const float sc = *scale;
+        v = div_by_scale(v, sc, 1.0f / sc);
+    }
+    out[i] = (uint8_t)(fp8_e4m3_pack4(v, 0.0f, 0.0f, 0.0f) & 0xFFu);
 }
 
 // ---------------------------------------------------------------------------
@@ -159,27 +231,37 @@ __global__ __launch_bounds__(kThreads) void debug_vit_kernel(const VitArgs a, in
 // ---------------------------------------------------------------------------
 using RmsFn = void (*)(RmsArgs);
 
-template <class E, int KIND, bool NT>
+template <class E, int KIND, bool NT, int MODE>
 RmsFn pick_vpl(int vpl)
 {
     switch (vpl) {
-    case 1: return rms_kernel<E, 1, KIND, NT>;
-    case 2: return rms_kernel<E, 2, KIND, NT>;
-    case 3: return rms_kernel<E, 3, KIND, NT>;
-    case 4: return rms_kernel<E, 4, KIND, NT>;
-    case 5: return rms_kernel<E, 5, KIND, NT>;
-    case 6: return rms_kernel<E, 6, KIND, NT>;
-    case 8: return rms_kernel<E, 8, KIND, NT>;
-    case 10: return rms_kernel<E, 10, KIND, NT>;
-    case 12: return rms_kernel<E, 12, KIND, NT>;
-    default: return rms_kernel<E, 16, KIND, NT>;
+    case 1: return rms_kernel<E, 1, KIND, NT, MODE>;
+    case 2: return rms_kernel<E, 2, KIND, NT, MODE>;
+    case 3: return rms_kernel<E, 3, KIND, NT, MODE>;
+    case 4: return rms_kernel<E, 4, KIND, NT, MODE>;
+    case 5: return rms_kernel<E, 5, KIND, NT, MODE>;
+    case 6: return rms_kernel<E, 6, KIND, NT, MODE>;
+    case 8: return rms_kernel<E, 8, KIND, NT, MODE>;
+    case 10: return rms_kernel<E, 10, KIND, NT, MODE>;
+    case 12: return rms_kernel<E, 12, KIND, NT, MODE>;
+    default: return rms_kernel<E, 16, KIND, NT, MODE>;
     }
 }
 
+// The plain norm comes with and without nontemporal accesses; the add and
+// FP8 modes are nontemporal only, and the add modes skip the split variant.
 template <class E, int KIND>
-RmsFn pick_rms_nt(bool nt, int vpl)
+RmsFn pick_rms_mode(bool nt, int mode, int vpl)
 {
-    return nt ? pick_vpl<E, KIND, true>(vpl) : pick_vpl<E, KIND, false>(vpl);
+    switch (mode) {
+    case 0: return nt ? pick_vpl<E, KIND, true, 0>(vpl) : pick_vpl<E, KIND, false, 0>(vpl);
+    case 2: return pick_vpl<E, KIND, true, 2>(vpl);
+    default:
+        if constexpr (KIND == 1)
+            return nullptr;
+        else
+            return mode == 1 ? pick_vpl<E, KIND, true, 1>(vpl) : pick_vpl<E, KIND, true, 3>(vpl);
+    }
 }
 
 int round_vpl(int need)
@@ -262,14 +344,21 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     return hipGetLastError();
 }
 
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, hipStream_t stream, const char** variant)
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, int mode, hipStream_t stream,
+                           const char** variant)
 {
     if (a.rows == 0)
         return hipSuccess;
+    const bool add = (mode & 1) != 0;
     if (kind < 0) {
-        // Few rows: spread each row over several compute units.
-        kind = a.rows < 256 ? 1 : 0;
+        // Few rows: spread each row over several compute units (split), or
+        // with a residual add over a whole workgroup (wide).
+        kind = a.rows < 256 ? (add ? 2 : 1) : 0;
     }
+    if (add && kind == 1)
+        kind = 2;
+    if (mode != 0)
+        nt = 1;
     int vpl = round_vpl(kind == 2 ? (a.nvec + kThreads - 1) / kThreads : (a.nvec + 63) / 64);
     if (vpl < 0 && kind != 2) {
         kind = 2;
@@ -292,15 +381,29 @@ hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, hipStream
     const bool use_nt = nt != 0;
     RmsFn fn;
     if (dtype == kBF16)
-        fn = kind == 0 ? pick_rms_nt<BF16, 0>(use_nt, vpl)
-                       : (kind == 1 ? pick_rms_nt<BF16, 1>(use_nt, vpl) : pick_rms_nt<BF16, 2>(use_nt, vpl));
+        fn = kind == 0 ? pick_rms_mode<BF16, 0>(use_nt, mode, vpl)
+                       : (kind == 1 ? pick_rms_mode<BF16, 1>(use_nt, mode, vpl)
+                                    : pick_rms_mode<BF16, 2>(use_nt, mode, vpl));
     else
-        fn = kind == 0 ? pick_rms_nt<F32, 0>(use_nt, vpl)
-                       : (kind == 1 ? pick_rms_nt<F32, 1>(use_nt, vpl) : pick_rms_nt<F32, 2>(use_nt, vpl));
+        fn = kind == 0 ? pick_rms_mode<F32, 0>(use_nt, mode, vpl)
+                       : (kind == 1 ? pick_rms_mode<F32, 1>(use_nt, mode, vpl)
+                                    : pick_rms_mode<F32, 2>(use_nt, mode, vpl));
+    if (fn == nullptr)
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
-    snprintf(g_variant, sizeof(g_variant), "rms:%s:nt%d:vpl%d:%s",
-             kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"), (int)use_nt, vpl, dtype == kBF16 ? "bf16" : "f32");
+    snprintf(g_variant, sizeof(g_variant), "rms:%s:nt%d:vpl%d:%s%s%s",
+             kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"), (int)use_nt, vpl, dtype == kBF16 ? "bf16" : "f32",
+             add ? ":add" : "", (mode & 2) ? ":fp8" : "");
     *variant = g_variant;
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_fp8(const float* x, int64_t n, const float* scale, uint8_t* out, hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(debug_fp8_kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, x, n, scale, out);
     return hipGetLastError();
 }
 
