@@ -73,6 +73,12 @@ def _load():
         lib.oracle_add_rms_norm.argtypes = [_f32p, _f32p, ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_float,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _f32p, _f32p,
                                             ctypes.POINTER(ctypes.c_uint8)]
+        lib.oracle_qk_norm_rope_cache.restype = None
+        lib.oracle_qk_norm_rope_cache.argtypes = [_f32p, ctypes.c_int32, _f32p, _f32p, ctypes.c_int32,
+                                                  ctypes.c_int64, ctypes.c_int32, _f32p, _f32p, ctypes.c_float,
+                                                  ctypes.c_int32, ctypes.POINTER(_Rope),
+                                                  ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, _f32p, _f32p,
+                                                  _f32p]
         lib.oracle_axis.restype = ctypes.c_int32
         lib.oracle_axis.argtypes = [ctypes.POINTER(_Rope), ctypes.c_int32]
         lib.oracle_qk_norm_rope.restype = None
@@ -227,6 +233,34 @@ def qk_norm_rope(x, weight, eps, rope=None, out_dtype="bf16"):
     lib.oracle_qk_norm_rope(xp, tokens, heads, head_dim, wp, eps, _OUT[out_dtype], rp,
                             out.ctypes.data_as(_f32p))
     return out
+
+
+def qk_norm_rope_cache(q, k, v, q_weight, k_weight, eps, rope, slots, k_cache, v_cache, out_dtype="bf16"):
+    """Q out [tokens, Hq, D] plus the caches [num_slots, Hkv, D] after writing
+    token t's rotated K and its V into row slots[t] (copies of the given
+    caches are updated and returned: (q_out, k_cache, v_cache))."""
+    lib = _load()
+    q, qp = _f32(q)
+    k, kp = _f32(k)
+    tokens, qh, d = q.shape
+    kvh = k.shape[1]
+    if v is not None:
+        v, vp = _f32(v)
+    else:
+        vp = None
+    wq, wqp = _f32(q_weight)
+    wk, wkp = _f32(k_weight)
+    sl = np.ascontiguousarray(slots, dtype=np.int64)
+    kc = np.array(k_cache, dtype=np.float32, copy=True)
+    vc = np.array(v_cache, dtype=np.float32, copy=True) if v_cache is not None else None
+    qo = np.empty_like(q)
+    r = rope._c() if rope is not None else None
+    lib.oracle_qk_norm_rope_cache(qp, qh, kp, vp, kvh, tokens, d, wqp, wkp, eps, _OUT[out_dtype],
+                                  ctypes.byref(r) if r is not None else None,
+                                  sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), kc.shape[0],
+                                  qo.ctypes.data_as(_f32p), kc.ctypes.data_as(_f32p),
+                                  vc.ctypes.data_as(_f32p) if vc is not None else None)
+    return qo, kc, vc
 
 
 def joint_qk_norm_rope(txt, img, eps, rope, out_dtype="bf16"):

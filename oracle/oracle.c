@@ -302,6 +302,34 @@ void oracle_qk_norm_rope(const float* x, int64_t tokens, int32_t heads, int32_t 
     free(n);
 }
 
+/* [IMROPE] "The change": the rotation kernel has a set_rows twin, which
+ * writes each rotated row into a destination row picked by an index (the
+ * step that stores K into the KV cache).  Reading: row slots[t] of the cache
+ * receives token t's K (normalised and rotated) and V (unchanged) for every
+ * KV head; a slot outside the cache writes nothing (the usual mark of a
+ * padding token); a mapping that sends two tokens to one slot leaves that
+ * slot's content unspecified, so the tests use injective mappings. */
+void oracle_qk_norm_rope_cache(const float* q, int32_t q_heads, const float* k, const float* v,
+                               int32_t kv_heads, int64_t tokens, int32_t head_dim, const float* q_weight,
+                               const float* k_weight, float eps, int32_t out_kind, const oracle_rope* rope,
+                               const int64_t* slots, int64_t num_slots, float* q_out, float* k_cache,
+                               float* v_cache)
+{
+    const int64_t row = (int64_t)kv_heads * head_dim;
+    float* k_rot = (float*)malloc(sizeof(float) * (size_t)(tokens * row > 0 ? tokens * row : 1));
+    oracle_qk_norm_rope(q, tokens, q_heads, head_dim, q_weight, eps, out_kind, rope, q_out);
+    oracle_qk_norm_rope(k, tokens, kv_heads, head_dim, k_weight, eps, out_kind, rope, k_rot);
+    for (int64_t t = 0; t < tokens; ++t) {
+        const int64_t slot = slots[t];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        memcpy(k_cache + slot * row, k_rot + t * row, sizeof(float) * (size_t)row);
+        if (v != NULL && v_cache != NULL)
+            memcpy(v_cache + slot * row, v + t * row, sizeof(float) * (size_t)row);
+    }
+    free(k_rot);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Joint text/image op                                                       */
 /* ------------------------------------------------------------------------ */

@@ -72,6 +72,18 @@ void oracle_qk_norm_rope(const float* x, int64_t tokens, int32_t heads, int32_t 
                          const float* weight, float eps, int32_t out_kind,
                          const oracle_rope* rope, float* out);
 
+/* QK RMSNorm + RoPE with the K rows written into a cache: Q as
+ * oracle_qk_norm_rope into q_out [tokens][q_heads][d]; the rotated K rows of
+ * token t and its V rows (copied unchanged) go to row slots[t] of k_cache and
+ * v_cache [num_slots][kv_heads][d]; a slot outside [0, num_slots) writes
+ * nothing, and cache rows no token maps to are left as they are.  v and
+ * v_cache may be NULL together. */
+void oracle_qk_norm_rope_cache(const float* q, int32_t q_heads, const float* k, const float* v,
+                               int32_t kv_heads, int64_t tokens, int32_t head_dim, const float* q_weight,
+                               const float* k_weight, float eps, int32_t out_kind, const oracle_rope* rope,
+                               const int64_t* slots, int64_t num_slots, float* q_out, float* k_cache,
+                               float* v_cache);
+
 /* Joint text/image op: each stream is normalised with its own weights, the
  * streams are concatenated text first and the joint sequence is rotated with
  * positions indexed by joint token.  V rows are copied unchanged.

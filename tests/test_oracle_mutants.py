@@ -58,6 +58,10 @@ MUTANTS = {
     "add_norm_sum_unrounded": ("s[i] = round_out(sum, act_kind);", "s[i] = (float)sum;"),
     "add_norm_residual_ignored": ("? (double)xr[i] + (double)r[row * width + i] : (double)xr[i]",
                                   "? (double)xr[i] : (double)xr[i]"),
+    "cache_written_at_token_row": ("memcpy(k_cache + slot * row, k_rot + t * row,", "memcpy(k_cache + t * row, k_rot + t * row,"),
+    "cache_v_receives_k": ("memcpy(v_cache + slot * row, v + t * row,", "memcpy(v_cache + slot * row, k_rot + t * row,"),
+    "cache_last_slot_dropped": ("if (slot < 0 || slot >= num_slots)\n            continue;",
+                                "if (slot < 0 || slot >= num_slots - 1)\n            continue;"),
     "passthrough_skipped": ("for (int32_t i = r; i < d; ++i)\n        out[i] = round_out(n[i], out_kind);",
                             "for (int32_t i = r; i < d; ++i)\n        out[i] = 0.0f;"),
 }

@@ -585,3 +585,54 @@ def test_add_rms_norm_fp8_codes(scale):
     assert (q[~inside] == np.where(quo[~inside] > 0, 0x7E, 0xFE)).all()
     if scale == 0.005:
         assert (~inside).any() and inside.any()
+
+
+# ---------------------------------------------------------------------------
+# K (and V) written into cache rows picked per token
+# ---------------------------------------------------------------------------
+
+def _cache_case(tokens=23, qh=6, kvh=2, d=64, seed=31):
+    rng = _rng(seed)
+    q = rng.normal(0, 1, (tokens, qh, d)).astype(np.float32)
+    k = rng.normal(0, 1, (tokens, kvh, d)).astype(np.float32)
+    v = rng.normal(0, 1, (tokens, kvh, d)).astype(np.float32)
+    wq = rng.normal(1, 0.1, d).astype(np.float32)
+    wk = rng.normal(1, 0.1, d).astype(np.float32)
+    pos = rng.integers(0, 3000, (1, tokens)).astype(np.int32)
+    rope = oracle.Rope("1d", d, "neox", inv_freq=inv_freq_ladder(1e4, d), positions=pos)
+    return q, k, v, wq, wk, rope
+
+
+def test_cache_write_with_identity_slots_is_the_plain_op():
+    q, k, v, wq, wk, rope = _cache_case()
+    n = q.shape[0]
+    kc0 = np.full((n,) + k.shape[1:], np.nan, np.float32)
+    qo, kc, vc = oracle.qk_norm_rope_cache(q, k, v, wq, wk, 1e-6, rope, np.arange(n), kc0, kc0.copy())
+    assert np.array_equal(qo, oracle.qk_norm_rope(q, wq, 1e-6, rope))
+    assert np.array_equal(kc, oracle.qk_norm_rope(k, wk, 1e-6, rope))
+    assert np.array_equal(vc, v)
+
+
+def test_cache_write_reversed_and_sparse_slots():
+    q, k, v, wq, wk, rope = _cache_case(seed=32)
+    n = q.shape[0]
+    kn = oracle.qk_norm_rope(k, wk, 1e-6, rope)
+    kc0 = np.full((n,) + k.shape[1:], -7.0, np.float32)
+    _, kc, vc = oracle.qk_norm_rope_cache(q, k, v, wq, wk, 1e-6, rope, np.arange(n)[::-1], kc0, kc0.copy())
+    assert np.array_equal(kc, kn[::-1]) and np.array_equal(vc, v[::-1])
+    # a larger cache, an injective random map with padding (-1) and out-of-range slots
+    rng = _rng(33)
+    num_slots = 101
+    slots = rng.permutation(num_slots)[:n].astype(np.int64)
+    slots[[2, 9, 15]] = -1
+    slots[[4, 20]] = [num_slots, 10 ** 12]
+    slots[0] = num_slots - 1
+    kc0 = np.full((num_slots,) + k.shape[1:], -7.0, np.float32)
+    _, kc, vc = oracle.qk_norm_rope_cache(q, k, v, wq, wk, 1e-6, rope, slots, kc0, kc0.copy())
+    ok = (slots >= 0) & (slots < num_slots)
+    ref_k, ref_v = kc0.copy(), kc0.copy()
+    ref_k[slots[ok]] = kn[ok]                                # numpy's scatter
+    ref_v[slots[ok]] = v[ok]
+    assert np.array_equal(kc, ref_k) and np.array_equal(vc, ref_v)
+    _, kc_nov, vc_nov = oracle.qk_norm_rope_cache(q, k, None, wq, wk, 1e-6, rope, slots, kc0, None)
+    assert np.array_equal(kc_nov, ref_k) and vc_nov is None
