@@ -2,7 +2,7 @@
 """Benchmark of the fused QK RMSNorm + RoPE hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload joint|joint-neox|imrope|vit|vit-fused|rows1|rows32|
-                                                 rows4096|addrms4096|addrms4096-fp8|addrms1|tiny|copy]
+                                                 rows4096|addrms4096|addrms4096-fp8|addrms1|cache|tiny|copy]
 
 Prints one JSON line.  A step is one pass of the workload's hot path over one
 batch of synthetic input already resident in HBM (default workload: the joint
@@ -25,6 +25,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -40,7 +42,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint",
                     choices=["joint", "joint-neox", "imrope", "vit", "vit-fused", "rows1", "rows32", "rows4096",
-                             "addrms4096", "addrms4096-fp8", "addrms1", "tiny", "copy"])
+                             "addrms4096", "addrms4096-fp8", "addrms1", "cache", "tiny", "copy"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--variant", default=None,
@@ -307,6 +309,63 @@ def build_rows(t):
     return w
 
 
+def build_cache():
+    """IMROPE QK norm + RoPE of 8192 tokens (16 Q, 8 K/V heads x 128, bf16) with
+    K and V written into a paged cache (2048 blocks x 16 slots) through a
+    random injective slot mapping, one launch."""
+    import torch
+
+    import transformer_qk_rmsnorm_amd as qkr
+    import workloads as W
+
+    case = W.imrope()
+    dev = torch.device("cuda")
+    T, H, KV, D = case.q.shape[0], case.q.shape[1], case.k.shape[1], 128
+    blocks, bs = 2048, 16
+    v_host = W.to_dtype(W.normal((T, KV, D), 0.0, 1.0, 61), "bf16")
+    slots_host = torch.from_numpy(np.random.default_rng(61).permutation(blocks * bs)[:T].astype(np.int64))
+    pos = torch.from_numpy(case.positions).to(dev)
+    inv = torch.from_numpy(case.inv_freq).to(dev)
+    rope = qkr.Rope("imrope", D, "neox", inv_freq=inv, positions=pos, sections=case.sections)
+    qw, kw = case.q_weight.to(dev), case.k_weight.to(dev)
+    slots = slots_host.to(dev)
+
+    def make_set():
+        q, k, v = case.q.to(dev), case.k.to(dev), v_host.to(dev)
+        kc = torch.zeros((blocks, bs, KV, D), dtype=torch.bfloat16, device=dev)
+        return q, k, v, kc, torch.zeros_like(kc), torch.empty_like(q)
+
+    def step(state):
+        q, k, v, kc, vc, qo = state
+        qkr.qk_norm_rope_cache(q, k, v, qw, kw, kc, vc, slots, case.eps, rope, q_out=qo)
+
+    nbytes = 2 * T * (H + 2 * KV) * D * 2 + T * 8 + case.positions.nbytes + 2 * D * 2 + case.inv_freq.nbytes
+
+    def cpu_step():
+        import oracle
+        orope = oracle.Rope("imrope", D, "neox", inv_freq=case.inv_freq, positions=case.positions,
+                            sections=case.sections)
+        q, k, v = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(v_host)
+        wq, wk = W.as_f32(case.q_weight), W.as_f32(case.k_weight)
+        kc0 = np.zeros((blocks * bs, KV, D), np.float32)
+        sl = slots_host.numpy()
+
+        def run():
+            oracle.qk_norm_rope_cache(q, k, v, wq, wk, case.eps, orope, sl, kc0, kc0)
+        return run
+
+    w = Workload()
+    w.name = "IMROPE QK RMSNorm + RoPE with K/V written into a paged cache by slot mapping"
+    w.config = {"workload": w.name, "tokens": T, "q_heads": H, "kv_heads": KV, "head_dim": D,
+                "sections": list(case.sections), "cache_blocks": blocks, "block_size": bs}
+    w.step_bytes = w.launch_bytes = nbytes
+    w.launches = 1
+    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.dtype = "bf16"
+    w.sample = "all 8192 tokens"
+    return w
+
+
 def build_addrms(t, fp8):
     """Residual add + RMSNorm of bf16 [t, 5120] rows, bf16 or static FP8 E4M3 output."""
     import torch
@@ -498,7 +557,7 @@ def main():
                 "imrope": build_imrope, "vit": build_vit, "vit-fused": build_vit_fused, "rows1": lambda: build_rows(1),
                 "rows32": lambda: build_rows(32), "rows4096": lambda: build_rows(4096), "tiny": build_tiny,
                 "addrms4096": lambda: build_addrms(4096, False), "addrms4096-fp8": lambda: build_addrms(4096, True),
-                "addrms1": lambda: build_addrms(1, False),
+                "addrms1": lambda: build_addrms(1, False), "cache": build_cache,
                 "copy": build_copy}
     w = builders[args.workload]()
     nsets = args.sets or max(3, -(-2 * MALL_BYTES // max(w.step_bytes, 1)))

@@ -158,6 +158,27 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
                             const void* k_weight_dev,
                             const qkr_rope* rope, qkr_stream_t stream);
 
+/* QK RMSNorm + RoPE with K written into a cache ([IMROPE] "The change": the
+ * rotation kernel's set_rows twin, which stores each rotated row into the row
+ * an index picks):
+ *   q_out  = the qk_norm_rope result for q (batch 1: views' stride_batch unused);
+ *   token t's rotated K rows (all kv_heads) -> row slot_mapping_dev[t] of k_cache,
+ *   token t's V rows, copied unchanged      -> the same row of v_cache.
+ * k_cache / v_cache are qkr_views over [num_slots][kv_heads][head_dim] (stride_tok
+ * = elements between slots, e.g. a paged [blocks][block_size][H][D] cache seen
+ * as blocks * block_size slots).  slot_mapping_dev: device int64 [tokens]; a
+ * slot outside [0, num_slots) writes nothing (e.g. -1 for padding tokens);
+ * two tokens mapped to one slot leave that slot's content unspecified; cache
+ * rows no token maps to are untouched.  v and v_cache are both NULL or both
+ * given.  The caches must not overlap the inputs or q_out.  Refusals as for
+ * qkr_qk_norm_rope, plus a null or misaligned slot mapping. */
+qkr_status qkr_qk_norm_rope_cache(int64_t tokens, int32_t head_dim, int32_t dtype, float eps, const qkr_view* q,
+                                  const qkr_view* q_out, int32_t q_heads, const void* q_weight_dev,
+                                  const qkr_view* k, const qkr_view* v, int32_t kv_heads, const void* k_weight_dev,
+                                  const qkr_view* k_cache, const qkr_view* v_cache,
+                                  const int64_t* slot_mapping_dev, int64_t num_slots, const qkr_rope* rope,
+                                  qkr_stream_t stream);
+
 /* One stream (text or image) of the joint op: Q, K, V views of `tokens`
  * tokens (e.g. chunked views of one packed QKV projection) and the stream's
  * own q/k norm weights [head_dim]. */

@@ -309,3 +309,38 @@ def test_vit_fused_refusals():
     assert call([[1, 64, 64]], qw=None) == INVALID
     assert call([[1, 64, 64]], pairing=7) == INVALID
     assert call([]) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# qk_norm_rope_cache refusals
+# ---------------------------------------------------------------------------
+
+def qkcache(tokens=64, head_dim=128, dtype=qkr.BF16, eps=1e-6, qh=16, kvh=8, qw=FAKE, kw=FAKE, v="view",
+            vc="view", slots=FAKE, num_slots=4096, kc=None, rope="default"):
+    q, qo, k = view(st=16 * 128), view(st=16 * 128), view(st=8 * 128)
+    kc = kc or view(st=8 * 128)
+    vv = view(st=8 * 128) if v == "view" else v
+    vcc = view(st=8 * 128) if vc == "view" else vc
+    r = rope_c(mode=0, sections=(0, 0, 0, 0)) if rope == "default" else rope
+    return qkr.lib().qkr_qk_norm_rope_cache(tokens, head_dim, dtype, eps, ctypes.byref(q), ctypes.byref(qo), qh, qw,
+                                            ctypes.byref(k), ctypes.byref(vv) if vv is not None else None, kvh, kw,
+                                            ctypes.byref(kc), ctypes.byref(vcc) if vcc is not None else None, slots,
+                                            num_slots, ctypes.byref(r) if r is not None else None, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(slots=None), INVALID), (dict(slots=FAKE + 4), MISALIGNED), (dict(v=None), INVALID),
+    (dict(vc=None), INVALID), (dict(num_slots=-1), INVALID), (dict(tokens=-1), INVALID),
+    (dict(kc=view(ptr=FAKE + 8, st=8 * 128)), MISALIGNED), (dict(kc=view(ptr=None)), INVALID),
+    (dict(kw=None), INVALID), (dict(head_dim=100), MISALIGNED), (dict(dtype=9), INVALID),
+    (dict(rope=rope_c(mode=0, rotary_dim=129, sections=(0, 0, 0, 0))), INVALID),
+    (dict(tokens=1 << 31), UNSUPPORTED),
+])
+def test_qk_norm_rope_cache_refusals(kwargs, code):
+    assert qkcache(**kwargs) == code
+    assert qkr.last_error() != ""
+
+
+def test_qk_norm_rope_cache_empty_calls_are_noops():
+    assert qkcache(tokens=0, slots=None) == OK
+    assert qkcache(qh=0, kvh=0, qw=None, kw=None, slots=None) == OK

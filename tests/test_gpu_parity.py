@@ -685,3 +685,76 @@ def test_add_rms_norm_strided_rows_and_separate_output():
     assert np.array_equal(host(s), rs)
     assert_bf16_close(host(y), ry)
     assert torch.equal(gbig[:, 1024:2048].cpu(), r)            # the residual input is untouched
+
+
+# ---------------------------------------------------------------------------
+# K and V written into cache rows picked per token
+# ---------------------------------------------------------------------------
+
+def _cache_case(tokens, qh, kvh, d, dtype, seed):
+    case = W.tiny(tokens=tokens, heads=qh, head_dim=d, dtype=dtype, seed_stream=seed)
+    k = W.to_dtype(W.normal((tokens, kvh, d), 0.0, 1.0, 51, seed, 0), dtype)
+    v = W.to_dtype(W.normal((tokens, kvh, d), 0.0, 1.0, 51, seed, 1), dtype)
+    pos = np.random.default_rng(seed).integers(0, 8000, (1, tokens)).astype(np.int32)
+    inv = W.inv_freq_ladder(1e4, d)
+    return case, k, v, pos, inv
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 80)])
+def test_cache_write_identity_slots_equal_plain_op(dtype, d):
+    case, k, v, pos, inv = _cache_case(57, 8, 2, d, dtype, d)
+    rope = qkr.Rope("1d", d, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    kc = torch.full((57, 2, d), float("nan"), dtype=case.q.dtype, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    qo = qkr.qk_norm_rope_cache(gpu(case.q), gpu(k), gpu(v), gpu(case.q_weight), gpu(case.k_weight), kc, vc,
+                                gpu(torch.arange(57, dtype=torch.int64)), case.eps, rope)
+    pq, pk = qkr.qk_norm_rope(gpu(case.q), gpu(k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+    assert torch.equal(qo, pq) and torch.equal(kc, pk) and torch.equal(vc, gpu(v))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cache_write_paged_sparse_slots(dtype):
+    """A paged [blocks, block_size, H, D] cache, an injective random map with
+    padding (-1) and out-of-range slots; unmapped rows keep their content."""
+    tokens, qh, kvh, d = 300, 16, 8, 128
+    case, k, v, pos, inv = _cache_case(tokens, qh, kvh, d, dtype, 77)
+    blocks, bs = 40, 16
+    num_slots = blocks * bs
+    rng = np.random.default_rng(3)
+    slots = rng.permutation(num_slots)[:tokens].astype(np.int64)
+    slots[rng.choice(tokens, 20, replace=False)] = -1
+    slots[[5, 6]] = [num_slots, 1 << 40]
+    fill = -3.0
+    kc = torch.full((blocks, bs, kvh, d), fill, dtype=case.q.dtype, device=DEV)
+    vc = torch.full_like(kc, fill)
+    rope = qkr.Rope("1d", d, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    qo = qkr.qk_norm_rope_cache(gpu(case.q), gpu(k), gpu(v), gpu(case.q_weight), gpu(case.k_weight), kc, vc,
+                                gpu(torch.from_numpy(slots)), case.eps, rope)
+    orope = oracle.Rope("1d", d, "neox", inv_freq=inv, positions=pos)
+    kc0 = np.full((num_slots, kvh, d), fill, np.float32)
+    rq, rk, rv = oracle.qk_norm_rope_cache(W.as_f32(case.q), W.as_f32(k), W.as_f32(v), W.as_f32(case.q_weight),
+                                           W.as_f32(case.k_weight), case.eps, orope, slots, kc0, kc0.copy(), dtype)
+    check(host(qo), rq, dtype, d, "neox", "q")
+    gk = host(kc).reshape(num_slots, kvh, d)
+    mapped = np.zeros(num_slots, bool)
+    mapped[slots[(slots >= 0) & (slots < num_slots)]] = True
+    assert np.array_equal(gk[~mapped], rk[~mapped])            # untouched rows, exactly
+    check(gk[mapped], rk[mapped], dtype, d, "neox", "k cache")
+    assert np.array_equal(host(vc).reshape(num_slots, kvh, d), rv)   # V copied bit for bit
+
+
+def test_cache_write_imrope_without_v_and_empty_cache():
+    case = W.imrope(tokens=64)
+    d = 128
+    pos, inv = gpu(torch.from_numpy(case.positions)), gpu(torch.from_numpy(case.inv_freq))
+    rope = qkr.Rope("imrope", d, "neox", inv_freq=inv, positions=pos, sections=case.sections)
+    slots = torch.arange(64, dtype=torch.int64).flip(0)
+    kc = torch.zeros((64, case.k.shape[1], d), dtype=torch.bfloat16, device=DEV)
+    qo = qkr.qk_norm_rope_cache(gpu(case.q), gpu(case.k), None, gpu(case.q_weight), gpu(case.k_weight), kc, None,
+                                gpu(slots), case.eps, rope)
+    pq, pk = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+    assert torch.equal(qo, pq) and torch.equal(kc, pk.flip(0))
+    empty = torch.zeros((0, case.k.shape[1], d), dtype=torch.bfloat16, device=DEV)
+    qo2 = qkr.qk_norm_rope_cache(gpu(case.q), gpu(case.k), None, gpu(case.q_weight), gpu(case.k_weight), empty,
+                                 None, gpu(slots), case.eps, rope)
+    assert torch.equal(qo2, pq)

@@ -67,6 +67,10 @@ _SIGNATURES = {
                                         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]),
     "qkr_debug_fp8_e4m3": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p]),
+    "qkr_qk_norm_rope_cache": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                              _P(_View), _P(_View), ctypes.c_int32, ctypes.c_void_p, _P(_View),
+                                              _P(_View), ctypes.c_int32, ctypes.c_void_p, _P(_View), _P(_View),
+                                              ctypes.c_void_p, ctypes.c_int64, _P(_Rope), ctypes.c_void_p]),
     "qkr_qk_norm_rope": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_float, _P(_View), _P(_View), ctypes.c_int32, ctypes.c_void_p,
                                         _P(_View), _P(_View), ctypes.c_int32, ctypes.c_void_p, _P(_Rope),
@@ -384,6 +388,75 @@ def qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_weight:
     return qo4, ko4
 
 
+def _slots_view(name: str, cache: torch.Tensor, heads: int, d: int) -> torch.Tensor:
+    """[num_slots, heads, d] view of a cache given as [slots, H, D] or as a
+    paged [blocks, block_size, H, D] tensor."""
+    if cache.dim() == 4:
+        if cache.stride(0) != cache.shape[1] * cache.stride(1):
+            raise QkrError(f"{name}: blocks and block slots must be evenly strided to be seen as slots")
+        cache = cache.view(cache.shape[0] * cache.shape[1], cache.shape[2], cache.shape[3]) \
+            if cache.is_contiguous() else cache.flatten(0, 1)
+    if cache.dim() != 3 or cache.shape[1] != heads or cache.shape[2] != d or cache.stride(2) != 1:
+        raise QkrError(f"{name} must be [slots, {heads}, {d}] (or paged [blocks, block_size, {heads}, {d}])")
+    return cache
+
+
+def qk_norm_rope_cache(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], q_weight: torch.Tensor,
+                       k_weight: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
+                       slot_mapping: torch.Tensor, eps: float = 1e-6, rope: Optional[Rope] = None,
+                       q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Q/K RMSNorm + RoPE of q [tokens, Hq, D] and k [tokens, Hkv, D] with K
+    (and V, copied) written into the cache rows slot_mapping [tokens] (int64)
+    picks (qkr_qk_norm_rope_cache).  Returns q_out; the caches are updated in
+    place."""
+    dev = q.device
+    for nm, t in (("q", q), ("k", k), ("q_weight", q_weight), ("k_weight", k_weight), ("k_cache", k_cache),
+                  ("slot_mapping", slot_mapping)):
+        _on_gpu(nm, t, dev)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise QkrError("q and k must be [tokens, heads, head_dim] with equal tokens and head_dim")
+    if k.dtype != q.dtype:
+        raise QkrError("q and k must share a dtype")
+    tokens, hq, d = q.shape
+    hkv = k.shape[1]
+    if (v is None) != (v_cache is None):
+        raise QkrError("v and v_cache come together")
+    if v is not None:
+        _on_gpu("v", v, dev)
+        _on_gpu("v_cache", v_cache, dev)
+        if v.shape != k.shape or v.dtype != q.dtype:
+            raise QkrError("v must match k")
+    for nm, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if w.dtype != q.dtype or not w.is_contiguous() or w.numel() != d:
+            raise QkrError(f"{nm} must be contiguous [head_dim] of the activation dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or slot_mapping.numel() != tokens \
+            or not slot_mapping.is_contiguous():
+        raise QkrError("slot_mapping must be contiguous int64 [tokens]")
+    kc = _slots_view("k_cache", k_cache, hkv, d)
+    if kc.dtype != q.dtype:
+        raise QkrError("k_cache must have the activation dtype")
+    vc = None
+    if v_cache is not None:
+        vc = _slots_view("v_cache", v_cache, hkv, d)
+        if vc.shape != kc.shape or vc.dtype != q.dtype:
+            raise QkrError("v_cache must match k_cache")
+    qo = torch.empty_like(q, memory_format=torch.contiguous_format) if q_out is None else q_out
+    if qo.shape != q.shape or qo.dtype != q.dtype:
+        raise QkrError("q_out must match q")
+    _on_gpu("q_out", qo, dev)
+    cr = rope.to_c(dev, tokens) if rope is not None else None
+    def v4(t):
+        return ctypes.byref(_view(t.unsqueeze(0)))
+
+    st = lib().qkr_qk_norm_rope_cache(tokens, d, _dtype_code(q), float(eps), v4(q), v4(qo), hq,
+                                      q_weight.data_ptr(), v4(k), v4(v) if v is not None else None, hkv,
+                                      k_weight.data_ptr(), v4(kc), v4(vc) if vc is not None else None,
+                                      slot_mapping.data_ptr(), kc.shape[0],
+                                      ctypes.byref(cr) if cr is not None else None, _stream(dev))
+    _check(st, "qk_norm_rope_cache")
+    return qo
+
+
 def joint_qk_norm_rope(text: dict, image: dict, eps: float = 1e-6, rope: Optional[Rope] = None,
                        out: Optional[Sequence[torch.Tensor]] = None):
     """Joint text/image QK RMSNorm + concatenation (text first) + RoPE.
@@ -567,6 +640,7 @@ def vit_positions_host(grid_thw, spatial_merge: int):
 qkr_rms_norm = rms_norm
 qkr_add_rms_norm = add_rms_norm
 qkr_qk_norm_rope = qk_norm_rope
+qkr_qk_norm_rope_cache = qk_norm_rope_cache
 qkr_joint_qk_norm_rope = joint_qk_norm_rope
 qkr_mrope_cos_sin_setup = mrope_cos_sin_setup
 qkr_vit_qk_norm_rope = vit_qk_norm_rope

@@ -557,6 +557,82 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
     return launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream));
 }
 
+qkr_status qkr_qk_norm_rope_cache(int64_t tokens, int32_t head_dim, int32_t dtype, float eps, const qkr_view* q,
+                                  const qkr_view* q_out, int32_t q_heads, const void* q_weight_dev,
+                                  const qkr_view* k, const qkr_view* v, int32_t kv_heads, const void* k_weight_dev,
+                                  const qkr_view* k_cache, const qkr_view* v_cache,
+                                  const int64_t* slot_mapping_dev, int64_t num_slots, const qkr_rope* rope,
+                                  qkr_stream_t stream)
+{
+    int esize = 0;
+    qkr_status st;
+    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+        return st;
+    if (tokens < 0 || q_heads < 0 || kv_heads < 0 || num_slots < 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "negative tokens, heads or num_slots");
+    if (tokens > INT32_MAX || tokens * ((int64_t)q_heads + 2 * kv_heads) >= ((int64_t)1 << 31))
+        return fail(QKR_ERR_UNSUPPORTED, "tokens * heads must stay below 2^31 rows per call");
+    if ((int64_t)q_heads + kv_heads > (1 << 20))
+        return fail(QKR_ERR_UNSUPPORTED, "too many heads");
+    if ((v == nullptr) != (v_cache == nullptr))
+        return fail(QKR_ERR_INVALID_ARGUMENT, "v and v_cache come together (both or neither)");
+    if ((st = check_view("q", q, esize, 1, tokens, q_heads)) ||
+        (st = check_view("q_out", q_out, esize, 1, tokens, q_heads)) ||
+        (st = check_view("k", k, esize, 1, tokens, kv_heads)) ||
+        (st = check_view("k_cache", k_cache, esize, 1, num_slots, kv_heads)))
+        return st;
+    if (v != nullptr && ((st = check_view("v", v, esize, 1, tokens, kv_heads)) ||
+                         (st = check_view("v_cache", v_cache, esize, 1, num_slots, kv_heads))))
+        return st;
+    if (q_heads > 0 && (st = check_weight("q_weight", q_weight_dev)))
+        return st;
+    if (kv_heads > 0 && (st = check_weight("k_weight", k_weight_dev)))
+        return st;
+    if (tokens > 0 && kv_heads > 0) {
+        if (slot_mapping_dev == nullptr)
+            return fail(QKR_ERR_INVALID_ARGUMENT, "null slot mapping");
+        if (!aligned(slot_mapping_dev, 8))
+            return fail(QKR_ERR_MISALIGNED, "slot mapping is not 8-byte aligned");
+        if (num_slots > 0 && (k_cache == nullptr || k_cache->ptr_dev == nullptr))
+            return fail(QKR_ERR_INVALID_ARGUMENT, "null k_cache");
+    }
+    NormRopeArgs a{};
+    int32_t pairing = 0, rotary_dim = 0;
+    if ((st = check_rope(rope, head_dim, esize, tokens, a.rope, pairing, rotary_dim)))
+        return st;
+    if (tokens == 0 || q_heads + kv_heads == 0)
+        return ok();
+
+    fill_in(a.t[0], 0, q_heads ? q : nullptr, esize);
+    fill_out(a.t[0], q_heads ? q_out : nullptr, esize);
+    a.t[0].weight[0] = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
+    a.t[0].heads = q_heads;
+    // K and V leave through the caches (num_slots == 0: every slot is
+    // outside, nothing is written).
+    const int32_t cache_heads = num_slots > 0 ? kv_heads : 0;
+    fill_in(a.t[1], 0, cache_heads ? k : nullptr, esize);
+    fill_out(a.t[1], cache_heads ? k_cache : nullptr, esize);
+    a.t[1].weight[0] = cache_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
+    a.t[1].heads = cache_heads;
+    a.t[1].slots = slot_mapping_dev;
+    a.t[1].nslots = num_slots;
+    if (v != nullptr) {
+        fill_in(a.t[2], 0, cache_heads ? v : nullptr, esize);
+        fill_out(a.t[2], cache_heads ? v_cache : nullptr, esize);
+        a.t[2].heads = cache_heads;
+        a.t[2].slots = slot_mapping_dev;
+        a.t[2].nslots = num_slots;
+    }
+    a.batch = 1;
+    a.tokens = (int32_t)tokens;
+    a.tokens0 = (int32_t)tokens;
+    a.head_dim = head_dim;
+    a.rotary_dim = rotary_dim;
+    a.eps = eps;
+    a.inv_d = 1.0f / (float)head_dim;
+    return launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream));
+}
+
 qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, float eps,
                                   const qkr_stream* text, const qkr_stream* image, const qkr_view* q_out,
                                   const qkr_view* k_out, const qkr_view* v_out, const qkr_rope* rope,

@@ -57,6 +57,8 @@ struct TensorArgs {
     const char* weight[2];
     char* out;
     int64_t out_sb, out_st, out_sh;
+    const int64_t* slots;       // non-null: token t's rows go to output row slots[t] (stride out_st)
+    int64_t nslots;             // slots outside [0, nslots) write nothing
     int32_t heads;
 };
 

@@ -145,13 +145,25 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     char* const out = QKR_TF(out);
     const int64_t out_sb = QKR_TF(out_sb), out_st = QKR_TF(out_st), out_sh = QKR_TF(out_sh);
     const int32_t heads = QKR_TF(heads);
+    const int64_t* const slots = QKR_TF(slots);
+    const int64_t nslots = QKR_TF(nslots);
 #undef QKR_TF
+
+    // The output row of the token: the token itself, or the cache row its
+    // slot picks ([IMROPE]: the rotation's set_rows twin).  A slot outside
+    // the cache writes nothing, so the tile has no work (wave-uniform).
+    int64_t orow = tok;
+    if (slots != nullptr) {
+        orow = slots[tok];
+        if (orow < 0 || orow >= nslots)
+            return;
+    }
 
     // Heads [h0, h0 + hrem) of the tensor are left from this tile on.
     const int32_t h0 = blk * RPP * NP;
     const int32_t hrem = heads - h0;
     const char* const in_t = in + (int64_t)b * in_sb + (int64_t)ltok * in_st + (int64_t)h0 * in_sh;
-    char* const out_t = out + (int64_t)b * out_sb + (int64_t)tok * out_st + (int64_t)h0 * out_sh;
+    char* const out_t = out + (int64_t)b * out_sb + orow * out_st + (int64_t)h0 * out_sh;
 
     // The two vectors this lane owns in every row.
     const int g = lane / LPR, j = lane % LPR;
