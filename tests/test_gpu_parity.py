@@ -181,8 +181,8 @@ def test_rms_norm_rows(t, variant):
         qkr.set_variant_override(None)
     if variant is not None:
         assert name.startswith(variant + ":"), name
-    elif t < 256:
-        assert name.startswith("rms:split"), name
+    else:
+        assert name.startswith("rms:wide" if t < 2048 else "rms:rows"), name
     ref = oracle.rms_norm(W.as_f32(case.x), W.as_f32(case.weight), case.eps, "bf16")
     assert_bf16_close(host(y), ref, what=f"rms t={t} {name}")
 
