@@ -106,6 +106,17 @@ def test_add_rms_norm_refusals(kwargs, code):
     assert qkr.last_error() != ""
 
 
+def test_add_rms_norm_refuses_row_sets_shifted_by_less_than_a_row():
+    """x, the residual and the residual output interleaved in one buffer (row
+    stride 3 x width, 2 KiB rows) share no element (the GPU tests run that
+    layout); a row set shifted into another by less than a row is refused."""
+    w = 1024
+    x, r = XA, XA + 2 * w
+    assert addrms(x=x, xs=3 * w, r=r, rs=3 * w, s=x + 1024, ss=3 * w, width=w) == INVALID
+    assert addrms(x=x, xs=3 * w, r=r, rs=3 * w, s=r + 16, ss=3 * w, width=w) == INVALID
+    assert addrms(x=x, xs=3 * w, r=r, rs=3 * w, s=r, ss=3 * w, y=x + 2 * 2 * w - 16, ys=3 * w, width=w) == INVALID
+
+
 def test_add_rms_norm_zero_rows_is_a_noop():
     assert addrms(rows=0, x=None, r=None, s=None, y=None, w=None) == OK
     assert qkr.lib().qkr_debug_fp8_e4m3(None, 0, None, None, None) == OK

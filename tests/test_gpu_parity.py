@@ -758,3 +758,83 @@ def test_cache_write_imrope_without_v_and_empty_cache():
     qo2 = qkr.qk_norm_rope_cache(gpu(case.q), gpu(case.k), None, gpu(case.q_weight), gpu(case.k_weight), empty,
                                  None, gpu(slots), case.eps, rope)
     assert torch.equal(qo2, pq)
+
+
+# ---------------------------------------------------------------------------
+# 64-bit addressing and graph capture of the cache-write and residual-add paths
+# ---------------------------------------------------------------------------
+
+def test_cache_write_past_4_gib():
+    """Cache rows past 2^31 elements (4 GiB of bf16): 16 tokens mapped to the
+    last slots of a 2^21 + 64 slot cache."""
+    tokens, qh, kvh, d = 16, 4, 8, 128
+    case, k, v, pos, inv = _cache_case(tokens, qh, kvh, d, "bf16", 91)
+    num_slots = (1 << 21) + 64                               # 2 KiB per slot
+    slots = np.arange(num_slots - tokens, num_slots, dtype=np.int64)[::-1].copy()
+    slots[3] = 5                                             # and one near the start
+    kc = torch.zeros((num_slots, kvh, d), dtype=torch.bfloat16, device=DEV)
+    rope = qkr.Rope("1d", d, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    qkr.qk_norm_rope_cache(gpu(case.q), gpu(k), None, gpu(case.q_weight), gpu(case.k_weight), kc, None,
+                           gpu(torch.from_numpy(slots)), case.eps, rope)
+    orope = oracle.Rope("1d", d, "neox", inv_freq=inv, positions=pos)
+    rk = oracle.qk_norm_rope(W.as_f32(k), W.as_f32(case.k_weight), case.eps, orope)
+    got = host(kc[torch.from_numpy(slots).to(DEV)])
+    assert_bf16_close(got, rk, d, "neox", "k rows past 4 GiB")
+    head = kc[: 1 << 10]                                     # slots 0..1023: only slot 5 is mapped
+    assert int(torch.count_nonzero(head)) == int(torch.count_nonzero(head[5])) == kvh * d
+    del kc
+    torch.cuda.empty_cache()
+
+
+def test_add_rms_norm_row_offsets_past_4_gib():
+    """Rows 2^20 elements apart: the last rows start past 2^32 bytes."""
+    rows, width, stride = 2100, 1024, 1 << 20
+    x, r, w = _addrms_case(rows, width, "bf16", 13)
+    big = torch.empty((rows, stride), dtype=torch.bfloat16, device=DEV)
+    big[:, :width].copy_(gpu(x))
+    big[:, width:2 * width].copy_(gpu(r))
+    xs, rs = big[:, :width], big[:, width:2 * width]
+    y, s = qkr.add_rms_norm(xs, gpu(w), 1e-6, residual=rs)
+    ref_s, ref_y = oracle.add_rms_norm(W.as_f32(x), W.as_f32(w), 1e-6, W.as_f32(r), "bf16", "bf16")
+    assert np.array_equal(host(s), ref_s)
+    assert_bf16_close(host(y), ref_y, what="rows past 4 GiB")
+    del big
+    torch.cuda.empty_cache()
+
+
+def test_graph_capture_of_cache_write_and_residual_add():
+    case, k, v, pos, inv = _cache_case(40, 8, 2, 128, "bf16", 95)
+    rope = qkr.Rope("1d", 128, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    slots = gpu(torch.from_numpy(np.random.default_rng(95).permutation(64)[:40].astype(np.int64)))
+    q, kk, vv, wq, wk = gpu(case.q), gpu(k), gpu(v), gpu(case.q_weight), gpu(case.k_weight)
+    x, r, w = (gpu(t) for t in _addrms_case(7, 2048, "bf16", 95))
+    scale = gpu(torch.tensor([0.03], dtype=torch.float32))
+
+    def run(kc, vc, qo, res, y8):
+        qkr.qk_norm_rope_cache(q, kk, vv, wq, wk, kc, vc, slots, case.eps, rope, q_out=qo)
+        res.copy_(r)
+        qkr.add_rms_norm(x, w, 1e-6, residual=res, out_dtype="fp8_e4m3", scale=scale, out=y8)
+
+    def fresh():
+        return (torch.zeros((64, 2, 128), dtype=torch.bfloat16, device=DEV),
+                torch.zeros((64, 2, 128), dtype=torch.bfloat16, device=DEV), torch.empty_like(q),
+                torch.empty_like(r), torch.empty(r.shape, dtype=torch.float8_e4m3fn, device=DEV))
+
+    ref = fresh()
+    run(*ref)
+    got = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(*got)
+    for _ in range(3):
+        got[0].zero_()                                         # cache rows no token maps to stay as they are
+        got[1].zero_()
+        for t in got[2:]:
+            t.view(torch.uint8).fill_(0x55)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+        run(*fresh())                                          # eager work between replays
+        torch.cuda.synchronize()

@@ -447,23 +447,38 @@ qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void*
     }
     // The residual output may overwrite the residual or x in place (same
     // rows); any other overlap of the outputs with the inputs is refused.
-    auto span = [&](const void* p, int64_t stride, int64_t es) {
-        const char* b = static_cast<const char*>(p);
-        return std::make_pair(b, b + ((rows - 1) * stride + width) * es);
+    // Row sets with the same byte stride overlap exactly when their start
+    // offsets, taken modulo the stride, are less than a row apart (rows of an
+    // interleaved [x | r] buffer do not); otherwise the address spans decide.
+    struct Rows {
+        const char* base;
+        int64_t stride, bytes;   // bytes between rows, bytes per row
     };
-    auto overlap = [](std::pair<const char*, const char*> u, std::pair<const char*, const char*> v) {
-        return u.first < v.second && v.first < u.second;
+    auto rows_of = [&](const void* p, int64_t stride, int64_t es) {
+        return Rows{static_cast<const char*>(p), rows > 1 ? stride * es : 0, (int64_t)width * es};
     };
-    const auto sx = span(x_dev, x_row_stride, esize), sy = span(y_dev, y_row_stride, y_esize);
-    if (overlap(sy, sx))
+    auto overlap = [&](const Rows& u, const Rows& v) {
+        const char* ue = u.base + (rows - 1) * u.stride + u.bytes;
+        const char* ve = v.base + (rows - 1) * v.stride + v.bytes;
+        if (!(u.base < ve && v.base < ue))
+            return false;
+        if (rows > 1 && u.stride == v.stride && u.stride >= u.bytes && u.stride >= v.bytes) {
+            const int64_t s = u.stride;
+            const int64_t d = ((v.base - u.base) % s + s) % s;   // v's rows start d bytes into u's
+            return d < u.bytes || s - d < v.bytes;
+        }
+        return true;
+    };
+    const Rows rx = rows_of(x_dev, x_row_stride, esize), ry = rows_of(y_dev, y_row_stride, y_esize);
+    if (overlap(ry, rx))
         return fail(QKR_ERR_INVALID_ARGUMENT, "y overlaps x");
     if (add) {
-        const auto sr = span(r_dev, r_row_stride, esize), so = span(s_dev, s_row_stride, esize);
-        if (overlap(sy, sr) || overlap(sy, so))
+        const Rows rr = rows_of(r_dev, r_row_stride, esize), ro = rows_of(s_dev, s_row_stride, esize);
+        if (overlap(ry, rr) || overlap(ry, ro))
             return fail(QKR_ERR_INVALID_ARGUMENT, "y overlaps the residual");
         const bool same_r = s_dev == r_dev && s_row_stride == r_row_stride;
         const bool same_x = s_dev == x_dev && s_row_stride == x_row_stride;
-        if ((overlap(so, sr) && !same_r) || (overlap(so, sx) && !same_x))
+        if ((overlap(ro, rr) && !same_r) || (overlap(ro, rx) && !same_x))
             return fail(QKR_ERR_INVALID_ARGUMENT, "the residual output overlaps an input other than in place");
     }
     if (rows * ((nvec + 63) / 64) >= ((int64_t)1 << 31))
