@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
             load_pass(p, d[p][0], d[p][1]);
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-            store_pass(p, d[p][0], d[p][1]);
+            if (p * RPP < hrem)   // wave-uniform: a pass past the tensor has nothing to store
+                store_pass(p, d[p][0], d[p][1]);
         return;
     }
 
@@ -339,6 +340,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const float eps = a.eps, inv_d = a.inv_d;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
+        // A pass wholly past the tensor (its loads re-read the last head) has
+        // no row to normalise: wave-uniform skip; the load count is unchanged.
+        if (p * RPP >= hrem)
+            break;
         const float s0 = E::sumsq(d[p][0], 0.0f);
         const float part = (own0 ? s0 : 0.0f) + (own1 ? E::sumsq(d[p][1], 0.0f) : 0.0f);
         const float rrms = rsqrtf(group_sum<LPR>(part) * inv_d + eps);
