@@ -582,16 +582,19 @@ def main():
             w.step(sets[i % nsets])
         t_end.record(stream)
     else:
-        # One graph holds one step per buffer set; replaying it runs the
-        # launches back to back with no host work in between.
+        # One graph holds up to 256 steps cycling over the buffer sets;
+        # replaying it runs the launches back to back with no host work in
+        # between.  Each replay boundary costs several microseconds of idle
+        # GPU, so the graph is made long enough to spread that over many steps.
+        per_graph = nsets * max(1, min(args.steps, 256) // nsets)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for st in sets:
-                w.step(st)
+            for i in range(per_graph):
+                w.step(sets[i % nsets])
         graph.replay()
         torch.cuda.synchronize()
-        replays = max(1, -(-args.steps // nsets))
-        K = replays * nsets
+        replays = max(1, -(-args.steps // per_graph))
+        K = replays * per_graph
         stream = torch.cuda.current_stream()
         t_start.record(stream)
         for _ in range(replays):
