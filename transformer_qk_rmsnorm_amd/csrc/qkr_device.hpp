@@ -234,6 +234,15 @@ __device__ __forceinline__ int32_t axis_of(const uint32_t (&bits)[kMaxPairs / 16
     return (int32_t)((v >> ((p & 15) << 1)) & 3u);
 }
 
+// A 4-byte load from global memory through a pointer the compiler cannot
+// trace back to a kernel argument (rebuilt by readfirstlane, or selected per
+// lane among several): without the address space it becomes a flat load, and
+// the wait for a flat load also waits for every vector load issued after it.
+__device__ __forceinline__ float load_global(const float* p)
+{
+    return *(const __attribute__((address_space(1))) float*)p;
+}
+
 // Orders one wave's LDS writes before its later LDS reads of other lanes'
 // data (and those reads before the next writes).  LDS executes a wave's
 // operations in order, so this only keeps the compiler from moving them.

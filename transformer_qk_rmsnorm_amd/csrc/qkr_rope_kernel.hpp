@@ -136,18 +136,16 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const bool s1 = tok >= a.tokens0;              // token of stream 1 (image)
     const int32_t ltok = s1 ? tok - a.tokens0 : tok;
 
-#define QKR_TF(f) sel3(ti, a.t[0].f, a.t[1].f, a.t[2].f)
-    const char* const in = s1 ? QKR_TF(in[1]) : QKR_TF(in[0]);
-    const int64_t in_sb = s1 ? QKR_TF(in_sb[1]) : QKR_TF(in_sb[0]);
-    const int64_t in_st = s1 ? QKR_TF(in_st[1]) : QKR_TF(in_st[0]);
-    const int64_t in_sh = s1 ? QKR_TF(in_sh[1]) : QKR_TF(in_sh[0]);
-    const char* const wt = s1 ? QKR_TF(weight[1]) : QKR_TF(weight[0]);
-    char* const out = QKR_TF(out);
-    const int64_t out_sb = QKR_TF(out_sb), out_st = QKR_TF(out_st), out_sh = QKR_TF(out_sh);
-    const int32_t heads = QKR_TF(heads);
-    const int64_t* const slots = QKR_TF(slots);
-    const int64_t nslots = QKR_TF(nslots);
-#undef QKR_TF
+    const TensorArgs& T = a.t[ti];
+    const int si = s1 ? 1 : 0;
+    const char* const in = T.in[si];
+    const int64_t in_sb = T.in_sb[si], in_st = T.in_st[si], in_sh = T.in_sh[si];
+    const char* const wt = T.weight[si];
+    char* const out = T.out;
+    const int64_t out_sb = T.out_sb, out_st = T.out_st, out_sh = T.out_sh;
+    const int32_t heads = T.heads;
+    const int64_t* const slots = T.slots;
+    const int64_t nslots = T.nslots;
 
     // The output row of the token: the token itself, or the cache row its
     // slot picks ([IMROPE]: the rotation's set_rows twin).  A slot outside
@@ -266,8 +264,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         os1 = rp.sin_planes[i1];
     }
     if constexpr (ROPE == 3) {
-        // ViT: contiguous t/h/w sections, one inverse-frequency ladder per axis.
-        pos = vit_token_positions(a.vit, (uint32_t)tabs);
+        // ViT: contiguous t/h/w sections, one inverse-frequency ladder per
+        // axis.  The token's (t, h, w) is found after the row loads are out.
         ax0 = axis_of(rp.axis_bits, p0);
         ax1 = axis_of(rp.axis_bits, p1);
         const int32_t o_h = rp.sec[0], o_w = rp.sec[0] + rp.sec[1];
@@ -276,8 +274,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         const float* const iw = uniform(a.vit.inv[2]);
         const float* const l0 = sel3(ax0, it, ih, iw);
         const float* const l1 = sel3(ax1, it, ih, iw);
-        op0 = l0[p0 - sel3(ax0, 0, o_h, o_w)];
-        op1 = l1[p1 - sel3(ax1, 0, o_h, o_w)];
+        op0 = load_global(l0 + (p0 - sel3(ax0, 0, o_h, o_w)));
+        op1 = load_global(l1 + (p1 - sel3(ax1, 0, o_h, o_w)));
     }
 
     // 1b) The tensor's weight vectors (tiny, cached), then every row load.
@@ -285,6 +283,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
 #pragma unroll
     for (int p = 0; p < NP; ++p)
         load_pass(p, d[p][0], d[p][1]);
+    if constexpr (ROPE == 3)
+        pos = vit_token_positions(a.vit, (uint32_t)tabs);   // scalar work, rows in flight
 
     // 2) cos/sin of the lane's VE pairs while the rows are in flight.
     float cs_c[VE], cs_s[VE];
@@ -311,6 +311,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
                 pair_cos_sin(ax1, pos, op1, c1, s1v);
             }
         }
+        // Pair p's values sit on lane p mod 64 (ds_bpermute takes the lane
+        // from address bits 7..2, so the address needs no mask).  Pairs at or
+        // past `half` are never rotated: whatever such a lane receives goes
+        // unused.
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
             int p;
@@ -318,11 +322,9 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
                 p = j * VE + e;
             else
                 p = (e < VE / 2 ? v0 : v1) * (VE / 2) + (e % (VE / 2));
-            p = p < half ? p : half - 1;
-            const int src = p & 63;
-            float c = bperm(src, c0), sn = bperm(src, s0);
+            float c = bperm(p, c0), sn = bperm(p, s0);
             if (wide) {
-                const float c_hi = bperm(src, c1), s_hi = bperm(src, s1v);
+                const float c_hi = bperm(p, c1), s_hi = bperm(p, s1v);
                 c = p >= 64 ? c_hi : c;
                 sn = p >= 64 ? s_hi : sn;
             }
