@@ -165,6 +165,28 @@ def test_q_only_and_k_only():
     assert_bf16_close(host(ko), oracle.qk_norm_rope(W.as_f32(case.k), W.as_f32(case.k_weight), 1e-6, orope), 64)
 
 
+@pytest.mark.parametrize("eps", [0.0, 1e-40])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_eps_below_the_normal_range(eps, dtype):
+    """An eps of zero or a subnormal eps takes the kernels' library reciprocal
+    square root (the bare instruction is used only for a normal eps)."""
+    case = W.tiny(tokens=23, heads=4, head_dim=128, dtype=dtype, seed_stream=4242)
+    case.eps = eps
+    pos = np.random.default_rng(11).integers(0, 3000, (1, 23)).astype(np.int32)
+    qo, ko, rq, rk = run_1d(case, "neox", positions=pos)
+    check(qo, rq, dtype, 128, "neox", "q")
+    check(ko, rk, dtype, 128, "neox", "k")
+    rows = W.rows(9, width=1000, dtype=dtype, seed_stream=4243)
+    for variant in (None, "rms:rows", "rms:wide"):
+        qkr.set_variant_override(variant)
+        try:
+            y = qkr.rms_norm(gpu(rows.x), gpu(rows.weight), eps)
+        finally:
+            qkr.set_variant_override(None)
+        ref = oracle.rms_norm(W.as_f32(rows.x), W.as_f32(rows.weight), eps, dtype)
+        check(host(y), ref, dtype, what=f"rms eps={eps} {variant}")
+
+
 # ---------------------------------------------------------------------------
 # rows: plain RMSNorm, bf16 [t, 5120], t in {1, 32, 4096}; every variant
 # ---------------------------------------------------------------------------

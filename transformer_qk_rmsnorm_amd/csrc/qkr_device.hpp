@@ -7,6 +7,8 @@
 //            RMSNorm + cat + RoPE into one Triton launch"
 #pragma once
 
+#include <cfloat>
+
 #include "qkr_internal.hpp"
 
 namespace qkr {
@@ -232,6 +234,17 @@ __device__ __forceinline__ int32_t axis_of(const uint32_t (&bits)[kMaxPairs / 16
     for (int k = 1; k < kMaxPairs / 16; ++k)
         v = w == k ? uniform(bits[k]) : v;
     return (int32_t)((v >> ((p & 15) << 1)) & 3u);
+}
+
+// 1 / sqrt(v) for v = mean square + eps.  The library routine is the
+// hardware reciprocal square root plus a rescaling that matters only for
+// subnormal arguments; when eps is a normal number v cannot be subnormal and
+// the bare instruction returns the same bits.  `eps_normal` is wave-uniform.
+__device__ __forceinline__ float rms_rsqrt(float v, bool eps_normal)
+{
+    if (eps_normal)
+        return __builtin_amdgcn_rsqf(v);
+    return rsqrtf(v);
 }
 
 // A 4-byte load from global memory through a pointer the compiler cannot

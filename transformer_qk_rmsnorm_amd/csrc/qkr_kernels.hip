@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
         for (int w = 1; w < kWaves; ++w)
             ss += part[w];
     }
-    const float rrms = rsqrtf(ss * a.inv_width + a.eps);
+    const float rrms = rms_rsqrt(ss * a.inv_width + a.eps, a.eps >= FLT_MIN);
     float scale = 1.0f, inv_scale = 1.0f;
     if constexpr (FP8) {
         scale = *a.scale;   // wave-uniform

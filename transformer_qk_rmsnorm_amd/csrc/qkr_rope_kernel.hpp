@@ -196,28 +196,40 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         x1 = load_row16<NT>(base + o0 + (off1 - off0));
     };
 
-    // Stores of pass p (heads past the tensor are skipped).
+    // Stores of pass p (heads past the tensor are skipped).  Every per-lane
+    // address is formed once; a pass adds the uniform offset of its heads.
     __shared__ uint4 stage_all[STAGE ? kWaves * 128 : 1];
     uint4* const stage = stage_all + (STAGE ? wave * 128 : 0);   // RPP * nv <= 2 * 64 vectors
+    char* const lane_out = out_t + (int64_t)g * out_sh;          // direct: this lane's row of pass 0
+    int slot_row[2];                                             // staged: row of each vector slot
+    char* slot_out[2];
+    if constexpr (STAGE) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int f = sl * 64 + lane;                               // vector of the pass
+            const int fr = (int)(((uint32_t)f * a.nv_recip) >> 16);     // its row in the pass
+            const int fv = f - fr * nv;
+            slot_row[sl] = fr < RPP ? fr : (1 << 30);                   // past the pass: no row
+            slot_out[sl] = out_t + (int64_t)fr * out_sh + (int64_t)fv * 16;
+        }
+    }
     auto store_pass = [&](int p, const uint4& o0, const uint4& o1) {
+        const int64_t pass_off = (int64_t)(p * RPP) * out_sh;           // wave-uniform
+        const int live = hrem - p * RPP;                                 // rows of the pass in the tensor
         if constexpr (STAGE) {
-            if (p * RPP + g < hrem) {
+            if (g < live) {
                 if (own0) stage[g * nv + v0] = o0;
                 if (own1) stage[g * nv + v1] = o1;
             }
             wave_lds_order();
 #pragma unroll
-            for (int sl = 0; sl < 2; ++sl) {
-                const int f = sl * 64 + lane;                               // vector of the pass
-                const int fr = (int)(((uint32_t)f * a.nv_recip) >> 16);     // its row in the pass
-                const int fv = f - fr * nv;
-                if (fr < RPP && p * RPP + fr < hrem)
-                    store_row16<NT>(out_t + (int64_t)(p * RPP + fr) * out_sh + (int64_t)fv * 16, stage[f]);
-            }
+            for (int sl = 0; sl < 2; ++sl)
+                if (slot_row[sl] < live)
+                    store_row16<NT>(slot_out[sl] + pass_off, stage[sl * 64 + lane]);
             wave_lds_order();
         } else {
-            if (p * RPP + g < hrem) {
-                char* const dst = out_t + (int64_t)(p * RPP + g) * out_sh;
+            if (g < live) {
+                char* const dst = lane_out + pass_off;
                 if (own0) store_row16<NT>(dst + off0, o0);
                 if (own1) store_row16<NT>(dst + off1, o1);
             }
@@ -340,6 +352,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     //    not own holds a re-read of another vector and must not count),
     //    normalise, round, rotate, store.
     const float eps = a.eps, inv_d = a.inv_d;
+    const bool eps_normal = eps >= FLT_MIN;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         // A pass wholly past the tensor (its loads re-read the last head) has
@@ -348,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
             break;
         const float s0 = E::sumsq(d[p][0], 0.0f);
         const float part = (own0 ? s0 : 0.0f) + (own1 ? E::sumsq(d[p][1], 0.0f) : 0.0f);
-        const float rrms = rsqrtf(group_sum<LPR>(part) * inv_d + eps);
+        const float rrms = rms_rsqrt(group_sum<LPR>(part) * inv_d + eps, eps_normal);
         float x0[VE], x1[VE];
         E::unpack(d[p][0], x0);
         E::unpack(d[p][1], x1);
