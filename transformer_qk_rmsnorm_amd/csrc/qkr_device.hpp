@@ -226,13 +226,21 @@ __device__ __forceinline__ const T* uniform(const T* ptr)
 }
 
 // Axis of pair p (p < kMaxPairs) from the host-built table of 2-bit fields.
+// The table is read whole, as two 16-byte vectors, before the per-lane
+// selection: a select whose operand is a lone load of one word is turned
+// into a branch around that load, one scalar-memory wait per word.
 __device__ __forceinline__ int32_t axis_of(const uint32_t (&bits)[kMaxPairs / 16], int32_t p)
 {
+    static_assert(kMaxPairs / 16 == 8, "the table is two 16-byte vectors");
+    const uint4 lo = *reinterpret_cast<const uint4*>(&bits[0]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&bits[4]);
+    const uint32_t word[8] = {uniform(lo.x), uniform(lo.y), uniform(lo.z), uniform(lo.w),
+                              uniform(hi.x), uniform(hi.y), uniform(hi.z), uniform(hi.w)};
     const int32_t w = p >> 4;
-    uint32_t v = uniform(bits[0]);
+    uint32_t v = word[0];
 #pragma unroll
-    for (int k = 1; k < kMaxPairs / 16; ++k)
-        v = w == k ? uniform(bits[k]) : v;
+    for (int k = 1; k < 8; ++k)
+        v = w == k ? word[k] : v;
     return (int32_t)((v >> ((p & 15) << 1)) & 3u);
 }
 

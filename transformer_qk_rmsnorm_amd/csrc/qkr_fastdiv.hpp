@@ -36,13 +36,15 @@ inline FastDiv make_fastdiv(uint32_t d)
 
 QKR_HD inline uint32_t mulhi32(uint32_t a, uint32_t b) { return (uint32_t)(((uint64_t)a * b) >> 32); }
 
-// n / f.d for every 32-bit n:  t = mulhi(m, n);  q = (t + ((n - t) >> 1)) >> (l - 1).
+// n / f.d for every 32-bit n:  t = mulhi(m, n);  q = (t + ((n - t) >> s1)) >> s2
+// with s1 = min(l, 1) and s2 = l - s1.  For d >= 2 that is the paper's
+// (t + ((n - t) >> 1)) >> (l - 1); for d = 1 (l = 0, m = 1) t is 0 and q = n.
+// No branch, so a kernel can fetch every divisor field in one batch.
 QKR_HD inline uint32_t fast_div(uint32_t n, const FastDiv& f)
 {
-    if (f.d == 1)
-        return n;
+    const uint32_t s1 = f.l < 1u ? f.l : 1u;
     const uint32_t t = mulhi32(f.m, n);
-    return (t + ((n - t) >> 1)) >> (f.l - 1);
+    return (t + ((n - t) >> s1)) >> (f.l - s1);
 }
 
 }  // namespace qkr

@@ -24,7 +24,7 @@ struct RopeArgs {
     int32_t mode;        // PosMode
     int32_t half;        // R / 2
     int32_t sec[4];      // raw sections (AXES/PLANES: pairs per axis; IMROPE: s0..s3)
-    uint32_t axis_bits[kMaxPairs / 16];   // axis of pair p: bits 2(p%16).. of word p/16 (host-built)
+    alignas(16) uint32_t axis_bits[kMaxPairs / 16];   // axis of pair p: bits 2(p%16).. of word p/16 (host-built)
     const float* inv_freq;
     const int32_t* positions;
     int64_t pos_stride;

@@ -122,10 +122,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     // Tile coordinates are wave-uniform and stay in scalar registers:
     // tile = (batch * tokens + token) * tiles_per_token + k, where tiles
     // [tile_first[i], tile_first[i + 1]) of a token belong to tensor i.
+    // The decode is arithmetic only, so it runs before the range check and
+    // every field it reads arrives in one batch of scalar loads.
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t tile = blockIdx.x * kWaves + wave;
-    if (tile >= a.ntiles)
-        return;   // wave-uniform
     const uint32_t bt = fast_div(tile, a.div_tpt);
     const int32_t k = (int32_t)(tile - bt * a.div_tpt.d);
     const int ti = k >= a.tile_first[2] ? 2 : (k >= a.tile_first[1] ? 1 : 0);
@@ -133,6 +133,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const uint32_t bq = fast_div(bt, a.div_tokens);
     const int32_t tok = (int32_t)(bt - bq * a.div_tokens.d);
     const int32_t b = (int32_t)bq;
+    if (tile >= a.ntiles)
+        return;   // wave-uniform
     const bool s1 = tok >= a.tokens0;              // token of stream 1 (image)
     const int32_t ltok = s1 ? tok - a.tokens0 : tok;
 
@@ -147,21 +149,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const int64_t* const slots = T.slots;
     const int64_t nslots = T.nslots;
 
-    // The output row of the token: the token itself, or the cache row its
-    // slot picks ([IMROPE]: the rotation's set_rows twin).  A slot outside
-    // the cache writes nothing, so the tile has no work (wave-uniform).
-    int64_t orow = tok;
-    if (slots != nullptr) {
-        orow = slots[tok];
-        if (orow < 0 || orow >= nslots)
-            return;
-    }
-
     // Heads [h0, h0 + hrem) of the tensor are left from this tile on.
     const int32_t h0 = blk * RPP * NP;
     const int32_t hrem = heads - h0;
     const char* const in_t = in + (int64_t)b * in_sb + (int64_t)ltok * in_st + (int64_t)h0 * in_sh;
-    char* const out_t = out + (int64_t)b * out_sb + orow * out_st + (int64_t)h0 * out_sh;
 
     // The two vectors this lane owns in every row.
     const int g = lane / LPR, j = lane % LPR;
@@ -196,24 +187,48 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         x1 = load_row16<NT>(base + o0 + (off1 - off0));
     };
 
+    // The output row of the token: the token itself, or the cache row its
+    // slot picks ([IMROPE]: the rotation's set_rows twin).  A slot outside
+    // the cache writes nothing, so the tile ends there (wave-uniform).  The
+    // slot is read once the tile's row loads are issued; those are in range
+    // and are simply dropped.
+    auto out_base = [&](char*& out_t) {
+        int64_t orow = tok;
+        if (slots != nullptr) {
+            orow = slots[tok];
+            if (orow < 0 || orow >= nslots)
+                return false;
+        }
+        out_t = out + (int64_t)b * out_sb + orow * out_st + (int64_t)h0 * out_sh;
+        return true;
+    };
+
     // Stores of pass p (heads past the tensor are skipped).  Every per-lane
-    // address is formed once; a pass adds the uniform offset of its heads.
+    // address is formed once from the tile's output base; a pass adds the
+    // uniform offset of its heads.
     __shared__ uint4 stage_all[STAGE ? kWaves * 128 : 1];
     uint4* const stage = stage_all + (STAGE ? wave * 128 : 0);   // RPP * nv <= 2 * 64 vectors
-    char* const lane_out = out_t + (int64_t)g * out_sh;          // direct: this lane's row of pass 0
-    int slot_row[2];                                             // staged: row of each vector slot
-    char* slot_out[2];
-    if constexpr (STAGE) {
+    struct Dst {
+        char* lane_out;      // direct: this lane's row of pass 0
+        int slot_row[2];     // staged: row of each vector slot of a pass (1 << 30: none)
+        char* slot_out[2];
+    };
+    auto dst_of = [&](char* out_t) {
+        Dst t;
+        t.lane_out = out_t + (int64_t)g * out_sh;
+        if constexpr (STAGE) {
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-            const int f = sl * 64 + lane;                               // vector of the pass
-            const int fr = (int)(((uint32_t)f * a.nv_recip) >> 16);     // its row in the pass
-            const int fv = f - fr * nv;
-            slot_row[sl] = fr < RPP ? fr : (1 << 30);                   // past the pass: no row
-            slot_out[sl] = out_t + (int64_t)fr * out_sh + (int64_t)fv * 16;
+            for (int sl = 0; sl < 2; ++sl) {
+                const int f = sl * 64 + lane;                               // vector of the pass
+                const int fr = (int)(((uint32_t)f * a.nv_recip) >> 16);     // its row in the pass
+                const int fv = f - fr * nv;
+                t.slot_row[sl] = fr < RPP ? fr : (1 << 30);
+                t.slot_out[sl] = out_t + (int64_t)fr * out_sh + (int64_t)fv * 16;
+            }
         }
-    }
-    auto store_pass = [&](int p, const uint4& o0, const uint4& o1) {
+        return t;
+    };
+    auto store_pass = [&](const Dst& t, int p, const uint4& o0, const uint4& o1) {
         const int64_t pass_off = (int64_t)(p * RPP) * out_sh;           // wave-uniform
         const int live = hrem - p * RPP;                                 // rows of the pass in the tensor
         if constexpr (STAGE) {
@@ -224,12 +239,12 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
             wave_lds_order();
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
-                if (slot_row[sl] < live)
-                    store_row16<NT>(slot_out[sl] + pass_off, stage[sl * 64 + lane]);
+                if (t.slot_row[sl] < live)
+                    store_row16<NT>(t.slot_out[sl] + pass_off, stage[sl * 64 + lane]);
             wave_lds_order();
         } else {
             if (g < live) {
-                char* const dst = lane_out + pass_off;
+                char* const dst = t.lane_out + pass_off;
                 if (own0) store_row16<NT>(dst + off0, o0);
                 if (own1) store_row16<NT>(dst + off1, o1);
             }
@@ -241,14 +256,23 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
 #pragma unroll
         for (int p = 0; p < NP; ++p)
             load_pass(p, d[p][0], d[p][1]);
+        char* out_t;
+        if (!out_base(out_t))
+            return;
+        const Dst t = dst_of(out_t);
 #pragma unroll
         for (int p = 0; p < NP; ++p)
             if (p * RPP < hrem)   // wave-uniform: a pass past the tensor has nothing to store
-                store_pass(p, d[p][0], d[p][1]);
+                store_pass(t, p, d[p][0], d[p][1]);
         return;
     }
 
-    // 1a) Rotation operands: positions (scalar), then the lane's pair operands.
+    // 1) Loads of a normed tile, in this order: the lane's pair operands
+    //    (inverse frequency, planes entries or ladder values; tiny, cached,
+    //    and first in the in-order vector queue, so the trig waits for them
+    //    alone), every row, the tensor's weight vectors (the first pass
+    //    waits for every row either way).  The token's positions are scalar
+    //    loads, counted apart from the vector loads, read after the rows.
     const RopeArgs& rp = a.rope;
     const int half = rp.half;
     const int64_t tabs = rp.token_base + tok;      // token inside the position planes
@@ -258,10 +282,6 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     int32_t ax0 = 0, ax1 = 0;
     float op0 = 0.0f, op1 = 0.0f, os0 = 0.0f, os1 = 0.0f;   // inv_freq or cos, and sin
     if constexpr (ROPE == 1) {
-        pos.t = rp.positions[rp.plane_off[0] + tabs];
-        pos.h = rp.positions[rp.plane_off[1] + tabs];
-        pos.w = rp.positions[rp.plane_off[2] + tabs];
-        pos.e = rp.positions[rp.plane_off[3] + tabs];
         op0 = rp.inv_freq[p0];
         op1 = rp.inv_freq[p1];
     }
@@ -289,12 +309,24 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         op0 = load_global(l0 + (p0 - sel3(ax0, 0, o_h, o_w)));
         op1 = load_global(l1 + (p1 - sel3(ax1, 0, o_h, o_w)));
     }
-
-    // 1b) The tensor's weight vectors (tiny, cached), then every row load.
-    const uint4 wv0 = load16(wt + off0), wv1 = load16(wt + off1);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
         load_pass(p, d[p][0], d[p][1]);
+    const uint4 wv0 = load16(wt + off0), wv1 = load16(wt + off1);
+
+    char* out_t;
+    if (!out_base(out_t))
+        return;
+    const Dst dst = dst_of(out_t);
+    if constexpr (ROPE == 1) {
+        // Held as scalar values: a per-lane choice among four loads would
+        // otherwise become one per-lane load from a chosen address, queued
+        // behind the rows.
+        pos.t = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[0] + tabs]);
+        pos.h = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[1] + tabs]);
+        pos.w = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[2] + tabs]);
+        pos.e = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[3] + tabs]);
+    }
     if constexpr (ROPE == 3)
         pos = vit_token_positions(a.vit, (uint32_t)tabs);   // scalar work, rows in flight
 
@@ -398,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
                 }
             }
         }
-        store_pass(p, E::pack(x0), E::pack(x1));
+        store_pass(dst, p, E::pack(x0), E::pack(x1));
     }
 }
 
