@@ -122,10 +122,13 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     // Tile coordinates are wave-uniform and stay in scalar registers:
     // tile = (batch * tokens + token) * tiles_per_token + k, where tiles
     // [tile_first[i], tile_first[i + 1]) of a token belong to tensor i.
-    // The decode is arithmetic only, so it runs before the range check and
-    // every field it reads arrives in one batch of scalar loads.
+    // Padding waves of the last workgroup (index >= ntiles) redo the loads
+    // of the last tile and store nothing: with no early exit, no branch
+    // splits the kernel-argument reads of the prologue into separate waits.
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t tile = blockIdx.x * kWaves + wave;
+    const uint32_t tile_raw = blockIdx.x * kWaves + wave;
+    const bool pad = tile_raw >= a.ntiles;         // wave-uniform
+    const uint32_t tile = pad ? a.ntiles - 1 : tile_raw;
     const uint32_t bt = fast_div(tile, a.div_tpt);
     const int32_t k = (int32_t)(tile - bt * a.div_tpt.d);
     const int ti = k >= a.tile_first[2] ? 2 : (k >= a.tile_first[1] ? 1 : 0);
@@ -133,8 +136,6 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const uint32_t bq = fast_div(bt, a.div_tokens);
     const int32_t tok = (int32_t)(bt - bq * a.div_tokens.d);
     const int32_t b = (int32_t)bq;
-    if (tile >= a.ntiles)
-        return;   // wave-uniform
     const bool s1 = tok >= a.tokens0;              // token of stream 1 (image)
     const int32_t ltok = s1 ? tok - a.tokens0 : tok;
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     };
     auto store_pass = [&](const Dst& t, int p, const uint4& o0, const uint4& o1) {
         const int64_t pass_off = (int64_t)(p * RPP) * out_sh;           // wave-uniform
-        const int live = hrem - p * RPP;                                 // rows of the pass in the tensor
+        const int live = pad ? 0 : hrem - p * RPP;                       // rows of the pass to store
         if constexpr (STAGE) {
             if (g < live) {
                 if (own0) stage[g * nv + v0] = o0;
