@@ -252,6 +252,15 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         }
     };
 
+    // The rotation's scalar parameters are read before the V branch, in the
+    // descriptor's batch of kernel-argument loads.
+    const RopeArgs& rp = a.rope;
+    const int half = (int)uniform((uint32_t)rp.half);
+    const int64_t tabs = rp.token_base + tok;      // token inside the position planes
+    const float* const inv_freq = uniform(rp.inv_freq);
+    const int p0 = lane < half ? lane : half - 1;
+    const int p1 = lane + 64 < half ? lane + 64 : half - 1;
+
     uint4 d[NP][2];
     if (wt == nullptr) {   // wave-uniform: a routed tensor (V), bit copy
 #pragma unroll
@@ -274,17 +283,12 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     //    alone), every row, the tensor's weight vectors (the first pass
     //    waits for every row either way).  The token's positions are scalar
     //    loads, counted apart from the vector loads, read after the rows.
-    const RopeArgs& rp = a.rope;
-    const int half = rp.half;
-    const int64_t tabs = rp.token_base + tok;      // token inside the position planes
-    const int p0 = lane < half ? lane : half - 1;
-    const int p1 = lane + 64 < half ? lane + 64 : half - 1;
     TokenPositions pos{0, 0, 0, 0};
     int32_t ax0 = 0, ax1 = 0;
     float op0 = 0.0f, op1 = 0.0f, os0 = 0.0f, os1 = 0.0f;   // inv_freq or cos, and sin
     if constexpr (ROPE == 1) {
-        op0 = rp.inv_freq[p0];
-        op1 = rp.inv_freq[p1];
+        op0 = load_global(inv_freq + p0);
+        op1 = load_global(inv_freq + p1);
     }
     if constexpr (ROPE == 2) {
         ax0 = axis_of(rp.axis_bits, p0);
