@@ -87,17 +87,22 @@ __device__ __forceinline__ T sel3(int i, T v0, T v1, T v2)
 // vectors j and j + ceil(nv/2), and adjacent pairs sit inside one vector.
 //
 // Order of work in a wave:
-//   1. loads: the token's positions (scalar), the lane's inverse frequency or
-//      planes entry, the tensor's weight vectors, then every row of the tile.
-//      All are unconditional (rows past the tensor re-read its last head, a
-//      cache hit, never stored), so the compiler counts them and each wait
-//      below covers only what it needs;
+//   0. the tile decode and the tensor descriptor: kernel-argument reads with
+//      no branch between them (padding waves past the tile count run the
+//      last tile with every store off instead of leaving early), so they
+//      arrive in few batches;
+//   1. vector loads, which complete in order: the lane's pair operands
+//      (inverse frequency, planes entry or ladder value), then every row of
+//      the tile, then the tensor's weight vectors.  All are unconditional
+//      (rows past the tensor re-read its last head, a cache hit, never
+//      stored), so the compiler counts them and each wait below covers only
+//      what it needs.  The token's positions follow as scalar loads;
 //   2. cos/sin of the token's pairs (lane i: pair i, axis from a host-built
 //      table) while the rows are in flight, handed to the lanes that need
 //      them with ds_bpermute; the weights unpacked once;
 //   3. per pass: DPP sum of squares over the row's LPR lanes, normalise,
 //      round per the contract, rotate, store.
-// A routed tensor (V) tile only loads and stores.
+// A routed tensor (V) tile only loads its rows and stores them.
 //
 // STAGE: where half a row is not a whole number of 128-byte lines (e.g.
 // head_dim 80 bf16: 80-byte halves), a store instruction of the lane-local
