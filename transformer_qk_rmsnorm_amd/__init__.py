@@ -157,13 +157,20 @@ def _on_gpu(name: str, t: torch.Tensor, device: torch.device):
         raise QkrError(f"{name} is on {t.device}, expected {device}")
 
 
+def _unit_stride(t: torch.Tensor, dim: int) -> bool:
+    """Whether dimension `dim` is laid out contiguously.  An empty tensor has
+    no elements to lay out (torch may give it any strides), and a dimension of
+    length 1 has no stride to speak of."""
+    return t.numel() == 0 or t.shape[dim] <= 1 or t.stride(dim) == 1
+
+
 def _rows4(name: str, t: torch.Tensor) -> torch.Tensor:
     """[tokens, heads, D] or [batch, tokens, heads, D] -> 4-D view."""
     if t.dim() == 3:
         t = t.unsqueeze(0)
     if t.dim() != 4:
         raise QkrError(f"{name} must be [tokens, heads, head_dim] or [batch, tokens, heads, head_dim]")
-    if t.shape[-1] > 1 and t.stride(-1) != 1:
+    if not _unit_stride(t, -1):
         raise QkrError(f"{name}: the head_dim dimension must be contiguous")
     return t
 
@@ -229,7 +236,7 @@ class Rope:
                 or self.inv_freq.numel() < half:
             raise QkrError(f"inv_freq must be contiguous float32 with >= {half} entries")
         pos = self.positions
-        if pos.dtype != torch.int32 or pos.dim() != 2 or pos.stride(1) != 1:
+        if pos.dtype != torch.int32 or pos.dim() != 2 or not _unit_stride(pos, 1):
             raise QkrError("positions must be int32 [planes, tokens] with contiguous rows")
         need = _PLANES_NEEDED[self.mode]
         if pos.shape[0] < need:
@@ -255,12 +262,12 @@ def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
     dev = x.device
     _on_gpu("x", x, dev)
     _on_gpu("weight", weight, dev)
-    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+    if x.dim() != 2 or not _unit_stride(x, 1):
         raise QkrError("x must be [rows, width] with contiguous rows")
     if weight.dtype != x.dtype or not weight.is_contiguous() or weight.numel() != x.shape[1]:
         raise QkrError("weight must be contiguous [width] of x's dtype")
     y = torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
-    if y.shape != x.shape or y.dtype != x.dtype or (y.shape[1] > 1 and y.stride(1) != 1):
+    if y.shape != x.shape or y.dtype != x.dtype or not _unit_stride(y, 1):
         raise QkrError("out must match x")
     _on_gpu("out", y, dev)
     st = lib().qkr_rms_norm(x.data_ptr(), x.stride(0), y.data_ptr(), y.stride(0), weight.data_ptr(),
@@ -283,14 +290,14 @@ def add_rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
     dev = x.device
     _on_gpu("x", x, dev)
     _on_gpu("weight", weight, dev)
-    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+    if x.dim() != 2 or not _unit_stride(x, 1):
         raise QkrError("x must be [rows, width] with contiguous rows")
     if weight.dtype != x.dtype or not weight.is_contiguous() or weight.numel() != x.shape[1]:
         raise QkrError("weight must be contiguous [width] of x's dtype")
 
     def rows_like(name, t):
         _on_gpu(name, t, dev)
-        if t.shape != x.shape or t.dtype != x.dtype or (t.shape[1] > 1 and t.stride(1) != 1):
+        if t.shape != x.shape or t.dtype != x.dtype or not _unit_stride(t, 1):
             raise QkrError(f"{name} must match x")
 
     if residual is not None:
@@ -304,7 +311,7 @@ def add_rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
         raise QkrError(f"unknown out_dtype {out_dtype!r}")
     ydt = torch.float8_e4m3fn if fp8 else x.dtype
     y = torch.empty(x.shape, dtype=ydt, device=dev) if out is None else out
-    if y.shape != x.shape or y.dtype != ydt or (y.shape[1] > 1 and y.stride(1) != 1):
+    if y.shape != x.shape or y.dtype != ydt or not _unit_stride(y, 1):
         raise QkrError(f"out must be {tuple(x.shape)} of {ydt}")
     _on_gpu("out", y, dev)
     if fp8:
@@ -564,7 +571,7 @@ def vit_qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_wei
             outs.append(None)
             views.append((None, None, 0, None))
             continue
-        if t.dim() != 3 or (t.shape[-1] > 1 and t.stride(-1) != 1):
+        if t.dim() != 3 or not _unit_stride(t, -1):
             raise QkrError(f"{nm} must be [tokens, heads, head_dim] with a contiguous last dimension")
         _on_gpu(nm, t, dev)
         if t.dtype != ref.dtype or t.shape[0] != ref.shape[0] or t.shape[2] != ref.shape[2]:
