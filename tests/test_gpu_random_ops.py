@@ -1,5 +1,6 @@
 """Seeded random sweeps of the row RMSNorm (plain, residual add, FP8 output),
-the joint text/image op and the KV-cache write against the oracle.
+the joint text/image op, the KV-cache write and the ViT entry points (fused
+norm + rotation from patch grids, and the cos/sin setup) against the oracle.
 
 Every case prints its parameters before it runs.  Residual streams, copied V
 rows and untouched cache rows are compared bit for bit; normalised outputs
@@ -217,3 +218,61 @@ def test_random_cache(i):
         check(gk[mapped], rk[mapped], dtype, rot, c["pairing"], f"{what} k cache")
     if c["with_v"]:
         assert np.array_equal(host(vc).reshape(num_slots, kvh, d), rv), f"{what}: V must be copied bit for bit"
+
+
+# ---------------------------------------------------------------- ViT ------
+
+def split_positive(rng, total, parts):
+    """`parts` ints >= 1 summing to `total` (total >= parts)."""
+    return [x + 1 for x in split(rng, total - parts, parts)]
+
+
+def draw_vit(i):
+    rng = np.random.default_rng([W.SEED, 5401, i])
+    c = {"dtype": str(rng.choice(["bf16", "f32"])), "pairing": str(rng.choice(["neox", "adjacent"]))}
+    ve = 8 if c["dtype"] == "bf16" else 4
+    c["merge"] = int(rng.choice([1, 2, 3]))
+    n_grids = int(rng.choice([1, 2, 3, 6, 33, 40]))
+    m = c["merge"]
+    c["grids"] = [[int(rng.integers(1, 4)), m * int(rng.integers(1, 6)), m * int(rng.integers(1, 6))]
+                  for _ in range(n_grids)]
+    c["d"] = int(rng.choice([d for d in HEAD_DIMS if d % ve == 0 and d >= 16]))
+    unit = ve if c["pairing"] == "neox" else 1            # NeoX halves are whole 16-byte vectors
+    max_half = c["d"] // 2
+    half = unit * int(rng.integers(max(1, -(-3 // unit)), max_half // unit + 1))
+    c["halves"] = tuple(split_positive(rng, half, 3))
+    c["hq"] = int(rng.integers(1, 5))
+    c["hk"] = int(rng.integers(1, 5))
+    return c
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_vit(i):
+    c = draw_vit(i)
+    print(f"vit case {i}: {c}", flush=True)
+    rng = np.random.default_rng([W.SEED, 5402, i])
+    dtype, d, grids, merge = c["dtype"], c["d"], c["grids"], c["merge"]
+    n = sum(t * h * w for t, h, w in grids)
+    ht, hh, hw = c["halves"]
+    half = ht + hh + hw
+    inv = [W.inv_freq_ladder(1e4, 2 * x) for x in (ht, hh, hw)]
+    ginv = [torch.from_numpy(a).to(DEV) for a in inv]
+    q = W.to_dtype(rng.normal(0, 1, (n, c["hq"], d)).astype(np.float32), dtype)
+    k = W.to_dtype(rng.normal(0, 1, (n, c["hk"], d)).astype(np.float32), dtype)
+    wq = W.to_dtype(rng.normal(1, 0.1, d).astype(np.float32), dtype)
+    wk = W.to_dtype(rng.normal(1, 0.1, d).astype(np.float32), dtype)
+    qo, ko = qkr.vit_qk_norm_rope(q.to(DEV), k.to(DEV), wq.to(DEV), wk.to(DEV), W.EPS, *ginv, grids, merge,
+                                  c["pairing"])
+    for name, x, w, out in (("q", q, wq, qo), ("k", k, wk, ko)):
+        ref = oracle.vit_qk_norm_rope(W.as_f32(x), W.as_f32(w), W.EPS, *inv, grids, merge, c["pairing"], dtype)
+        check(host(out), ref, dtype, 2 * half, c["pairing"], f"vit case {i} {name}")
+    # The setup planes of the same grids: each plane's own columns, nothing else.
+    cos = torch.full((3, n, half), float("nan"), device=DEV)
+    sin = torch.full((3, n, half), float("nan"), device=DEV)
+    qkr.mrope_cos_sin_setup(*ginv, grids, merge, out=(cos, sin))
+    rc, rs = oracle.vit_cos_sin(*inv, grids, merge)
+    gc, gs = cos.cpu().numpy(), sin.cpu().numpy()
+    written = ~np.isnan(rc)
+    assert np.array_equal(np.isnan(gc), ~written) and np.array_equal(np.isnan(gs), ~written)
+    assert_f32_close(gc[written], rc[written], f"vit case {i} cos")
+    assert_f32_close(gs[written], rs[written], f"vit case {i} sin")
