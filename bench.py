@@ -13,9 +13,10 @@ last-level (Infinity) cache, so every step streams from HBM.
 
 value   = algorithmic bytes per step / time per step (GB/s), whole job.
 roofline.achieved = algorithmic bytes per launch of the dominant kernel /
-          its average launch duration, measured with HIP events recorded on
-          the stream the kernel runs on, around every launch of the timed
-          region.
+          its average launch duration: HIP events recorded on the stream the
+          kernels run on bracket the timed region (exactly K steps replayed
+          from captured graphs, launches back to back), divided by the
+          launches it holds.
 cpu_baseline: the CPU oracle on a bounded sample of the same workload, on
           the host cores (single-threaded C).
 """
@@ -38,7 +39,7 @@ METRIC = "fused QK-norm+RoPE µs/call and achieved HBM GB/s (% of peak), 1 MI355
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint",
                     choices=["joint", "joint-neox", "imrope", "vit", "vit-fused", "rows1", "rows32", "rows4096",
@@ -582,23 +583,29 @@ def main():
             w.step(sets[i % nsets])
         t_end.record(stream)
     else:
-        # One graph holds up to 256 steps cycling over the buffer sets;
-        # replaying it runs the launches back to back with no host work in
-        # between.  Each replay boundary costs several microseconds of idle
-        # GPU, so the graph is made long enough to spread that over many steps.
-        per_graph = nsets * max(1, min(args.steps, 256) // nsets)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(per_graph):
-                w.step(sets[i % nsets])
-        graph.replay()
+        # Exactly K steps cycling over the buffer sets, captured in graphs of
+        # up to 1024 kernel launches (plus one graph for the remainder);
+        # replaying a graph runs its launches back to back with no host work
+        # in between.  Each replay boundary costs several microseconds of idle
+        # GPU, so the graphs are long; a single graph of 4096 launches measured
+        # slower per launch (IMROPE chunk 6.39 us against 5.93-5.97 us with
+        # 200 to 2000 launches split over graphs of up to 1024).
+        K = args.steps
+        chunk = max(1, min(K, 1024 // w.launches))
+        plan = [chunk] * (K // chunk) + ([K % chunk] if K % chunk else [])
+        graphs = {}
+        for n in sorted(set(plan)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    w.step(sets[i % nsets])
+            g.replay()
+            graphs[n] = g
         torch.cuda.synchronize()
-        replays = max(1, -(-args.steps // per_graph))
-        K = replays * per_graph
         stream = torch.cuda.current_stream()
         t_start.record(stream)
-        for _ in range(replays):
-            graph.replay()
+        for n in plan:
+            graphs[n].replay()
         t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
