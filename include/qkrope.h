@@ -24,6 +24,12 @@
  *     QKR_ERR_MISALIGNED.  Offsets are computed in 64 bits, so views deep
  *     inside buffers larger than 4 GiB are fine ([Ovis] 64-bit row
  *     addressing).
+ *   - Size limits: one call covers fewer than 2^31 rows (batch x tokens x
+ *     heads, or `rows`) and at most 2^20 heads, and every view, row set,
+ *     position or cos/sin plane it touches spans at most 2^48 bytes (the
+ *     GPU's virtual address space); every stride, used or not, lies within
+ *     +-2^48 bytes.  The checks cannot overflow; a call beyond them returns
+ *     QKR_ERR_UNSUPPORTED.
  *   - Activations, weights and outputs share `dtype`.  Positions are int32,
  *     inverse frequencies and cos/sin planes are fp32.
  *   - `stream` is the caller's HIP stream (NULL: the null stream).  Work is
@@ -262,18 +268,22 @@ const char* qkr_last_variant(void);
 
 /* The position axis (0 t, 1 h, 2 w, 3 e) of each of n_pairs (<= 128) pairs
  * under `rope`, as the kernels see it: the host-built axis table they receive,
- * decoded by the same device function, written to out_dev [n_pairs] int32. */
+ * decoded by the same device function, written to out_dev [n_pairs] int32.
+ * Only rope->mode and rope->sections are read; each section must lie in
+ * [0, 2^20] (QKR_ERR_INVALID_ARGUMENT otherwise), with a positive sum for
+ * IMROPE. */
 qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* out_dev,
                               qkr_stream_t stream);
 
 /* The (t, h, w) position of every ViT token, computed by the same device
- * function the setup kernel uses, written to out_dev [3][n_tokens] int32. */
+ * function the setup kernel uses, written to out_dev [3][n_tokens] int32.
+ * n_tokens must equal the sum of t*h*w, which stays below 2^31. */
 qkr_status qkr_debug_vit_positions(const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
                                    int32_t* out_dev, int64_t n_tokens, qkr_stream_t stream);
 
 /* The FP8 E4M3 quantiser of qkr_add_rms_norm applied to x_dev [n] fp32:
  * out_dev [n] uint8 = code(x / *scale_dev) with the kernel's quotient, or
- * code(x) when scale_dev is NULL. */
+ * code(x) when scale_dev is NULL.  n < 2^31. */
 qkr_status qkr_debug_fp8_e4m3(const float* x_dev, int64_t n, const float* scale_dev, uint8_t* out_dev,
                               qkr_stream_t stream);
 

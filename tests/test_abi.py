@@ -355,3 +355,106 @@ def test_qk_norm_rope_cache_refusals(kwargs, code):
 def test_qk_norm_rope_cache_empty_calls_are_noops():
     assert qkcache(tokens=0, slots=None) == OK
     assert qkcache(qh=0, kvh=0, qw=None, kw=None, slots=None) == OK
+
+
+# ---------------------------------------------------------------------------
+# size arithmetic: counts whose products leave 64 bits are refused, never
+# wrapped into a small launch
+# ---------------------------------------------------------------------------
+
+BIG = 1 << 62
+
+
+def test_row_counts_beyond_the_grid_are_refused():
+    # rows x blocks-per-row wraps to 0 in 64 bits when rows = 2^62 and a row takes 4 blocks
+    assert rms(rows=BIG, width=2048, xs=2048, ys=2048) == UNSUPPORTED
+    assert rms(rows=(1 << 31), width=64, xs=64, ys=64) == UNSUPPORTED
+    assert addrms(rows=BIG) == UNSUPPORTED
+    # the row set (rows - 1) x stride leaves the address space before any overlap check runs
+    assert rms(rows=1 << 20, xs=1 << 40) == UNSUPPORTED
+    assert addrms(rows=1 << 20, ys=1 << 40) == UNSUPPORTED
+    assert qkr.lib().qkr_debug_fp8_e4m3(FAKE, 1 << 31, None, FAKE, None) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(qh=(1 << 31) - 1, kh=2),                        # q_heads + k_heads wraps in 32 bits
+    dict(qh=(1 << 30), kh=(1 << 30)),
+    dict(batch=(1 << 31) - 1, tokens=(1 << 31) - 1, qh=1 << 20, kh=0),   # product wraps in 64 bits
+    dict(tokens=1 << 31),
+    dict(tokens=BIG, batch=0),                           # an empty batch does not hide the token bound
+    dict(q=view(st=1 << 50)),                            # stride past the address space
+    dict(q=view(sb=-(1 << 60), st=16 * 128)),            # unused strides are bounded too
+    dict(tokens=1 << 20, q=view(st=1 << 32)),            # (tokens - 1) x stride spans > 2^48 bytes
+])
+def test_qk_norm_rope_size_refusals(kwargs):
+    assert qknr(**kwargs) == UNSUPPORTED, qkr.last_error()
+
+
+@pytest.mark.parametrize("rope,code", [
+    # sections whose 32-bit sum wraps onto rotary_dim / 2
+    (rope_c(mode=1, sections=((1 << 31) - 1, (1 << 31) - 1, 66, 0)), INVALID),
+    # token_base + tokens leaves 64 bits
+    (rope_c(token_base=(1 << 63) - 100), INVALID),
+    (rope_c(mode=3, sections=(16, 24, 24, 0), cosp=FAKE, sinp=FAKE, planes_tokens=4096,
+            token_base=(1 << 63) - 100), INVALID),
+    (rope_c(pos_stride=1 << 60), UNSUPPORTED),           # position planes past the address space
+    (rope_c(mode=3, sections=(16, 24, 24, 0), cosp=FAKE, sinp=FAKE, planes_tokens=1 << 50), UNSUPPORTED),
+])
+def test_rope_size_refusals(rope, code):
+    assert qknr(rope=rope) == code, qkr.last_error()
+
+
+def test_axis_map_sections_that_wrap_are_refused():
+    out = (ctypes.c_int32 * 4)()
+    m = (1 << 31) - 1
+    for sections in ((m, m, 3, 0), (m, 1, 0, 0), (1 << 21, 0, 0, 0), (4, -1, 4, 0)):
+        # (m, m, 3, 0) sums to 1 in 32 bits; 3 x 2^21 still fits but exceeds the stated range
+        big = rope_c(mode=2, sections=sections)
+        assert qkr.lib().qkr_axis_map_host(ctypes.byref(big), 4, out) == INVALID, sections
+        assert qkr.lib().qkr_debug_axis_map(ctypes.byref(big), 4, FAKE, None) == INVALID, sections
+
+
+def test_cache_and_joint_size_refusals():
+    assert qkcache(kvh=(1 << 30), qh=(1 << 30)) == UNSUPPORTED                  # 2 x kv_heads in 32 bits
+    assert qkcache(tokens=1 << 20, kvh=1 << 19, qh=0, qw=None) == UNSUPPORTED   # 2^20 x 2^20 rows
+    assert qkcache(num_slots=1 << 40) == UNSUPPORTED                            # cache spans > 2^48 bytes
+    L = qkr.lib()
+
+    def stream(tokens):
+        v = view(st=9216, sh=128)
+        return qkr._Stream(v, v, v, tokens, FAKE, FAKE)
+
+    out = view(st=24 * 128)
+    r = rope_c(mode=1, pairing=1, sections=(8, 28, 28, 0), pos_stride=4608)
+
+    def call(text, image, heads=24, batch=1):
+        return L.qkr_joint_qk_norm_rope(batch, heads, 128, qkr.BF16, 1e-6, ctypes.byref(text), ctypes.byref(image),
+                                        ctypes.byref(out), ctypes.byref(out), ctypes.byref(out), ctypes.byref(r),
+                                        None)
+
+    assert call(stream((1 << 63) - 1), stream(2)) == UNSUPPORTED    # text + image tokens leave 64 bits
+    assert call(stream(1 << 30), stream(1 << 30), heads=1 << 18, batch=1 << 30) == UNSUPPORTED
+
+
+def test_grid_products_that_leave_64_bits_are_refused():
+    L = qkr.lib()
+    m = (1 << 31) - 1
+    # t x h x w = (2^31 - 1)^3 and its sum over grids wrap in 64 bits
+    flat = [m, m - 1, m - 1] * 3
+    arr = (ctypes.c_int32 * len(flat))(*flat)
+    assert L.qkr_vit_positions_host(arr, 3, 1, None, 0) == UNSUPPORTED
+    assert L.qkr_mrope_cos_sin_setup(FAKE, 8, FAKE, 16, FAKE, 16, arr, 3, 1, FAKE, FAKE, 0, None) == UNSUPPORTED
+    # one grid of 2^30 tokens with 64 columns: 2^36 setup threads
+    one = (ctypes.c_int32 * 3)(1, 1 << 15, 1 << 15)
+    assert L.qkr_mrope_cos_sin_setup(FAKE, 16, FAKE, 16, FAKE, 32, one, 1, 1, FAKE, FAKE, 1 << 30,
+                                     None) == UNSUPPORTED
+    # ViT fused: head counts whose 32-bit sum wraps
+    v = view(st=16 * 80, sh=80)
+    g = (ctypes.c_int32 * 3)(1, 64, 64)
+    assert L.qkr_vit_qk_norm_rope(4096, 80, qkr.BF16, 1e-6, ctypes.byref(v), ctypes.byref(v), (1 << 31) - 1, FAKE,
+                                  ctypes.byref(v), ctypes.byref(v), 2, FAKE, 0, FAKE, 8, FAKE, 16, FAKE, 16, g, 1, 2,
+                                  None) == UNSUPPORTED
+    # ViT fused: axis halves whose 32-bit sum wraps past head_dim / 2
+    assert L.qkr_vit_qk_norm_rope(4096, 80, qkr.BF16, 1e-6, ctypes.byref(v), ctypes.byref(v), 16, FAKE,
+                                  ctypes.byref(v), ctypes.byref(v), 16, FAKE, 0, FAKE, (1 << 31) - 1, FAKE,
+                                  (1 << 31) - 1, FAKE, 8, g, 1, 2, None) == INVALID

@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <climits>
 #include <cstring>
+#include <initializer_list>
 #include <utility>
 #include <vector>
 
@@ -52,6 +53,35 @@ qkr_status ok()
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+// Size arithmetic on caller-supplied counts.  Every byte offset into a real
+// device buffer fits the GPU's 48-bit virtual address space, so strides and
+// spans are held to it; then no offset that the host or a kernel forms
+// (index * stride, summed over the dimensions) can leave 64 bits.  Rows,
+// tiles and tokens of one launch stay below 2^31 (32-bit tile indices).
+constexpr int64_t kAddrBytes = (int64_t)1 << 48;
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+// a * b for a, b >= 0, or -1 when the product exceeds `limit`; never overflows.
+int64_t mul_capped(int64_t a, int64_t b, int64_t limit)
+{
+    if (a == 0 || b == 0)
+        return 0;
+    return a > limit / b ? -1 : a * b;
+}
+
+// Whether the product of non-negative factors is below `limit`.
+bool product_below(std::initializer_list<int64_t> factors, int64_t limit)
+{
+    for (const int64_t f : factors)
+        if (f == 0)
+            return true;
+    int64_t p = 1;
+    for (const int64_t f : factors)
+        if ((p = mul_capped(p, f, limit - 1)) < 0)
+            return false;
+    return true;
+}
 
 qkr_status hip_status(hipError_t e, const char* what)
 {
@@ -101,17 +131,36 @@ qkr_status check_view(const char* name, const qkr_view* v, int esize, int32_t ba
     if (!aligned(v->ptr_dev, 16))
         return fail(QKR_ERR_MISALIGNED, "%s: pointer is not 16-byte aligned", name);
     const int64_t st[3] = {v->stride_batch, v->stride_tok, v->stride_head};
-    const bool used[3] = {batch > 1, tokens > 1, heads > 1};
+    const int64_t n[3] = {batch, tokens, heads};
     static const char* what[3] = {"stride_batch", "stride_tok", "stride_head"};
+    const int64_t lim = kAddrBytes / esize;
+    int64_t span = 0;
     for (int i = 0; i < 3; ++i) {
-        if (!used[i])
+        // Unused strides are still turned into bytes, so they are bounded too.
+        if (st[i] > lim || st[i] < -lim)
+            return fail(QKR_ERR_UNSUPPORTED, "%s: %s %lld reaches past a 2^48-byte address space", name, what[i],
+                        (long long)st[i]);
+        if (n[i] <= 1)
             continue;
         if (st[i] < 0)
             return fail(QKR_ERR_INVALID_ARGUMENT, "%s: negative %s", name, what[i]);
         if ((st[i] * esize) % 16 != 0)
             return fail(QKR_ERR_MISALIGNED, "%s: %s %lld is not a multiple of 16 bytes", name, what[i],
                         (long long)st[i]);
+        const int64_t reach = mul_capped(n[i] - 1, st[i] * esize, kAddrBytes);
+        if (reach < 0 || (span += reach) > kAddrBytes)
+            return fail(QKR_ERR_UNSUPPORTED, "%s: the view spans more than 2^48 bytes", name);
     }
+    return QKR_OK;
+}
+
+// `rows` rows spaced `stride` elements of `es` bytes (0 <= stride, checked
+// before): the row set spans at most the address space.
+qkr_status check_row_span(const char* name, int64_t rows, int64_t stride, int64_t es)
+{
+    if (rows > 1 && (stride > kAddrBytes / es || mul_capped(rows - 1, stride * es, kAddrBytes) < 0))
+        return fail(QKR_ERR_UNSUPPORTED, "%s: %lld rows %lld elements apart span more than 2^48 bytes", name,
+                    (long long)rows, (long long)stride);
     return QKR_OK;
 }
 
@@ -154,7 +203,7 @@ qkr_status check_rope(const qkr_rope* r, int32_t head_dim, int esize, int64_t to
     const int32_t* s = r->sections;
     const int32_t half = R / 2;
     if (r->mode == QKR_POS_AXES || r->mode == QKR_POS_PLANES) {
-        if (s[0] < 0 || s[1] < 0 || s[2] < 0 || s[3] != 0 || s[0] + s[1] + s[2] != half)
+        if (s[0] < 0 || s[1] < 0 || s[2] < 0 || s[3] != 0 || (int64_t)s[0] + s[1] + s[2] != half)
             return fail(QKR_ERR_INVALID_ARGUMENT,
                         "axis sections (%d, %d, %d, %d) must be >= 0, end with 0 and sum to rotary_dim/2 = %d",
                         s[0], s[1], s[2], s[3], half);
@@ -173,18 +222,26 @@ qkr_status check_rope(const qkr_rope* r, int32_t head_dim, int esize, int64_t to
             return fail(QKR_ERR_INVALID_ARGUMENT, "PLANES mode needs cos and sin planes");
         if (!aligned(r->cos_planes_dev, 4) || !aligned(r->sin_planes_dev, 4))
             return fail(QKR_ERR_MISALIGNED, "cos/sin planes are not 4-byte aligned");
-        if (tokens > 0 && r->planes_tokens < r->token_base + tokens)
-            return fail(QKR_ERR_INVALID_ARGUMENT, "planes hold %lld tokens, the call reads up to %lld",
-                        (long long)r->planes_tokens, (long long)(r->token_base + tokens));
+        if (tokens > 0 && (r->planes_tokens < tokens || r->planes_tokens - tokens < r->token_base))
+            return fail(QKR_ERR_INVALID_ARGUMENT, "planes hold %lld tokens, the call reads %lld from token %lld",
+                        (long long)r->planes_tokens, (long long)tokens, (long long)r->token_base);
+        // Three planes of planes_tokens x rotary_dim/2 floats.
+        if (!product_below({r->planes_tokens, 3, half, 4}, kAddrBytes + 1))
+            return fail(QKR_ERR_UNSUPPORTED, "cos/sin planes of %lld tokens span more than 2^48 bytes",
+                        (long long)r->planes_tokens);
     } else {
         if (r->inv_freq_dev == nullptr || r->positions_dev == nullptr)
             return fail(QKR_ERR_INVALID_ARGUMENT, "position mode %d needs inv_freq and positions", r->mode);
         if (!aligned(r->inv_freq_dev, 4) || !aligned(r->positions_dev, 4))
             return fail(QKR_ERR_MISALIGNED, "inv_freq/positions are not 4-byte aligned");
-        if (tokens > 0 && r->pos_stride < r->token_base + tokens)
+        if (tokens > 0 && (r->pos_stride < tokens || r->pos_stride - tokens < r->token_base))
             return fail(QKR_ERR_INVALID_ARGUMENT,
-                        "position planes hold %lld tokens (pos_stride), the call reads up to %lld",
-                        (long long)r->pos_stride, (long long)(r->token_base + tokens));
+                        "position planes hold %lld tokens (pos_stride), the call reads %lld from token %lld",
+                        (long long)r->pos_stride, (long long)tokens, (long long)r->token_base);
+        // Up to four planes of pos_stride int32 positions.
+        if (!product_below({r->pos_stride, 4, 4}, kAddrBytes + 1))
+            return fail(QKR_ERR_UNSUPPORTED, "position planes of stride %lld span more than 2^48 bytes",
+                        (long long)r->pos_stride);
     }
     out.mode = r->mode;
     out.half = half;
@@ -236,6 +293,23 @@ qkr_status launch(NormRopeArgs& a, int32_t dtype, int32_t pairing, hipStream_t s
     return ok();
 }
 
+// Mode and sections of the axis-map entries, which take sections on their
+// own (no rotary_dim bounds them): each in [0, 2^20], so the sector rule's
+// sums and 3 x section products stay in 32 bits, and a positive sum for
+// IMROPE.
+qkr_status check_map_rope(const qkr_rope* rope)
+{
+    if (rope->mode < QKR_POS_1D || rope->mode > QKR_POS_PLANES)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown position mode %d", rope->mode);
+    const int32_t* s = rope->sections;
+    for (int i = 0; i < 4; ++i)
+        if (s[i] < 0 || s[i] > (1 << 20))
+            return fail(QKR_ERR_INVALID_ARGUMENT, "section %d = %d outside [0, 2^20]", i, s[i]);
+    if (rope->mode == QKR_POS_IMROPE && s[0] + s[1] + s[2] + s[3] <= 0)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "IMROPE needs a positive section sum");
+    return QKR_OK;
+}
+
 // Shared set-up of the ViT grid table; validates and returns the total.
 qkr_status check_grids(const int32_t* grid_thw, int32_t num_grids, int32_t merge, int64_t& total)
 {
@@ -251,7 +325,11 @@ qkr_status check_grids(const int32_t* grid_thw, int32_t num_grids, int32_t merge
         if (h % merge != 0 || w % merge != 0)
             return fail(QKR_ERR_INVALID_ARGUMENT, "grid %d: h %d and w %d must be multiples of spatial_merge %d",
                         g, h, w, merge);
-        total += (int64_t)t * h * w;
+        // t * h * w < 2^31 each (t * h <= 2^62 cannot overflow), and so is the sum.
+        const int64_t th = (int64_t)t * h;
+        if (th >= kMaxRows || !product_below({th, w}, kMaxRows - total))
+            return fail(QKR_ERR_UNSUPPORTED, "grids hold 2^31 tokens or more (grid %d)", g);
+        total += th * w;
     }
     return QKR_OK;
 }
@@ -364,6 +442,8 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
         return fail(QKR_ERR_UNSUPPORTED, "width %d exceeds %d elements", width, 16 * kThreads * 16 / esize);
     if (rows == 0)
         return ok();
+    if (!product_below({rows, (nvec + 63) / 64}, kMaxRows))
+        return fail(QKR_ERR_UNSUPPORTED, "rows %lld exceed the launch grid", (long long)rows);
     if (x_dev == nullptr || y_dev == nullptr)
         return fail(QKR_ERR_INVALID_ARGUMENT, "null x or y");
     if ((st = check_weight("weight", weight_dev)))
@@ -373,11 +453,12 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
     if (rows > 1) {
         if (x_row_stride < width || y_row_stride < width)
             return fail(QKR_ERR_INVALID_ARGUMENT, "row strides must be >= width");
+        if ((st = check_row_span("x", rows, x_row_stride, esize)) ||
+            (st = check_row_span("y", rows, y_row_stride, esize)))
+            return st;
         if ((x_row_stride * esize) % 16 != 0 || (y_row_stride * esize) % 16 != 0)
             return fail(QKR_ERR_MISALIGNED, "row strides are not multiples of 16 bytes");
     }
-    if (rows * ((nvec + 63) / 64) >= ((int64_t)1 << 31))
-        return fail(QKR_ERR_UNSUPPORTED, "rows %lld exceed the launch grid", (long long)rows);
 
     RmsArgs a{};
     a.x = static_cast<const char*>(x_dev);
@@ -427,6 +508,8 @@ qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void*
         return fail(QKR_ERR_INVALID_ARGUMENT, "FP8 output needs a device scale");
     if (rows == 0)
         return ok();
+    if (!product_below({rows, (nvec + 63) / 64}, kMaxRows))
+        return fail(QKR_ERR_UNSUPPORTED, "rows %lld exceed the launch grid", (long long)rows);
     if (x_dev == nullptr || y_dev == nullptr)
         return fail(QKR_ERR_INVALID_ARGUMENT, "null x or y");
     if ((st = check_weight("weight", weight_dev)))
@@ -439,10 +522,20 @@ qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void*
         return fail(QKR_ERR_MISALIGNED, "y or scale is not aligned");
     if (rows > 1) {
         const int64_t strides[3] = {x_row_stride, add ? r_row_stride : width, add ? s_row_stride : width};
-        for (int i = 0; i < 3; ++i)
-            if (strides[i] < width || (strides[i] * esize) % 16 != 0)
+        static const char* names[3] = {"x", "residual", "residual output"};
+        for (int i = 0; i < 3; ++i) {
+            if (strides[i] < width)
                 return fail(QKR_ERR_MISALIGNED, "row strides must be >= width and multiples of 16 bytes");
-        if (y_row_stride < width || (y_row_stride * y_esize) % (fp8 ? ve : 16) != 0)
+            if ((st = check_row_span(names[i], rows, strides[i], esize)))
+                return st;
+            if ((strides[i] * esize) % 16 != 0)
+                return fail(QKR_ERR_MISALIGNED, "row strides must be >= width and multiples of 16 bytes");
+        }
+        if (y_row_stride < width)
+            return fail(QKR_ERR_MISALIGNED, "y row stride must be >= width and keep rows aligned");
+        if ((st = check_row_span("y", rows, y_row_stride, y_esize)))
+            return st;
+        if ((y_row_stride * y_esize) % (fp8 ? ve : 16) != 0)
             return fail(QKR_ERR_MISALIGNED, "y row stride must be >= width and keep rows aligned");
     }
     // The residual output may overwrite the residual or x in place (same
@@ -481,8 +574,6 @@ qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void*
         if ((overlap(ro, rr) && !same_r) || (overlap(ro, rx) && !same_x))
             return fail(QKR_ERR_INVALID_ARGUMENT, "the residual output overlaps an input other than in place");
     }
-    if (rows * ((nvec + 63) / 64) >= ((int64_t)1 << 31))
-        return fail(QKR_ERR_UNSUPPORTED, "rows %lld exceed the launch grid", (long long)rows);
 
     RmsArgs a{};
     a.x = static_cast<const char*>(x_dev);
@@ -515,7 +606,7 @@ qkr_status qkr_debug_fp8_e4m3(const float* x_dev, int64_t n, const float* scale_
 {
     if (n < 0 || (n > 0 && (x_dev == nullptr || out_dev == nullptr)))
         return fail(QKR_ERR_INVALID_ARGUMENT, "debug_fp8_e4m3: null pointers or negative n");
-    if (n >= ((int64_t)1 << 38))
+    if (n >= kMaxRows)
         return fail(QKR_ERR_UNSUPPORTED, "debug_fp8_e4m3: n too large");
     (void)hipGetLastError();
     return hip_status(launch_debug_fp8(x_dev, n, scale_dev, out_dev, reinterpret_cast<hipStream_t>(stream)),
@@ -533,10 +624,11 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
         return st;
     if (batch < 0 || tokens < 0 || q_heads < 0 || k_heads < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative batch, tokens or heads");
-    if (tokens > INT32_MAX || (int64_t)batch * tokens * (q_heads + k_heads) >= ((int64_t)1 << 31))
-        return fail(QKR_ERR_UNSUPPORTED, "batch * tokens * heads must stay below 2^31 rows per call");
-    if ((int64_t)q_heads + k_heads > (1 << 20))
+    const int64_t heads_total = (int64_t)q_heads + k_heads;
+    if (heads_total > (1 << 20))
         return fail(QKR_ERR_UNSUPPORTED, "too many heads");
+    if (tokens >= kMaxRows || !product_below({batch, tokens, heads_total}, kMaxRows))
+        return fail(QKR_ERR_UNSUPPORTED, "batch * tokens * heads must stay below 2^31 rows per call");
     if ((st = check_view("q", q, esize, batch, tokens, q_heads)) ||
         (st = check_view("q_out", q_out, esize, batch, tokens, q_heads)) ||
         (st = check_view("k", k, esize, batch, tokens, k_heads)) ||
@@ -585,10 +677,10 @@ qkr_status qkr_qk_norm_rope_cache(int64_t tokens, int32_t head_dim, int32_t dtyp
         return st;
     if (tokens < 0 || q_heads < 0 || kv_heads < 0 || num_slots < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative tokens, heads or num_slots");
-    if (tokens > INT32_MAX || tokens * ((int64_t)q_heads + 2 * kv_heads) >= ((int64_t)1 << 31))
-        return fail(QKR_ERR_UNSUPPORTED, "tokens * heads must stay below 2^31 rows per call");
     if ((int64_t)q_heads + kv_heads > (1 << 20))
         return fail(QKR_ERR_UNSUPPORTED, "too many heads");
+    if (tokens >= kMaxRows || !product_below({tokens, (int64_t)q_heads + 2 * (int64_t)kv_heads}, kMaxRows))
+        return fail(QKR_ERR_UNSUPPORTED, "tokens * heads must stay below 2^31 rows per call");
     if ((v == nullptr) != (v_cache == nullptr))
         return fail(QKR_ERR_INVALID_ARGUMENT, "v and v_cache come together (both or neither)");
     if ((st = check_view("q", q, esize, 1, tokens, q_heads)) ||
@@ -663,8 +755,10 @@ qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative batch, heads or tokens");
     if (heads > (1 << 18))
         return fail(QKR_ERR_UNSUPPORTED, "too many heads");
+    if (text->tokens >= kMaxRows || image->tokens >= kMaxRows)
+        return fail(QKR_ERR_UNSUPPORTED, "a stream holds 2^31 tokens or more");
     const int64_t joint = text->tokens + image->tokens;
-    if (joint > INT32_MAX || (int64_t)batch * joint * 3 * heads >= ((int64_t)1 << 31))
+    if (joint >= kMaxRows || !product_below({batch, joint, 3, heads}, kMaxRows))
         return fail(QKR_ERR_UNSUPPORTED, "batch * tokens * 3 heads must stay below 2^31 rows per call");
     const qkr_stream* streams[2] = {text, image};
     static const char* names[2][3] = {{"text.q", "text.k", "text.v"}, {"image.q", "image.k", "image.v"}};
@@ -718,7 +812,7 @@ qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t, 
                                    const int32_t* grid_thw, int32_t num_grids, int32_t spatial_merge,
                                    float* cos_out_dev, float* sin_out_dev, int64_t n_tokens, qkr_stream_t stream)
 {
-    if (half_t < 0 || half_h < 0 || half_w < 0 || half_t + half_h + half_w <= 0)
+    if (half_t < 0 || half_h < 0 || half_w < 0 || (int64_t)half_t + half_h + half_w <= 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "axis halves (%d, %d, %d) must be >= 0 with a positive sum",
                     half_t, half_h, half_w);
     const float* inv[3] = {inv_freq_t_dev, inv_freq_h_dev, inv_freq_w_dev};
@@ -736,6 +830,9 @@ qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t, 
     if (n_tokens != total)
         return fail(QKR_ERR_INVALID_ARGUMENT, "n_tokens %lld != sum of t*h*w = %lld", (long long)n_tokens,
                     (long long)total);
+    // One thread per (token, column) on a 1-D grid.
+    if (!product_below({n_tokens, (int64_t)half_t + half_h + half_w}, kMaxRows))
+        return fail(QKR_ERR_UNSUPPORTED, "n_tokens * (half_t + half_h + half_w) must stay below 2^31");
     if (cos_out_dev == nullptr || sin_out_dev == nullptr)
         return fail(QKR_ERR_INVALID_ARGUMENT, "null cos or sin output");
     if (!aligned(cos_out_dev, 4) || !aligned(sin_out_dev, 4))
@@ -776,7 +873,9 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
         return st;
     if (tokens < 0 || q_heads < 0 || k_heads < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative tokens or heads");
-    if (tokens > INT32_MAX || tokens * (q_heads + k_heads) >= ((int64_t)1 << 31))
+    if ((int64_t)q_heads + k_heads > (1 << 20))
+        return fail(QKR_ERR_UNSUPPORTED, "too many heads");
+    if (tokens >= kMaxRows || !product_below({tokens, (int64_t)q_heads + k_heads}, kMaxRows))
         return fail(QKR_ERR_UNSUPPORTED, "tokens * heads must stay below 2^31 rows per call");
     if ((st = check_view("q", q, esize, 1, tokens, q_heads)) ||
         (st = check_view("q_out", q_out, esize, 1, tokens, q_heads)) ||
@@ -789,12 +888,13 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
         return st;
     if (pairing != QKR_PAIR_NEOX && pairing != QKR_PAIR_ADJACENT)
         return fail(QKR_ERR_INVALID_ARGUMENT, "unknown pairing %d", pairing);
-    if (half_t < 0 || half_h < 0 || half_w < 0 || half_t + half_h + half_w <= 0)
+    if (half_t < 0 || half_h < 0 || half_w < 0 || (int64_t)half_t + half_h + half_w <= 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "axis halves (%d, %d, %d) must be >= 0 with a positive sum",
                     half_t, half_h, half_w);
+    if ((int64_t)half_t + half_h + half_w > head_dim / 2)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "rotary dims 2 * (%d + %d + %d) exceed head_dim %d", half_t,
+                    half_h, half_w, head_dim);
     const int32_t half = half_t + half_h + half_w;
-    if (2 * half > head_dim)
-        return fail(QKR_ERR_INVALID_ARGUMENT, "rotary dims 2 * %d exceed head_dim %d", half, head_dim);
     if (pairing == QKR_PAIR_NEOX && half % (16 / esize) != 0)
         return fail(QKR_ERR_UNSUPPORTED, "NeoX pairing needs rotary_dim/2 (%d) to be a multiple of %d elements",
                     half, 16 / esize);
@@ -851,8 +951,9 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
         for (int32_t k2 = 0; k2 < n; ++k2) {
             const int32_t* g = grid_thw + 3 * (g0 + k2);
             a.vit.cu[k2] = cu;
-            a.vit.div_area[k2] = make_fastdiv((uint32_t)(g[1] * g[2]));
-            a.vit.div_mw[k2] = make_fastdiv((uint32_t)(spatial_merge * g[2]));
+            // h * w and merge * w are at most t * h * w < 2^31 (h is a multiple of merge).
+            a.vit.div_area[k2] = make_fastdiv((uint32_t)((int64_t)g[1] * g[2]));
+            a.vit.div_mw[k2] = make_fastdiv((uint32_t)((int64_t)spatial_merge * g[2]));
             cu += (int64_t)g[0] * g[1] * g[2];
         }
         a.vit.cu[n] = cu;
@@ -881,13 +982,11 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
 
 qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* out_dev, qkr_stream_t stream)
 {
+    qkr_status st;
     if (rope == nullptr || n_pairs < 0 || (n_pairs > 0 && out_dev == nullptr))
         return fail(QKR_ERR_INVALID_ARGUMENT, "debug_axis_map: null rope/output or negative n_pairs");
-    if (rope->mode < QKR_POS_1D || rope->mode > QKR_POS_PLANES)
-        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown position mode %d", rope->mode);
-    if (rope->mode == QKR_POS_IMROPE && rope->sections[0] + rope->sections[1] + rope->sections[2] +
-                                                rope->sections[3] <= 0)
-        return fail(QKR_ERR_INVALID_ARGUMENT, "IMROPE needs a positive section sum");
+    if ((st = check_map_rope(rope)))
+        return st;
     if (n_pairs > kMaxPairs)
         return fail(QKR_ERR_UNSUPPORTED, "debug_axis_map: at most %d pairs", kMaxPairs);
     RopeArgs r{};
@@ -899,13 +998,11 @@ qkr_status qkr_debug_axis_map(const qkr_rope* rope, int32_t n_pairs, int32_t* ou
 
 qkr_status qkr_axis_map_host(const qkr_rope* rope, int32_t n_pairs, int32_t* out_host)
 {
+    qkr_status st;
     if (rope == nullptr || n_pairs < 0 || (n_pairs > 0 && out_host == nullptr))
         return fail(QKR_ERR_INVALID_ARGUMENT, "axis_map_host: null rope/output or negative n_pairs");
-    if (rope->mode < QKR_POS_1D || rope->mode > QKR_POS_PLANES)
-        return fail(QKR_ERR_INVALID_ARGUMENT, "unknown position mode %d", rope->mode);
-    if (rope->mode == QKR_POS_IMROPE && rope->sections[0] + rope->sections[1] + rope->sections[2] +
-                                                rope->sections[3] <= 0)
-        return fail(QKR_ERR_INVALID_ARGUMENT, "IMROPE needs a positive section sum");
+    if ((st = check_map_rope(rope)))
+        return st;
     for (int32_t p = 0; p < n_pairs; ++p)
         out_host[p] = pair_axis(rope->mode, rope->sections, p);
     return ok();
