@@ -248,7 +248,8 @@ class Rope:
             raise QkrError("position planes overlap")
         r.inv_freq_dev = self.inv_freq.data_ptr()
         r.positions_dev = pos.data_ptr()
-        r.pos_stride = pos.stride(0) if pos.shape[0] > 1 else pos.shape[1]
+        # One plane read (1d): its length bounds the reads, whatever the planes' stride.
+        r.pos_stride = pos.stride(0) if need > 1 else pos.shape[1]
         return r
 
 
@@ -424,6 +425,9 @@ def qk_norm_rope_cache(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tenso
         raise QkrError("q and k must be [tokens, heads, head_dim] with equal tokens and head_dim")
     if k.dtype != q.dtype:
         raise QkrError("q and k must share a dtype")
+    for nm, t in (("q", q), ("k", k), ("v", v), ("q_out", q_out)):
+        if t is not None and not _unit_stride(t, -1):
+            raise QkrError(f"{nm}: the head_dim dimension must be contiguous")
     tokens, hq, d = q.shape
     hkv = k.shape[1]
     if (v is None) != (v_cache is None):
@@ -582,8 +586,8 @@ def vit_qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_wei
         if w.dtype != t.dtype or not w.is_contiguous() or w.numel() != t.shape[2]:
             raise QkrError(f"{nm}_weight must be contiguous [head_dim] of the activation dtype")
         oo = torch.empty(t.shape, dtype=t.dtype, device=dev) if o is None else o
-        if oo.shape != t.shape or oo.dtype != t.dtype:
-            raise QkrError(f"{nm}_out must match {nm}")
+        if oo.shape != t.shape or oo.dtype != t.dtype or not _unit_stride(oo, -1):
+            raise QkrError(f"{nm}_out must match {nm}, with a contiguous last dimension")
         _on_gpu(f"{nm}_out", oo, dev)
         outs.append(oo)
         views.append((t, oo, t.shape[1], w))
