@@ -767,6 +767,35 @@ def test_cache_write_paged_sparse_slots(dtype):
     assert np.array_equal(host(vc).reshape(num_slots, kvh, d), rv)   # V copied bit for bit
 
 
+def test_cache_write_full_size():
+    """The timed cache-write configuration: 8192 tokens of the IMROPE workload
+    (16 Q, 8 K/V heads x 128, bf16) into a paged cache of 2048 blocks x 16
+    slots through a random injective slot map, one launch."""
+    case = W.imrope()
+    T, H, KV, D = case.q.shape[0], case.q.shape[1], case.k.shape[1], 128
+    blocks, bs = 2048, 16
+    v = W.to_dtype(W.normal((T, KV, D), 0.0, 1.0, 61), "bf16")
+    slots = np.random.default_rng(61).permutation(blocks * bs)[:T].astype(np.int64)
+    kc = torch.zeros((blocks, bs, KV, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    rope = qkr.Rope("imrope", D, "neox", inv_freq=gpu(torch.from_numpy(case.inv_freq)),
+                    positions=gpu(torch.from_numpy(case.positions)), sections=case.sections)
+    qo = qkr.qk_norm_rope_cache(gpu(case.q), gpu(case.k), gpu(v), gpu(case.q_weight), gpu(case.k_weight), kc, vc,
+                                gpu(torch.from_numpy(slots)), case.eps, rope)
+    orope = oracle.Rope("imrope", D, "neox", inv_freq=case.inv_freq, sections=case.sections,
+                        positions=case.positions)
+    kc0 = np.zeros((blocks * bs, KV, D), np.float32)
+    rq, rk, rv = oracle.qk_norm_rope_cache(W.as_f32(case.q), W.as_f32(case.k), W.as_f32(v), W.as_f32(case.q_weight),
+                                           W.as_f32(case.k_weight), case.eps, orope, slots, kc0, kc0.copy(), "bf16")
+    check(host(qo), rq, "bf16", D, "neox", "q")
+    gk = host(kc).reshape(blocks * bs, KV, D)
+    mapped = np.zeros(blocks * bs, bool)
+    mapped[slots] = True
+    assert np.array_equal(gk[~mapped], rk[~mapped])
+    check(gk[mapped], rk[mapped], "bf16", D, "neox", "k cache")
+    assert np.array_equal(host(vc).reshape(blocks * bs, KV, D), rv)
+
+
 def test_cache_write_imrope_without_v_and_empty_cache():
     case = W.imrope(tokens=64)
     d = 128
