@@ -440,6 +440,39 @@ def test_large_storage_offset():
 # HIP graph capture: replays match eager calls, every replay
 # ---------------------------------------------------------------------------
 
+def test_maximum_row_count():
+    """A call at the row limit: 2^31 - 64 rows (2^25 - 1 tokens x 64 heads of
+    fp32 x 8, 64 GiB each way), checked against the oracle on sampled tokens,
+    the first and last included."""
+    tokens, heads, d = (1 << 25) - 1, 64, 8
+    rows = tokens * heads
+    assert rows == (1 << 31) - 64
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 2 * rows * d * 4 + (4 << 30):
+        pytest.skip(f"needs {2 * rows * d * 4 / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} GiB free")
+    g = torch.Generator(device=DEV).manual_seed(W.SEED)
+    q = torch.randn((tokens, heads, d), device=DEV, generator=g)
+    w = torch.rand(d, device=DEV, generator=g) + 0.5
+    pos = torch.randint(0, 8192, (1, tokens), dtype=torch.int32, device=DEV, generator=g)
+    inv = W.inv_freq_ladder(1e4, d)
+    rope = qkr.Rope("1d", d, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=pos)
+    try:
+        qo, ko = qkr.qk_norm_rope(q, None, w, None, W.EPS, rope)
+        assert ko is None
+        rng = np.random.default_rng(W.SEED)
+        toks = torch.from_numpy(np.unique(np.concatenate([[0, 1, tokens - 2, tokens - 1],
+                                                          rng.integers(0, tokens, 1024)]))).to(DEV)
+        qs, got, ps = host(q[toks]), host(qo[toks]), pos[:, toks].cpu().numpy()
+    finally:
+        del q
+        qo = None
+        torch.cuda.empty_cache()
+    orope = oracle.Rope("1d", d, "neox", inv_freq=inv, positions=ps)
+    ref = oracle.qk_norm_rope(qs, host(w), W.EPS, orope, "f32")
+    assert_f32_close(got, ref, "maximum row count")
+
+
 def test_graph_capture_replays_match_eager():
     case = W.joint(tokens_txt=40, grid=(8, 12), heads=6, seed_stream=31)
     g, rope = joint_gpu(case, "adjacent")
