@@ -593,6 +593,28 @@ def _with_variants(names, fn):
         qkr.set_variant_override(None)
 
 
+@pytest.mark.parametrize("dtype,head_dim,pairing", [
+    ("bf16", 128, "neox"), ("f32", 64, "adjacent"), ("bf16", 80, "neox"), ("f32", 256, "neox"),
+])
+def test_pass_counts_and_cache_policy_agree_bitwise(dtype, head_dim, pairing):
+    """Every passes-per-tile count (1 to 4, so tiles with partial and wholly
+    unused passes) with nontemporal accesses on and off gives the same bits;
+    the first is also checked against the oracle.  13 heads: ragged passes."""
+    case = W.tiny(tokens=37, heads=13, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 101)
+    pos = np.random.default_rng(head_dim + 1).integers(0, 8000, (1, 37)).astype(np.int32)
+    ref = None
+    for np_ in ("rope:np1", "rope:np2", "rope:np3", "rope:np4"):
+        for nt in ("nt:0", "nt:1"):
+            (qo, ko, rq, rk), name = _with_variants([np_, nt], lambda: run_1d(case, pairing, positions=pos))
+            assert name.startswith(f"rope:np{np_[-1]}:nt{nt[-1]}:"), name
+            if ref is None:
+                check(qo, rq, dtype, head_dim, pairing, "q")
+                check(ko, rk, dtype, head_dim, pairing, "k")
+                ref = (qo, ko)
+            else:
+                assert np.array_equal(qo, ref[0]) and np.array_equal(ko, ref[1]), name
+
+
 @pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing", [
     ("bf16", 80, 80, "neox"), ("bf16", 64, 64, "adjacent"), ("bf16", 96, 64, "neox"),
     ("f32", 40, 40, "adjacent"), ("bf16", 72, 48, "neox"), ("f32", 32, 16, "neox"),
