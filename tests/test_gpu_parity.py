@@ -700,6 +700,28 @@ def _addrms_case(rows, width, act, seed):
     return x, r, w
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_row_kernels_cache_policy_agrees_bitwise(act):
+    """Every row variant with nontemporal accesses on and off: the plain norm,
+    the residual add (both outputs) and the FP8 output give the same bits."""
+    # 10 KB rows: one wave per row holds them whole in either type
+    x, r, w = _addrms_case(37, 5120 if act == "bf16" else 2560, act, 7)
+    scale = gpu(torch.tensor([0.03], dtype=torch.float32))
+    for kind in ("rms:rows", "rms:wide", "rms:split"):
+        outs = {}
+        for nt in ("nt:0", "nt:1"):
+            (y, name) = _with_variants([kind, nt], lambda: qkr.rms_norm(gpu(x), gpu(w), 1e-6))
+            assert name.startswith(f"{kind}:nt{nt[-1]}:"), name
+            gr = gpu(r)
+            (ya, s), _ = _with_variants([kind, nt], lambda: qkr.add_rms_norm(gpu(x), gpu(w), 1e-6, residual=gr))
+            gr8 = gpu(r)
+            (y8, s8), _ = _with_variants([kind, nt], lambda: qkr.add_rms_norm(
+                gpu(x), gpu(w), 1e-6, residual=gr8, out_dtype="fp8_e4m3", scale=scale))
+            outs[nt] = [host(y), host(ya), host(s), _fp8_codes(y8), host(s8)]
+        for a_, b_ in zip(outs["nt:0"], outs["nt:1"]):
+            assert np.array_equal(a_, b_), kind
+
+
 @pytest.mark.parametrize("rows", [1, 7, 300, 4096])
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 @pytest.mark.parametrize("out", ["act", "fp8_e4m3"])
