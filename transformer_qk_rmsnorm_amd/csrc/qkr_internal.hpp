@@ -181,8 +181,8 @@ __host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*
     *wpos = (int32_t)(bw * merge + r2 % merge);
 }
 
-// QK RMSNorm + RoPE kernel for one lanes-per-row value (LPR in 1, 2, 4, 5, 8,
-// 16, 32), chosen by element type, rotation source (0 none, 1 positions, 2
+// QK RMSNorm + RoPE kernel for one lanes-per-row value (LPR in 1, 2, 4, 8, 16,
+// 32), chosen by element type, rotation source (0 none, 1 positions, 2
 // planes, 3 ViT grids), pairing, nontemporal accesses, staged stores and
 // passes per wave.  Each LPR is defined in its own build of qkr_rope_part.hip.
 using NormRopeFn = void (*)(NormRopeArgs);

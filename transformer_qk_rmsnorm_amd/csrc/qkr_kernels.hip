@@ -296,10 +296,10 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
         max_heads = a.t[i].heads > max_heads ? a.t[i].heads : max_heads;
     if (np <= 0) {
         // Two passes per tile where the tensor has two or more passes of
-        // heads.  Measured on MI355X: the joint op (24 heads of 128) runs at
-        // 31.7 us with two and 32.8 us with three; ViT (16 heads of 80) at
-        // 22.5 / 24.1 us (one pass: 30.4 us); 16 + 8 heads of 128 at 7.8-8.0
-        // us either way.
+        // heads.  Measured on MI355X with two / one / three passes: the joint
+        // op (24 heads of 128) 29.7 / 30.0 / 30.3 us, fused ViT (16 + 16
+        // heads of 80) 19.8 / 24.1 / 21.2 us, a 2048-token IMROPE chunk
+        // (16 + 8 heads of 128) 5.94 / 6.61 / 6.15 us.
         const int passes = (max_heads + rpp - 1) / rpp;
         np = passes >= 2 ? 2 : 1;
     }
