@@ -500,6 +500,54 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_graph_capture_of_chunked_imrope_vit_and_setup():
+    """A chunked IMROPE call (token_base), the fused ViT call over 70 grids
+    (three launches) and the ViT setup (two launches) feeding a planes-mode
+    apply, captured in one graph: every replay equals the eager results bit
+    for bit, with eager work between replays."""
+    im = W.imrope(tokens=600, chunk=256, seed_stream=41)
+    pos, inv = gpu(torch.from_numpy(im.positions)), gpu(torch.from_numpy(im.inv_freq))
+    q, k = gpu(im.q), gpu(im.k)
+    wq, wk = gpu(im.q_weight), gpu(im.k_weight)
+    rope = qkr.Rope("imrope", 128, "neox", inv_freq=inv, positions=pos, sections=im.sections, token_base=256)
+    vt = W.vit(grid_thw=[[1, 4, 4]] * 70, heads=4, seed_stream=41)
+    vq, vk, vwq, vwk = gpu(vt.q), gpu(vt.k), gpu(vt.q_weight), gpu(vt.k_weight)
+    vinv = [gpu(torch.from_numpy(a_)) for a_ in (vt.inv_t, vt.inv_h, vt.inv_w)]
+    half = sum(a_.size for a_ in (vt.inv_t, vt.inv_h, vt.inv_w))
+    secs = (vt.inv_t.size, vt.inv_h.size, vt.inv_w.size, 0)
+    n = vq.shape[0]
+
+    def run(o):
+        qkr.qk_norm_rope(q[256:512], k[256:512], wq, wk, im.eps, rope, q_out=o[0], k_out=o[1])
+        qkr.vit_qk_norm_rope(vq, vk, vwq, vwk, 1e-6, *vinv, vt.grid_thw, vt.merge, q_out=o[2], k_out=o[3])
+        qkr.mrope_cos_sin_setup(*vinv, vt.grid_thw, vt.merge, out=(o[4], o[5]))
+        pr = qkr.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=o[4], sin_planes=o[5])
+        qkr.qk_norm_rope(vq, vk, vwq, vwk, 1e-6, pr, q_out=o[6], k_out=o[7])
+
+    def fresh():
+        return [torch.empty_like(q[256:512]), torch.empty_like(k[256:512]), torch.empty_like(vq),
+                torch.empty_like(vk), torch.zeros((3, n, half), device=DEV), torch.zeros((3, n, half), device=DEV),
+                torch.empty_like(vq), torch.empty_like(vk)]
+
+    eager = fresh()
+    run(eager)
+    outs = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(outs)
+    for _ in range(3):
+        for i, t in enumerate(outs):
+            t.fill_(0.0 if i in (4, 5) else float("nan"))   # setup planes keep unwritten columns
+        graph.replay()
+        torch.cuda.synchronize()
+        for a_, b_ in zip(outs, eager):
+            assert torch.equal(a_, b_)
+        whole = qkr.Rope("imrope", 128, "neox", inv_freq=inv, positions=pos, sections=im.sections)
+        qkr.qk_norm_rope(q, k, wq, wk, im.eps, whole)         # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------------------
 # ViT setup folded into the rotation (positions from the grids in the kernel)
 # ---------------------------------------------------------------------------
