@@ -493,11 +493,17 @@ KERNEL_SOURCES = ["transformer_qk_rmsnorm_amd/csrc/" + f for f in
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code with comments removed: the counters
+    depend on the code, so a comment edit keeps them valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(text.encode("utf-8"))
     return h.hexdigest()
 
 

@@ -355,7 +355,7 @@ hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, int mode,
         // Measured on MI355X, rows of 5120 bf16 (wide / one wave per row /
         // split): 1 row 2.16 / 3.27 / 2.23 us, 32 rows 2.82 / 4.50 / 3.31,
         // 128 rows 3.04 / 4.78 / 4.30, 1024 rows 4.95 / 5.97, 2048 rows 7.95
-        // / 8.18, 4096 rows 16.7 / 15.0.  The split variant never wins; it
+        // / 8.18, 4096 rows 15.6 / 13.8.  The split variant never wins; it
         // stays reachable through the variant override.
         kind = a.rows < 2048 && a.nvec >= 64 ? 2 : 0;
     }
