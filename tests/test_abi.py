@@ -458,3 +458,22 @@ def test_grid_products_that_leave_64_bits_are_refused():
     assert L.qkr_vit_qk_norm_rope(4096, 80, qkr.BF16, 1e-6, ctypes.byref(v), ctypes.byref(v), 16, FAKE,
                                   ctypes.byref(v), ctypes.byref(v), 16, FAKE, 0, FAKE, (1 << 31) - 1, FAKE,
                                   (1 << 31) - 1, FAKE, 8, g, 1, 2, None) == INVALID
+
+
+def test_missing_library_fails_loudly():
+    """With no built library the binding raises at once (no fallback path):
+    loading it and calling an entry point both raise QkrError."""
+    import subprocess
+    import sys
+    code = ("import transformer_qk_rmsnorm_amd as qkr\n"
+            "qkr.LIB_PATH = '/nonexistent/libqkrope.so'\n"
+            "for f in (qkr.lib, lambda: qkr.status_of(0)):\n"
+            "    try:\n"
+            "        f()\n"
+            "    except qkr.QkrError as e:\n"
+            "        assert 'is not built' in str(e), e\n"
+            "    else:\n"
+            "        raise SystemExit('no error')\n"
+            "print('raised')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "raised" in r.stdout, r.stdout + r.stderr
