@@ -477,3 +477,15 @@ def test_missing_library_fails_loudly():
             "print('raised')\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "raised" in r.stdout, r.stdout + r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and a
+    JSON message, before touching a GPU."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2, r.stdout + r.stderr
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
