@@ -549,7 +549,7 @@ def cpu_baseline(w, seconds):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: every row of the path is per-row "
+        print(json.dumps({"error": "the benchmark runs on one GPU only: every row of the path is per-row "
                                    "independent and shards without communication; run with --gpus 1"}))
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
