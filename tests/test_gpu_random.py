@@ -19,7 +19,7 @@ from parity import assert_bf16_close, assert_f32_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = 480
 DEV = "cuda"
 HEAD_DIMS = (8, 16, 24, 32, 40, 48, 64, 72, 80, 96, 120, 128, 136, 160, 192, 200, 256)
 

@@ -56,7 +56,7 @@ def draw_rows(i):
     return c
 
 
-@pytest.mark.parametrize("i", range(64))
+@pytest.mark.parametrize("i", range(160))
 def test_random_rows(i):
     c = draw_rows(i)
     print(f"rows case {i}: {c}", flush=True)
@@ -121,7 +121,7 @@ def draw_joint(i):
     return c
 
 
-@pytest.mark.parametrize("i", range(32))
+@pytest.mark.parametrize("i", range(96))
 def test_random_joint(i):
     c = draw_joint(i)
     print(f"joint case {i}: {c}", flush=True)
@@ -170,7 +170,7 @@ def draw_cache(i):
     return c
 
 
-@pytest.mark.parametrize("i", range(32))
+@pytest.mark.parametrize("i", range(96))
 def test_random_cache(i):
     c = draw_cache(i)
     print(f"cache case {i}: {c}", flush=True)
@@ -246,7 +246,7 @@ def draw_vit(i):
     return c
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(64))
 def test_random_vit(i):
     c = draw_vit(i)
     print(f"vit case {i}: {c}", flush=True)
