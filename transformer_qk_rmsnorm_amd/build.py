@@ -50,6 +50,26 @@ def _scratch_users(lines):
     return users
 
 
+# The largest LDS a kernel is meant to use per workgroup: the QK kernel's
+# staging slice (4 waves x 128 vectors x 16 bytes).  More means the compiler
+# has moved a private array into LDS (indexed by the work-item id, which also
+# costs a read of the dispatch packet in every wave).
+LDS_LIMIT = 8192
+
+
+def _lds_overruns(lines):
+    """Kernels whose resource remark reports more LDS than LDS_LIMIT."""
+    over, name = [], None
+    for ln in lines:
+        if "Function Name:" in ln:
+            name = ln.split("Function Name:")[1].split()[0]
+        elif "LDS Size [bytes/block]:" in ln:
+            size = int(ln.split("LDS Size [bytes/block]:")[1].split()[0])
+            if size > LDS_LIMIT and name:
+                over.append((name, size))
+    return over
+
+
 def _compile(unit, verbose: bool) -> str:
     src, extra, name = unit
     obj = os.path.join(BUILD_DIR, name + ".o")
@@ -65,6 +85,9 @@ def _compile(unit, verbose: bool) -> str:
     users = _scratch_users(lines)
     if users:
         raise RuntimeError(f"{name}: kernels using scratch memory: {users[:5]}")
+    over = _lds_overruns(lines)
+    if over:
+        raise RuntimeError(f"{name}: kernels using more than {LDS_LIMIT} bytes of LDS: {over[:5]}")
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
     return obj
