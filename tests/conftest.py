@@ -34,4 +34,6 @@ def _announce_gpu_case(request):
     if "gpu" in request.keywords:
         sys.__stderr__.write(f"[gpu case] {request.node.nodeid}\n")
         sys.__stderr__.flush()
+    import parity
+    parity.CURRENT_TEST = request.node.nodeid
     yield

@@ -16,13 +16,34 @@ rounding order against a double reference), so a code may differ by one step
 where the quotient sits at a rounding boundary, and nowhere else: every code
 equal or adjacent in sign-magnitude order (+0 and -0 equal), and at least
 99.9% of them equal.
+bf16 outputs must also agree bit for bit almost everywhere: the pages fix
+the rounding points (the bf16-rounded normalised value with the weight
+included, an fp32 rotation, one final rounding), so a correct kernel differs
+from the oracle only where its fp32 arithmetic (reciprocal square root, sum
+order, sincos) lands on the other side of a bf16 rounding boundary, about 4
+in 100 000 elements for an fp32 emulation of the contract.  At most 0.1% of
+the elements (plus 4, for small arrays) may differ in their bits.  A kernel
+that skips the contract rounding agrees on about 69% of the elements, one
+that rounds x * rrms before the weight on about 73%: both fail.
 Exact: integer maps, copied rows, the residual stream and the bitwise
 invariants.
+
+With QKR_PARITY_REPORT set to a file name, every bf16 comparison appends
+one JSON line with its statistics (maximum pair-relative and raw relative
+error, bit-equal fraction, ulp histogram, NMSE) to that file.
 """
+import json
+import os
+
 import numpy as np
 
 F32_ATOL = 1e-5
 BF16_RTOL = 1.6e-2
+BF16_EQUAL_FLOOR = 0.999
+BF16_EQUAL_SLACK = 4
+
+# Name of the running test, set by tests/conftest.py (report lines carry it).
+CURRENT_TEST = ""
 
 
 def pair_index(d, rotary_dim, pairing):
@@ -52,11 +73,63 @@ def bf16_errors(got, ref, rotary_dim=0, pairing="neox"):
     return err
 
 
-def assert_bf16_close(got, ref, rotary_dim=0, pairing="neox", what=""):
+def _bf16_bits(a):
+    """bf16 bit patterns (as int32) of float32 values that lie on the bf16 grid."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    if (u & 0xFFFF).any():
+        raise ValueError("values are not bf16")
+    return (u >> 16).astype(np.int32)
+
+
+def _bf16_ordinal(bits):
+    """Position of each bf16 value on the number line (+0 and -0 both 0)."""
+    mag = bits & 0x7FFF
+    return np.where(bits & 0x8000, -mag, mag)
+
+
+def bf16_stats(got, ref, rotary_dim=0, pairing="neox"):
+    """Agreement of two bf16 arrays (as float32 values on the bf16 grid)."""
+    got = np.asarray(got, np.float32)
+    ref = np.asarray(ref, np.float32)
+    n = int(ref.size)
+    if n == 0:
+        return {"n": 0, "max_pair_rel": 0.0, "max_raw_rel": 0.0, "bit_equal": 1.0, "unequal": 0,
+                "ulp_hist": {"0": 0, "1": 0, "2": 0, ">2": 0}, "nmse": 0.0}
     err = bf16_errors(got, ref, rotary_dim, pairing)
-    worst = float(err.max()) if err.size else 0.0
-    equal = float(np.mean(np.asarray(got) == np.asarray(ref))) if err.size else 1.0
-    assert worst <= BF16_RTOL, f"{what}: max pair-relative error {worst:.3g} > {BF16_RTOL} (bit-equal {equal:.4f})"
+    gb, rb = _bf16_bits(got), _bf16_bits(ref)
+    ulp = np.abs(_bf16_ordinal(gb) - _bf16_ordinal(rb))
+    g64, r64 = got.astype(np.float64), ref.astype(np.float64)
+    nz = r64 != 0
+    raw = np.abs(g64[nz] - r64[nz]) / np.abs(r64[nz])
+    den = float(np.sum(r64 * r64))
+    unequal = int(np.count_nonzero(gb != rb))
+    return {
+        "n": n,
+        "max_pair_rel": float(err.max()),
+        "max_raw_rel": float(raw.max()) if raw.size else 0.0,
+        "bit_equal": 1.0 - unequal / n,
+        "unequal": unequal,
+        "ulp_hist": {"0": int(np.count_nonzero(ulp == 0)), "1": int(np.count_nonzero(ulp == 1)),
+                     "2": int(np.count_nonzero(ulp == 2)), ">2": int(np.count_nonzero(ulp > 2))},
+        "nmse": float(np.sum((g64 - r64) ** 2) / den) if den > 0 else 0.0,
+    }
+
+
+def _report(what, stats):
+    path = os.environ.get("QKR_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": CURRENT_TEST, "what": what, **stats}) + "\n")
+
+
+def assert_bf16_close(got, ref, rotary_dim=0, pairing="neox", what="", floor=BF16_EQUAL_FLOOR):
+    st = bf16_stats(got, ref, rotary_dim, pairing)
+    _report(what, st)
+    worst, equal = st["max_pair_rel"], st["bit_equal"]
+    assert worst <= BF16_RTOL, f"{what}: max pair-relative error {worst:.3g} > {BF16_RTOL} (bit-equal {equal:.5f})"
+    allowed = int((1.0 - floor) * st["n"]) + BF16_EQUAL_SLACK
+    assert st["unequal"] <= allowed, (f"{what}: {st['unequal']} of {st['n']} bf16 elements differ in their bits "
+                                      f"(bit-equal {equal:.5f}, at most {allowed} may differ)")
     return worst, equal
 
 
