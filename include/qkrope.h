@@ -253,17 +253,26 @@ const char* qkr_last_error(void);
 /* ---- Introspection and test hooks (not for the hot path) ---------------- */
 
 /* Force a kernel variant by name for subsequent calls on any thread, or NULL
- * for the automatic choice.  Names: "rms:rows", "rms:split", "rms:wide",
- * "rope:np1", "rope:np2", "rope:np3", "rope:np4" (passes of rows per wavefront),
- * "rope:lpr4", "rope:lpr8", "rope:lpr16", "rope:lpr32" (lanes per
- * row; ignored where the row needs more lanes), "rope:stage0" / "rope:stage1"
- * (QK stores straight from registers / through LDS in contiguous runs),
- * "nt:0" / "nt:1" (plain / nontemporal row accesses).  Overrides accumulate until NULL
- * resets all of them.  Unknown names are refused. */
+ * for the automatic choice ([Vulkan] PR description: an override forces a
+ * module so that every arm runs on every machine).  Names: "rms:rows",
+ * "rms:split", "rms:wide", "rope:np1", "rope:np2", "rope:np3", "rope:np4"
+ * (passes of rows per wavefront), "rope:lpr4", "rope:lpr8", "rope:lpr16",
+ * "rope:lpr32" (lanes per row), "rope:stage0" / "rope:stage1" (QK stores
+ * straight from registers / through LDS in contiguous runs), "nt:0" / "nt:1"
+ * (plain / nontemporal row accesses).  Overrides accumulate until NULL
+ * resets all of them.  Unknown names are refused.  A forced variant is
+ * never swapped for another: a call it cannot run (a row longer than one
+ * wavefront holds under "rms:rows" or "rms:split", the residual add under
+ * "rms:split", too few lanes per row for the head_dim, staged stores outside
+ * 2 to 8 lanes per row) returns QKR_ERR_UNSUPPORTED before any HIP call. */
 qkr_status qkr_set_variant_override(const char* name);
 
 /* Name of the kernel variant the last successful launch on the calling
- * thread used ("" if none). */
+ * thread used ("" if none) ([Vulkan] PR description: the test pins the
+ * module by name through the dispatch record). */
+const char* qkr_debug_last_variant(void);
+
+/* The same text as qkr_debug_last_variant (earlier name, kept). */
 const char* qkr_last_variant(void);
 
 /* The position axis (0 t, 1 h, 2 w, 3 e) of each of n_pairs (<= 128) pairs

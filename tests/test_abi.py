@@ -248,11 +248,36 @@ def test_mrope_setup_refusals():
 
 
 def test_variant_override_names():
-    for name in ("rms:rows", "rms:split", "rms:wide", "rope:np1", "rope:np2", "rope:np3", "rope:np4"):
+    for name in ("rms:rows", "rms:split", "rms:wide", "rope:np1", "rope:np2", "rope:np3", "rope:np4",
+                 "rope:lpr4", "rope:lpr8", "rope:lpr16", "rope:lpr32", "rope:stage0", "rope:stage1", "nt:0",
+                 "nt:1"):
         qkr.set_variant_override(name)
     qkr.set_variant_override(None)
     with pytest.raises(qkr.QkrError):
         qkr.set_variant_override("rms:fastest")
+
+
+@pytest.mark.parametrize("variant,call", [
+    ("rms:split", lambda: addrms()),                                    # the split rows cannot take the add
+    ("rms:rows", lambda: rms(width=16384, xs=16384, ys=16384)),         # 2048 vectors: more than one wave holds
+    ("rms:split", lambda: rms(width=16384, xs=16384, ys=16384)),
+    ("rope:lpr4", lambda: qknr()),                                      # 16 vectors need 8 lanes per row
+    ("rope:stage1", lambda: qknr(head_dim=256, q=view(st=16 * 256, sh=256), qo=view(st=16 * 256, sh=256),
+                                 k=view(st=8 * 256, sh=256), ko=view(st=8 * 256, sh=256),
+                                 rope=rope_c(rotary_dim=256, sections=(48, 40, 40, 0)))),   # 16 lanes per row
+])
+def test_forced_variant_that_cannot_run_is_refused_before_any_launch(variant, call):
+    """A forced variant is never swapped for another: the call returns
+    QKR_ERR_UNSUPPORTED from the host planner (stand-in pointers, no GPU)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("stand-in pointers: run where no GPU is visible")
+    qkr.set_variant_override(variant)
+    try:
+        assert call() == UNSUPPORTED, qkr.last_error()
+        assert "forced variant" in qkr.last_error()
+    finally:
+        qkr.set_variant_override(None)
 
 
 def test_binding_refuses_host_tensors():

@@ -217,10 +217,18 @@ def test_rms_norm_widths(dtype, width):
     if dtype == "f32" and width > 16384:
         pytest.skip("fp32 rows are limited to 16384 elements (65536 bytes, the bf16 maximum of 32768)")
     case = W.rows(7, width=width, dtype=dtype, seed_stream=width)
+    nvec = width // (8 if dtype == "bf16" else 4)
     for variant in (None, "rms:rows", "rms:split", "rms:wide"):
         qkr.set_variant_override(variant)
         try:
+            if variant in ("rms:rows", "rms:split") and nvec > 1024:
+                # one wavefront holds at most 1024 vectors: refused, not swapped
+                with pytest.raises(qkr.QkrError, match="forced variant"):
+                    qkr.rms_norm(gpu(case.x), gpu(case.weight), case.eps)
+                continue
             y = qkr.rms_norm(gpu(case.x), gpu(case.weight), case.eps)
+            if variant is not None:
+                assert qkr.last_variant().startswith(variant + ":"), qkr.last_variant()
         finally:
             qkr.set_variant_override(None)
         ref = oracle.rms_norm(W.as_f32(case.x), W.as_f32(case.weight), case.eps, dtype)
@@ -471,6 +479,64 @@ def test_maximum_row_count():
     orope = oracle.Rope("1d", d, "neox", inv_freq=inv, positions=ps)
     ref = oracle.qk_norm_rope(qs, host(w), W.EPS, orope, "f32")
     assert_f32_close(got, ref, "maximum row count")
+
+
+def _sampled_rows(n, boundary, rng):
+    """Row indices to check: both ends, both sides of a launch boundary and a
+    random sample."""
+    edge = [0, 1, boundary - 2, boundary - 1, boundary, boundary + 1, n - 2, n - 1]
+    return np.unique(np.concatenate([edge, rng.integers(0, n, 2048)]))
+
+
+@pytest.mark.parametrize("variant", [None, "rms:wide"])
+def test_rms_norm_rows_past_one_dispatch(variant):
+    """2^26 rows of 8 bf16: one wavefront per row needs 2^32 work-items and
+    one workgroup per row 2^34, more than one dispatch counts, so the call
+    takes several launches, each told its first row; sampled rows on both
+    sides of each launch boundary match the oracle."""
+    rows, width = 1 << 26, 8
+    g = torch.Generator(device=DEV).manual_seed(W.SEED)
+    x = torch.randn((rows, width), device=DEV, generator=g).to(torch.bfloat16)
+    w = (torch.rand(width, device=DEV, generator=g) + 0.5).to(torch.bfloat16)
+    qkr.set_variant_override(variant)
+    try:
+        y = qkr.rms_norm(x, w, W.EPS)
+        name = qkr.last_variant()
+    finally:
+        qkr.set_variant_override(None)
+    assert name.startswith("rms:rows" if variant is None else variant), name
+    per_launch = (1 << 23) * (4 if variant is None else 1)     # rows of one launch
+    idx = _sampled_rows(rows, per_launch, np.random.default_rng(1))
+    for b in range(per_launch, rows, per_launch):
+        idx = np.union1d(idx, [b - 1, b])
+    ti = torch.from_numpy(idx).to(DEV)
+    got, xs = host(y[ti]), host(x[ti])
+    del x, y
+    torch.cuda.empty_cache()
+    ref = oracle.rms_norm(xs, host(w), W.EPS, "bf16")
+    assert_bf16_close(got, ref, what=f"rows past one dispatch {name}")
+
+
+def test_qk_norm_rope_tiles_past_one_dispatch():
+    """2^26 tokens of one fp32 head of 8: 2^26 tiles of one wavefront, 2^32
+    work-items, two launches; sampled tokens on both sides of the boundary
+    match the oracle."""
+    tokens, d = 1 << 26, 8
+    g = torch.Generator(device=DEV).manual_seed(W.SEED + 1)
+    q = torch.randn((tokens, 1, d), device=DEV, generator=g)
+    w = torch.rand(d, device=DEV, generator=g) + 0.5
+    pos = torch.randint(0, 8192, (1, tokens), dtype=torch.int32, device=DEV, generator=g)
+    inv = W.inv_freq_ladder(1e4, d)
+    rope = qkr.Rope("1d", d, "neox", inv_freq=gpu(torch.from_numpy(inv)), positions=pos)
+    qo, _ = qkr.qk_norm_rope(q, None, w, None, W.EPS, rope)
+    assert ":lpr1:" in qkr.last_variant(), qkr.last_variant()
+    idx = _sampled_rows(tokens, (1 << 23) * 4, np.random.default_rng(2))
+    ti = torch.from_numpy(idx).to(DEV)
+    got, qs, ps = host(qo[ti]), host(q[ti]), pos[:, ti].cpu().numpy()
+    del q, qo
+    torch.cuda.empty_cache()
+    ref = oracle.qk_norm_rope(qs, host(w), W.EPS, oracle.Rope("1d", d, "neox", inv_freq=inv, positions=ps), "f32")
+    assert_f32_close(got, ref, "tiles past one dispatch")
 
 
 def test_graph_capture_replays_match_eager():
@@ -760,12 +826,21 @@ def test_row_kernels_cache_policy_agrees_bitwise(act):
         for nt in ("nt:0", "nt:1"):
             (y, name) = _with_variants([kind, nt], lambda: qkr.rms_norm(gpu(x), gpu(w), 1e-6))
             assert name.startswith(f"{kind}:nt{nt[-1]}:"), name
+            (y8n, name), _ = _with_variants([kind, nt], lambda: (qkr.add_rms_norm(
+                gpu(x), gpu(w), 1e-6, out_dtype="fp8_e4m3", scale=scale)[0], qkr.last_variant()))
+            assert name.startswith(f"{kind}:nt{nt[-1]}:") and name.endswith(":fp8"), name
+            outs[nt] = [host(y), _fp8_codes(y8n)]
+            if kind == "rms:split":      # the split rows cannot take the residual add
+                continue
             gr = gpu(r)
-            (ya, s), _ = _with_variants([kind, nt], lambda: qkr.add_rms_norm(gpu(x), gpu(w), 1e-6, residual=gr))
+            (ya, s, name), _ = _with_variants([kind, nt], lambda: qkr.add_rms_norm(
+                gpu(x), gpu(w), 1e-6, residual=gr) + (qkr.last_variant(),))
+            assert name.startswith(f"{kind}:nt{nt[-1]}:") and name.endswith(":add"), name
             gr8 = gpu(r)
-            (y8, s8), _ = _with_variants([kind, nt], lambda: qkr.add_rms_norm(
-                gpu(x), gpu(w), 1e-6, residual=gr8, out_dtype="fp8_e4m3", scale=scale))
-            outs[nt] = [host(y), host(ya), host(s), _fp8_codes(y8), host(s8)]
+            (y8, s8, name), _ = _with_variants([kind, nt], lambda: qkr.add_rms_norm(
+                gpu(x), gpu(w), 1e-6, residual=gr8, out_dtype="fp8_e4m3", scale=scale) + (qkr.last_variant(),))
+            assert name.startswith(f"{kind}:nt{nt[-1]}:") and name.endswith(":add:fp8"), name
+            outs[nt] += [host(ya), host(s), _fp8_codes(y8), host(s8)]
         for a_, b_ in zip(outs["nt:0"], outs["nt:1"]):
             assert np.array_equal(a_, b_), kind
 
@@ -794,17 +869,24 @@ def test_add_rms_norm(rows, act, out):
 
 @pytest.mark.parametrize("variant", ["rms:rows", "rms:wide", "rms:split"])
 def test_add_rms_norm_variants_and_in_place_on_x(variant):
-    """Every row variant (the split one is replaced by the workgroup-wide one
-    for the add), with the residual output written over x."""
+    """Every row variant that takes the residual add, with the residual
+    output written over x; the split rows refuse the add (never swapped for
+    another variant) and leave x untouched."""
     x, r, w = _addrms_case(9, 2048, "bf16", 5)
     gx = gpu(x)
     qkr.set_variant_override(variant)
     try:
+        if variant == "rms:split":
+            with pytest.raises(qkr.QkrError, match="forced variant"):
+                qkr.add_rms_norm(gx, gpu(w), 1e-6, residual=gpu(r), residual_out=gx)
+            torch.cuda.synchronize()
+            assert torch.equal(gx.cpu(), x)
+            return
         y, s = qkr.add_rms_norm(gx, gpu(w), 1e-6, residual=gpu(r), residual_out=gx)
         name = qkr.last_variant()
     finally:
         qkr.set_variant_override(None)
-    assert name.startswith("rms:wide" if variant == "rms:split" else variant), name
+    assert name.startswith(variant), name
     rs, ry = oracle.add_rms_norm(W.as_f32(x), W.as_f32(w), 1e-6, W.as_f32(r), "bf16", "bf16")
     assert np.array_equal(host(s), rs) and s.data_ptr() == gx.data_ptr()
     assert_bf16_close(host(y), ry, what=name)

@@ -70,19 +70,33 @@ def test_random_rows(i):
     scale = torch.tensor([c["scale"]], dtype=torch.float32, device=DEV)
     x_in, r_in = W.as_f32(xb[:, :width]), W.as_f32(rb[:, :width])
 
-    qkr.set_variant_override(c["variant"])
-    try:
+    nvec = width // (8 if dtype == "bf16" else 4)
+    variant = c["variant"]
+    # A forced variant that cannot run the call is refused, never swapped:
+    # one wavefront holds at most 1024 vectors, and the split rows cannot
+    # take the residual add.
+    runs = variant in (None, "rms:wide") or (nvec <= 1024 and not (variant == "rms:split" and c["add"]))
+
+    def call():
         if not c["add"] and not c["fp8"]:
-            y = qkr.rms_norm(x, w.to(DEV), W.EPS)
-            s = None
-        else:
-            res_out = None
-            if c["res_out"] == "x":
-                res_out = x
-            elif c["res_out"] == "separate":
-                res_out = torch.empty((rows, width), dtype=x.dtype, device=DEV)
-            y, s = qkr.add_rms_norm(x, w.to(DEV), W.EPS, residual=r if c["add"] else None, residual_out=res_out,
-                                    out_dtype="fp8_e4m3" if c["fp8"] else None, scale=scale)
+            return qkr.rms_norm(x, w.to(DEV), W.EPS), None
+        res_out = None
+        if c["res_out"] == "x":
+            res_out = x
+        elif c["res_out"] == "separate":
+            res_out = torch.empty((rows, width), dtype=x.dtype, device=DEV)
+        return qkr.add_rms_norm(x, w.to(DEV), W.EPS, residual=r if c["add"] else None, residual_out=res_out,
+                                out_dtype="fp8_e4m3" if c["fp8"] else None, scale=scale)
+
+    qkr.set_variant_override(variant)
+    try:
+        if not runs:
+            with pytest.raises(qkr.QkrError, match="forced variant"):
+                call()
+            qkr.set_variant_override(None)
+        y, s = call()
+        if runs and variant is not None:
+            assert qkr.last_variant().startswith(variant + ":"), qkr.last_variant()
         torch.cuda.synchronize()
     finally:
         qkr.set_variant_override(None)

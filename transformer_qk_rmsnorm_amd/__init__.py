@@ -91,6 +91,7 @@ _SIGNATURES = {
     "qkr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qkr_last_error": (ctypes.c_char_p, []),
     "qkr_set_variant_override": (ctypes.c_int, [ctypes.c_char_p]),
+    "qkr_debug_last_variant": (ctypes.c_char_p, []),
     "qkr_last_variant": (ctypes.c_char_p, []),
     "qkr_debug_axis_map": (ctypes.c_int, [_P(_Rope), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "qkr_debug_vit_positions": (ctypes.c_int, [_P(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32,
@@ -131,7 +132,7 @@ def last_error() -> str:
 
 
 def last_variant() -> str:
-    return lib().qkr_last_variant().decode()
+    return lib().qkr_debug_last_variant().decode()
 
 
 def set_variant_override(name: Optional[str]):

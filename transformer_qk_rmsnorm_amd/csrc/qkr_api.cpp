@@ -281,16 +281,47 @@ void fill_out(TensorArgs& t, const qkr_view* v, int esize)
     t.out_sh = v ? v->stride_head * esize : 0;
 }
 
-qkr_status launch(NormRopeArgs& a, int32_t dtype, int32_t pairing, hipStream_t stream)
+// The kernel variant of a QK call (pure host code): a forced variant that
+// cannot run the call is refused, never replaced.
+qkr_status plan_rope(const NormRopeArgs& a, int32_t dtype, RopePlan& plan)
+{
+    int32_t max_heads = 0;
+    for (int i = 0; i < 3; ++i)
+        max_heads = a.t[i].heads > max_heads ? a.t[i].heads : max_heads;
+    const char* why = plan_norm_rope(dtype, a.head_dim, max_heads, g_rope_np.load(), g_rope_lpr.load(),
+                                     g_rope_stage.load(), g_nt.load(), &plan);
+    if (why != nullptr)
+        return fail(QKR_ERR_UNSUPPORTED, "forced variant: %s", why);
+    return QKR_OK;
+}
+
+qkr_status launch_planned(NormRopeArgs& a, int32_t dtype, int32_t pairing, const RopePlan& plan, hipStream_t stream)
 {
     (void)hipGetLastError();   // clear a stale error so the launch reports its own
     const char* variant = "";
-    hipError_t e = launch_norm_rope(a, dtype, pairing, g_rope_np.load(), g_rope_lpr.load(), g_rope_stage.load(), g_nt.load(),
-                                    stream, &variant);
+    hipError_t e = launch_norm_rope(a, dtype, pairing, plan, stream, &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "norm_rope launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
     return ok();
+}
+
+qkr_status launch(NormRopeArgs& a, int32_t dtype, int32_t pairing, hipStream_t stream)
+{
+    RopePlan plan;
+    qkr_status st;
+    if ((st = plan_rope(a, dtype, plan)))
+        return st;
+    return launch_planned(a, dtype, pairing, plan, stream);
+}
+
+// The row kernel variant (pure host code), as plan_rope.
+qkr_status plan_rows(int64_t nvec, int64_t rows, int mode, RmsPlan& plan)
+{
+    const char* why = plan_rms_norm((int32_t)nvec, rows, g_rms_kind.load(), g_nt.load(), mode, &plan);
+    if (why != nullptr)
+        return fail(QKR_ERR_UNSUPPORTED, "forced variant: %s", why);
+    return QKR_OK;
 }
 
 // Mode and sections of the axis-map entries, which take sections on their
@@ -381,6 +412,8 @@ const char* qkr_status_string(qkr_status status)
 
 const char* qkr_last_error(void) { return g_error; }
 
+const char* qkr_debug_last_variant(void) { return g_variant; }
+
 const char* qkr_last_variant(void) { return g_variant; }
 
 qkr_status qkr_set_variant_override(const char* name)
@@ -470,10 +503,12 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
     a.nvec = (int32_t)nvec;
     a.eps = eps;
     a.inv_width = 1.0f / (float)width;
+    RmsPlan plan;
+    if ((st = plan_rows(nvec, rows, 0, plan)))
+        return st;
     (void)hipGetLastError();
     const char* variant = "";
-    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), g_nt.load(), 0,
-                                   reinterpret_cast<hipStream_t>(stream), &variant);
+    hipError_t e = launch_rms_norm(a, dtype, plan, reinterpret_cast<hipStream_t>(stream), &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "rms_norm launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
@@ -590,11 +625,13 @@ qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void*
     a.nvec = (int32_t)nvec;
     a.eps = eps;
     a.inv_width = 1.0f / (float)width;
+    const int mode = (add ? 1 : 0) | (fp8 ? 2 : 0);
+    RmsPlan plan;
+    if ((st = plan_rows(nvec, rows, mode, plan)))
+        return st;
     (void)hipGetLastError();
     const char* variant = "";
-    const int mode = (add ? 1 : 0) | (fp8 ? 2 : 0);
-    hipError_t e = launch_rms_norm(a, dtype, g_rms_kind.load(), g_nt.load(), mode,
-                                   reinterpret_cast<hipStream_t>(stream), &variant);
+    hipError_t e = launch_rms_norm(a, dtype, plan, reinterpret_cast<hipStream_t>(stream), &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "add_rms_norm launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
@@ -939,9 +976,11 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
     base.vit.div_m = make_fastdiv((uint32_t)spatial_merge);
     base.vit.div_mm = make_fastdiv((uint32_t)(spatial_merge * spatial_merge));
 
+    RopePlan plan;
+    if ((st = plan_rope(base, dtype, plan)))
+        return st;
     // One launch per group of grids; views start at the group's first token,
     // positions use absolute token indices (token_base).
-    (void)hipGetLastError();
     int64_t start = 0;
     for (int32_t g0 = 0; g0 < num_grids; g0 += kMaxFusedGrids) {
         const int32_t n = num_grids - g0 < kMaxFusedGrids ? num_grids - g0 : kMaxFusedGrids;
@@ -973,7 +1012,7 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
         a.tokens = (int32_t)count;
         a.tokens0 = (int32_t)count;
         a.rope.token_base = start;
-        if ((st = launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream))))
+        if ((st = launch_planned(a, dtype, pairing, plan, reinterpret_cast<hipStream_t>(stream))))
             return st;
         start = cu;
     }

@@ -12,6 +12,10 @@ namespace qkr {
 constexpr int kMaxGrids = 64;     // ViT grids per setup launch (metadata rides in kernel arguments)
 constexpr int kMaxFusedGrids = 32; // ViT grids per fused norm + rotation launch
 constexpr int kThreads = 256;     // threads per workgroup of the row kernels (4 waves)
+// Workgroups per launch.  A dispatch counts its work-items in 32 bits; calls
+// that need more workgroups take several launches, each told its first tile
+// or row.
+constexpr int64_t kMaxBlocksPerLaunch = (int64_t)1 << 23;
 
 enum PosMode : int32_t { kPos1D = 0, kPosAxes = 1, kPosImrope = 2, kPosPlanes = 3, kPosNone = 4, kPosVit = 5 };
 enum Pairing : int32_t { kNeox = 0, kAdjacent = 1 };
@@ -72,6 +76,7 @@ struct NormRopeArgs {
     int32_t head_dim;
     int32_t rotary_dim;
     uint32_t ntiles;            // batch * tokens * tiles per token (< 2^31), set by the launcher
+    uint32_t tile_base;         // first tile of this launch (set by the launcher)
     int32_t tile_first[3];      // first tile of tensors 0, 1, 2 within a token (set by the launcher)
     FastDiv div_tpt;            // tiles per token
     FastDiv div_tokens;         // tokens per batch
@@ -94,6 +99,7 @@ struct RmsArgs {
     int64_t r_stride;           // bytes
     int64_t s_stride;           // bytes
     int64_t rows;
+    int64_t item_base;          // first row (split: first row slice) of this launch, set by the launcher
     int32_t nvec;               // 16-byte vectors per row
     int32_t splits;             // workgroups per row (split variant)
     int32_t split_len;          // vectors stored by one split
@@ -189,18 +195,35 @@ using NormRopeFn = void (*)(NormRopeArgs);
 template <int LPR>
 NormRopeFn pick_norm_rope(int32_t dtype, int rope, int32_t pairing, bool nt, bool stage, int np);
 
+// Kernel variant of a QK norm + rotation call.
+struct RopePlan {
+    int lpr;     // lanes per row
+    int np;      // passes (row groups) per wave
+    bool stage;  // stores through LDS in contiguous runs
+    bool nt;     // nontemporal row accesses
+};
+
+// Kernel variant of a row norm call.
+struct RmsPlan {
+    int kind;    // 0 rows, 1 split, 2 wide
+    int vpl;     // 16-byte vectors per lane
+    bool nt;
+    int mode;    // bit 0 residual add, bit 1 FP8 E4M3 output
+};
+
+// Variant choice, pure host code.  Requests: np / lpr 0 = automatic, stage
+// -1 = automatic, kind -1 = automatic; nt 1 nontemporal, 0 plain.  Returns
+// nullptr, or (static text) why a forced choice cannot run the call: a
+// forced variant is never replaced by another.
+const char* plan_norm_rope(int32_t dtype, int32_t head_dim, int32_t max_heads, int np_req, int lpr_req,
+                           int stage_req, int nt_req, RopePlan* plan);
+const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, int mode, RmsPlan* plan);
+
 // Kernel launchers (qkr_kernels.hip).  Each returns the variant name it
 // launched through *variant; launch errors surface through hipGetLastError.
-// norm_rope: np = passes (row groups) per wave and lpr = lanes per row, 0 =
-// automatic (an lpr too small for the row is ignored); stage = 1 stores
-// through LDS in contiguous runs, 0 directly, -1 automatic; nt = 1
-// nontemporal row accesses, 0 plain.
-hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, int np, int lpr, int stage,
-                            int nt, hipStream_t stream, const char** variant);
-// rms: kind 0 rows, 1 split, 2 wide; -1 = automatic.  mode: bit 0 residual
-// add, bit 1 FP8 E4M3 output (add modes never take the split variant: its
-// workgroups read the whole row while others write the residual).
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, int mode, hipStream_t stream,
+hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, const RopePlan& plan,
+                            hipStream_t stream, const char** variant);
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, const RmsPlan& plan, hipStream_t stream,
                            const char** variant);
 hipError_t launch_debug_fp8(const float* x, int64_t n, const float* scale, uint8_t* out, hipStream_t stream);
 hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream);

@@ -45,18 +45,18 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
     int split = 0;
     int first, step;   // vector index of the lane's slot 0, distance between slots
     if constexpr (KIND == 0) {
-        row = blockIdx.x * kWaves + wave;
+        row = a.item_base + blockIdx.x * kWaves + wave;
         first = lane;
         step = 64;
     } else if constexpr (KIND == 1) {
-        const uint32_t item = blockIdx.x * kWaves + wave;
+        const uint32_t item = (uint32_t)a.item_base + blockIdx.x * kWaves + wave;
         const uint32_t r = fast_div(item, a.div_splits);
         row = r;
         split = (int)(item - r * a.div_splits.d);
         first = lane;
         step = 64;
     } else {
-        row = blockIdx.x;
+        row = a.item_base + blockIdx.x;
         first = threadIdx.x;
         step = kThreads;
     }
@@ -248,20 +248,27 @@ RmsFn pick_vpl(int vpl)
     }
 }
 
-// The plain norm comes with and without nontemporal accesses; the add and
-// FP8 modes are nontemporal only, and the add modes skip the split variant.
-template <class E, int KIND>
-RmsFn pick_rms_mode(bool nt, int mode, int vpl)
+// Every mode comes with and without nontemporal accesses; the add modes skip
+// the split variant (its workgroups read the whole row while others write
+// the residual).
+template <class E, int KIND, bool NT>
+RmsFn pick_rms_nt(int mode, int vpl)
 {
     switch (mode) {
-    case 0: return nt ? pick_vpl<E, KIND, true, 0>(vpl) : pick_vpl<E, KIND, false, 0>(vpl);
-    case 2: return pick_vpl<E, KIND, true, 2>(vpl);
+    case 0: return pick_vpl<E, KIND, NT, 0>(vpl);
+    case 2: return pick_vpl<E, KIND, NT, 2>(vpl);
     default:
         if constexpr (KIND == 1)
             return nullptr;
         else
-            return mode == 1 ? pick_vpl<E, KIND, true, 1>(vpl) : pick_vpl<E, KIND, true, 3>(vpl);
+            return mode == 1 ? pick_vpl<E, KIND, NT, 1>(vpl) : pick_vpl<E, KIND, NT, 3>(vpl);
     }
+}
+
+template <class E, int KIND>
+RmsFn pick_rms_mode(bool nt, int mode, int vpl)
+{
+    return nt ? pick_rms_nt<E, KIND, true>(mode, vpl) : pick_rms_nt<E, KIND, false>(mode, vpl);
 }
 
 int round_vpl(int need)
@@ -277,25 +284,25 @@ thread_local char g_variant[96];
 
 }  // namespace
 
-hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, int np, int lpr_req,
-                            int stage_req, int nt, hipStream_t stream, const char** variant)
+const char* plan_norm_rope(int32_t dtype, int32_t head_dim, int32_t max_heads, int np_req, int lpr_req,
+                           int stage_req, int nt_req, RopePlan* plan)
 {
-    NormRopeArgs a = a_in;
     const int ve = dtype == kBF16 ? 8 : 4;
-    const int nv = a.head_dim / ve;
+    const int nv = head_dim / ve;
     // Lanes per row: the smallest power of two that gives every lane at most
     // two vectors of the row.
     int lpr = 1;
     while (2 * lpr < nv)
         lpr *= 2;
-    if (lpr_req > 0 && (lpr_req & (lpr_req - 1)) == 0 && lpr_req <= 32 && 2 * lpr_req >= nv)
+    if (lpr_req > 0) {
+        if (2 * lpr_req < nv)
+            return "rope:lpr: too few lanes per row for this head_dim (each lane holds at most two vectors)";
         lpr = lpr_req;
+    }
     const int rpp = 64 / lpr;
-    int max_heads = 0;
-    for (int i = 0; i < 3; ++i)
-        max_heads = a.t[i].heads > max_heads ? a.t[i].heads : max_heads;
+    int np = np_req;
     if (np <= 0) {
-        // Two passes per tile where the tensor has two or more passes of
+        // Two passes per tile where a tensor has two or more passes of
         // heads.  Measured on MI355X with two / one / three passes: the joint
         // op (24 heads of 128) 29.7 / 30.0 / 30.3 us, fused ViT (16 + 16
         // heads of 80) 19.8 / 24.1 / 21.2 us, a 2048-token IMROPE chunk
@@ -303,10 +310,34 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
         const int passes = (max_heads + rpp - 1) / rpp;
         np = passes >= 2 ? 2 : 1;
     }
-    np = np < 1 ? 1 : (np > 4 ? 4 : np);
+    if (np < 1 || np > 4)
+        return "rope:np: passes per wave must be 1 to 4";
+    // Staged stores where a half row is not a whole number of 128-byte lines;
+    // they exist for 2 to 8 lanes per row (rows of up to 16 vectors).
+    const bool can_stage = lpr >= 2 && lpr <= 8;
+    bool stage = nv % 16 != 0 && can_stage;
+    if (stage_req >= 0) {
+        if (stage_req != 0 && !can_stage)
+            return "rope:stage1: staged stores exist for 2 to 8 lanes per row only";
+        stage = stage_req != 0;
+    }
+    plan->lpr = lpr;
+    plan->np = np;
+    plan->stage = stage;
+    plan->nt = nt_req != 0;
+    return nullptr;
+}
+
+hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, const RopePlan& plan,
+                            hipStream_t stream, const char** variant)
+{
+    NormRopeArgs a = a_in;
+    const int ve = dtype == kBF16 ? 8 : 4;
+    const int nv = a.head_dim / ve;
+    const int lpr = plan.lpr, np = plan.np;
     const int rope = a.rope.mode == kPosNone ? 0
                      : (a.rope.mode == kPosPlanes ? 2 : (a.rope.mode == kPosVit ? 3 : 1));
-    const int rpw = rpp * np;
+    const int rpw = (64 / lpr) * np;
     int32_t tpt = 0;
     for (int i = 0; i < 3; ++i) {
         a.tile_first[i] = tpt;
@@ -320,86 +351,114 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     a.ntiles = (uint32_t)tiles;
     a.div_tpt = make_fastdiv((uint32_t)tpt);
     a.div_tokens = make_fastdiv((uint32_t)a.tokens);
-    const int64_t blocks = (tiles + kWaves - 1) / kWaves;
-    const bool use_nt = nt != 0;
-    // Staged stores where a half row is not a whole number of 128-byte lines.
-    bool stage = stage_req < 0 ? nv % 16 != 0 : stage_req != 0;
-    stage = stage && lpr >= 2 && lpr <= 8;
     a.nv_recip = (65536u + (uint32_t)nv - 1) / (uint32_t)nv;
     NormRopeFn fn;
     switch (lpr) {
-    case 1: fn = pick_norm_rope<1>(dtype, rope, pairing, use_nt, stage, np); break;
-    case 2: fn = pick_norm_rope<2>(dtype, rope, pairing, use_nt, stage, np); break;
-    case 4: fn = pick_norm_rope<4>(dtype, rope, pairing, use_nt, stage, np); break;
-    case 8: fn = pick_norm_rope<8>(dtype, rope, pairing, use_nt, stage, np); break;
-    case 16: fn = pick_norm_rope<16>(dtype, rope, pairing, use_nt, stage, np); break;
-    default: fn = pick_norm_rope<32>(dtype, rope, pairing, use_nt, stage, np); break;
+    case 1: fn = pick_norm_rope<1>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 2: fn = pick_norm_rope<2>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 4: fn = pick_norm_rope<4>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 8: fn = pick_norm_rope<8>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 16: fn = pick_norm_rope<16>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    default: fn = pick_norm_rope<32>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
     }
-    hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
-    snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s:stage%d", np, (int)use_nt, lpr,
+    // One launch per kMaxBlocksPerLaunch workgroups, each told its first tile.
+    const int64_t blocks = (tiles + kWaves - 1) / kWaves;
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        a.tile_base = (uint32_t)(b0 * kWaves);
+        hipLaunchKernelGGL(fn, dim3((uint32_t)nb), dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s:stage%d", np, (int)plan.nt, lpr,
              dtype == kBF16 ? "bf16" : "f32",
              rope == 0 ? "none" : (rope == 1 ? "pos" : (rope == 2 ? "planes" : "vit")),
-             pairing == kNeox ? "neox" : "adjacent", (int)stage);
+             pairing == kNeox ? "neox" : "adjacent", (int)plan.stage);
     *variant = g_variant;
-    return hipGetLastError();
+    return hipSuccess;
 }
 
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, int kind, int nt, int mode, hipStream_t stream,
-                           const char** variant)
+const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, int mode, RmsPlan* plan)
 {
-    if (a.rows == 0)
-        return hipSuccess;
     const bool add = (mode & 1) != 0;
+    const int vpl_wave = round_vpl((nvec + 63) / 64);              // rows, split
+    const int vpl_wide = round_vpl((nvec + kThreads - 1) / kThreads);
+    int kind = kind_req;
     if (kind < 0) {
         // A workgroup per row below 2048 rows, a wavefront per row above.
         // Measured on MI355X, rows of 5120 bf16 (wide / one wave per row /
         // split): 1 row 2.16 / 3.27 / 2.23 us, 32 rows 2.82 / 4.50 / 3.31,
         // 128 rows 3.04 / 4.78 / 4.30, 1024 rows 4.95 / 5.97, 2048 rows 7.95
         // / 8.18, 4096 rows 15.6 / 13.8.  The split variant never wins; it
-        // stays reachable through the variant override.
-        kind = a.rows < 2048 && a.nvec >= 64 ? 2 : 0;
+        // stays reachable through the variant override.  Rows too long for
+        // one wavefront go to the workgroup-wide variant.
+        kind = rows < 2048 && nvec >= 64 ? 2 : 0;
+        if (kind == 0 && vpl_wave < 0)
+            kind = 2;
+    } else {
+        if (kind == 1 && add)
+            return "rms:split: the split variant cannot take the residual add (its workgroups read the whole "
+                   "row while others write the residual)";
+        if (kind != 2 && vpl_wave < 0)
+            return "rms:rows / rms:split: the row does not fit one wavefront (more than 1024 vectors)";
     }
-    if (add && kind == 1)
-        kind = 2;
-    if (mode != 0)
-        nt = 1;
-    int vpl = round_vpl(kind == 2 ? (a.nvec + kThreads - 1) / kThreads : (a.nvec + 63) / 64);
-    if (vpl < 0 && kind != 2) {
-        kind = 2;
-        vpl = round_vpl((a.nvec + kThreads - 1) / kThreads);
-    }
+    const int vpl = kind == 2 ? vpl_wide : vpl_wave;
     if (vpl < 0)
-        return hipErrorInvalidValue;
-    int64_t blocks;
+        return "rms: the row is longer than 4096 vectors";
+    plan->kind = kind;
+    plan->vpl = vpl;
+    plan->nt = nt_req != 0;
+    plan->mode = mode;
+    return nullptr;
+}
+
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, const RmsPlan& plan, hipStream_t stream,
+                           const char** variant)
+{
+    if (a.rows == 0)
+        return hipSuccess;
+    const int kind = plan.kind, vpl = plan.vpl, mode = plan.mode;
+    int64_t items, per_block;   // work items (rows, or row slices) and items per workgroup
     if (kind == 0) {
-        blocks = (a.rows + kWaves - 1) / kWaves;
+        items = a.rows;
+        per_block = kWaves;
     } else if (kind == 1) {
         // one slice of 64 vectors per wave (each lane stores one vector)
         a.split_len = 64;
         a.splits = (a.nvec + a.split_len - 1) / a.split_len;
         a.div_splits = make_fastdiv((uint32_t)a.splits);
-        blocks = (a.rows * a.splits + kWaves - 1) / kWaves;
+        items = a.rows * a.splits;
+        per_block = kWaves;
     } else {
-        blocks = a.rows;
+        items = a.rows;
+        per_block = 1;
     }
-    const bool use_nt = nt != 0;
     RmsFn fn;
     if (dtype == kBF16)
-        fn = kind == 0 ? pick_rms_mode<BF16, 0>(use_nt, mode, vpl)
-                       : (kind == 1 ? pick_rms_mode<BF16, 1>(use_nt, mode, vpl)
-                                    : pick_rms_mode<BF16, 2>(use_nt, mode, vpl));
+        fn = kind == 0 ? pick_rms_mode<BF16, 0>(plan.nt, mode, vpl)
+                       : (kind == 1 ? pick_rms_mode<BF16, 1>(plan.nt, mode, vpl)
+                                    : pick_rms_mode<BF16, 2>(plan.nt, mode, vpl));
     else
-        fn = kind == 0 ? pick_rms_mode<F32, 0>(use_nt, mode, vpl)
-                       : (kind == 1 ? pick_rms_mode<F32, 1>(use_nt, mode, vpl)
-                                    : pick_rms_mode<F32, 2>(use_nt, mode, vpl));
+        fn = kind == 0 ? pick_rms_mode<F32, 0>(plan.nt, mode, vpl)
+                       : (kind == 1 ? pick_rms_mode<F32, 1>(plan.nt, mode, vpl)
+                                    : pick_rms_mode<F32, 2>(plan.nt, mode, vpl));
     if (fn == nullptr)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, a);
+        return hipErrorInvalidValue;   // plan_rms_norm refuses such calls first
+    const int64_t blocks = (items + per_block - 1) / per_block;
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        a.item_base = b0 * per_block;
+        hipLaunchKernelGGL(fn, dim3((uint32_t)nb), dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     snprintf(g_variant, sizeof(g_variant), "rms:%s:nt%d:vpl%d:%s%s%s",
-             kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"), (int)use_nt, vpl, dtype == kBF16 ? "bf16" : "f32",
-             add ? ":add" : "", (mode & 2) ? ":fp8" : "");
+             kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"), (int)plan.nt, vpl, dtype == kBF16 ? "bf16" : "f32",
+             (mode & 1) ? ":add" : "", (mode & 2) ? ":fp8" : "");
     *variant = g_variant;
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_debug_fp8(const float* x, int64_t n, const float* scale, uint8_t* out, hipStream_t stream)

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     // of the last tile and store nothing: with no early exit, no branch
     // splits the kernel-argument reads of the prologue into separate waits.
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t tile_raw = blockIdx.x * kWaves + wave;
+    const uint32_t tile_raw = a.tile_base + blockIdx.x * kWaves + wave;
     const bool pad = tile_raw >= a.ntiles;         // wave-uniform
     const uint32_t tile = pad ? a.ntiles - 1 : tile_raw;
     const uint32_t bt = fast_div(tile, a.div_tpt);
