@@ -29,6 +29,7 @@ PAIR_NEOX, PAIR_ADJACENT = 0, 1
 _MODES = {"1d": POS_1D, "axes": POS_AXES, "imrope": POS_IMROPE, "planes": POS_PLANES}
 _PAIRS = {"neox": PAIR_NEOX, "adjacent": PAIR_ADJACENT}
 _OUT = {"f32": 0, "bf16": 1}
+_NUMERICS = {"contract": 0, "eager": 1}
 
 _f32p = ctypes.POINTER(ctypes.c_float)
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -64,39 +65,39 @@ def _load():
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_rms_norm.restype = None
         lib.oracle_rms_norm.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, _f32p,
-                                        ctypes.c_float, ctypes.c_int32, _f32p]
+                                        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _f32p]
         lib.oracle_fp8_e4m3_decode.restype = ctypes.c_double
         lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
         lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_double]
         lib.oracle_add_rms_norm.restype = None
         lib.oracle_add_rms_norm.argtypes = [_f32p, _f32p, ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_float,
-                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _f32p, _f32p,
-                                            ctypes.POINTER(ctypes.c_uint8)]
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _f32p,
+                                            _f32p, ctypes.POINTER(ctypes.c_uint8)]
         lib.oracle_qk_norm_rope_cache.restype = None
         lib.oracle_qk_norm_rope_cache.argtypes = [_f32p, ctypes.c_int32, _f32p, _f32p, ctypes.c_int32,
                                                   ctypes.c_int64, ctypes.c_int32, _f32p, _f32p, ctypes.c_float,
-                                                  ctypes.c_int32, ctypes.POINTER(_Rope),
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Rope),
                                                   ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, _f32p, _f32p,
                                                   _f32p]
         lib.oracle_axis.restype = ctypes.c_int32
         lib.oracle_axis.argtypes = [ctypes.POINTER(_Rope), ctypes.c_int32]
         lib.oracle_qk_norm_rope.restype = None
         lib.oracle_qk_norm_rope.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                            _f32p, ctypes.c_float, ctypes.c_int32,
+                                            _f32p, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(_Rope), _f32p]
         lib.oracle_joint_qk_norm_rope.restype = None
         lib.oracle_joint_qk_norm_rope.argtypes = (
             [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
             + [_f32p] * 3 + [ctypes.c_int64] + [_f32p] * 2
             + [_f32p] * 3 + [ctypes.c_int64] + [_f32p] * 2
-            + [ctypes.c_float, ctypes.c_int32, ctypes.POINTER(_Rope)] + [_f32p] * 3)
+            + [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Rope)] + [_f32p] * 3)
         lib.oracle_vit_positions.restype = None
         lib.oracle_vit_positions.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, _i32p,
                                              ctypes.c_int64]
         lib.oracle_vit_qk_norm_rope.restype = None
         lib.oracle_vit_qk_norm_rope.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _f32p,
-                                                ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 _f32p, ctypes.c_int32, _f32p, ctypes.c_int32, _f32p,
                                                 ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _f32p]
         lib.oracle_vit_cos_sin.restype = None
@@ -166,14 +167,15 @@ def round_bf16(v) -> np.ndarray:
     return np.vectorize(lib.oracle_round_bf16, otypes=[np.float64])(v) if v.size else v.copy()
 
 
-def rms_norm(x, weight, eps, out_dtype="bf16"):
-    """Plain row RMSNorm of x [rows, width]."""
+def rms_norm(x, weight, eps, out_dtype="bf16", numerics="contract"):
+    """Plain row RMSNorm of x [rows, width].  numerics "contract" (one
+    rounding) or "eager" (the eager chain's rounding points)."""
     lib = _load()
     x, xp = _f32(x)
     w, wp = _f32(weight)
     rows, width = x.shape
     y = np.empty_like(x)
-    lib.oracle_rms_norm(xp, rows, width, wp, eps, _OUT[out_dtype], y.ctypes.data_as(_f32p))
+    lib.oracle_rms_norm(xp, rows, width, wp, eps, _OUT[out_dtype], _NUMERICS[numerics], y.ctypes.data_as(_f32p))
     return y
 
 
@@ -191,10 +193,13 @@ def fp8_e4m3_encode(values) -> np.ndarray:
     return np.array([lib.oracle_fp8_e4m3_encode(float(a)) for a in v.ravel()], dtype=np.uint8).reshape(v.shape)
 
 
-def add_rms_norm(x, weight, eps, residual=None, act_dtype="bf16", out_dtype="bf16", scale=1.0):
+def add_rms_norm(x, weight, eps, residual=None, act_dtype="bf16", out_dtype="bf16", scale=1.0,
+                 numerics="contract"):
     """Residual add + RMSNorm of x [rows, width]: returns (s, y) where s is the
     new residual stream and y the output (float array, or uint8 FP8 E4M3
-    codes for out_dtype "fp8_e4m3")."""
+    codes for out_dtype "fp8_e4m3", which has no eager numerics)."""
+    if numerics != "contract" and out_dtype == "fp8_e4m3":
+        raise ValueError("the FP8 output is defined for the contract numerics only")
     lib = _load()
     x, xp = _f32(x)
     w, wp = _f32(weight)
@@ -209,7 +214,7 @@ def add_rms_norm(x, weight, eps, residual=None, act_dtype="bf16", out_dtype="bf1
     fp8 = out_dtype == "fp8_e4m3"
     y = np.empty(x.shape, np.uint8 if fp8 else np.float32)
     out_kind = 2 if fp8 else _OUT[out_dtype]
-    lib.oracle_add_rms_norm(xp, rp, rows, width, wp, eps, _OUT[act_dtype], out_kind, scale,
+    lib.oracle_add_rms_norm(xp, rp, rows, width, wp, eps, _OUT[act_dtype], out_kind, _NUMERICS[numerics], scale,
                             s.ctypes.data_as(_f32p), None if fp8 else y.ctypes.data_as(_f32p),
                             y.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)) if fp8 else None)
     return s, y
@@ -222,7 +227,7 @@ def axis_map(rope: Rope, n_pairs: int) -> np.ndarray:
     return np.array([lib.oracle_axis(ctypes.byref(r), p) for p in range(n_pairs)], np.int32)
 
 
-def qk_norm_rope(x, weight, eps, rope=None, out_dtype="bf16"):
+def qk_norm_rope(x, weight, eps, rope=None, out_dtype="bf16", numerics="contract"):
     """Per-(token, head) RMSNorm + RoPE of x [tokens, heads, head_dim]."""
     lib = _load()
     x, xp = _f32(x)
@@ -230,12 +235,13 @@ def qk_norm_rope(x, weight, eps, rope=None, out_dtype="bf16"):
     tokens, heads, head_dim = x.shape
     out = np.empty_like(x)
     rp = ctypes.byref(rope._c()) if rope is not None else None
-    lib.oracle_qk_norm_rope(xp, tokens, heads, head_dim, wp, eps, _OUT[out_dtype], rp,
+    lib.oracle_qk_norm_rope(xp, tokens, heads, head_dim, wp, eps, _OUT[out_dtype], _NUMERICS[numerics], rp,
                             out.ctypes.data_as(_f32p))
     return out
 
 
-def qk_norm_rope_cache(q, k, v, q_weight, k_weight, eps, rope, slots, k_cache, v_cache, out_dtype="bf16"):
+def qk_norm_rope_cache(q, k, v, q_weight, k_weight, eps, rope, slots, k_cache, v_cache, out_dtype="bf16",
+                       numerics="contract"):
     """Q out [tokens, Hq, D] plus the caches [num_slots, Hkv, D] after writing
     token t's rotated K and its V into row slots[t] (copies of the given
     caches are updated and returned: (q_out, k_cache, v_cache))."""
@@ -255,7 +261,7 @@ def qk_norm_rope_cache(q, k, v, q_weight, k_weight, eps, rope, slots, k_cache, v
     vc = np.array(v_cache, dtype=np.float32, copy=True) if v_cache is not None else None
     qo = np.empty_like(q)
     r = rope._c() if rope is not None else None
-    lib.oracle_qk_norm_rope_cache(qp, qh, kp, vp, kvh, tokens, d, wqp, wkp, eps, _OUT[out_dtype],
+    lib.oracle_qk_norm_rope_cache(qp, qh, kp, vp, kvh, tokens, d, wqp, wkp, eps, _OUT[out_dtype], _NUMERICS[numerics],
                                   ctypes.byref(r) if r is not None else None,
                                   sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), kc.shape[0],
                                   qo.ctypes.data_as(_f32p), kc.ctypes.data_as(_f32p),
@@ -263,7 +269,7 @@ def qk_norm_rope_cache(q, k, v, q_weight, k_weight, eps, rope, slots, k_cache, v
     return qo, kc, vc
 
 
-def joint_qk_norm_rope(txt, img, eps, rope, out_dtype="bf16"):
+def joint_qk_norm_rope(txt, img, eps, rope, out_dtype="bf16", numerics="contract"):
     """Joint text/image op.
 
     txt / img: dicts with q, k, v float32 [batch, tokens_s, heads, head_dim]
@@ -288,7 +294,7 @@ def joint_qk_norm_rope(txt, img, eps, rope, out_dtype="bf16"):
     qo, ko, vo = (np.empty(shape, np.float32) for _ in range(3))
     r = rope._c()
     lib.oracle_joint_qk_norm_rope(batch, heads, d, qtp, ktp, vtp, st, qwtp, kwtp,
-                                  qip, kip, vip, si, qwip, kwip, eps, _OUT[out_dtype],
+                                  qip, kip, vip, si, qwip, kwip, eps, _OUT[out_dtype], _NUMERICS[numerics],
                                   ctypes.byref(r), qo.ctypes.data_as(_f32p),
                                   ko.ctypes.data_as(_f32p), vo.ctypes.data_as(_f32p))
     return qo, ko, vo
@@ -323,7 +329,8 @@ def vit_cos_sin(inv_t, inv_h, inv_w, grid_thw, merge, fill=np.nan):
     return cos, sin
 
 
-def vit_qk_norm_rope(x, weight, eps, inv_t, inv_h, inv_w, grid_thw, merge, pairing="neox", out_dtype="bf16"):
+def vit_qk_norm_rope(x, weight, eps, inv_t, inv_h, inv_w, grid_thw, merge, pairing="neox", out_dtype="bf16",
+                     numerics="contract"):
     """Per-head RMSNorm + RoPE of x [N, heads, head_dim] with (t, h, w)
     positions computed from the ViT grids (no cos/sin planes)."""
     lib = _load()
@@ -335,6 +342,7 @@ def vit_qk_norm_rope(x, weight, eps, inv_t, inv_h, inv_w, grid_thw, merge, pairi
     g, gp = _i32(np.asarray(grid_thw).reshape(-1, 3))
     n, heads, d = x.shape
     out = np.empty_like(x)
-    lib.oracle_vit_qk_norm_rope(xp, n, heads, d, wp, eps, _OUT[out_dtype], _PAIRS[pairing], itp, it.size, ihp,
+    lib.oracle_vit_qk_norm_rope(xp, n, heads, d, wp, eps, _OUT[out_dtype], _NUMERICS[numerics], _PAIRS[pairing],
+                                itp, it.size, ihp,
                                 ih.size, iwp, iw.size, gp, g.shape[0], merge, out.ctypes.data_as(_f32p))
     return out

@@ -59,6 +59,14 @@ static float round_out(double v, int32_t out_kind)
     return (float)v;                          /* round to nearest even fp32 */
 }
 
+/* Products and differences of two floats taken in double and then rounded
+ * to float are the correctly rounded float results (double carries more
+ * than twice float's 24 bits plus two), so the helpers below are IEEE fp32
+ * operations, each rounded once. */
+static float mul32(float a, float b) { return (float)((double)a * (double)b); }
+static float sub32(float a, float b) { return (float)((double)a - (double)b); }
+static float add32(float a, float b) { return (float)((double)a + (double)b); }
+
 /* ------------------------------------------------------------------------ */
 /* RMSNorm of one row                                                        */
 /* ------------------------------------------------------------------------ */
@@ -67,25 +75,42 @@ static float round_out(double v, int32_t out_kind)
  * The normalisation statistic is the mean of the squares and eps is added
  * inside the square root ([Ovis] and [VecRMS]: RMSNorm with eps 1e-6; the
  * weight multiplies the normalised value, [VecRMS] review thread quoting the
- * output expression of rms_norm_kernel). */
-static void norm_row(const float* x, const float* w, int32_t d, float eps, double* u)
+ * output expression of rms_norm_kernel).
+ *
+ * Eager numerics (ORACLE_NUMERICS_EAGER): the rounding points of an eager
+ * RMSNorm kernel, whose output expression the [VecRMS] review thread quotes
+ * as ((scalar_t)(x * s_variance)) * weight[idx].  Reading: s_variance is the
+ * fp32 value of rrms; x * s_variance is one fp32 product; it is rounded to the
+ * activation type (scalar_t); that value times the weight is rounded to the
+ * activation type once more.  u_i then already lies on the activation grid. */
+static void norm_row(const float* x, const float* w, int32_t d, float eps, int32_t numerics,
+                     int32_t act_kind, double* u)
 {
     double ss = 0.0;
     for (int32_t i = 0; i < d; ++i)
         ss += (double)x[i] * (double)x[i];
     double rrms = 1.0 / sqrt(ss / (double)d + (double)eps);
+    if (numerics == ORACLE_NUMERICS_EAGER) {
+        const float r32 = (float)rrms;
+        for (int32_t i = 0; i < d; ++i) {
+            const double xs = (double)round_out((double)mul32(x[i], r32), act_kind);
+            u[i] = (double)round_out(xs * (double)w[i], act_kind);
+        }
+        return;
+    }
     for (int32_t i = 0; i < d; ++i)
         u[i] = (double)x[i] * rrms * (double)w[i];
 }
 
 /* Plain row RMSNorm ([Vulkan] decode RmsNorm of width 5120; [VecRMS]).
- * Reading: one rounding of x * rrms * w to the output type. */
+ * Reading: one rounding of x * rrms * w to the output type (eager numerics:
+ * the two roundings of norm_row). */
 void oracle_rms_norm(const float* x, int64_t rows, int32_t width, const float* weight,
-                     float eps, int32_t out_kind, float* y)
+                     float eps, int32_t out_kind, int32_t numerics, float* y)
 {
     double* u = (double*)malloc(sizeof(double) * (size_t)width);
     for (int64_t r = 0; r < rows; ++r) {
-        norm_row(x + r * width, weight, width, eps, u);
+        norm_row(x + r * width, weight, width, eps, numerics, out_kind, u);
         for (int32_t i = 0; i < width; ++i)
             y[r * width + i] = round_out(u[i], out_kind);
     }
@@ -146,8 +171,8 @@ uint8_t oracle_fp8_e4m3_encode(double v)
  * rounded fp32 quotient by the scale (a double quotient of two floats rounded
  * to float is the correctly rounded float quotient), then the encoding. */
 void oracle_add_rms_norm(const float* x, const float* r, int64_t rows, int32_t width, const float* weight,
-                         float eps, int32_t act_kind, int32_t out_kind, float scale, float* s_out,
-                         float* y_out, uint8_t* code_out)
+                         float eps, int32_t act_kind, int32_t out_kind, int32_t numerics, float scale,
+                         float* s_out, float* y_out, uint8_t* code_out)
 {
     float* s = (float*)malloc(sizeof(float) * (size_t)width);
     double* u = (double*)malloc(sizeof(double) * (size_t)width);
@@ -159,7 +184,7 @@ void oracle_add_rms_norm(const float* x, const float* r, int64_t rows, int32_t w
         }
         if (s_out)
             memcpy(s_out + row * width, s, sizeof(float) * (size_t)width);
-        norm_row(s, weight, width, eps, u);
+        norm_row(s, weight, width, eps, numerics, act_kind, u);
         for (int32_t i = 0; i < width; ++i) {
             if (out_kind == ORACLE_OUT_FP8_E4M3) {
                 const float y32 = (float)u[i];
@@ -263,10 +288,11 @@ static void pair_cos_sin(const oracle_rope* rope, int64_t tok, int32_t p, double
  * convention a' = a cos - b sin, b' = b cos + a sin (the pages print no sign).
  * Elements at or beyond R pass through. */
 static void norm_rope_row(const float* x, const float* w, int32_t d, float eps, int32_t out_kind,
-                          const oracle_rope* rope, int64_t tok, double* n, float* out)
+                          int32_t numerics, const oracle_rope* rope, int64_t tok, double* n, float* out)
 {
-    norm_row(x, w, d, eps, n);
-    if (out_kind == ORACLE_OUT_BF16)
+    const int eager = numerics == ORACLE_NUMERICS_EAGER;
+    norm_row(x, w, d, eps, numerics, out_kind, n);
+    if (out_kind == ORACLE_OUT_BF16 && !eager)
         for (int32_t i = 0; i < d; ++i)
             n[i] = oracle_round_bf16(n[i]);
 
@@ -284,20 +310,35 @@ static void norm_rope_row(const float* x, const float* w, int32_t d, float eps, 
         }
         double c, s;
         pair_cos_sin(rope, tok, p, &c, &s);
+        if (eager) {
+            /* Eager numerics ([Ovis] "Supplemental eager bitwise measurements":
+             * the preset that reproduced the eager chain turns floating-point
+             * fusion off, and that chain reads its RoPE table in the
+             * activation type, bf16 in the measured case).  Reading: the table
+             * holds cos and sin computed in fp32 (each rounded once to fp32)
+             * and stored in the activation type; each product is rounded to
+             * fp32; their difference or sum is rounded to fp32; then the final
+             * rounding to the output type. */
+            const float ct = round_out((double)(float)c, out_kind), st = round_out((double)(float)s, out_kind);
+            const float ni = (float)n[i], nj = (float)n[j];
+            out[i] = round_out((double)sub32(mul32(ni, ct), mul32(nj, st)), out_kind);
+            out[j] = round_out((double)add32(mul32(nj, ct), mul32(ni, st)), out_kind);
+            continue;
+        }
         out[i] = round_out(n[i] * c - n[j] * s, out_kind);
         out[j] = round_out(n[j] * c + n[i] * s, out_kind);
     }
 }
 
 void oracle_qk_norm_rope(const float* x, int64_t tokens, int32_t heads, int32_t head_dim,
-                         const float* weight, float eps, int32_t out_kind,
+                         const float* weight, float eps, int32_t out_kind, int32_t numerics,
                          const oracle_rope* rope, float* out)
 {
     double* n = (double*)malloc(sizeof(double) * (size_t)head_dim);
     for (int64_t t = 0; t < tokens; ++t)
         for (int32_t h = 0; h < heads; ++h) {
             int64_t row = (t * heads + h) * (int64_t)head_dim;
-            norm_rope_row(x + row, weight, head_dim, eps, out_kind, rope, t, n, out + row);
+            norm_rope_row(x + row, weight, head_dim, eps, out_kind, numerics, rope, t, n, out + row);
         }
     free(n);
 }
@@ -311,14 +352,14 @@ void oracle_qk_norm_rope(const float* x, int64_t tokens, int32_t heads, int32_t 
  * slot's content unspecified, so the tests use injective mappings. */
 void oracle_qk_norm_rope_cache(const float* q, int32_t q_heads, const float* k, const float* v,
                                int32_t kv_heads, int64_t tokens, int32_t head_dim, const float* q_weight,
-                               const float* k_weight, float eps, int32_t out_kind, const oracle_rope* rope,
-                               const int64_t* slots, int64_t num_slots, float* q_out, float* k_cache,
-                               float* v_cache)
+                               const float* k_weight, float eps, int32_t out_kind, int32_t numerics,
+                               const oracle_rope* rope, const int64_t* slots, int64_t num_slots, float* q_out,
+                               float* k_cache, float* v_cache)
 {
     const int64_t row = (int64_t)kv_heads * head_dim;
     float* k_rot = (float*)malloc(sizeof(float) * (size_t)(tokens * row > 0 ? tokens * row : 1));
-    oracle_qk_norm_rope(q, tokens, q_heads, head_dim, q_weight, eps, out_kind, rope, q_out);
-    oracle_qk_norm_rope(k, tokens, kv_heads, head_dim, k_weight, eps, out_kind, rope, k_rot);
+    oracle_qk_norm_rope(q, tokens, q_heads, head_dim, q_weight, eps, out_kind, numerics, rope, q_out);
+    oracle_qk_norm_rope(k, tokens, kv_heads, head_dim, k_weight, eps, out_kind, numerics, rope, k_rot);
     for (int64_t t = 0; t < tokens; ++t) {
         const int64_t slot = slots[t];
         if (slot < 0 || slot >= num_slots)
@@ -344,7 +385,7 @@ void oracle_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim,
                                int64_t tokens_txt, const float* qw_txt, const float* kw_txt,
                                const float* q_img, const float* k_img, const float* v_img,
                                int64_t tokens_img, const float* qw_img, const float* kw_img,
-                               float eps, int32_t out_kind, const oracle_rope* rope,
+                               float eps, int32_t out_kind, int32_t numerics, const oracle_rope* rope,
                                float* q_out, float* k_out, float* v_out)
 {
     int64_t joint = tokens_txt + tokens_img;
@@ -365,8 +406,8 @@ void oracle_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim,
             int64_t dst = ((int64_t)b * joint + tau) * row_elems;
             for (int32_t h = 0; h < heads; ++h) {
                 int64_t o = (int64_t)h * head_dim;
-                norm_rope_row(q + o, qw, head_dim, eps, out_kind, rope, tau, n, q_out + dst + o);
-                norm_rope_row(k + o, kw, head_dim, eps, out_kind, rope, tau, n, k_out + dst + o);
+                norm_rope_row(q + o, qw, head_dim, eps, out_kind, numerics, rope, tau, n, q_out + dst + o);
+                norm_rope_row(k + o, kw, head_dim, eps, out_kind, numerics, rope, tau, n, k_out + dst + o);
             }
             memcpy(v_out + dst, v, sizeof(float) * (size_t)row_elems);
         }
@@ -446,7 +487,7 @@ void oracle_vit_cos_sin(const float* inv_t, int32_t half_t, const float* inv_h, 
  * buffer and the per-axis inv_freq a single [R/2] ladder, then the row goes
  * through the same norm and rotation as every other mode. */
 void oracle_vit_qk_norm_rope(const float* x, int64_t n_tokens, int32_t heads, int32_t head_dim,
-                             const float* weight, float eps, int32_t out_kind, int32_t pairing,
+                             const float* weight, float eps, int32_t out_kind, int32_t numerics, int32_t pairing,
                              const float* inv_t, int32_t half_t, const float* inv_h, int32_t half_h,
                              const float* inv_w, int32_t half_w, const int32_t* grid_thw,
                              int32_t num_grids, int32_t merge, float* out)
@@ -477,7 +518,7 @@ void oracle_vit_qk_norm_rope(const float* x, int64_t n_tokens, int32_t heads, in
         rope.token_base = 0;
         for (int32_t h = 0; h < heads; ++h) {
             int64_t row = (tok * heads + h) * (int64_t)head_dim;
-            norm_rope_row(x + row, weight, head_dim, eps, out_kind, &rope, 0, n, out + row);
+            norm_rope_row(x + row, weight, head_dim, eps, out_kind, numerics, &rope, 0, n, out + row);
         }
     }
     free(n);

@@ -25,6 +25,13 @@ enum { ORACLE_OUT_F32 = 0, ORACLE_OUT_BF16 = 1, ORACLE_OUT_FP8_E4M3 = 2 };
 enum { ORACLE_POS_1D = 0, ORACLE_POS_AXES = 1, ORACLE_POS_IMROPE = 2, ORACLE_POS_PLANES = 3 };
 enum { ORACLE_PAIR_NEOX = 0, ORACLE_PAIR_ADJACENT = 1 };
 enum { ORACLE_AXIS_T = 0, ORACLE_AXIS_H = 1, ORACLE_AXIS_W = 2, ORACLE_AXIS_E = 3 };
+/* Rounding points.  CONTRACT: the normalised value (weight included) rounded
+ * once to the output type, the rotation exact, one final rounding.  EAGER: an
+ * eager RMSNorm + RoPE chain's points -- fl32(x * fl32(rrms)) rounded to the
+ * activation type, times the weight, rounded again; cos and sin rounded to
+ * the activation type; every product and sum of the rotation rounded to fp32
+ * (no fused multiply-add); the final rounding. */
+enum { ORACLE_NUMERICS_CONTRACT = 0, ORACLE_NUMERICS_EAGER = 1 };
 
 typedef struct {
     int32_t mode;            /* ORACLE_POS_*                                         */
@@ -44,9 +51,10 @@ typedef struct {
 /* Round a real to the nearest bf16 value, ties to even. */
 double oracle_round_bf16(double v);
 
-/* Plain row RMSNorm: y = round(x * rrms * w), rrms = 1/sqrt(mean(x^2) + eps). */
+/* Plain row RMSNorm: y = round(x * rrms * w), rrms = 1/sqrt(mean(x^2) + eps)
+ * (EAGER numerics: y = round(round(fl32(x * fl32(rrms))) * w)). */
 void oracle_rms_norm(const float* x, int64_t rows, int32_t width, const float* weight,
-                     float eps, int32_t out_kind, float* y);
+                     float eps, int32_t out_kind, int32_t numerics, float* y);
 
 /* OCP FP8 E4M3 ("fn": no infinities, NaN = S.1111.111): value of a code, and
  * the code of a finite real (round half to even, saturating at +-448). */
@@ -59,8 +67,8 @@ uint8_t oracle_fp8_e4m3_encode(double v);
  * encode(fl32(fl32(y) / scale)) (a static per-tensor scale).  r == NULL means
  * no residual (s = x).  Unused outputs may be NULL. */
 void oracle_add_rms_norm(const float* x, const float* r, int64_t rows, int32_t width, const float* weight,
-                         float eps, int32_t act_kind, int32_t out_kind, float scale, float* s_out,
-                         float* y_out, uint8_t* code_out);
+                         float eps, int32_t act_kind, int32_t out_kind, int32_t numerics, float scale,
+                         float* s_out, float* y_out, uint8_t* code_out);
 
 /* Position axis that pair p reads (ORACLE_AXIS_*). */
 int32_t oracle_axis(const oracle_rope* rope, int32_t p);
@@ -69,7 +77,7 @@ int32_t oracle_axis(const oracle_rope* rope, int32_t p);
  * x, out: [tokens][heads][head_dim].  rope == NULL or rotary_dim == 0 means
  * norm only. */
 void oracle_qk_norm_rope(const float* x, int64_t tokens, int32_t heads, int32_t head_dim,
-                         const float* weight, float eps, int32_t out_kind,
+                         const float* weight, float eps, int32_t out_kind, int32_t numerics,
                          const oracle_rope* rope, float* out);
 
 /* QK RMSNorm + RoPE with the K rows written into a cache: Q as
@@ -80,9 +88,9 @@ void oracle_qk_norm_rope(const float* x, int64_t tokens, int32_t heads, int32_t 
  * v_cache may be NULL together. */
 void oracle_qk_norm_rope_cache(const float* q, int32_t q_heads, const float* k, const float* v,
                                int32_t kv_heads, int64_t tokens, int32_t head_dim, const float* q_weight,
-                               const float* k_weight, float eps, int32_t out_kind, const oracle_rope* rope,
-                               const int64_t* slots, int64_t num_slots, float* q_out, float* k_cache,
-                               float* v_cache);
+                               const float* k_weight, float eps, int32_t out_kind, int32_t numerics,
+                               const oracle_rope* rope, const int64_t* slots, int64_t num_slots, float* q_out,
+                               float* k_cache, float* v_cache);
 
 /* Joint text/image op: each stream is normalised with its own weights, the
  * streams are concatenated text first and the joint sequence is rotated with
@@ -94,7 +102,7 @@ void oracle_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim,
                                int64_t tokens_txt, const float* qw_txt, const float* kw_txt,
                                const float* q_img, const float* k_img, const float* v_img,
                                int64_t tokens_img, const float* qw_img, const float* kw_img,
-                               float eps, int32_t out_kind, const oracle_rope* rope,
+                               float eps, int32_t out_kind, int32_t numerics, const oracle_rope* rope,
                                float* q_out, float* k_out, float* v_out);
 
 /* ViT patch positions: pos[3][n_tokens] = (t, h, w) of every token of the
@@ -115,7 +123,8 @@ void oracle_vit_cos_sin(const float* inv_t, int32_t half_t, const float* inv_h, 
  * fl32(fl32(pos_a(n)) * inv_a[p - off_a]).  x, out: [n_tokens][heads][head_dim];
  * rotary_dim = 2 * (half_t + half_h + half_w). */
 void oracle_vit_qk_norm_rope(const float* x, int64_t n_tokens, int32_t heads, int32_t head_dim,
-                             const float* weight, float eps, int32_t out_kind, int32_t pairing,
+                             const float* weight, float eps, int32_t out_kind, int32_t numerics,
+                             int32_t pairing,
                              const float* inv_t, int32_t half_t, const float* inv_h, int32_t half_h,
                              const float* inv_w, int32_t half_w, const int32_t* grid_thw,
                              int32_t num_grids, int32_t merge, float* out);

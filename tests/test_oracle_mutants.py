@@ -64,6 +64,18 @@ MUTANTS = {
                                 "if (slot < 0 || slot >= num_slots - 1)\n            continue;"),
     "passthrough_skipped": ("for (int32_t i = r; i < d; ++i)\n        out[i] = round_out(n[i], out_kind);",
                             "for (int32_t i = r; i < d; ++i)\n        out[i] = 0.0f;"),
+    "eager_x_rrms_not_rounded": ("const double xs = (double)round_out((double)mul32(x[i], r32), act_kind);",
+                                 "const double xs = (double)mul32(x[i], r32);"),
+    "eager_weight_product_not_rounded": ("u[i] = (double)round_out(xs * (double)w[i], act_kind);",
+                                         "u[i] = xs * (double)w[i];"),
+    "eager_rrms_not_fp32": ("(double)mul32(x[i], r32)", "(double)(float)((double)x[i] * rrms)"),
+    "eager_table_not_in_activation_type": (
+        "const float ct = round_out((double)(float)c, out_kind), st = round_out((double)(float)s, out_kind);",
+        "const float ct = (float)c, st = (float)s;"),
+    "eager_fused_multiply_add": ("out[i] = round_out((double)sub32(mul32(ni, ct), mul32(nj, st)), out_kind);",
+                                 "out[i] = round_out((double)(float)((double)ni * (double)ct - "
+                                 "(double)mul32(nj, st)), out_kind);"),
+    "eager_rotation_sign": ("sub32(mul32(ni, ct), mul32(nj, st))", "add32(mul32(ni, ct), mul32(nj, st))"),
 }
 
 

@@ -636,3 +636,143 @@ def test_cache_write_reversed_and_sparse_slots():
     assert np.array_equal(kc, ref_k) and np.array_equal(vc, ref_v)
     _, kc_nov, vc_nov = oracle.qk_norm_rope_cache(q, k, None, wq, wk, 1e-6, rope, slots, kc0, None)
     assert np.array_equal(kc_nov, ref_k) and vc_nov is None
+
+
+# ----------------------------------------------------------------------------
+# Eager numerics: the rounding points of an eager RMSNorm + RoPE chain
+# ([VecRMS] review thread: the RMSNorm output is ((scalar_t)(x * s_variance))
+# * weight; [Ovis] "Supplemental eager bitwise measurements": floating-point
+# fusion off, a RoPE table in the activation type).  The reconstructions below
+# run the same chain through torch's bf16 arithmetic and casts and numpy's
+# float32 arithmetic, not through the oracle's own rounding code.
+# ----------------------------------------------------------------------------
+
+def _rrms32(x, eps):
+    """fp32 value of 1 / sqrt(mean(x^2) + eps), from a double computation."""
+    xd = x.astype(np.float64)
+    return (1.0 / np.sqrt(np.mean(xd * xd, axis=-1) + np.float64(np.float32(eps)))).astype(np.float32)
+
+
+def _eager_norm_torch(x, w, eps, act):
+    """(act)((act)(x * s_variance) * w) with s_variance the fp32 rrms."""
+    t = (x * _rrms32(x, eps)[..., None]).astype(np.float32)              # one fp32 product
+    if act == "f32":
+        return (t * w).astype(np.float32)
+    tb = torch.from_numpy(t).to(torch.bfloat16)                          # (scalar_t)(x * s_variance)
+    wb = torch.from_numpy(w).to(torch.bfloat16)
+    return (tb * wb).float().numpy()                                     # bf16 * bf16 -> bf16
+
+
+def _bf16_inputs(shape, k, mean=0.0, std=1.0):
+    a = _rng(k).normal(mean, std, shape).astype(np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_eager_rms_norm_equals_torch_cast_chain(act):
+    x = _bf16_inputs((64, 1024), 90) if act == "bf16" else _rng(90).normal(0, 1, (64, 1024)).astype(np.float32)
+    w = _bf16_inputs((1024,), 91, 1.0, 0.1) if act == "bf16" else _rng(91).normal(1, 0.1, 1024).astype(np.float32)
+    got = oracle.rms_norm(x, w, 1e-6, act, numerics="eager")
+    assert np.array_equal(got, _eager_norm_torch(x, w, 1e-6, act))
+    # the eager chain rounds twice: a visible share of elements differs from
+    # the contract's single rounding, each by at most a couple of steps
+    one = oracle.rms_norm(x, w, 1e-6, act)
+    frac = np.mean(got != one)
+    assert (0.05 < frac < 0.6) if act == "bf16" else (frac > 0.05)
+    np.testing.assert_allclose(got, one, rtol=2 ** -6 if act == "bf16" else 2 ** -22)
+
+
+def _eager_rotation(n, c, s, pairing, rotary_dim):
+    """Eager rotation of rows n by per-(token, pair) cos/sin tables c, s
+    (already in the table's type, as float32): fp32 products and sums as
+    separate numpy float32 operations (no fused multiply-add)."""
+    out = n.copy()
+    half = rotary_dim // 2
+    p = np.arange(half)
+    i, j = (p, p + half) if pairing == "neox" else (2 * p, 2 * p + 1)
+    a, b = n[..., i], n[..., j]
+    cc, ss = c[:, None, :], s[:, None, :]
+    out[..., i] = (a * cc).astype(np.float32) - (b * ss).astype(np.float32)
+    out[..., j] = (b * cc).astype(np.float32) + (a * ss).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("act,pairing", [("bf16", "neox"), ("bf16", "adjacent"), ("f32", "neox")])
+def test_eager_rope_equals_torch_chain(act, pairing):
+    tokens, heads, d = 96, 6, 128
+    if act == "bf16":
+        x, w = _bf16_inputs((tokens, heads, d), 92), _bf16_inputs((d,), 93, 1.0, 0.1)
+    else:
+        x, w = _rng(92).normal(0, 1, (tokens, heads, d)).astype(np.float32), \
+            _rng(93).normal(1, 0.1, d).astype(np.float32)
+    pos = _rng(94).integers(0, 8192, (1, tokens)).astype(np.int32)
+    inv = inv_freq_ladder(1e4, d)
+    rope = oracle.Rope("1d", d, pairing, inv_freq=inv, positions=pos)
+    got = oracle.qk_norm_rope(x, w, 1e-6, rope, act, numerics="eager")
+
+    n = _eager_norm_torch(x, w, 1e-6, act)
+    theta = (pos[0, :, None].astype(np.float32) * inv[None, :]).astype(np.float32)
+    c32 = np.cos(theta.astype(np.float64)).astype(np.float32)       # fp32 table values
+    s32 = np.sin(theta.astype(np.float64)).astype(np.float32)
+    if act == "bf16":
+        c32 = torch.from_numpy(c32).to(torch.bfloat16).float().numpy()
+        s32 = torch.from_numpy(s32).to(torch.bfloat16).float().numpy()
+    o = _eager_rotation(n, c32, s32, pairing, d)
+    expect = torch.from_numpy(o).to(torch.bfloat16).float().numpy() if act == "bf16" else o
+    assert np.array_equal(got, expect)
+    if act == "f32":
+        # with a fused multiply-add the first element of a pair would be
+        # fl32(a c - fl32(b s)): the fp32 products are not exact here, and
+        # the eager result must differ from that on a visible share
+        half = d // 2
+        a, b = n[..., :half].astype(np.float64), n[..., half:].astype(np.float64)
+        fused = (a * c32[:, None, :] - (n[..., half:] * s32[:, None, :]).astype(np.float32)).astype(np.float32)
+        assert np.mean(fused != got[..., :half]) > 0.01
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_eager_position_zero_and_norm_only_agree(act):
+    """At position 0 cos is 1 and sin 0 in every type, so the eager rotation
+    returns the eager norm bit for bit; the eager norm of a row is the eager
+    row RMSNorm of it."""
+    x, w = _bf16_inputs((20, 4, 64), 95), _bf16_inputs((64,), 96, 1.0, 0.1)
+    zeros = np.zeros((1, 20), np.int32)
+    rot = oracle.qk_norm_rope(x, w, 1e-6, oracle.Rope("1d", 64, "neox", inv_freq=inv_freq_ladder(1e4, 64),
+                                                      positions=zeros), act, numerics="eager")
+    plain = oracle.qk_norm_rope(x, w, 1e-6, None, act, numerics="eager")
+    assert np.array_equal(rot, plain)
+    rows = oracle.rms_norm(x.reshape(-1, 64), w, 1e-6, act, numerics="eager")
+    assert np.array_equal(plain.reshape(-1, 64), rows)
+
+
+def test_eager_numerics_carry_through_joint_cache_and_vit():
+    """The joint, cache-write and ViT entries apply the same eager rounding
+    points as the plain op on their rows."""
+    heads, d = 3, 128
+    txt = {k: _bf16_inputs((1, 5, heads, d), 97 + i) for i, k in enumerate("qkv")}
+    img = {k: _bf16_inputs((1, 7, heads, d), 100 + i) for i, k in enumerate("qkv")}
+    for st, k in ((txt, 103), (img, 105)):
+        st["q_weight"], st["k_weight"] = _bf16_inputs((d,), k, 1, 0.1), _bf16_inputs((d,), k + 1, 1, 0.1)
+    pos = _rng(107).integers(0, 64, (3, 12)).astype(np.int32)
+    inv = inv_freq_ladder(1e4, d)
+    rope = oracle.Rope("axes", d, "adjacent", inv_freq=inv, sections=(8, 28, 28, 0), positions=pos)
+    q, k, _ = oracle.joint_qk_norm_rope(txt, img, 1e-6, rope, "bf16", numerics="eager")
+    ri = oracle.Rope("axes", d, "adjacent", inv_freq=inv, sections=(8, 28, 28, 0), positions=pos, token_base=5)
+    assert np.array_equal(q[0, 5:], oracle.qk_norm_rope(img["q"][0], img["q_weight"], 1e-6, ri, "bf16",
+                                                        numerics="eager"))
+    slots = np.arange(5, dtype=np.int64)[::-1].copy()
+    r1 = oracle.Rope("1d", d, "neox", inv_freq=inv, positions=pos[:1])
+    qo, kc, _ = oracle.qk_norm_rope_cache(txt["q"][0], txt["k"][0], None, txt["q_weight"], txt["k_weight"], 1e-6,
+                                          r1, slots, np.zeros((5, heads, d), np.float32), None, "bf16",
+                                          numerics="eager")
+    ek = oracle.qk_norm_rope(txt["k"][0], txt["k_weight"], 1e-6, r1, "bf16", numerics="eager")
+    assert np.array_equal(kc, ek[::-1])
+    grids = [[1, 4, 4]]
+    vx = _bf16_inputs((16, 2, 80), 108)
+    vw = _bf16_inputs((80,), 109, 1, 0.1)
+    it, ih, iw = inv_freq_ladder(1e4, 16), inv_freq_ladder(1e4, 32), inv_freq_ladder(1e4, 32)
+    fused = oracle.vit_qk_norm_rope(vx, vw, 1e-6, it, ih, iw, grids, 2, numerics="eager")
+    vpos = oracle.vit_positions(grids, 2)
+    ra = oracle.Rope("axes", 80, "neox", inv_freq=np.concatenate([it, ih, iw]), sections=(8, 16, 16, 0),
+                     positions=vpos)
+    assert np.array_equal(fused, oracle.qk_norm_rope(vx, vw, 1e-6, ra, "bf16", numerics="eager"))
