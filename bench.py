@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the fused QK RMSNorm + RoPE hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload joint|joint-neox|imrope|vit|vit-fused|rows1|rows32|
-                                                 rows4096|addrms4096|addrms4096-fp8|addrms1|cache|tiny|copy]
+    python bench.py [--steps K] [--warmup W] [--numerics contract|eager]
+                    [--workload joint|joint-neox|imrope|vit|vit-fused|rows1|rows32|rows4096|
+                                addrms4096|addrms4096-fp8|addrms1|cache|tiny|copy]
 
 Prints one JSON line.  A step is one pass of the workload's hot path over one
 batch of synthetic input already resident in HBM (default workload: the joint
@@ -11,14 +12,20 @@ tokens, 24 heads x 128, bf16; one launch per step).  Consecutive steps rotate
 over several input/output buffer sets whose total exceeds the 256 MB
 last-level (Infinity) cache, so every step streams from HBM.
 
-value   = algorithmic bytes per step / time per step (GB/s), whole job.
+value   = algorithmic bytes per step / time per step (GB/s), whole job, over
+          exactly K steps bracketed by HIP events on the stream the kernels
+          run on (replays of captured graphs, launches back to back).
+gpu_samples: the same K steps cut into at least six samples at graph-replay
+          boundaries, each event-timed: median, minimum and maximum per step.
 roofline.achieved = algorithmic bytes per launch of the dominant kernel /
-          its average launch duration: HIP events recorded on the stream the
-          kernels run on bracket the timed region (exactly K steps replayed
-          from captured graphs, launches back to back), divided by the
-          launches it holds.
-cpu_baseline: the CPU oracle on a bounded sample of the same workload, on
-          the host cores (single-threaded C).
+          its average launch duration over the K steps.
+cpu_baseline: the CPU oracle (plain C, double precision) on the same step,
+          once on all the host cores the process may use (the step's rows
+          split into one contiguous part per thread; the oracle releases the
+          interpreter lock while it runs) and once on one thread; median of 5
+          repetitions each; `value` is the all-cores leg.
+--numerics eager times the eager-chain rounding points instead of the
+          contract (the preset's cost).
 """
 import argparse
 import json
@@ -34,6 +41,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20         # MI355X Infinity Cache
 METRIC = "fused QK-norm+RoPE µs/call and achieved HBM GB/s (% of peak), 1 MI355X"
+GPU_SAMPLES = 6                # event-timed samples of the K steps
+CPU_REPS = 5                   # repetitions of each CPU leg (median)
+CPU_MAX_THREADS = 16           # the host share of one GPU
+
+NUMERICS = "contract"          # set from --numerics before any workload is built
 
 
 def _parse():
@@ -44,8 +56,11 @@ def _parse():
     ap.add_argument("--workload", default="joint",
                     choices=["joint", "joint-neox", "imrope", "vit", "vit-fused", "rows1", "rows32", "rows4096",
                              "addrms4096", "addrms4096-fp8", "addrms1", "cache", "tiny", "copy"])
+    ap.add_argument("--numerics", default="contract", choices=["contract", "eager"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the cache)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=60.0,
+                    help="budget of the CPU oracle legs (0: skip): each leg repeats the step 5 times, or "
+                         "3 times once its share of the budget is spent")
     ap.add_argument("--variant", default=None,
                     help="comma-separated kernel variant overrides (qkr_set_variant_override)")
     ap.add_argument("--eager", action="store_true",
@@ -53,10 +68,18 @@ def _parse():
     return ap.parse_args()
 
 
+def shard_ranges(total, n):
+    """n contiguous [a, b) parts of range(total), sizes differing by at most one."""
+    n = max(1, min(n, total))
+    cuts = [total * i // n for i in range(n + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(n)]
+
+
 class Workload:
-    """name, description, bytes per step, dominant-kernel bytes per launch,
+    """name, config, bytes per step, dominant-kernel bytes per launch,
     launches of it per step, make_set() -> state, step(state) launches the
-    path, cpu_step() runs the oracle on one step's input."""
+    path; cpu_parts(n) -> (n callables that together run the oracle on one
+    step's input, share of the step they cover), each on its own rows."""
 
 
 def build_joint(pairing):
@@ -86,25 +109,26 @@ def build_joint(pairing):
 
     def step(state):
         g, outs = state
-        qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope, out=outs)
+        qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope, out=outs, numerics=NUMERICS)
 
     qkv_bytes = joint * 3 * H * D * 2
     nbytes = 2 * qkv_bytes + case.positions.nbytes + 4 * D * 2 + case.inv_freq.nbytes
 
-    def cpu_step():
+    def cpu_parts(n):
         import oracle
 
-        def stream(s):
-            return {"q": W.as_f32(s.view(0, H, D)), "k": W.as_f32(s.view(1, H, D)), "v": W.as_f32(s.view(2, H, D)),
-                    "q_weight": W.as_f32(s.q_weight), "k_weight": W.as_f32(s.k_weight)}
-
-        tx, im = stream(case.text), stream(case.image)
         orope = oracle.Rope("axes", D, pairing, inv_freq=case.inv_freq, sections=case.sections,
                             positions=case.positions)
 
-        def run():
-            oracle.joint_qk_norm_rope(tx, im, case.eps, orope, "bf16")
-        return run
+        def stream(s, h0, h1):
+            return {"q": W.as_f32(s.view(0, H, D)[:, :, h0:h1]), "k": W.as_f32(s.view(1, H, D)[:, :, h0:h1]),
+                    "v": W.as_f32(s.view(2, H, D)[:, :, h0:h1]), "q_weight": W.as_f32(s.q_weight),
+                    "k_weight": W.as_f32(s.k_weight)}
+
+        def part(h0, h1):
+            tx, im = stream(case.text, h0, h1), stream(case.image, h0, h1)
+            return lambda: oracle.joint_qk_norm_rope(tx, im, case.eps, orope, "bf16", numerics=NUMERICS)
+        return [part(a, b) for a, b in shard_ranges(H, n)], 1.0
 
     w = Workload()
     w.name = f"joint text/image QK RMSNorm + cat + 3-axis RoPE ({pairing})"
@@ -113,9 +137,9 @@ def build_joint(pairing):
     w.step_bytes = nbytes
     w.launch_bytes = nbytes
     w.launches = 1
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "bf16"
-    w.sample = "the full joint step (512 text + 4096 image tokens, Q/K/V)"
+    w.sample = "the full joint step (512 text + 4096 image tokens, Q/K/V), split over heads"
     return w
 
 
@@ -143,21 +167,25 @@ def build_imrope():
         for r in ropes:
             b = r.token_base
             qkr.qk_norm_rope(q[b:b + chunk], k[b:b + chunk], qw, kw, case.eps, r, q_out=qo[b:b + chunk],
-                             k_out=ko[b:b + chunk])
+                             k_out=ko[b:b + chunk], numerics=NUMERICS)
 
     rows = case.q.shape[1] + case.k.shape[1]
     chunk_bytes = 2 * chunk * rows * 128 * 2 + 4 * chunk * 4 + 2 * 128 * 2 + case.inv_freq.nbytes
 
-    def cpu_step():
+    def cpu_parts(n):
         import oracle
         qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
-        orope = oracle.Rope("imrope", 128, "neox", inv_freq=case.inv_freq, sections=case.sections,
-                            positions=case.positions)
 
-        def run():
-            oracle.qk_norm_rope(qf, wq, case.eps, orope)
-            oracle.qk_norm_rope(kf, wk, case.eps, orope)
-        return run
+        def part(t0, t1):
+            orope = oracle.Rope("imrope", 128, "neox", inv_freq=case.inv_freq, sections=case.sections,
+                                positions=case.positions, token_base=t0)
+            q, k = qf[t0:t1], kf[t0:t1]
+
+            def run():
+                oracle.qk_norm_rope(q, wq, case.eps, orope, numerics=NUMERICS)
+                oracle.qk_norm_rope(k, wk, case.eps, orope, numerics=NUMERICS)
+            return run
+        return [part(a, b) for a, b in shard_ranges(T, n)], 1.0
 
     w = Workload()
     w.name = "IMROPE after per-head QK RMSNorm, 2048-token chunks"
@@ -166,9 +194,9 @@ def build_imrope():
     w.step_bytes = chunk_bytes * (T // chunk)
     w.launch_bytes = chunk_bytes
     w.launches = T // chunk
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "bf16"
-    w.sample = "all 8192 tokens (4 chunks), Q and K"
+    w.sample = "all 8192 tokens, Q and K, split over tokens"
     return w
 
 
@@ -195,22 +223,43 @@ def build_vit():
         q, k, qo, ko, cos, sin = state
         qkr.mrope_cos_sin_setup(*inv, case.grid_thw, case.merge, out=(cos, sin))
         rope = qkr.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=cos, sin_planes=sin)
-        qkr.qk_norm_rope(q, k, qw, kw, case.eps, rope, q_out=qo, k_out=ko)
+        qkr.qk_norm_rope(q, k, qw, kw, case.eps, rope, q_out=qo, k_out=ko, numerics=NUMERICS)
 
     heads = case.q.shape[1]
     planes = 2 * n * half * 4
     apply_bytes = 4 * n * heads * 2 * half * 2 + planes + 2 * 2 * half * 2
 
-    def cpu_step():
+    def cpu_parts(nparts):
+        import threading
+
         import oracle
         qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
+        planes = {}
 
-        def run():
-            c, s = oracle.vit_cos_sin(case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
-            orope = oracle.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=c, sin_planes=s)
-            oracle.qk_norm_rope(qf, wq, case.eps, orope)
-            oracle.qk_norm_rope(kf, wk, case.eps, orope)
-        return run
+        def part(i, t0, t1):
+            q, k = qf[t0:t1], kf[t0:t1]
+
+            def run():
+                # the planes are the setup's output: part 0 computes them for
+                # the whole step, the other parts apply them once they exist
+                if i == 0:
+                    planes["cs"] = oracle.vit_cos_sin(case.inv_t, case.inv_h, case.inv_w, case.grid_thw,
+                                                      case.merge)
+                    planes["ready"].set()
+                else:
+                    planes["ready"].wait()
+                c, s = planes["cs"]
+                orope = oracle.Rope("planes", 2 * half, "neox", sections=secs, cos_planes=c, sin_planes=s,
+                                    token_base=t0)
+                oracle.qk_norm_rope(q, wq, case.eps, orope, numerics=NUMERICS)
+                oracle.qk_norm_rope(k, wk, case.eps, orope, numerics=NUMERICS)
+            return run
+
+        def reset():
+            planes["ready"] = threading.Event()
+        reset()
+        w.cpu_reset = reset
+        return [part(i, a, b) for i, (a, b) in enumerate(shard_ranges(n, nparts))], 1.0
 
     w = Workload()
     w.name = "ViT mrope cos/sin setup + apply after per-head QK RMSNorm"
@@ -219,9 +268,9 @@ def build_vit():
     w.step_bytes = planes + apply_bytes
     w.launch_bytes = apply_bytes
     w.launches = 1
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "bf16"
-    w.sample = "setup + apply over all 7952 tokens"
+    w.sample = "setup + apply over all 7952 tokens, the apply split over tokens"
     return w
 
 
@@ -244,19 +293,26 @@ def build_vit_fused():
 
     def step(state):
         q, k, qo, ko = state
-        qkr.vit_qk_norm_rope(q, k, qw, kw, case.eps, *inv, case.grid_thw, case.merge, q_out=qo, k_out=ko)
+        qkr.vit_qk_norm_rope(q, k, qw, kw, case.eps, *inv, case.grid_thw, case.merge, q_out=qo, k_out=ko,
+                             numerics=NUMERICS)
 
     heads = case.q.shape[1]
     nbytes = 4 * n * heads * 2 * half * 2 + 2 * 2 * half * 2 + 4 * half
 
-    def cpu_step():
+    def cpu_parts(nparts):
         import oracle
         qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
 
-        def run():
-            oracle.vit_qk_norm_rope(qf, wq, case.eps, case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
-            oracle.vit_qk_norm_rope(kf, wk, case.eps, case.inv_t, case.inv_h, case.inv_w, case.grid_thw, case.merge)
-        return run
+        def part(h0, h1):
+            q, k = np.ascontiguousarray(qf[:, h0:h1]), np.ascontiguousarray(kf[:, h0:h1])
+
+            def run():
+                oracle.vit_qk_norm_rope(q, wq, case.eps, case.inv_t, case.inv_h, case.inv_w, case.grid_thw,
+                                        case.merge, numerics=NUMERICS)
+                oracle.vit_qk_norm_rope(k, wk, case.eps, case.inv_t, case.inv_h, case.inv_w, case.grid_thw,
+                                        case.merge, numerics=NUMERICS)
+            return run
+        return [part(a, b) for a, b in shard_ranges(heads, nparts)], 1.0
 
     w = Workload()
     w.name = "ViT QK RMSNorm + mrope with positions from the grids (setup folded in)"
@@ -264,9 +320,9 @@ def build_vit_fused():
                 "heads": heads, "head_dim": 2 * half, "halves": [case.inv_t.size, case.inv_h.size, case.inv_w.size]}
     w.step_bytes = w.launch_bytes = nbytes
     w.launches = 1
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "bf16"
-    w.sample = "all 7952 tokens, Q and K"
+    w.sample = "all 7952 tokens, Q and K, split over heads"
     return w
 
 
@@ -286,27 +342,28 @@ def build_rows(t):
 
     def step(state):
         x, y = state
-        qkr.rms_norm(x, wgt, case.eps, out=y)
+        qkr.rms_norm(x, wgt, case.eps, out=y, numerics=NUMERICS)
 
     width = case.x.shape[1]
     nbytes = 2 * t * width * 2 + width * 2
 
-    def cpu_step():
+    def cpu_parts(n):
         import oracle
         xf, wf = W.as_f32(case.x), W.as_f32(case.weight)
 
-        def run():
-            oracle.rms_norm(xf, wf, case.eps, "bf16")
-        return run
+        def part(r0, r1):
+            x = xf[r0:r1]
+            return lambda: oracle.rms_norm(x, wf, case.eps, "bf16", numerics=NUMERICS)
+        return [part(a, b) for a, b in shard_ranges(t, n)], 1.0
 
     w = Workload()
     w.name = f"plain row RMSNorm bf16 [{t}, {width}]"
     w.config = {"workload": w.name, "rows": t, "width": width, "eps": case.eps}
     w.step_bytes = w.launch_bytes = nbytes
     w.launches = 1
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "bf16"
-    w.sample = f"the full [{t}, {width}] input"
+    w.sample = f"the full [{t}, {width}] input, split over rows"
     return w
 
 
@@ -338,22 +395,30 @@ def build_cache():
 
     def step(state):
         q, k, v, kc, vc, qo = state
-        qkr.qk_norm_rope_cache(q, k, v, qw, kw, kc, vc, slots, case.eps, rope, q_out=qo)
+        qkr.qk_norm_rope_cache(q, k, v, qw, kw, kc, vc, slots, case.eps, rope, q_out=qo, numerics=NUMERICS)
 
     nbytes = 2 * T * (H + 2 * KV) * D * 2 + T * 8 + case.positions.nbytes + 2 * D * 2 + case.inv_freq.nbytes
 
-    def cpu_step():
+    def cpu_parts(n):
         import oracle
-        orope = oracle.Rope("imrope", D, "neox", inv_freq=case.inv_freq, positions=case.positions,
-                            sections=case.sections)
         q, k, v = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(v_host)
         wq, wk = W.as_f32(case.q_weight), W.as_f32(case.k_weight)
-        kc0 = np.zeros((blocks * bs, KV, D), np.float32)
         sl = slots_host.numpy()
+        orope = oracle.Rope("imrope", D, "neox", inv_freq=case.inv_freq, positions=case.positions,
+                            sections=case.sections)
+        n = max(1, min(n, H))
 
-        def run():
-            oracle.qk_norm_rope_cache(q, k, v, wq, wk, case.eps, orope, sl, kc0, kc0)
-        return run
+        def part(qh, kh):
+            # Q heads [qh) and K/V heads [kh) of every token; the part's cache
+            # holds its own K/V heads of every slot
+            qs = np.ascontiguousarray(q[:, qh[0]:qh[1]])
+            ks, vs = np.ascontiguousarray(k[:, kh[0]:kh[1]]), np.ascontiguousarray(v[:, kh[0]:kh[1]])
+            cache = np.zeros((blocks * bs, kh[1] - kh[0], D), np.float32)
+            return lambda: oracle.qk_norm_rope_cache(qs, ks, vs, wq, wk, case.eps, orope, sl, cache, cache,
+                                                     numerics=NUMERICS)
+        qparts = [(H * i // n, H * (i + 1) // n) for i in range(n)]
+        kparts = [(KV * i // n, KV * (i + 1) // n) for i in range(n)]
+        return [part(a, b) for a, b in zip(qparts, kparts)], 1.0
 
     w = Workload()
     w.name = "IMROPE QK RMSNorm + RoPE with K/V written into a paged cache by slot mapping"
@@ -361,9 +426,9 @@ def build_cache():
                 "sections": list(case.sections), "cache_blocks": blocks, "block_size": bs}
     w.step_bytes = w.launch_bytes = nbytes
     w.launches = 1
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "bf16"
-    w.sample = "all 8192 tokens"
+    w.sample = "all 8192 tokens, split over heads"
     return w
 
 
@@ -388,27 +453,29 @@ def build_addrms(t, fp8):
     def step(state):
         x, r, s_out, y = state
         qkr.add_rms_norm(x, wgt, case.eps, residual=r, residual_out=s_out, out_dtype="fp8_e4m3" if fp8 else None,
-                         scale=scale, out=y)
+                         scale=scale, out=y, numerics=NUMERICS)
 
     width = case.x.shape[1]
     nbytes = t * width * (2 + 2 + 2 + (1 if fp8 else 2)) + width * 2 + (4 if fp8 else 0)
 
-    def cpu_step():
+    def cpu_parts(n):
         import oracle
         xf, rf, wf = W.as_f32(case.x), W.as_f32(res), W.as_f32(case.weight)
 
-        def run():
-            oracle.add_rms_norm(xf, wf, case.eps, rf, "bf16", "fp8_e4m3" if fp8 else "bf16", 0.02)
-        return run
+        def part(r0, r1):
+            x, r = xf[r0:r1], rf[r0:r1]
+            return lambda: oracle.add_rms_norm(x, wf, case.eps, r, "bf16", "fp8_e4m3" if fp8 else "bf16", 0.02,
+                                               numerics=NUMERICS)
+        return [part(a, b) for a, b in shard_ranges(t, n)], 1.0
 
     w = Workload()
     w.name = f"residual add + RMSNorm bf16 [{t}, {width}] -> {'FP8 E4M3 (static scale)' if fp8 else 'bf16'}"
     w.config = {"workload": w.name, "rows": t, "width": width, "eps": case.eps, "out": "fp8_e4m3" if fp8 else "bf16"}
     w.step_bytes = w.launch_bytes = nbytes
     w.launches = 1
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "bf16"
-    w.sample = f"the full [{t}, {width}] input"
+    w.sample = f"the full [{t}, {width}] input, split over rows"
     return w
 
 
@@ -430,33 +497,29 @@ def build_tiny():
 
     def step(state):
         q, k, qo, ko = state
-        qkr.qk_norm_rope(q, k, ws[0], ws[1], case.eps, rope, q_out=qo, k_out=ko)
+        qkr.qk_norm_rope(q, k, ws[0], ws[1], case.eps, rope, q_out=qo, k_out=ko, numerics=NUMERICS)
 
-    nbytes = 2 * 2 * q_numel(case) * 4 + 2 * 64 * 4 + 4 * 4 + 32 * 4
+    nbytes = 2 * 2 * case.q.numel() * 4 + 2 * 64 * 4 + 4 * 4 + 32 * 4
 
-    def cpu_step():
+    def cpu_parts(n):
         import oracle
         orope = oracle.Rope("1d", 64, "neox", inv_freq=case.inv_freq, positions=case.positions)
         qf, kf, wq, wk = W.as_f32(case.q), W.as_f32(case.k), W.as_f32(case.q_weight), W.as_f32(case.k_weight)
 
         def run():
-            oracle.qk_norm_rope(qf, wq, case.eps, orope, "f32")
-            oracle.qk_norm_rope(kf, wk, case.eps, orope, "f32")
-        return run
+            oracle.qk_norm_rope(qf, wq, case.eps, orope, "f32", numerics=NUMERICS)
+            oracle.qk_norm_rope(kf, wk, case.eps, orope, "f32", numerics=NUMERICS)
+        return [run], 1.0
 
     w = Workload()
     w.name = "tiny fp32 QK RMSNorm + NeoX RoPE [4, 2, 64]"
     w.config = {"workload": w.name, "tokens": 4, "heads": 2, "head_dim": 64}
     w.step_bytes = w.launch_bytes = nbytes
     w.launches = 1
-    w.make_set, w.step, w.cpu_step = make_set, step, cpu_step
+    w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
     w.dtype = "f32"
-    w.sample = "the full [4, 2, 64] input"
+    w.sample = "the full [4, 2, 64] input (too small to split)"
     return w
-
-
-def q_numel(case):
-    return case.q.numel()
 
 
 def build_copy():
@@ -481,7 +544,7 @@ def build_copy():
     w.step_bytes = w.launch_bytes = 2 * nbytes
     w.launches = 1
     w.make_set, w.step = make_set, step
-    w.cpu_step = None
+    w.cpu_parts = None
     w.dtype = "f32"
     w.sample = "none"
     return w
@@ -530,23 +593,80 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(w, seconds):
-    run = w.cpu_step()
-    run()   # warm (page in, first-touch)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        run()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_threads():
+    """Threads the all-cores leg uses: the cores this process may run on,
+    at most the host share of one GPU (OMP_NUM_THREADS where it is set)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, CPU_MAX_THREADS))
+
+
+def _time_leg(w, nthreads, budget):
+    """Median, minimum and maximum seconds per step over CPU_REPS repetitions
+    of one step split into nthreads parts run on as many threads."""
+    import concurrent.futures
+    parts, share = w.cpu_parts(nthreads)
+    reset = getattr(w, "cpu_reset", None)
+
+    def one():
+        if reset is not None:
+            reset()
+        t0 = time.perf_counter()
+        if len(parts) == 1:
+            parts[0]()
+        else:
+            with concurrent.futures.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+                for f in [ex.submit(p) for p in parts]:
+                    f.result()
+        return time.perf_counter() - t0
+
+    one()                                   # warm: page in, first touch
+    times = []
+    t_start = time.perf_counter()
+    for _ in range(CPU_REPS):
+        times.append(one())
+        if time.perf_counter() - t_start > budget and len(times) >= 3:
             break
-    gbs = w.step_bytes * reps / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_step": round(el / reps * 1e6, 1),
-            "sample": f"{reps} x {w.sample}, single-threaded C oracle"}
+    times.sort()
+    return {"threads": len(parts), "reps": len(times), "s_median": times[len(times) // 2] / share,
+            "s_min": times[0] / share, "s_max": times[-1] / share}
+
+
+def cpu_baseline(w, seconds):
+    """The oracle on the host cores: an all-cores leg and a one-thread leg."""
+    nthreads = host_threads()
+    legs = {}
+    for name, n, budget in (("all_cores", nthreads, seconds * 0.3), ("one_thread", 1, seconds * 0.7)):
+        leg = _time_leg(w, n, budget)
+        legs[name] = {"threads": leg["threads"], "reps": leg["reps"],
+                      "us_per_step_median": round(leg["s_median"] * 1e6, 1),
+                      "us_per_step_min": round(leg["s_min"] * 1e6, 1),
+                      "us_per_step_max": round(leg["s_max"] * 1e6, 1),
+                      "GB/s": round(w.step_bytes / leg["s_median"] / 1e9, 4)}
+    main_leg = legs["all_cores"]
+    return {"value": main_leg["GB/s"], "unit": "GB/s", "cores": main_leg["threads"], "kind": "oracle",
+            "sample": f"median of {main_leg['reps']} repetitions of {w.sample} (plain C oracle, double "
+                      f"precision, one part per thread), numerics {NUMERICS}",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "legs": legs}
 
 
 def main():
+    global NUMERICS
     args = _parse()
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only: every row of the path is per-row "
@@ -555,6 +675,7 @@ def main():
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: one process, one GPU; WORLD_SIZE > 1 is not supported", file=sys.stderr)
         sys.exit(2)
+    NUMERICS = args.numerics
 
     import torch
 
@@ -579,25 +700,19 @@ def main():
     torch.cuda.synchronize()
     variant = qkr.last_variant()
 
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    K = args.steps
     if args.eager:
-        K = args.steps
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for i in range(K):
-            w.step(sets[i % nsets])
-        t_end.record(stream)
+        plan = [1] * K
     else:
         # Exactly K steps cycling over the buffer sets, captured in graphs of
-        # up to 1024 kernel launches (plus one graph for the remainder);
-        # replaying a graph runs its launches back to back with no host work
-        # in between.  Each replay boundary costs several microseconds of idle
-        # GPU, so the graphs are long; a single graph of 4096 launches measured
-        # slower per launch (IMROPE chunk 6.39 us against 5.93-5.97 us with
-        # 200 to 2000 launches split over graphs of up to 1024).
-        K = args.steps
-        chunk = max(1, min(K, 1024 // w.launches))
+        # at most 1024 kernel launches and at most K / GPU_SAMPLES steps, so
+        # the timed region holds at least GPU_SAMPLES replays; replaying a
+        # graph runs its launches back to back with no host work in between.
+        # Each replay boundary costs several microseconds of idle GPU, so the
+        # graphs stay long; a single graph of 4096 launches measured slower
+        # per launch (IMROPE chunk 6.39 us against 5.93-5.97 us with 200 to
+        # 2000 launches split over graphs of up to 1024).
+        chunk = max(1, min(-(-K // GPU_SAMPLES), 1024 // w.launches))
         plan = [chunk] * (K // chunk) + ([K % chunk] if K % chunk else [])
         graphs = {}
         for n in sorted(set(plan)):
@@ -609,12 +724,26 @@ def main():
             graphs[n] = g
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        t_start.record(stream)
-        for n in plan:
-            graphs[n].replay()
-        t_end.record(stream)
+    # Sample boundaries at replay (or eager step) boundaries: GPU_SAMPLES
+    # groups of consecutive replays, as even as the plan allows.
+    nsamp = min(GPU_SAMPLES, len(plan))
+    cuts = [len(plan) * i // nsamp for i in range(nsamp + 1)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(nsamp + 1)]
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    events[0].record(stream)
+    step_i = 0
+    for s in range(nsamp):
+        for j in range(cuts[s], cuts[s + 1]):
+            if args.eager:
+                w.step(sets[step_i % nsets])
+                step_i += 1
+            else:
+                graphs[plan[j]].replay()
+        events[s + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = events[0].elapsed_time(events[-1])
+    sample_us = sorted(events[s].elapsed_time(events[s + 1]) * 1e3 / sum(plan[cuts[s]:cuts[s + 1]])
+                       for s in range(nsamp))
     ms_per_step = total_ms / K
     launch_us = ms_per_step * 1e3 / w.launches
 
@@ -636,12 +765,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded, workloads.py)",
         "config": dict(w.config, buffer_sets=nsets, variant=variant, bytes_per_step=w.step_bytes,
-                       launch="eager" if args.eager else "hipGraph replay"),
+                       numerics=NUMERICS, launch="eager" if args.eager else "hipGraph replay"),
+        "gpu_samples": {"n": nsamp, "us_per_step_median": round(sample_us[len(sample_us) // 2], 3),
+                        "us_per_step_min": round(sample_us[0], 3), "us_per_step_max": round(sample_us[-1], 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload) if NUMERICS == "contract" else None,
                      "bytes_per_launch": w.launch_bytes, "kernel": variant},
     }
-    if args.cpu_seconds > 0 and w.cpu_step is not None:
+    if args.cpu_seconds > 0 and w.cpu_parts is not None:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -63,6 +63,27 @@ typedef enum {
 
 typedef enum { QKR_F32 = 0, QKR_BF16 = 1 } qkr_dtype;
 
+/* Rounding points, OR-ed into the dtype argument of every entry point that
+ * takes one (dtype = QKR_BF16 | QKR_NUMERICS_EAGER):
+ *   QKR_NUMERICS_CONTRACT (the default): the normalised value, weight
+ *     included, rounded once to the activation type; the rotation in fp32;
+ *     one final rounding ([Ovis] kernel review: the documented rounding
+ *     contract).  qkr_rms_norm: one rounding of x * rrms * w.
+ *   QKR_NUMERICS_EAGER: the rounding points of an eager RMSNorm + RoPE chain
+ *     ([Ovis] "Supplemental eager bitwise measurements": a preset that turns
+ *     floating-point fusion off and reproduced such a chain bit for bit;
+ *     [VecRMS] review thread: that chain's RMSNorm output expression
+ *     ((scalar_t)(x * s_variance)) * weight): x * rrms rounded to the
+ *     activation type, times the weight, rounded again; cos and sin computed
+ *     in fp32 and rounded to the activation type (the chain's RoPE table);
+ *     every product and sum of the rotation rounded to fp32 on its own (no
+ *     fused multiply-add); one final rounding.  It fixes the rounding points
+ *     only: the sum of squares and the reciprocal square root stay this
+ *     library's, so bit-for-bit equality with another library's chain is not
+ *     promised.  Not defined for FP8 outputs (QKR_ERR_UNSUPPORTED).
+ * Any other bit above the low byte is refused (QKR_ERR_INVALID_ARGUMENT). */
+typedef enum { QKR_NUMERICS_CONTRACT = 0, QKR_NUMERICS_EAGER = 0x100 } qkr_numerics;
+
 /* Rotary pairing.  NEOX pairs element p with p + R/2 ([IMROPE]: the sectioned
  * mode keeps the NeoX pairing); ADJACENT pairs 2p with 2p + 1 ([Ovis]:
  * interleaved=True). */

@@ -57,6 +57,8 @@ def rms(x=FAKE, xs=5120, y=FAKE, ys=5120, w=FAKE, rows=4, width=5120, eps=1e-6, 
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(dtype=7), INVALID),
+    (dict(dtype=qkr.BF16 | 0x200), INVALID),                            # unknown numerics bits
+    (dict(dtype=qkr.BF16 | 0x10000), INVALID),
     (dict(eps=-1.0), INVALID),
     (dict(eps=float("nan")), INVALID),
     (dict(width=0), INVALID),
@@ -100,6 +102,8 @@ def addrms(x=XA, xs=5120, r=RA, rs=5120, s=RA, ss=5120, y=YA, ys=5120, kind=0, s
     (dict(s=RA, ss=6144), INVALID), (dict(ys=5000), MISALIGNED), (dict(xs=5124), MISALIGNED),
     (dict(kind=1, scale=FAKE, y=YA + 4), MISALIGNED), (dict(kind=1, scale=FAKE + 2), MISALIGNED),
     (dict(kind=1, scale=FAKE, ys=5124), MISALIGNED), (dict(width=16 * 256 * 8 + 8), UNSUPPORTED),
+    (dict(kind=1, scale=FAKE, dtype=qkr.BF16 | qkr.NUMERICS["eager"]), UNSUPPORTED),   # FP8 has no eager chain
+    (dict(dtype=qkr.F32 | 0x300), INVALID),
 ])
 def test_add_rms_norm_refusals(kwargs, code):
     assert addrms(**kwargs) == code
@@ -151,6 +155,8 @@ def qknr(batch=1, tokens=2048, head_dim=128, dtype=qkr.BF16, eps=1e-6, q=None, q
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(dtype=3), INVALID),
+    (dict(dtype=qkr.NUMERICS["eager"] | 2), INVALID),
+    (dict(dtype=qkr.BF16 | 0x400), INVALID),
     (dict(head_dim=0), INVALID),
     (dict(head_dim=512), INVALID),
     (dict(head_dim=100), MISALIGNED),                                 # 200 B rows

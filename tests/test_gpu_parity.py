@@ -1098,3 +1098,153 @@ def test_graph_capture_of_cache_write_and_residual_add():
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
         run(*fresh())                                          # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Eager numerics: the rounding points of an eager RMSNorm + RoPE chain
+# ([Ovis] "Supplemental eager bitwise measurements"; [VecRMS] review thread)
+# ---------------------------------------------------------------------------
+
+def _differs(a, b):
+    return float(np.mean(np.asarray(a) != np.asarray(b)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("t,variant", [(1, None), (37, "rms:rows"), (37, "rms:wide"), (37, "rms:split"),
+                                       (4096, None)])
+def test_eager_rms_norm(dtype, t, variant):
+    case = W.rows(t, width=5120 if dtype == "bf16" else 2560, dtype=dtype, seed_stream=300 + t)
+    qkr.set_variant_override(variant)
+    try:
+        y = qkr.rms_norm(gpu(case.x), gpu(case.weight), case.eps, numerics="eager")
+        name = qkr.last_variant()
+    finally:
+        qkr.set_variant_override(None)
+    assert name.endswith(":eager") and (variant is None or name.startswith(variant + ":")), name
+    ref = oracle.rms_norm(W.as_f32(case.x), W.as_f32(case.weight), case.eps, dtype, numerics="eager")
+    check(host(y), ref, dtype, what=f"eager rms {name}")
+    if dtype == "bf16" and t > 1:
+        contract = qkr.rms_norm(gpu(case.x), gpu(case.weight), case.eps)
+        assert _differs(host(y), host(contract)) > 0.05      # a different rounding chain, really taken
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_eager_add_rms_norm(act):
+    x, r, w = _addrms_case(300, 5120, act, 77)
+    gr = gpu(r)
+    y, s = qkr.add_rms_norm(gpu(x), gpu(w), 1e-6, residual=gr, numerics="eager")
+    assert qkr.last_variant().endswith(":add:eager"), qkr.last_variant()
+    rs, ry = oracle.add_rms_norm(W.as_f32(x), W.as_f32(w), 1e-6, W.as_f32(r), act, act, numerics="eager")
+    assert np.array_equal(host(s), rs)
+    check(host(y), ry, act, what="eager add_rms_norm")
+    with pytest.raises(qkr.QkrError, match="UNSUPPORTED"):
+        qkr.add_rms_norm(gpu(x), gpu(w), 1e-6, out_dtype="fp8_e4m3",
+                         scale=gpu(torch.tensor([0.02], dtype=torch.float32)), numerics="eager")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("head_dim,pairing", [(128, "neox"), (128, "adjacent"), (64, "neox"), (80, "adjacent")])
+def test_eager_qk_norm_rope_1d(dtype, head_dim, pairing):
+    case = W.tiny(tokens=61, heads=7, head_dim=head_dim, dtype=dtype, seed_stream=400 + head_dim)
+    pos = np.random.default_rng(head_dim + 4).integers(0, 8192, (1, 61)).astype(np.int32)
+    inv = W.inv_freq_ladder(1e4, head_dim)
+    rope = qkr.Rope("1d", head_dim, pairing, inv_freq=gpu(torch.from_numpy(inv)), positions=gpu(torch.from_numpy(pos)))
+    qo, ko = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope,
+                              numerics="eager")
+    assert qkr.last_variant().endswith(":eager"), qkr.last_variant()
+    orope = oracle.Rope("1d", head_dim, pairing, inv_freq=inv, positions=pos)
+    for got, x, w, nm in ((qo, case.q, case.q_weight, "q"), (ko, case.k, case.k_weight, "k")):
+        ref = oracle.qk_norm_rope(W.as_f32(x), W.as_f32(w), case.eps, orope, dtype, numerics="eager")
+        check(host(got), ref, dtype, head_dim, pairing, f"eager {nm}")
+    if dtype == "bf16":
+        cq, _ = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+        assert _differs(host(qo), host(cq)) > 0.05
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_eager_rotation_is_unfused_bitwise(dtype):
+    """Rows of +-1 with eps = 0 normalise exactly (rrms = 1), and planes mode
+    hands every kernel the same cos/sin, so the eager output is fixed bit
+    for bit by its rounding points: each fp32 product and sum rounded on its
+    own.  With fp32 operands a fused multiply-add would change a visible
+    share of the results, as the contract path's output shows."""
+    tokens, heads, d = 300, 4, 128
+    rng = np.random.default_rng(500)
+    x = W.to_dtype(rng.choice([-1.0, 1.0], (tokens, heads, d)).astype(np.float32), dtype)
+    w = W.to_dtype(rng.normal(1.0, 0.3, d).astype(np.float32), dtype)
+    cosp = rng.uniform(-1, 1, (3, tokens, d // 2)).astype(np.float32)
+    sinp = rng.uniform(-1, 1, (3, tokens, d // 2)).astype(np.float32)
+    secs = (16, 24, 24, 0)
+    rope = qkr.Rope("planes", d, "neox", sections=secs, cos_planes=gpu(torch.from_numpy(cosp)),
+                    sin_planes=gpu(torch.from_numpy(sinp)))
+    eager, _ = qkr.qk_norm_rope(gpu(x), None, gpu(w), None, 0.0, rope, numerics="eager")
+    contract, _ = qkr.qk_norm_rope(gpu(x), None, gpu(w), None, 0.0, rope)
+    orope = oracle.Rope("planes", d, "neox", sections=secs, cos_planes=cosp, sin_planes=sinp)
+    ref = oracle.qk_norm_rope(W.as_f32(x), W.as_f32(w), 0.0, orope, dtype, numerics="eager")
+    assert np.array_equal(host(eager), ref)
+    if dtype == "f32":
+        assert _differs(host(contract), ref) > 0.01
+
+
+def test_eager_imrope_full_size_chunked():
+    case = W.imrope()
+    pos, inv = gpu(torch.from_numpy(case.positions)), gpu(torch.from_numpy(case.inv_freq))
+    q, k = gpu(case.q), gpu(case.k)
+    outs = []
+    for b in range(0, 8192, case.chunk):
+        rope = qkr.Rope("imrope", 128, "neox", inv_freq=inv, positions=pos, sections=case.sections, token_base=b)
+        outs.append(qkr.qk_norm_rope(q[b:b + case.chunk], k[b:b + case.chunk], gpu(case.q_weight),
+                                     gpu(case.k_weight), case.eps, rope, numerics="eager"))
+    orope = oracle.Rope("imrope", 128, "neox", inv_freq=case.inv_freq, sections=case.sections,
+                        positions=case.positions)
+    for i, (x, w, nm) in enumerate(((case.q, case.q_weight, "q"), (case.k, case.k_weight, "k"))):
+        got = torch.cat([o[i] for o in outs])
+        ref = oracle.qk_norm_rope(W.as_f32(x), W.as_f32(w), case.eps, orope, "bf16", numerics="eager")
+        assert_bf16_close(host(got), ref, 128, "neox", f"eager imrope {nm}")
+
+
+@pytest.mark.parametrize("pairing", ["adjacent", "neox"])
+def test_eager_joint_full_size(pairing):
+    case = W.joint()
+    g, rope = joint_gpu(case, pairing)
+    q, k, v = qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope, numerics="eager")
+    hd = case.head_dim
+
+    def stream(s):
+        return {"q": W.as_f32(s.view(0, case.heads, hd)), "k": W.as_f32(s.view(1, case.heads, hd)),
+                "v": W.as_f32(s.view(2, case.heads, hd)), "q_weight": W.as_f32(s.q_weight),
+                "k_weight": W.as_f32(s.k_weight)}
+
+    orope = oracle.Rope("axes", hd, pairing, inv_freq=case.inv_freq, sections=case.sections, positions=case.positions)
+    rq, rk, rv = oracle.joint_qk_norm_rope(stream(case.text), stream(case.image), case.eps, orope, "bf16",
+                                           numerics="eager")
+    assert_bf16_close(host(q), rq, 128, pairing, "eager joint q")
+    assert_bf16_close(host(k), rk, 128, pairing, "eager joint k")
+    assert np.array_equal(host(v), rv)
+
+
+def test_eager_vit_fused_and_cache_write():
+    case = W.vit()
+    inv = [gpu(torch.from_numpy(a)) for a in (case.inv_t, case.inv_h, case.inv_w)]
+    qo, ko = qkr.vit_qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, *inv,
+                                  case.grid_thw, case.merge, numerics="eager")
+    for got, x, w, nm in ((qo, case.q, case.q_weight, "q"), (ko, case.k, case.k_weight, "k")):
+        ref = oracle.vit_qk_norm_rope(W.as_f32(x), W.as_f32(w), case.eps, case.inv_t, case.inv_h, case.inv_w,
+                                      case.grid_thw, case.merge, numerics="eager")
+        assert_bf16_close(host(got), ref, 2 * case.half_rot, "neox", f"eager vit {nm}")
+    tokens, qh, kvh, d = 300, 16, 8, 128
+    cc, k, v, pos, inv1 = _cache_case(tokens, qh, kvh, d, "bf16", 501)
+    slots = np.random.default_rng(501).permutation(640)[:tokens].astype(np.int64)
+    kc = torch.zeros((640, kvh, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    rope = qkr.Rope("1d", d, "neox", inv_freq=gpu(torch.from_numpy(inv1)), positions=gpu(torch.from_numpy(pos)))
+    q_out = qkr.qk_norm_rope_cache(gpu(cc.q), gpu(k), gpu(v), gpu(cc.q_weight), gpu(cc.k_weight), kc, vc,
+                                   gpu(torch.from_numpy(slots)), cc.eps, rope, numerics="eager")
+    orope = oracle.Rope("1d", d, "neox", inv_freq=inv1, positions=pos)
+    rq, rk, rv = oracle.qk_norm_rope_cache(W.as_f32(cc.q), W.as_f32(k), W.as_f32(v), W.as_f32(cc.q_weight),
+                                           W.as_f32(cc.k_weight), cc.eps, orope, slots,
+                                           np.zeros((640, kvh, d), np.float32), np.zeros((640, kvh, d), np.float32),
+                                           "bf16", numerics="eager")
+    assert_bf16_close(host(q_out), rq, d, "neox", "eager cache q")
+    assert_bf16_close(host(kc)[slots], rk[slots], d, "neox", "eager cache k")
+    assert np.array_equal(host(vc), rv)

@@ -7,7 +7,8 @@ fallback: if the library is missing, or a tensor is not on the GPU, the call
 raises.
 
 Functions (same names as the C entry points, without the ``qkr_`` prefix;
-the prefixed spellings are aliases):
+the prefixed spellings are aliases; every entry point with a dtype takes
+``numerics="contract"`` (default) or ``"eager"``):
     rms_norm(x, weight, eps)                         -> y
     qk_norm_rope(q, k, q_weight, k_weight, eps, rope) -> (q_out, k_out)
     joint_qk_norm_rope(text, image, eps, rope)        -> (q, k, v)
@@ -26,6 +27,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqkrope.so")
 
 F32, BF16 = 0, 1
+NUMERICS = {"contract": 0, "eager": 0x100}
 MODES = {"1d": 0, "axes": 1, "imrope": 2, "planes": 3}
 PAIRINGS = {"neox": 0, "adjacent": 1}
 _PLANES_NEEDED = {"1d": 1, "axes": 3, "imrope": 4}
@@ -143,11 +145,14 @@ def set_variant_override(name: Optional[str]):
 # marshalling helpers
 # ----------------------------------------------------------------------------
 
-def _dtype_code(t: torch.Tensor) -> int:
+def _dtype_code(t: torch.Tensor, numerics: str = "contract") -> int:
+    """The C dtype argument: the element type OR-ed with the numerics bits."""
+    if numerics not in NUMERICS:
+        raise QkrError(f"unknown numerics {numerics!r} (contract or eager)")
     if t.dtype == torch.float32:
-        return F32
+        return F32 | NUMERICS[numerics]
     if t.dtype == torch.bfloat16:
-        return BF16
+        return BF16 | NUMERICS[numerics]
     raise QkrError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
@@ -259,8 +264,9 @@ class Rope:
 # ----------------------------------------------------------------------------
 
 def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Row RMSNorm of x [rows, width] (qkr_rms_norm)."""
+             out: Optional[torch.Tensor] = None, numerics: str = "contract") -> torch.Tensor:
+    """Row RMSNorm of x [rows, width] (qkr_rms_norm).  numerics "contract"
+    (one rounding) or "eager" (the eager chain's rounding points)."""
     dev = x.device
     _on_gpu("x", x, dev)
     _on_gpu("weight", weight, dev)
@@ -273,7 +279,7 @@ def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
         raise QkrError("out must match x")
     _on_gpu("out", y, dev)
     st = lib().qkr_rms_norm(x.data_ptr(), x.stride(0), y.data_ptr(), y.stride(0), weight.data_ptr(),
-                            x.shape[0], x.shape[1], float(eps), _dtype_code(x), _stream(dev))
+                            x.shape[0], x.shape[1], float(eps), _dtype_code(x, numerics), _stream(dev))
     _check(st, "rms_norm")
     return y
 
@@ -281,7 +287,7 @@ def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
 def add_rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
                  residual: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
                  out_dtype: Optional[str] = None, scale: Optional[torch.Tensor] = None,
-                 out: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, numerics: str = "contract"):
     """Residual add + RMSNorm of x [rows, width] (qkr_add_rms_norm).
 
     With `residual`, s = x + residual rounded to x's dtype is written to
@@ -329,7 +335,7 @@ def add_rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
                                 residual_out.stride(0) if residual is not None else 0,
                                 y.data_ptr(), y.stride(0), 1 if fp8 else 0,
                                 scale.data_ptr() if fp8 else None, weight.data_ptr(),
-                                x.shape[0], x.shape[1], float(eps), _dtype_code(x), _stream(dev))
+                                x.shape[0], x.shape[1], float(eps), _dtype_code(x, numerics), _stream(dev))
     _check(st, "add_rms_norm")
     return y, residual_out
 
@@ -352,7 +358,8 @@ def debug_fp8_e4m3(x: torch.Tensor, scale: Optional[torch.Tensor] = None) -> tor
 
 def qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_weight: Optional[torch.Tensor],
                  k_weight: Optional[torch.Tensor], eps: float = 1e-6, rope: Optional[Rope] = None,
-                 q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None):
+                 q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                 numerics: str = "contract"):
     """Per-head RMSNorm + RoPE of q [.., tokens, Hq, D] and k [.., tokens, Hk, D]."""
     ref = q if q is not None else k
     if ref is None:
@@ -384,7 +391,7 @@ def qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_weight:
     qo4, ko4 = outs
     cr = rope.to_c(dev, tokens) if rope is not None else None
     L = lib()
-    st = L.qkr_qk_norm_rope(batch, tokens, d, _dtype_code(r4), float(eps),
+    st = L.qkr_qk_norm_rope(batch, tokens, d, _dtype_code(r4, numerics), float(eps),
                             ctypes.byref(_view(q4)), ctypes.byref(_view(qo4)), q4.shape[2] if q4 is not None else 0,
                             q_weight.data_ptr() if q4 is not None else None,
                             ctypes.byref(_view(k4)), ctypes.byref(_view(ko4)), k4.shape[2] if k4 is not None else 0,
@@ -413,7 +420,7 @@ def _slots_view(name: str, cache: torch.Tensor, heads: int, d: int) -> torch.Ten
 def qk_norm_rope_cache(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], q_weight: torch.Tensor,
                        k_weight: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
                        slot_mapping: torch.Tensor, eps: float = 1e-6, rope: Optional[Rope] = None,
-                       q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       q_out: Optional[torch.Tensor] = None, numerics: str = "contract") -> torch.Tensor:
     """Q/K RMSNorm + RoPE of q [tokens, Hq, D] and k [tokens, Hkv, D] with K
     (and V, copied) written into the cache rows slot_mapping [tokens] (int64)
     picks (qkr_qk_norm_rope_cache).  Returns q_out; the caches are updated in
@@ -460,7 +467,7 @@ def qk_norm_rope_cache(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tenso
     def v4(t):
         return ctypes.byref(_view(t.unsqueeze(0)))
 
-    st = lib().qkr_qk_norm_rope_cache(tokens, d, _dtype_code(q), float(eps), v4(q), v4(qo), hq,
+    st = lib().qkr_qk_norm_rope_cache(tokens, d, _dtype_code(q, numerics), float(eps), v4(q), v4(qo), hq,
                                       q_weight.data_ptr(), v4(k), v4(v) if v is not None else None, hkv,
                                       k_weight.data_ptr(), v4(kc), v4(vc) if vc is not None else None,
                                       slot_mapping.data_ptr(), kc.shape[0],
@@ -470,7 +477,7 @@ def qk_norm_rope_cache(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tenso
 
 
 def joint_qk_norm_rope(text: dict, image: dict, eps: float = 1e-6, rope: Optional[Rope] = None,
-                       out: Optional[Sequence[torch.Tensor]] = None):
+                       out: Optional[Sequence[torch.Tensor]] = None, numerics: str = "contract"):
     """Joint text/image QK RMSNorm + concatenation (text first) + RoPE.
 
     text / image: dicts with q, k, v [batch, tokens_s, heads, head_dim] views
@@ -509,7 +516,7 @@ def joint_qk_norm_rope(text: dict, image: dict, eps: float = 1e-6, rope: Optiona
             if tuple(o.shape) != shape or o.dtype != q0.dtype:
                 raise QkrError(f"outputs must be {shape} of the activation dtype")
     cr = rope.to_c(dev, joint) if rope is not None else None
-    st = lib().qkr_joint_qk_norm_rope(batch, heads, d, _dtype_code(q0), float(eps), ctypes.byref(streams[0]),
+    st = lib().qkr_joint_qk_norm_rope(batch, heads, d, _dtype_code(q0, numerics), float(eps), ctypes.byref(streams[0]),
                                       ctypes.byref(streams[1]), ctypes.byref(_view(outs[0])),
                                       ctypes.byref(_view(outs[1])), ctypes.byref(_view(outs[2])),
                                       ctypes.byref(cr) if cr is not None else None, _stream(dev))
@@ -557,7 +564,8 @@ def mrope_cos_sin_setup(inv_t: torch.Tensor, inv_h: torch.Tensor, inv_w: torch.T
 def vit_qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_weight: Optional[torch.Tensor],
                      k_weight: Optional[torch.Tensor], eps: float, inv_t: torch.Tensor, inv_h: torch.Tensor,
                      inv_w: torch.Tensor, grid_thw, spatial_merge: int, pairing: str = "neox",
-                     q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None):
+                     q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                     numerics: str = "contract"):
     """ViT per-head RMSNorm + RoPE of q, k [N, heads, head_dim] with (t, h, w)
     positions computed from the patch grids in the kernel (no cos/sin planes)."""
     ref = q if q is not None else k
@@ -598,7 +606,7 @@ def vit_qk_norm_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor], q_wei
 
     arr, g, n = _grid_array(grid_thw)
     (qi, qo, qh, qw), (ki, ko, kh, kw) = views
-    st = lib().qkr_vit_qk_norm_rope(ref.shape[0], ref.shape[2], _dtype_code(ref), float(eps),
+    st = lib().qkr_vit_qk_norm_rope(ref.shape[0], ref.shape[2], _dtype_code(ref, numerics), float(eps),
                                     ctypes.byref(view3(qi)), ctypes.byref(view3(qo)), qh,
                                     qw.data_ptr() if qw is not None else None,
                                     ctypes.byref(view3(ki)), ctypes.byref(view3(ko)), kh,

@@ -19,10 +19,12 @@ LIB = os.path.join(PKG, "libqkrope.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 # (source, extra flags, object name): the QK RMSNorm + RoPE kernels are
-# instantiated once per lanes-per-row value, in parallel compilations.
+# instantiated once per lanes-per-row value and numerics, in parallel
+# compilations.
 LANES_PER_ROW = (1, 2, 4, 8, 16, 32)
 UNITS = ([("qkr_kernels.hip", [], "qkr_kernels"), ("qkr_api.cpp", [], "qkr_api")] +
-         [("qkr_rope_part.hip", [f"-DQKR_LPR={n}"], f"qkr_rope_lpr{n}") for n in LANES_PER_ROW])
+         [("qkr_rope_part.hip", [f"-DQKR_LPR={n}", f"-DQKR_EAGER={e}"], f"qkr_rope_lpr{n}_eager{e}")
+          for n in LANES_PER_ROW for e in (0, 1)])
 # Kernels must not use private (scratch) memory: a stray dynamic index into a
 # by-value kernel argument or a local array silently costs a per-lane copy in
 # scratch.  The compiler's resource remarks are checked on every build.

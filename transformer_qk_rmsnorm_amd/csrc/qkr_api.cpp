@@ -90,8 +90,15 @@ qkr_status hip_status(hipError_t e, const char* what)
     return ok();
 }
 
-qkr_status check_dtype(int32_t dtype, int& esize)
+// The dtype argument: QKR_F32 or QKR_BF16, optionally OR-ed with
+// QKR_NUMERICS_EAGER.  On return dtype holds the element type alone.
+qkr_status check_dtype(int32_t& dtype, int& esize, bool& eager)
 {
+    const int32_t numerics = dtype & ~(int32_t)0xFF;
+    if (numerics != QKR_NUMERICS_CONTRACT && numerics != QKR_NUMERICS_EAGER)
+        return fail(QKR_ERR_INVALID_ARGUMENT, "dtype %d carries unknown numerics bits", dtype);
+    eager = numerics == QKR_NUMERICS_EAGER;
+    dtype &= 0xFF;
     if (dtype == QKR_F32) {
         esize = 4;
         return QKR_OK;
@@ -295,24 +302,25 @@ qkr_status plan_rope(const NormRopeArgs& a, int32_t dtype, RopePlan& plan)
     return QKR_OK;
 }
 
-qkr_status launch_planned(NormRopeArgs& a, int32_t dtype, int32_t pairing, const RopePlan& plan, hipStream_t stream)
+qkr_status launch_planned(NormRopeArgs& a, int32_t dtype, bool eager, int32_t pairing, const RopePlan& plan,
+                          hipStream_t stream)
 {
     (void)hipGetLastError();   // clear a stale error so the launch reports its own
     const char* variant = "";
-    hipError_t e = launch_norm_rope(a, dtype, pairing, plan, stream, &variant);
+    hipError_t e = launch_norm_rope(a, dtype, pairing, eager, plan, stream, &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "norm_rope launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
     return ok();
 }
 
-qkr_status launch(NormRopeArgs& a, int32_t dtype, int32_t pairing, hipStream_t stream)
+qkr_status launch(NormRopeArgs& a, int32_t dtype, bool eager, int32_t pairing, hipStream_t stream)
 {
     RopePlan plan;
     qkr_status st;
     if ((st = plan_rope(a, dtype, plan)))
         return st;
-    return launch_planned(a, dtype, pairing, plan, stream);
+    return launch_planned(a, dtype, eager, pairing, plan, stream);
 }
 
 // The row kernel variant (pure host code), as plan_rope.
@@ -461,8 +469,9 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
                         qkr_stream_t stream)
 {
     int esize = 0;
+    bool eager = false;
     qkr_status st;
-    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)))
+    if ((st = check_dtype(dtype, esize, eager)) || (st = check_eps(eps)))
         return st;
     if (rows < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "rows %lld < 0", (long long)rows);
@@ -508,7 +517,7 @@ qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, in
         return st;
     (void)hipGetLastError();
     const char* variant = "";
-    hipError_t e = launch_rms_norm(a, dtype, plan, reinterpret_cast<hipStream_t>(stream), &variant);
+    hipError_t e = launch_rms_norm(a, dtype, eager, plan, reinterpret_cast<hipStream_t>(stream), &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "rms_norm launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
@@ -521,13 +530,16 @@ qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void*
                             int32_t dtype, qkr_stream_t stream)
 {
     int esize = 0;
+    bool eager = false;
     qkr_status st;
-    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)))
+    if ((st = check_dtype(dtype, esize, eager)) || (st = check_eps(eps)))
         return st;
     if (y_kind != QKR_OUT_ACT && y_kind != QKR_OUT_FP8_E4M3)
         return fail(QKR_ERR_INVALID_ARGUMENT, "unknown output kind %d", y_kind);
     const bool fp8 = y_kind == QKR_OUT_FP8_E4M3;
     const bool add = r_dev != nullptr;
+    if (fp8 && eager)
+        return fail(QKR_ERR_UNSUPPORTED, "the eager numerics are defined for activation-type outputs, not FP8");
     if (rows < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "rows %lld < 0", (long long)rows);
     if (width <= 0)
@@ -631,7 +643,7 @@ qkr_status qkr_add_rms_norm(const void* x_dev, int64_t x_row_stride, const void*
         return st;
     (void)hipGetLastError();
     const char* variant = "";
-    hipError_t e = launch_rms_norm(a, dtype, plan, reinterpret_cast<hipStream_t>(stream), &variant);
+    hipError_t e = launch_rms_norm(a, dtype, eager, plan, reinterpret_cast<hipStream_t>(stream), &variant);
     if (e != hipSuccess)
         return fail(QKR_ERR_HIP, "add_rms_norm launch: %s", hipGetErrorString(e));
     std::snprintf(g_variant, sizeof(g_variant), "%s", variant);
@@ -656,8 +668,9 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
                             const qkr_rope* rope, qkr_stream_t stream)
 {
     int esize = 0;
+    bool eager = false;
     qkr_status st;
-    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+    if ((st = check_dtype(dtype, esize, eager)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
         return st;
     if (batch < 0 || tokens < 0 || q_heads < 0 || k_heads < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative batch, tokens or heads");
@@ -698,7 +711,7 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
     a.rotary_dim = rotary_dim;
     a.eps = eps;
     a.inv_d = 1.0f / (float)head_dim;
-    return launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream));
+    return launch(a, dtype, eager, pairing, reinterpret_cast<hipStream_t>(stream));
 }
 
 qkr_status qkr_qk_norm_rope_cache(int64_t tokens, int32_t head_dim, int32_t dtype, float eps, const qkr_view* q,
@@ -709,8 +722,9 @@ qkr_status qkr_qk_norm_rope_cache(int64_t tokens, int32_t head_dim, int32_t dtyp
                                   qkr_stream_t stream)
 {
     int esize = 0;
+    bool eager = false;
     qkr_status st;
-    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+    if ((st = check_dtype(dtype, esize, eager)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
         return st;
     if (tokens < 0 || q_heads < 0 || kv_heads < 0 || num_slots < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative tokens, heads or num_slots");
@@ -774,7 +788,7 @@ qkr_status qkr_qk_norm_rope_cache(int64_t tokens, int32_t head_dim, int32_t dtyp
     a.rotary_dim = rotary_dim;
     a.eps = eps;
     a.inv_d = 1.0f / (float)head_dim;
-    return launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream));
+    return launch(a, dtype, eager, pairing, reinterpret_cast<hipStream_t>(stream));
 }
 
 qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, float eps,
@@ -783,8 +797,9 @@ qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim
                                   qkr_stream_t stream)
 {
     int esize = 0;
+    bool eager = false;
     qkr_status st;
-    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+    if ((st = check_dtype(dtype, esize, eager)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
         return st;
     if (text == nullptr || image == nullptr)
         return fail(QKR_ERR_INVALID_ARGUMENT, "null text or image stream");
@@ -841,7 +856,7 @@ qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim
     a.rotary_dim = rotary_dim;
     a.eps = eps;
     a.inv_d = 1.0f / (float)head_dim;
-    return launch(a, dtype, pairing, reinterpret_cast<hipStream_t>(stream));
+    return launch(a, dtype, eager, pairing, reinterpret_cast<hipStream_t>(stream));
 }
 
 qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t, const float* inv_freq_h_dev,
@@ -905,8 +920,9 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
                                 int32_t num_grids, int32_t spatial_merge, qkr_stream_t stream)
 {
     int esize = 0;
+    bool eager = false;
     qkr_status st;
-    if ((st = check_dtype(dtype, esize)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
+    if ((st = check_dtype(dtype, esize, eager)) || (st = check_eps(eps)) || (st = check_head_dim(head_dim, esize)))
         return st;
     if (tokens < 0 || q_heads < 0 || k_heads < 0)
         return fail(QKR_ERR_INVALID_ARGUMENT, "negative tokens or heads");
@@ -1012,7 +1028,7 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
         a.tokens = (int32_t)count;
         a.tokens0 = (int32_t)count;
         a.rope.token_base = start;
-        if ((st = launch_planned(a, dtype, pairing, plan, reinterpret_cast<hipStream_t>(stream))))
+        if ((st = launch_planned(a, dtype, eager, pairing, plan, reinterpret_cast<hipStream_t>(stream))))
             return st;
         start = cu;
     }

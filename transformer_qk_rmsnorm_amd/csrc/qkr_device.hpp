@@ -43,6 +43,8 @@ struct F32 {
     }
     // fp32 outputs keep the normalised value unrounded.
     __device__ __forceinline__ static void round_trip(float*) {}
+    // A table value in the activation type: fp32 already.
+    __device__ __forceinline__ static void round_pair(float&, float&) {}
     __device__ __forceinline__ static float sumsq(const uint4& v, float acc)
     {
         acc = fmaf(__uint_as_float(v.x), __uint_as_float(v.x), acc);
@@ -87,6 +89,13 @@ struct BF16 {
             x[2 * i] = __uint_as_float(w << 16);
             x[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
         }
+    }
+    // Two fp32 values rounded to bf16 (a cos/sin table stored in bf16).
+    __device__ __forceinline__ static void round_pair(float& a, float& b)
+    {
+        const uint32_t w = pack2(a, b);
+        a = __uint_as_float(w << 16);
+        b = __uint_as_float(w & 0xffff0000u);
     }
     // Sum of squares straight from the packed pairs (v_dot2c_f32_bf16: the
     // bf16 products are exact in fp32, accumulation in fp32), so no unpacked
@@ -262,6 +271,18 @@ __device__ __forceinline__ float rms_rsqrt(float v, bool eps_normal)
 __device__ __forceinline__ float load_global(const float* p)
 {
     return *(const __attribute__((address_space(1))) float*)p;
+}
+
+// The rotation of one pair with every product and sum rounded to fp32 on
+// its own: no fused multiply-add (the eager numerics; [Ovis] "Supplemental
+// eager bitwise measurements": the preset that reproduced an eager chain
+// turned floating-point fusion off).
+__device__ __forceinline__ void rotate_unfused(float& a, float& b, float c, float s)
+{
+#pragma clang fp contract(off)
+    const float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+    a = ac - bs;
+    b = bc + as;
 }
 
 // Orders one wave's LDS writes before its later LDS reads of other lanes'

@@ -189,10 +189,11 @@ __host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*
 
 // QK RMSNorm + RoPE kernel for one lanes-per-row value (LPR in 1, 2, 4, 8, 16,
 // 32), chosen by element type, rotation source (0 none, 1 positions, 2
-// planes, 3 ViT grids), pairing, nontemporal accesses, staged stores and
-// passes per wave.  Each LPR is defined in its own build of qkr_rope_part.hip.
+// planes, 3 ViT grids), pairing, nontemporal accesses, staged stores, the
+// eager numerics and passes per wave.  Each (LPR, EAGER) pair is defined in its own build of
+// qkr_rope_part.hip.
 using NormRopeFn = void (*)(NormRopeArgs);
-template <int LPR>
+template <int LPR, bool EAGER>
 NormRopeFn pick_norm_rope(int32_t dtype, int rope, int32_t pairing, bool nt, bool stage, int np);
 
 // Kernel variant of a QK norm + rotation call.
@@ -221,9 +222,10 @@ const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, 
 
 // Kernel launchers (qkr_kernels.hip).  Each returns the variant name it
 // launched through *variant; launch errors surface through hipGetLastError.
-hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, const RopePlan& plan,
+// eager: the eager-chain rounding points instead of the contract.
+hipError_t launch_norm_rope(const NormRopeArgs& a, int32_t dtype, int32_t pairing, bool eager, const RopePlan& plan,
                             hipStream_t stream, const char** variant);
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, const RmsPlan& plan, hipStream_t stream,
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, bool eager, const RmsPlan& plan, hipStream_t stream,
                            const char** variant);
 hipError_t launch_debug_fp8(const float* x, int64_t n, const float* scale, uint8_t* out, hipStream_t stream);
 hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream);

@@ -32,13 +32,17 @@ namespace {
 //   KIND 2 wide : one workgroup of 4 wavefronts per row, one LDS exchange.
 // Every lane holds VPL 16-byte vectors of the row, all loaded up front
 // ([VecRMS]: 16-byte vectorized reads of the row).
+// EAGER: y = (act)((act)(x * rrms) * w), the output expression of the eager
+// RMSNorm kernel the [VecRMS] review thread quotes, instead of one rounding
+// of x * rrms * w (activation-type outputs only).
 // ---------------------------------------------------------------------------
-template <class E, int VPL, int KIND, bool NT, int MODE>
+template <class E, int VPL, int KIND, bool NT, int MODE, bool EAGER>
 __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
 {
     constexpr int VE = E::VE;
     constexpr bool ADD = (MODE & 1) != 0, FP8 = (MODE & 2) != 0;
     static_assert(!(ADD && KIND == 1), "the split variant cannot update the residual in place");
+    static_assert(!(FP8 && EAGER), "the eager numerics are defined for activation-type outputs");
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t row;
@@ -127,9 +131,19 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
             float xv[VE], wv[VE];
             E::unpack(d[k], xv);
             E::unpack(load16(a.w + (int64_t)v * 16), wv);
+            if constexpr (EAGER) {
 #pragma unroll
-            for (int e = 0; e < VE; ++e)
-                xv[e] = xv[e] * rrms * wv[e];
+                for (int e = 0; e < VE; ++e)
+                    xv[e] = xv[e] * rrms;
+                E::round_trip(xv);
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    xv[e] = xv[e] * wv[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    xv[e] = xv[e] * rrms * wv[e];
+            }
             if constexpr (FP8) {
                 // One E4M3 code per element (VE bytes per vector): the code of
                 // the fp32 quotient y / scale.
@@ -231,44 +245,52 @@ __global__ __launch_bounds__(kThreads) void debug_vit_kernel(const VitArgs a, in
 // ---------------------------------------------------------------------------
 using RmsFn = void (*)(RmsArgs);
 
-template <class E, int KIND, bool NT, int MODE>
+template <class E, int KIND, bool NT, int MODE, bool EAGER>
 RmsFn pick_vpl(int vpl)
 {
     switch (vpl) {
-    case 1: return rms_kernel<E, 1, KIND, NT, MODE>;
-    case 2: return rms_kernel<E, 2, KIND, NT, MODE>;
-    case 3: return rms_kernel<E, 3, KIND, NT, MODE>;
-    case 4: return rms_kernel<E, 4, KIND, NT, MODE>;
-    case 5: return rms_kernel<E, 5, KIND, NT, MODE>;
-    case 6: return rms_kernel<E, 6, KIND, NT, MODE>;
-    case 8: return rms_kernel<E, 8, KIND, NT, MODE>;
-    case 10: return rms_kernel<E, 10, KIND, NT, MODE>;
-    case 12: return rms_kernel<E, 12, KIND, NT, MODE>;
-    default: return rms_kernel<E, 16, KIND, NT, MODE>;
+    case 1: return rms_kernel<E, 1, KIND, NT, MODE, EAGER>;
+    case 2: return rms_kernel<E, 2, KIND, NT, MODE, EAGER>;
+    case 3: return rms_kernel<E, 3, KIND, NT, MODE, EAGER>;
+    case 4: return rms_kernel<E, 4, KIND, NT, MODE, EAGER>;
+    case 5: return rms_kernel<E, 5, KIND, NT, MODE, EAGER>;
+    case 6: return rms_kernel<E, 6, KIND, NT, MODE, EAGER>;
+    case 8: return rms_kernel<E, 8, KIND, NT, MODE, EAGER>;
+    case 10: return rms_kernel<E, 10, KIND, NT, MODE, EAGER>;
+    case 12: return rms_kernel<E, 12, KIND, NT, MODE, EAGER>;
+    default: return rms_kernel<E, 16, KIND, NT, MODE, EAGER>;
     }
 }
 
 // Every mode comes with and without nontemporal accesses; the add modes skip
 // the split variant (its workgroups read the whole row while others write
-// the residual).
-template <class E, int KIND, bool NT>
+// the residual); the eager numerics exist for activation-type outputs.
+template <class E, int KIND, bool NT, bool EAGER>
 RmsFn pick_rms_nt(int mode, int vpl)
 {
-    switch (mode) {
-    case 0: return pick_vpl<E, KIND, NT, 0>(vpl);
-    case 2: return pick_vpl<E, KIND, NT, 2>(vpl);
-    default:
-        if constexpr (KIND == 1)
-            return nullptr;
-        else
-            return mode == 1 ? pick_vpl<E, KIND, NT, 1>(vpl) : pick_vpl<E, KIND, NT, 3>(vpl);
+    if (mode == 0)
+        return pick_vpl<E, KIND, NT, 0, EAGER>(vpl);
+    if constexpr (KIND != 1) {
+        if (mode == 1)
+            return pick_vpl<E, KIND, NT, 1, EAGER>(vpl);
     }
+    if constexpr (!EAGER) {
+        if (mode == 2)
+            return pick_vpl<E, KIND, NT, 2, false>(vpl);
+        if constexpr (KIND != 1) {
+            if (mode == 3)
+                return pick_vpl<E, KIND, NT, 3, false>(vpl);
+        }
+    }
+    return nullptr;
 }
 
 template <class E, int KIND>
-RmsFn pick_rms_mode(bool nt, int mode, int vpl)
+RmsFn pick_rms_mode(bool nt, bool eager, int mode, int vpl)
 {
-    return nt ? pick_rms_nt<E, KIND, true>(mode, vpl) : pick_rms_nt<E, KIND, false>(mode, vpl);
+    if (eager)
+        return nt ? pick_rms_nt<E, KIND, true, true>(mode, vpl) : pick_rms_nt<E, KIND, false, true>(mode, vpl);
+    return nt ? pick_rms_nt<E, KIND, true, false>(mode, vpl) : pick_rms_nt<E, KIND, false, false>(mode, vpl);
 }
 
 int round_vpl(int need)
@@ -328,7 +350,7 @@ const char* plan_norm_rope(int32_t dtype, int32_t head_dim, int32_t max_heads, i
     return nullptr;
 }
 
-hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, const RopePlan& plan,
+hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, bool eager, const RopePlan& plan,
                             hipStream_t stream, const char** variant)
 {
     NormRopeArgs a = a_in;
@@ -354,12 +376,18 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     a.nv_recip = (65536u + (uint32_t)nv - 1) / (uint32_t)nv;
     NormRopeFn fn;
     switch (lpr) {
-    case 1: fn = pick_norm_rope<1>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
-    case 2: fn = pick_norm_rope<2>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
-    case 4: fn = pick_norm_rope<4>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
-    case 8: fn = pick_norm_rope<8>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
-    case 16: fn = pick_norm_rope<16>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
-    default: fn = pick_norm_rope<32>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 1: fn = eager ? pick_norm_rope<1, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
+                       : pick_norm_rope<1, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 2: fn = eager ? pick_norm_rope<2, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
+                       : pick_norm_rope<2, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 4: fn = eager ? pick_norm_rope<4, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
+                       : pick_norm_rope<4, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 8: fn = eager ? pick_norm_rope<8, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
+                       : pick_norm_rope<8, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    case 16: fn = eager ? pick_norm_rope<16, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
+                        : pick_norm_rope<16, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
+    default: fn = eager ? pick_norm_rope<32, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
+                        : pick_norm_rope<32, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
     }
     // One launch per kMaxBlocksPerLaunch workgroups, each told its first tile.
     const int64_t blocks = (tiles + kWaves - 1) / kWaves;
@@ -371,10 +399,10 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
         if (e != hipSuccess)
             return e;
     }
-    snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s:stage%d", np, (int)plan.nt, lpr,
+    snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s:stage%d%s", np, (int)plan.nt, lpr,
              dtype == kBF16 ? "bf16" : "f32",
              rope == 0 ? "none" : (rope == 1 ? "pos" : (rope == 2 ? "planes" : "vit")),
-             pairing == kNeox ? "neox" : "adjacent", (int)plan.stage);
+             pairing == kNeox ? "neox" : "adjacent", (int)plan.stage, eager ? ":eager" : "");
     *variant = g_variant;
     return hipSuccess;
 }
@@ -413,7 +441,7 @@ const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, 
     return nullptr;
 }
 
-hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, const RmsPlan& plan, hipStream_t stream,
+hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, bool eager, const RmsPlan& plan, hipStream_t stream,
                            const char** variant)
 {
     if (a.rows == 0)
@@ -436,13 +464,13 @@ hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, const RmsPlan& plan, hipStr
     }
     RmsFn fn;
     if (dtype == kBF16)
-        fn = kind == 0 ? pick_rms_mode<BF16, 0>(plan.nt, mode, vpl)
-                       : (kind == 1 ? pick_rms_mode<BF16, 1>(plan.nt, mode, vpl)
-                                    : pick_rms_mode<BF16, 2>(plan.nt, mode, vpl));
+        fn = kind == 0 ? pick_rms_mode<BF16, 0>(plan.nt, eager, mode, vpl)
+                       : (kind == 1 ? pick_rms_mode<BF16, 1>(plan.nt, eager, mode, vpl)
+                                    : pick_rms_mode<BF16, 2>(plan.nt, eager, mode, vpl));
     else
-        fn = kind == 0 ? pick_rms_mode<F32, 0>(plan.nt, mode, vpl)
-                       : (kind == 1 ? pick_rms_mode<F32, 1>(plan.nt, mode, vpl)
-                                    : pick_rms_mode<F32, 2>(plan.nt, mode, vpl));
+        fn = kind == 0 ? pick_rms_mode<F32, 0>(plan.nt, eager, mode, vpl)
+                       : (kind == 1 ? pick_rms_mode<F32, 1>(plan.nt, eager, mode, vpl)
+                                    : pick_rms_mode<F32, 2>(plan.nt, eager, mode, vpl));
     if (fn == nullptr)
         return hipErrorInvalidValue;   // plan_rms_norm refuses such calls first
     const int64_t blocks = (items + per_block - 1) / per_block;
@@ -454,9 +482,9 @@ hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, const RmsPlan& plan, hipStr
         if (e != hipSuccess)
             return e;
     }
-    snprintf(g_variant, sizeof(g_variant), "rms:%s:nt%d:vpl%d:%s%s%s",
+    snprintf(g_variant, sizeof(g_variant), "rms:%s:nt%d:vpl%d:%s%s%s%s",
              kind == 0 ? "rows" : (kind == 1 ? "split" : "wide"), (int)plan.nt, vpl, dtype == kBF16 ? "bf16" : "f32",
-             (mode & 1) ? ":add" : "", (mode & 2) ? ":fp8" : "");
+             (mode & 1) ? ":add" : "", (mode & 2) ? ":fp8" : "", eager ? ":eager" : "");
     *variant = g_variant;
     return hipSuccess;
 }

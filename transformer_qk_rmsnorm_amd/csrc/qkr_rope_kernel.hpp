@@ -114,8 +114,13 @@ __device__ __forceinline__ T sel3(int i, T v0, T v1, T v2)
 // ROPE: 0 norm only, 1 positions + inv_freq (1D / AXES / IMROPE: the axis
 // table carries the difference), 2 cos/sin planes, 3 ViT positions computed
 // from the grid table.
+//
+// EAGER: the rounding points of an eager RMSNorm + RoPE chain instead of the
+// contract: (act)((act)(x * rrms) * w) ([VecRMS] review thread: the RMSNorm
+// kernel's output expression), cos and sin rounded to the activation type
+// (the chain's RoPE table), and no fused multiply-add in the rotation.
 // ---------------------------------------------------------------------------
-template <class E, int LPR, int NP, int ROPE, int PAIRING, bool NT, bool STAGE>
+template <class E, int LPR, int NP, int ROPE, int PAIRING, bool NT, bool STAGE, bool EAGER>
 __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs a)
 {
     constexpr int VE = E::VE;
@@ -365,6 +370,10 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
                 pair_cos_sin(ax1, pos, op1, c1, s1v);
             }
         }
+        if constexpr (EAGER) {
+            E::round_pair(c0, s0);
+            E::round_pair(c1, s1v);
+        }
         // Pair p's values sit on lane p mod 64 (ds_bpermute takes the lane
         // from address bits 7..2, so the address needs no mask).  Pairs at or
         // past `half` are never rotated: whatever such a lane receives goes
@@ -407,36 +416,53 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         float x0[VE], x1[VE];
         E::unpack(d[p][0], x0);
         E::unpack(d[p][1], x1);
+        if constexpr (EAGER) {
+            // (act)((act)(x * rrms) * w)
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            x0[e] = x0[e] * rrms * w0[e];
-            x1[e] = x1[e] * rrms * w1[e];
+            for (int e = 0; e < VE; ++e) {
+                x0[e] = x0[e] * rrms;
+                x1[e] = x1[e] * rrms;
+            }
+            E::round_trip(x0);
+            E::round_trip(x1);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                x0[e] = x0[e] * w0[e];
+                x1[e] = x1[e] * w1[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                x0[e] = x0[e] * rrms * w0[e];
+                x1[e] = x1[e] * rrms * w1[e];
+            }
         }
         E::round_trip(x0);
         E::round_trip(x1);
+        // One pair: a' = a c - b s, b' = b c + a s (unfused for EAGER).
+        auto rot = [](float& xa, float& xb, float c, float sn) {
+            if constexpr (EAGER) {
+                rotate_unfused(xa, xb, c, sn);
+            } else {
+                const float a0 = xa, b0 = xb;
+                xa = a0 * c - b0 * sn;
+                xb = b0 * c + a0 * sn;
+            }
+        };
         if constexpr (ROT) {
             if constexpr (PAIRING == kNeox) {
                 if (rot_lane) {
 #pragma unroll
-                    for (int e = 0; e < VE; ++e) {
-                        const float xa = x0[e], xb = x1[e];
-                        x0[e] = xa * cs_c[e] - xb * cs_s[e];
-                        x1[e] = xb * cs_c[e] + xa * cs_s[e];
-                    }
+                    for (int e = 0; e < VE; ++e)
+                        rot(x0[e], x1[e], cs_c[e], cs_s[e]);
                 }
             } else {
 #pragma unroll
                 for (int q = 0; q < VE / 2; ++q) {
-                    if (v0 * (VE / 2) + q < half) {
-                        const float xa = x0[2 * q], xb = x0[2 * q + 1];
-                        x0[2 * q] = xa * cs_c[q] - xb * cs_s[q];
-                        x0[2 * q + 1] = xb * cs_c[q] + xa * cs_s[q];
-                    }
-                    if (v1 * (VE / 2) + q < half) {
-                        const float xa = x1[2 * q], xb = x1[2 * q + 1];
-                        x1[2 * q] = xa * cs_c[VE / 2 + q] - xb * cs_s[VE / 2 + q];
-                        x1[2 * q + 1] = xb * cs_c[VE / 2 + q] + xa * cs_s[VE / 2 + q];
-                    }
+                    if (v0 * (VE / 2) + q < half)
+                        rot(x0[2 * q], x0[2 * q + 1], cs_c[q], cs_s[q]);
+                    if (v1 * (VE / 2) + q < half)
+                        rot(x1[2 * q], x1[2 * q + 1], cs_c[VE / 2 + q], cs_s[VE / 2 + q]);
                 }
             }
         }
@@ -444,44 +470,45 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     }
 }
 
-template <class E, int LPR, int ROPE, int PAIRING, bool NT, bool STAGE>
+template <class E, int LPR, int ROPE, int PAIRING, bool NT, bool STAGE, bool EAGER>
 NormRopeFn pick_np(int np)
 {
     switch (np) {
-    case 1: return norm_rope_kernel<E, LPR, 1, ROPE, PAIRING, NT, STAGE>;
-    case 2: return norm_rope_kernel<E, LPR, 2, ROPE, PAIRING, NT, STAGE>;
-    case 3: return norm_rope_kernel<E, LPR, 3, ROPE, PAIRING, NT, STAGE>;
-    default: return norm_rope_kernel<E, LPR, 4, ROPE, PAIRING, NT, STAGE>;
+    case 1: return norm_rope_kernel<E, LPR, 1, ROPE, PAIRING, NT, STAGE, EAGER>;
+    case 2: return norm_rope_kernel<E, LPR, 2, ROPE, PAIRING, NT, STAGE, EAGER>;
+    case 3: return norm_rope_kernel<E, LPR, 3, ROPE, PAIRING, NT, STAGE, EAGER>;
+    default: return norm_rope_kernel<E, LPR, 4, ROPE, PAIRING, NT, STAGE, EAGER>;
     }
 }
 
 // Staged stores exist for 2..8 lanes per row (rows up to 16 vectors, the
 // only ones whose halves can miss 128-byte lines).
-template <class E, int LPR, int ROPE, int PAIRING>
+template <class E, int LPR, int ROPE, int PAIRING, bool EAGER>
 NormRopeFn pick_nt(bool nt, bool stage, int np)
 {
     constexpr bool kCanStage = LPR >= 2 && LPR <= 8;
     if (kCanStage && stage)
-        return nt ? pick_np<E, LPR, ROPE, PAIRING, true, kCanStage>(np)
-                  : pick_np<E, LPR, ROPE, PAIRING, false, kCanStage>(np);
-    return nt ? pick_np<E, LPR, ROPE, PAIRING, true, false>(np) : pick_np<E, LPR, ROPE, PAIRING, false, false>(np);
+        return nt ? pick_np<E, LPR, ROPE, PAIRING, true, kCanStage, EAGER>(np)
+                  : pick_np<E, LPR, ROPE, PAIRING, false, kCanStage, EAGER>(np);
+    return nt ? pick_np<E, LPR, ROPE, PAIRING, true, false, EAGER>(np)
+              : pick_np<E, LPR, ROPE, PAIRING, false, false, EAGER>(np);
 }
 
-template <class E, int LPR, int ROPE>
+template <class E, int LPR, int ROPE, bool EAGER>
 NormRopeFn pick_pairing(int pairing, bool nt, bool stage, int np)
 {
-    return pairing == kNeox ? pick_nt<E, LPR, ROPE, kNeox>(nt, stage, np)
-                            : pick_nt<E, LPR, ROPE, kAdjacent>(nt, stage, np);
+    return pairing == kNeox ? pick_nt<E, LPR, ROPE, kNeox, EAGER>(nt, stage, np)
+                            : pick_nt<E, LPR, ROPE, kAdjacent, EAGER>(nt, stage, np);
 }
 
-template <class E, int LPR>
+template <class E, int LPR, bool EAGER>
 NormRopeFn pick_rope(int rope, int pairing, bool nt, bool stage, int np)
 {
     switch (rope) {
-    case 0: return pick_pairing<E, LPR, 0>(pairing, nt, stage, np);
-    case 1: return pick_pairing<E, LPR, 1>(pairing, nt, stage, np);
-    case 2: return pick_pairing<E, LPR, 2>(pairing, nt, stage, np);
-    default: return pick_pairing<E, LPR, 3>(pairing, nt, stage, np);
+    case 0: return pick_pairing<E, LPR, 0, EAGER>(pairing, nt, stage, np);
+    case 1: return pick_pairing<E, LPR, 1, EAGER>(pairing, nt, stage, np);
+    case 2: return pick_pairing<E, LPR, 2, EAGER>(pairing, nt, stage, np);
+    default: return pick_pairing<E, LPR, 3, EAGER>(pairing, nt, stage, np);
     }
 }
 
