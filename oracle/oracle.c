@@ -207,11 +207,13 @@ void oracle_add_rms_norm(const float* x, const float* r, int64_t rows, int32_t w
 /* AXES / PLANES: the pairs are split into contiguous runs, sections[0] pairs
  * on t, then sections[1] on h, then sections[2] on w ([ViT] setup kernel: the
  * t, h and w column ranges of the planes follow one another).
- * IMROPE: sector = p mod (s0+s1+s2+s3); sector mod 3 == 1 selects h while
- * sector < 3*s1, == 2 selects w while sector < 3*s2, == 0 selects t while
- * sector < 3*s0; every other pair reads the fourth component e ([IMROPE]
- * "The change", and the review comment that sets the rule beside
- * ggml_mrope_cache_init). */
+ * IMROPE ([IMROPE] "The change", and the review comment that sets the rule
+ * beside ggml_mrope_cache_init): the pairs repeat in periods of
+ * S = s0+s1+s2+s3; inside a period the t, h and w pairs interleave, the k-th
+ * pair of axis a (t = 0, h = 1, w = 2) sitting at offset 3k + a for k < s_a,
+ * and every offset no axis claims reads the fourth component e.  Written here
+ * by laying one period out, axis by axis, and reading pair p at offset
+ * p mod S. */
 int32_t oracle_axis(const oracle_rope* rope, int32_t p)
 {
     const int32_t* s = rope->sections;
@@ -229,15 +231,16 @@ int32_t oracle_axis(const oracle_rope* rope, int32_t p)
         return -1;   /* pair outside every section: invalid input */
     }
     case ORACLE_POS_IMROPE: {
-        int32_t sect_dims = s[0] + s[1] + s[2] + s[3];
-        int32_t sector = p % sect_dims;
-        if (sector % 3 == 1 && sector < 3 * s[1])
-            return ORACLE_AXIS_H;
-        if (sector % 3 == 2 && sector < 3 * s[2])
-            return ORACLE_AXIS_W;
-        if (sector % 3 == 0 && sector < 3 * s[0])
-            return ORACLE_AXIS_T;
-        return ORACLE_AXIS_E;
+        const int32_t period = s[0] + s[1] + s[2] + s[3];
+        int32_t* layout = (int32_t*)malloc(sizeof(int32_t) * (size_t)period);
+        for (int32_t o = 0; o < period; ++o)
+            layout[o] = ORACLE_AXIS_E;
+        for (int32_t a = 0; a < 3; ++a)
+            for (int32_t k = 0; k < s[a] && 3 * k + a < period; ++k)
+                layout[3 * k + a] = a;
+        const int32_t axis = layout[p % period];
+        free(layout);
+        return axis;
     }
     default:
         return -1;
@@ -418,42 +421,39 @@ void oracle_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim,
 /* ViT positions and cos/sin planes                                          */
 /* ------------------------------------------------------------------------ */
 
-/* [ViT] setup kernel.  A token's grid is the number of grid ends it has
- * reached; within its grid, local = token - start, the frame is
- * local div (h*w), and inside a frame tokens run by spatial-merge block
- * (block row bh, block column bw, then the m x m cells of the block):
- *   bh = rem div (m*w), r = rem mod (m*w), bw = r div m^2, r2 = r mod m^2,
- *   hpos = bh*m + r2 div m, wpos = bw*m + r2 mod m. */
-static void vit_token_position(const int32_t* grid_thw, int32_t num_grids, int32_t m,
-                               int64_t tok, int32_t* tpos, int32_t* hpos, int32_t* wpos)
-{
-    int64_t start = 0, end = 0;
-    int32_t g = 0;
-    for (int32_t k = 0; k < num_grids; ++k) {
-        end += (int64_t)grid_thw[3 * k] * grid_thw[3 * k + 1] * grid_thw[3 * k + 2];
-        if (tok >= end) {
-            g = k + 1;
-            start = end;
-        }
-    }
-    int64_t h = grid_thw[3 * g + 1], w = grid_thw[3 * g + 2];
-    int64_t local = tok - start;
-    int64_t rem = local % (h * w);
-    int64_t bh = rem / (m * w);
-    int64_t r = rem % (m * w);
-    int64_t bw = r / ((int64_t)m * m);
-    int64_t r2 = r % ((int64_t)m * m);
-    *tpos = (int32_t)(local / (h * w));
-    *hpos = (int32_t)(bh * m + r2 / m);
-    *wpos = (int32_t)(bw * m + r2 % m);
-}
-
+/* [ViT] setup kernel's token order: the grids follow one another; a grid's
+ * tokens run frame by frame; inside a frame they run over the spatial-merge
+ * blocks (m x m patches) in raster order of the block grid (block row, then
+ * block column), and inside a block over its m x m cells row by row.  The
+ * (t, h, w) of every token is written out by walking that order, one token
+ * after the other. */
 void oracle_vit_positions(const int32_t* grid_thw, int32_t num_grids, int32_t merge,
                           int32_t* pos, int64_t n_tokens)
 {
-    for (int64_t n = 0; n < n_tokens; ++n)
-        vit_token_position(grid_thw, num_grids, merge, n, &pos[n], &pos[n_tokens + n],
-                           &pos[2 * n_tokens + n]);
+    int64_t n = 0;
+    for (int32_t g = 0; g < num_grids; ++g) {
+        const int32_t frames = grid_thw[3 * g], h = grid_thw[3 * g + 1], w = grid_thw[3 * g + 2];
+        for (int32_t t = 0; t < frames; ++t)
+            for (int32_t brow = 0; brow < h / merge; ++brow)
+                for (int32_t bcol = 0; bcol < w / merge; ++bcol)
+                    for (int32_t i = 0; i < merge; ++i)
+                        for (int32_t j = 0; j < merge; ++j) {
+                            if (n < n_tokens) {
+                                pos[n] = t;
+                                pos[n_tokens + n] = brow * merge + i;
+                                pos[2 * n_tokens + n] = bcol * merge + j;
+                            }
+                            ++n;
+                        }
+    }
+}
+
+/* (3, n_tokens) positions, freshly allocated (the caller frees them). */
+static int32_t* vit_position_table(const int32_t* grid_thw, int32_t num_grids, int32_t merge, int64_t n_tokens)
+{
+    int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(3 * (n_tokens > 0 ? n_tokens : 1)));
+    oracle_vit_positions(grid_thw, num_grids, merge, pos, n_tokens);
+    return pos;
 }
 
 /* Plane a, columns [off_a, off_a + half_a): cos and sin of
@@ -468,17 +468,17 @@ void oracle_vit_cos_sin(const float* inv_t, int32_t half_t, const float* inv_h, 
     const float* inv[3] = {inv_t, inv_h, inv_w};
     int32_t len[3] = {half_t, half_h, half_w};
     int32_t off[3] = {0, half_t, half_t + half_h};
+    int32_t* table = vit_position_table(grid_thw, num_grids, merge, n_tokens);
     for (int64_t n = 0; n < n_tokens; ++n) {
-        int32_t pos[3];
-        vit_token_position(grid_thw, num_grids, merge, n, &pos[0], &pos[1], &pos[2]);
         for (int32_t a = 0; a < 3; ++a)
             for (int32_t j = 0; j < len[a]; ++j) {
-                float theta = (float)((float)pos[a] * inv[a][j]);
+                float theta = (float)((float)table[(int64_t)a * n_tokens + n] * inv[a][j]);
                 int64_t idx = ((int64_t)a * n_tokens + n) * half_rot + off[a] + j;
                 cos_out[idx] = (float)cos((double)theta);
                 sin_out[idx] = (float)sin((double)theta);
             }
     }
+    free(table);
 }
 
 /* Setup and rotation in one step ([ViT] positions computed arithmetically
@@ -501,9 +501,9 @@ void oracle_vit_qk_norm_rope(const float* x, int64_t n_tokens, int32_t heads, in
     for (int32_t j = 0; j < half_w; ++j)
         inv[half_t + half_h + j] = inv_w[j];
     double* n = (double*)malloc(sizeof(double) * (size_t)head_dim);
+    int32_t* table = vit_position_table(grid_thw, num_grids, merge, n_tokens);
     for (int64_t tok = 0; tok < n_tokens; ++tok) {
-        int32_t pos[3];
-        vit_token_position(grid_thw, num_grids, merge, tok, &pos[0], &pos[1], &pos[2]);
+        int32_t pos[3] = {table[tok], table[n_tokens + tok], table[2 * n_tokens + tok]};
         oracle_rope rope;
         memset(&rope, 0, sizeof(rope));
         rope.mode = ORACLE_POS_AXES;
@@ -521,6 +521,7 @@ void oracle_vit_qk_norm_rope(const float* x, int64_t n_tokens, int32_t heads, in
             norm_rope_row(x + row, weight, head_dim, eps, out_kind, numerics, &rope, 0, n, out + row);
         }
     }
+    free(table);
     free(n);
     free(inv);
 }

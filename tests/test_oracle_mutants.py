@@ -29,20 +29,31 @@ MUTANTS = {
     "plane_stride_ignored": ("(int64_t)a * rope->pos_stride + t", "(int64_t)a + t"),
     "angle_not_rounded_to_fp32": ("float theta = (float)((float)pos * rope->inv_freq[p]);",
                                   "double theta = (double)pos * rope->inv_freq[p];"),
-    "imrope_h_limit_from_w": ("sector < 3 * s[1]", "sector < 3 * s[2]"),
-    "imrope_h_w_residues_swapped": ("sector % 3 == 1 && sector < 3 * s[1]", "sector % 3 == 2 && sector < 3 * s[1]"),
-    "imrope_t_limit_off": ("sector < 3 * s[0]", "sector < 3 * s[0] - 3"),
     "axes_sections_shifted": ("if (p < end)", "if (p <= end)"),
+    "imrope_residues_rotated": ("layout[3 * k + a] = a;", "layout[3 * k + (a + 1) % 3] = a;"),
+    "imrope_count_from_next_axis": ("k < s[a] && 3 * k + a < period", "k < s[(a + 1) % 3] && 3 * k + a < period"),
+    "imrope_t_run_short": ("k < s[a] && 3 * k + a < period", "k < s[a] - (a == 0) && 3 * k + a < period"),
+    "imrope_period_without_e": ("const int32_t period = s[0] + s[1] + s[2] + s[3];",
+                                "const int32_t period = s[0] + s[1] + s[2];"),
+    "vit_cells_column_major": ("pos[n_tokens + n] = brow * merge + i;\n                                "
+                               "pos[2 * n_tokens + n] = bcol * merge + j;",
+                               "pos[n_tokens + n] = brow * merge + j;\n                                "
+                               "pos[2 * n_tokens + n] = bcol * merge + i;"),
+    "vit_blocks_column_major": ("for (int32_t brow = 0; brow < h / merge; ++brow)\n"
+                                "                for (int32_t bcol = 0; bcol < w / merge; ++bcol)",
+                                "for (int32_t bcol = 0; bcol < w / merge; ++bcol)\n"
+                                "                for (int32_t brow = 0; brow < h / merge; ++brow)"),
+    "vit_h_w_swapped": ("pos[n_tokens + n] = brow * merge + i;\n                                "
+                        "pos[2 * n_tokens + n] = bcol * merge + j;",
+                        "pos[2 * n_tokens + n] = brow * merge + i;\n                                "
+                        "pos[n_tokens + n] = bcol * merge + j;"),
+    "vit_frame_not_counted": ("pos[n] = t;", "pos[n] = 0;"),
     "no_contract_rounding": ("n[i] = oracle_round_bf16(n[i]);", "n[i] = n[i];"),
     "ties_away_from_zero": ("nearbyint(ldexp(v, -q))", "round(ldexp(v, -q))"),
     "truncating_bf16": ("nearbyint(ldexp(v, -q))", "trunc(ldexp(v, -q))"),
     "joint_weights_swapped": ("qw = qw_img; kw = kw_img;", "qw = qw_txt; kw = kw_txt;"),
     "joint_local_token_positions": ("rope, tau, n, q_out", "rope, tau % (tau < tokens_txt ? tokens_txt : tokens_img), n, q_out"),
     "joint_v_from_text_only": ("memcpy(v_out + dst, v,", "memcpy(v_out + dst, v_txt,"),
-    "vit_block_column_divisor": ("int64_t bw = r / ((int64_t)m * m);", "int64_t bw = r / m;"),
-    "vit_h_w_swapped": ("*hpos = (int32_t)(bh * m + r2 / m);\n    *wpos = (int32_t)(bw * m + r2 % m);",
-                        "*wpos = (int32_t)(bh * m + r2 / m);\n    *hpos = (int32_t)(bw * m + r2 % m);"),
-    "vit_frame_not_divided": ("*tpos = (int32_t)(local / (h * w));", "*tpos = (int32_t)(local / w);"),
     "vit_plane_column_offset": ("idx = ((int64_t)a * n_tokens + n) * half_rot + off[a] + j;",
                                 "idx = ((int64_t)a * n_tokens + n) * half_rot + j;"),
     "planes_read_wrong_plane": ("int64_t idx = ((int64_t)a * rope->planes_tokens + t) * half + p;",

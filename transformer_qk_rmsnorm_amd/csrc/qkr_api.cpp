@@ -1006,9 +1006,9 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
         for (int32_t k2 = 0; k2 < n; ++k2) {
             const int32_t* g = grid_thw + 3 * (g0 + k2);
             a.vit.cu[k2] = cu;
-            // h * w and merge * w are at most t * h * w < 2^31 (h is a multiple of merge).
+            // h * w is at most t * h * w < 2^31; w / merge >= 1 (w is a multiple of merge).
             a.vit.div_area[k2] = make_fastdiv((uint32_t)((int64_t)g[1] * g[2]));
-            a.vit.div_mw[k2] = make_fastdiv((uint32_t)((int64_t)spatial_merge * g[2]));
+            a.vit.div_bcols[k2] = make_fastdiv((uint32_t)(g[2] / spatial_merge));
             cu += (int64_t)g[0] * g[1] * g[2];
         }
         a.vit.cu[n] = cu;

@@ -48,7 +48,7 @@ struct VitGridArgs {
     FastDiv div_mm;                      // merge * merge
     int64_t cu[kMaxFusedGrids + 1];      // first token of each grid, then the end
     FastDiv div_area[kMaxFusedGrids];    // h * w of each grid
-    FastDiv div_mw[kMaxFusedGrids];      // merge * w of each grid
+    FastDiv div_bcols[kMaxFusedGrids];   // w / merge (merge blocks per block row) of each grid
     const float* inv[3];                 // per-axis inverse frequencies
 };
 
@@ -126,20 +126,20 @@ struct VitArgs {
 
 // Axis of pair p (0 t, 1 h, 2 w, 3 e).  Host and device share this one
 // definition so the host can be checked without a GPU.
+//   IMROPE: pairs repeat with period S = s0 + s1 + s2 + s3.  At offset
+//     o = p mod S, the residue o mod 3 names an axis (t, h, w) and o div 3
+//     counts that axis's pairs so far in the period: the pair belongs to the
+//     axis while the count is below the axis's section, otherwise to e.
+//   AXES / PLANES: contiguous runs of s0 (t), s1 (h) and the rest (w).
 __host__ __device__ inline int32_t pair_axis(int32_t mode, const int32_t* sec, int32_t p)
 {
     if (mode == kPosImrope) {
-        // interleaved multi-section sector rule
-        const int32_t sect_dims = sec[0] + sec[1] + sec[2] + sec[3];
-        const int32_t sector = p % sect_dims;
-        const int32_t m3 = sector % 3;
-        if (m3 == 1 && sector < 3 * sec[1]) return 1;
-        if (m3 == 2 && sector < 3 * sec[2]) return 2;
-        if (m3 == 0 && sector < 3 * sec[0]) return 0;
-        return 3;
+        const int32_t o = p % (sec[0] + sec[1] + sec[2] + sec[3]);
+        const int32_t axis = o % 3, count = o / 3;
+        const int32_t limit = axis == 0 ? sec[0] : (axis == 1 ? sec[1] : sec[2]);
+        return count < limit ? axis : 3;
     }
     if (mode == kPosAxes || mode == kPosPlanes) {
-        // contiguous runs: [0, s0) t, [s0, s0+s1) h, the rest w
         if (p < sec[0]) return 0;
         if (p < sec[0] + sec[1]) return 1;
         return 2;
@@ -157,11 +157,13 @@ inline void build_axis_bits(int32_t mode, const int32_t* sec, int32_t n_pairs, u
         bits[p >> 4] |= (uint32_t)pair_axis(mode, sec, p) << ((p & 15) * 2);
 }
 
-// (t, h, w) of ViT token `tok`: its grid is the last one whose first token
-// it has reached (grids are non-empty, so this is the number of grid ends
-// reached), then frame, spatial-merge block and cell inside the block.  The
-// grid is picked by a select loop, not an index, so the device build never
-// indexes kernel arguments with a per-lane value.
+// (t, h, w) of ViT token `tok`.  Its grid is the last one whose first token
+// it has reached (grids are non-empty).  Inside the grid, a frame holds h * w
+// tokens; inside a frame, tokens come in merge blocks of m * m cells, the
+// blocks numbered in raster order over the (h / m) x (w / m) block grid and
+// the cells row by row: frame-local index = block * m^2 + cell.  The grid is
+// picked by a select loop, not an index, so the device build never indexes
+// kernel arguments with a per-lane value.
 __host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*hw)[2], int32_t num_grids,
                                              int32_t merge, int64_t tok, int32_t* tpos, int32_t* hpos,
                                              int32_t* wpos)
@@ -173,18 +175,15 @@ __host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*
         h = in_k ? hw[k][0] : h;
         w = in_k ? hw[k][1] : w;
     }
+    const int64_t m = merge;
     const int64_t local = tok - start;
-    const int64_t area = h * w;
-    const int64_t rem = local % area;
-    const int64_t mw = (int64_t)merge * w;
-    const int64_t bh = rem / mw;
-    const int64_t r = rem - bh * mw;
-    const int64_t mm = (int64_t)merge * merge;
-    const int64_t bw = r / mm;
-    const int64_t r2 = r - bw * mm;
-    *tpos = (int32_t)(local / area);
-    *hpos = (int32_t)(bh * merge + r2 / merge);
-    *wpos = (int32_t)(bw * merge + r2 % merge);
+    const int64_t frame_len = h * w;
+    const int64_t in_frame = local % frame_len;
+    const int64_t block = in_frame / (m * m), cell = in_frame % (m * m);
+    const int64_t bcols = w / m;
+    *tpos = (int32_t)(local / frame_len);
+    *hpos = (int32_t)((block / bcols) * m + cell / m);
+    *wpos = (int32_t)((block % bcols) * m + cell % m);
 }
 
 // QK RMSNorm + RoPE kernel for one lanes-per-row value (LPR in 1, 2, 4, 8, 16,

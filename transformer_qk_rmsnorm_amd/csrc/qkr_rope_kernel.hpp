@@ -21,39 +21,40 @@ struct TokenPositions {
 };
 
 // (t, h, w) of ViT token `tok` for the fused mode, wave-uniform: the grid is
-// the last one whose first token has been reached (a select loop, scalar),
-// then frame, spatial-merge block and cell ([ViT] setup kernel's token
-// order), with the host's divisors instead of hardware divides.
+// the last one whose first token has been reached (a select loop, scalar);
+// then frame, merge block (raster order over the block grid) and cell, as in
+// vit_position ([ViT] setup kernel's token order), with the host's divisors
+// instead of hardware divides.
 __device__ __forceinline__ TokenPositions vit_token_positions(const VitGridArgs& v, uint32_t tok)
 {
     // Scalar fields only: selecting whole structs out of the kernel-argument
     // table would make the compiler copy the table to private memory.
     uint32_t start = (uint32_t)v.cu[0];
     uint32_t a_d = v.div_area[0].d, a_m = v.div_area[0].m, a_l = v.div_area[0].l;
-    uint32_t w_d = v.div_mw[0].d, w_m = v.div_mw[0].m, w_l = v.div_mw[0].l;
+    uint32_t b_d = v.div_bcols[0].d, b_m = v.div_bcols[0].m, b_l = v.div_bcols[0].l;
     for (int k = 1; k < v.num_grids; ++k) {
         const bool in_k = tok >= (uint32_t)v.cu[k];
         start = in_k ? (uint32_t)v.cu[k] : start;
         a_d = in_k ? v.div_area[k].d : a_d;
         a_m = in_k ? v.div_area[k].m : a_m;
         a_l = in_k ? v.div_area[k].l : a_l;
-        w_d = in_k ? v.div_mw[k].d : w_d;
-        w_m = in_k ? v.div_mw[k].m : w_m;
-        w_l = in_k ? v.div_mw[k].l : w_l;
+        b_d = in_k ? v.div_bcols[k].d : b_d;
+        b_m = in_k ? v.div_bcols[k].m : b_m;
+        b_l = in_k ? v.div_bcols[k].l : b_l;
     }
-    const FastDiv da{a_d, a_m, a_l}, dmw{w_d, w_m, w_l};
+    const FastDiv d_frame{a_d, a_m, a_l}, d_bcols{b_d, b_m, b_l};
     const uint32_t local = tok - start;
-    const uint32_t t = fast_div(local, da);
-    const uint32_t rem = local - t * da.d;
-    const uint32_t bh = fast_div(rem, dmw);
-    const uint32_t r = rem - bh * dmw.d;
-    const uint32_t bw = fast_div(r, v.div_mm);
-    const uint32_t r2 = r - bw * v.div_mm.d;
-    const uint32_t mh = fast_div(r2, v.div_m);
+    const uint32_t t = fast_div(local, d_frame);
+    const uint32_t in_frame = local - t * d_frame.d;
+    const uint32_t block = fast_div(in_frame, v.div_mm);
+    const uint32_t cell = in_frame - block * v.div_mm.d;
+    const uint32_t brow = fast_div(block, d_bcols);
+    const uint32_t bcol = block - brow * d_bcols.d;
+    const uint32_t crow = fast_div(cell, v.div_m);
     TokenPositions p;
     p.t = (int32_t)t;
-    p.h = (int32_t)(bh * v.div_m.d + mh);
-    p.w = (int32_t)(bw * v.div_m.d + (r2 - mh * v.div_m.d));
+    p.h = (int32_t)(brow * v.div_m.d + crow);
+    p.w = (int32_t)(bcol * v.div_m.d + (cell - crow * v.div_m.d));
     p.e = 0;
     return p;
 }
