@@ -46,6 +46,7 @@ CPU_REPS = 5                   # repetitions of each CPU leg (median)
 CPU_MAX_THREADS = 16           # the host share of one GPU
 
 NUMERICS = "contract"          # set from --numerics before any workload is built
+STREAMS = 1                    # set from --streams (imrope)
 
 
 def _parse():
@@ -57,6 +58,11 @@ def _parse():
                     choices=["joint", "joint-neox", "imrope", "vit", "vit-fused", "rows1", "rows32", "rows4096",
                              "addrms4096", "addrms4096-fp8", "addrms1", "cache", "tiny", "copy"])
     ap.add_argument("--numerics", default="contract", choices=["contract", "eager"])
+    ap.add_argument("--streams", type=int, default=1,
+                    help="imrope: issue the chunk launches of a step round-robin on this many streams "
+                         "(default priority) that fork from and join the main stream, so one chunk's ramp "
+                         "can overlap the previous chunk's tail; the line then reports the step time, and "
+                         "the roofline's per-launch time is not a kernel duration")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the cache)")
     ap.add_argument("--cpu-seconds", type=float, default=60.0,
                     help="budget of the CPU oracle legs (0: skip): each leg repeats the step 5 times, or "
@@ -162,12 +168,31 @@ def build_imrope():
         q, k = case.q.to(dev), case.k.to(dev)
         return q, k, torch.empty_like(q), torch.empty_like(k)
 
+    side = []
+
     def step(state):
         q, k, qo, ko = state
-        for r in ropes:
+        if STREAMS <= 1:
+            for r in ropes:
+                b = r.token_base
+                qkr.qk_norm_rope(q[b:b + chunk], k[b:b + chunk], qw, kw, case.eps, r, q_out=qo[b:b + chunk],
+                                 k_out=ko[b:b + chunk], numerics=NUMERICS)
+            return
+        # The chunks are independent: fork side streams from the current one,
+        # launch chunk i on stream i mod STREAMS, join them back.
+        main = torch.cuda.current_stream()
+        while len(side) < STREAMS - 1:
+            side.append(torch.cuda.Stream())
+        streams = [main] + side[:STREAMS - 1]
+        for st in streams[1:]:
+            st.wait_stream(main)
+        for i, r in enumerate(ropes):
             b = r.token_base
-            qkr.qk_norm_rope(q[b:b + chunk], k[b:b + chunk], qw, kw, case.eps, r, q_out=qo[b:b + chunk],
-                             k_out=ko[b:b + chunk], numerics=NUMERICS)
+            with torch.cuda.stream(streams[i % STREAMS]):
+                qkr.qk_norm_rope(q[b:b + chunk], k[b:b + chunk], qw, kw, case.eps, r, q_out=qo[b:b + chunk],
+                                 k_out=ko[b:b + chunk], numerics=NUMERICS)
+        for st in streams[1:]:
+            main.wait_stream(st)
 
     rows = case.q.shape[1] + case.k.shape[1]
     chunk_bytes = 2 * chunk * rows * 128 * 2 + 4 * chunk * 4 + 2 * 128 * 2 + case.inv_freq.nbytes
@@ -666,7 +691,7 @@ def cpu_baseline(w, seconds):
 
 
 def main():
-    global NUMERICS
+    global NUMERICS, STREAMS
     args = _parse()
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only: every row of the path is per-row "
@@ -676,6 +701,7 @@ def main():
         print("bench.py: one process, one GPU; WORLD_SIZE > 1 is not supported", file=sys.stderr)
         sys.exit(2)
     NUMERICS = args.numerics
+    STREAMS = max(1, args.streams)
 
     import torch
 
@@ -765,7 +791,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded, workloads.py)",
         "config": dict(w.config, buffer_sets=nsets, variant=variant, bytes_per_step=w.step_bytes,
-                       numerics=NUMERICS, launch="eager" if args.eager else "hipGraph replay"),
+                       numerics=NUMERICS, launch="eager" if args.eager else "hipGraph replay",
+                       **({"streams": STREAMS} if STREAMS > 1 else {})),
         "gpu_samples": {"n": nsamp, "us_per_step_median": round(sample_us[len(sample_us) // 2], 3),
                         "us_per_step_min": round(sample_us[0], 3), "us_per_step_max": round(sample_us[-1], 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
