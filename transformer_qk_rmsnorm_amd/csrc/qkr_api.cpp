@@ -373,7 +373,8 @@ qkr_status check_grids(const int32_t* grid_thw, int32_t num_grids, int32_t merge
     return QKR_OK;
 }
 
-// Grid groups of at most kMaxGrids per launch; token offsets stay absolute.
+// Grid groups of at most kMaxGrids per launch; token offsets stay absolute
+// (every total stays below 2^31: check_grids).
 template <class F>
 hipError_t for_grid_groups(const int32_t* grid_thw, int32_t num_grids, int32_t merge, VitArgs base, F&& fn)
 {
@@ -384,15 +385,17 @@ hipError_t for_grid_groups(const int32_t* grid_thw, int32_t num_grids, int32_t m
         a.merge = merge;
         a.num_grids = n;
         a.tok_begin = start;
+        a.div_m = make_fastdiv((uint32_t)merge);
+        a.div_mm = make_fastdiv((uint32_t)(merge * merge));
         int64_t cu = start;
         for (int32_t k = 0; k < n; ++k) {
             const int32_t* g = grid_thw + 3 * (g0 + k);
-            a.cu[k] = cu;
-            a.hw[k][0] = g[1];
-            a.hw[k][1] = g[2];
+            a.cu[k] = (uint32_t)cu;
+            a.div_area[k] = make_fastdiv((uint32_t)((int64_t)g[1] * g[2]));
+            a.div_bcols[k] = make_fastdiv((uint32_t)(g[2] / merge));
             cu += (int64_t)g[0] * g[1] * g[2];
         }
-        a.cu[n] = cu;
+        a.cu[n] = (uint32_t)cu;
         a.tok_count = cu - start;
         const hipError_t e = fn(a);
         if (e != hipSuccess)
@@ -902,6 +905,10 @@ qkr_status qkr_mrope_cos_sin_setup(const float* inv_freq_t_dev, int32_t half_t, 
     base.cos_out = cos_out_dev;
     base.sin_out = sin_out_dev;
     base.n_tokens = n_tokens;
+    base.div_groups = make_fastdiv((uint32_t)((base.half_rot + 3) / 4));
+    // 16-byte stores need aligned planes and sections of whole 4-column groups.
+    base.vec_ok = aligned(cos_out_dev, 16) && aligned(sin_out_dev, 16) && half_t % 4 == 0 && half_h % 4 == 0 &&
+                  half_w % 4 == 0;
     (void)hipGetLastError();
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e = for_grid_groups(grid_thw, num_grids, spatial_merge, base,
@@ -1090,17 +1097,15 @@ qkr_status qkr_vit_positions_host(const int32_t* grid_thw, int32_t num_grids, in
         return st;
     if (n_tokens != total || out_host == nullptr)
         return fail(QKR_ERR_INVALID_ARGUMENT, "n_tokens must equal sum t*h*w and out must be non-null");
-    std::vector<int64_t> cu(num_grids + 1, 0);
-    std::vector<int32_t> hw(2 * (size_t)num_grids);
-    for (int32_t g = 0; g < num_grids; ++g) {
-        cu[g + 1] = cu[g] + (int64_t)grid_thw[3 * g] * grid_thw[3 * g + 1] * grid_thw[3 * g + 2];
-        hw[2 * g] = grid_thw[3 * g + 1];
-        hw[2 * g + 1] = grid_thw[3 * g + 2];
-    }
-    const int32_t(*hwp)[2] = reinterpret_cast<const int32_t(*)[2]>(hw.data());
-    for (int64_t n = 0; n < n_tokens; ++n)
-        vit_position(cu.data(), hwp, num_grids, spatial_merge, n, &out_host[n], &out_host[n_tokens + n],
-                     &out_host[2 * n_tokens + n]);
+    VitArgs base{};
+    base.n_tokens = n_tokens;
+    for_grid_groups(grid_thw, num_grids, spatial_merge, base, [&](const VitArgs& a) {
+        for (int64_t i = 0; i < a.tok_count; ++i) {
+            const int64_t n = a.tok_begin + i;
+            vit_position(a, (uint32_t)n, &out_host[n], &out_host[n_tokens + n], &out_host[2 * n_tokens + n]);
+        }
+        return hipSuccess;
+    });
     return ok();
 }
 

@@ -108,6 +108,9 @@ struct RmsArgs {
     float inv_width;
 };
 
+// ViT setup (and position map) launch over at most kMaxGrids grids.  Token
+// counts stay below 2^31, so positions are found with 32-bit arithmetic and
+// host-built divisors.
 struct VitArgs {
     const float* inv[3];
     float* cos_out;
@@ -120,8 +123,12 @@ struct VitArgs {
     int32_t half_rot;
     int32_t merge;
     int32_t num_grids;          // grids in this launch
-    int64_t cu[kMaxGrids + 1];  // token offsets of this launch's grids (absolute)
-    int32_t hw[kMaxGrids][2];   // h, w of each grid
+    int32_t vec_ok;             // whole 4-column groups may leave as 16-byte stores (host-checked)
+    uint32_t cu[kMaxGrids + 1]; // token offsets of this launch's grids (absolute)
+    FastDiv div_area[kMaxGrids];   // h * w of each grid
+    FastDiv div_bcols[kMaxGrids];  // w / merge of each grid
+    FastDiv div_m, div_mm;         // merge, merge^2
+    FastDiv div_groups;            // 4-column groups per token: ceil(half_rot / 4)
 };
 
 // Axis of pair p (0 t, 1 h, 2 w, 3 e).  Host and device share this one
@@ -162,28 +169,33 @@ inline void build_axis_bits(int32_t mode, const int32_t* sec, int32_t n_pairs, u
 // tokens; inside a frame, tokens come in merge blocks of m * m cells, the
 // blocks numbered in raster order over the (h / m) x (w / m) block grid and
 // the cells row by row: frame-local index = block * m^2 + cell.  The grid is
-// picked by a select loop, not an index, so the device build never indexes
-// kernel arguments with a per-lane value.
-__host__ __device__ inline void vit_position(const int64_t* cu, const int32_t (*hw)[2], int32_t num_grids,
-                                             int32_t merge, int64_t tok, int32_t* tpos, int32_t* hpos,
+// picked by a select loop over the launch's grids; the divisions use the
+// host's divisors.  Host and device share this one definition.
+__host__ __device__ inline void vit_position(const VitArgs& a, uint32_t tok, int32_t* tpos, int32_t* hpos,
                                              int32_t* wpos)
 {
-    int64_t start = cu[0], h = hw[0][0], w = hw[0][1];
-    for (int32_t k = 1; k < num_grids; ++k) {
-        const bool in_k = tok >= cu[k];
-        start = in_k ? cu[k] : start;
-        h = in_k ? hw[k][0] : h;
-        w = in_k ? hw[k][1] : w;
+    uint32_t start = a.cu[0];
+    FastDiv d_frame = a.div_area[0], d_bcols = a.div_bcols[0];
+    for (int32_t k = 1; k < a.num_grids; ++k) {
+        const bool in_k = tok >= a.cu[k];
+        start = in_k ? a.cu[k] : start;
+        d_frame.d = in_k ? a.div_area[k].d : d_frame.d;
+        d_frame.m = in_k ? a.div_area[k].m : d_frame.m;
+        d_frame.l = in_k ? a.div_area[k].l : d_frame.l;
+        d_bcols.d = in_k ? a.div_bcols[k].d : d_bcols.d;
+        d_bcols.m = in_k ? a.div_bcols[k].m : d_bcols.m;
+        d_bcols.l = in_k ? a.div_bcols[k].l : d_bcols.l;
     }
-    const int64_t m = merge;
-    const int64_t local = tok - start;
-    const int64_t frame_len = h * w;
-    const int64_t in_frame = local % frame_len;
-    const int64_t block = in_frame / (m * m), cell = in_frame % (m * m);
-    const int64_t bcols = w / m;
-    *tpos = (int32_t)(local / frame_len);
-    *hpos = (int32_t)((block / bcols) * m + cell / m);
-    *wpos = (int32_t)((block % bcols) * m + cell % m);
+    const uint32_t local = tok - start;
+    const uint32_t frame = fast_div(local, d_frame);
+    const uint32_t in_frame = local - frame * d_frame.d;
+    const uint32_t block = fast_div(in_frame, a.div_mm);
+    const uint32_t cell = in_frame - block * a.div_mm.d;
+    const uint32_t brow = fast_div(block, d_bcols);
+    const uint32_t crow = fast_div(cell, a.div_m);
+    *tpos = (int32_t)frame;
+    *hpos = (int32_t)(brow * a.div_m.d + crow);
+    *wpos = (int32_t)((block - brow * d_bcols.d) * a.div_m.d + (cell - crow * a.div_m.d));
 }
 
 // QK RMSNorm + RoPE kernel for one lanes-per-row value (LPR in 1, 2, 4, 8, 16,

@@ -193,29 +193,51 @@ __global__ __launch_bounds__(kThreads) void debug_fp8_kernel(const float* x, int
 }
 
 // ---------------------------------------------------------------------------
-// ViT cos/sin planes ([ViT] setup kernel): one thread per (token, column).
-// Column c belongs to axis a (t, h, w contiguous); plane a receives
-// cos/sin(fl32(pos_a) * inv_a[c - off_a]) at [a][token][c].
+// ViT cos/sin planes ([ViT] setup kernel): one thread per (token, group of 4
+// columns).  Column c belongs to axis a (t, h, w contiguous); plane a receives
+// cos/sin(fl32(pos_a) * inv_a[c - off_a]) at [a][token][c].  A group whose
+// four columns lie in one plane leaves as one 16-byte store per plane when
+// the host allows it (aligned planes, sections of whole groups); otherwise
+// column by column.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void vit_setup_kernel(const VitArgs a)
 {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (idx >= a.tok_count * a.half_rot)
+    const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t groups = a.div_groups.d;
+    if (idx >= (uint32_t)a.tok_count * groups)
         return;
-    const int64_t tok = a.tok_begin + idx / a.half_rot;
-    const int32_t col = (int32_t)(idx % a.half_rot);
+    const uint32_t tl = fast_div(idx, a.div_groups);
+    const int32_t c0 = 4 * (int32_t)(idx - tl * groups);
+    const uint32_t tok = (uint32_t)a.tok_begin + tl;
     int32_t pos[3];
-    vit_position(a.cu, a.hw, a.num_grids, a.merge, tok, &pos[0], &pos[1], &pos[2]);
-    const int axis = col < a.off[1] ? 0 : (col < a.off[2] ? 1 : 2);
-    const float* inv = axis == 0 ? a.inv[0] : (axis == 1 ? a.inv[1] : a.inv[2]);
-    const int32_t off = axis == 0 ? a.off[0] : (axis == 1 ? a.off[1] : a.off[2]);
-    const int32_t p = axis == 0 ? pos[0] : (axis == 1 ? pos[1] : pos[2]);
-    const float theta = (float)p * inv[col - off];
-    float s, c;
-    sincosf(theta, &s, &c);
-    const int64_t o = ((int64_t)axis * a.n_tokens + tok) * a.half_rot + col;
-    a.cos_out[o] = c;
-    a.sin_out[o] = s;
+    vit_position(a, tok, &pos[0], &pos[1], &pos[2]);
+    float cv[4], sv[4];
+    int axis[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int32_t col = c0 + e < a.half_rot ? c0 + e : a.half_rot - 1;
+        const int ax = col < a.off[1] ? 0 : (col < a.off[2] ? 1 : 2);
+        const float* inv = ax == 0 ? a.inv[0] : (ax == 1 ? a.inv[1] : a.inv[2]);
+        const int32_t off = ax == 0 ? a.off[0] : (ax == 1 ? a.off[1] : a.off[2]);
+        const int32_t p = ax == 0 ? pos[0] : (ax == 1 ? pos[1] : pos[2]);
+        sincosf((float)p * inv[col - off], &sv[e], &cv[e]);
+        axis[e] = ax;
+    }
+    const int64_t row = ((int64_t)axis[0] * a.n_tokens + tok) * a.half_rot + c0;
+    if (a.vec_ok) {
+        // groups never straddle a section and rows are whole groups
+        *reinterpret_cast<float4*>(a.cos_out + row) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+        *reinterpret_cast<float4*>(a.sin_out + row) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (c0 + e >= a.half_rot)
+            break;
+        const int64_t o = ((int64_t)axis[e] * a.n_tokens + tok) * a.half_rot + c0 + e;
+        a.cos_out[o] = cv[e];
+        a.sin_out[o] = sv[e];
+    }
 }
 
 // The axis of every pair as the rotation kernels decode it from the table.
@@ -234,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void debug_vit_kernel(const VitArgs a, in
         return;
     const int64_t tok = a.tok_begin + i;
     int32_t t, h, w;
-    vit_position(a.cu, a.hw, a.num_grids, a.merge, tok, &t, &h, &w);
+    vit_position(a, (uint32_t)tok, &t, &h, &w);
     out[tok] = t;
     out[a.n_tokens + tok] = h;
     out[2 * a.n_tokens + tok] = w;
@@ -500,7 +522,7 @@ hipError_t launch_debug_fp8(const float* x, int64_t n, const float* scale, uint8
 
 hipError_t launch_vit_setup(const VitArgs& a, hipStream_t stream)
 {
-    const int64_t n = a.tok_count * a.half_rot;
+    const int64_t n = a.tok_count * (int64_t)a.div_groups.d;
     if (n == 0)
         return hipSuccess;
     hipLaunchKernelGGL(vit_setup_kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
