@@ -111,6 +111,9 @@ __device__ __forceinline__ T sel3(int i, T v0, T v1, T v2)
 // writes cost HBM efficiency.  The pass's results then go through a per-wave
 // LDS slice indexed by (row, vector) and leave as vectors lane and 64 + lane
 // of the pass, i.e. contiguous 1 KB runs when a token's heads are adjacent.
+// In the planes mode the rows also arrive that way and reach the lane-local
+// layout through the same slice (8 more VGPRs: a gain where cos/sin come
+// from memory, a loss where the wave computes them, measured both ways).
 //
 // ROPE: 0 norm only, 1 positions + inv_freq (1D / AXES / IMROPE: the axis
 // table carries the difference), 2 cos/sin planes, 3 ViT positions computed
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     constexpr int VE = E::VE;
     constexpr int RPP = 64 / LPR;
     constexpr bool ROT = ROPE != 0;
+    constexpr bool STAGE_LD = STAGE && ROPE == 2;   // staged loads as well as stores
     static_assert((LPR & (LPR - 1)) == 0 && LPR <= 32, "lanes per row: a power of two up to 32");
 
     const int lane = threadIdx.x & 63;
@@ -190,13 +194,31 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const int32_t off0 = (own0 ? v0 : 0) * 16, off1 = (own1 ? v1 : 0) * 16;
 
     // Loads of pass p: head p * RPP + g of the tile, clamped into the tensor.
+    // Staged loads: the pass's vectors in (row, vector) order instead, vector
+    // sl * 64 + lane in slot sl (past the pass's last vector: a re-read of
+    // it), handed to the lane-local layout through LDS (unstage below).
     const int64_t lane_in0 = (int64_t)g * in_sh + off0;
+    int ld_row[2] = {0, 0}, ld_col[2] = {0, 0};
+    if constexpr (STAGE_LD) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int f = sl * 64 + lane < RPP * nv ? sl * 64 + lane : RPP * nv - 1;
+            const int fr = (int)(((uint32_t)f * a.nv_recip) >> 16);
+            ld_row[sl] = fr;
+            ld_col[sl] = (f - fr * nv) * 16;
+        }
+    }
     auto load_pass = [&](int p, uint4& x0, uint4& x1) {
-        const int lim = hrem - 1 - p * RPP;    // last valid g of the pass (may be < 0)
+        const int lim = hrem - 1 - p * RPP;    // last valid row of the pass (may be < 0)
         const char* base = in_t + (int64_t)(p * RPP) * in_sh;
-        const int64_t o0 = (p + 1) * RPP <= hrem ? lane_in0 : (int64_t)(g < lim ? g : lim) * in_sh + off0;
-        x0 = load_row16<NT>(base + o0);
-        x1 = load_row16<NT>(base + o0 + (off1 - off0));
+        if constexpr (STAGE_LD) {
+            x0 = load_row16<NT>(base + (int64_t)(ld_row[0] < lim ? ld_row[0] : lim) * in_sh + ld_col[0]);
+            x1 = load_row16<NT>(base + (int64_t)(ld_row[1] < lim ? ld_row[1] : lim) * in_sh + ld_col[1]);
+        } else {
+            const int64_t o0 = (p + 1) * RPP <= hrem ? lane_in0 : (int64_t)(g < lim ? g : lim) * in_sh + off0;
+            x0 = load_row16<NT>(base + o0);
+            x1 = load_row16<NT>(base + o0 + (off1 - off0));
+        }
     };
 
     // The output row of the token: the token itself, or the cache row its
@@ -240,6 +262,26 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         }
         return t;
     };
+    // Staged: the pass's flat vectors (slots as loaded) to the lane-local
+    // layout: vectors v0, v1 of row g (a vector the lane does not own: the
+    // row's first, which the sum of squares skips).
+    auto unstage = [&](uint4& x0, uint4& x1) {
+        stage[lane] = x0;
+        stage[64 + lane] = x1;     // slots past the pass's vectors are never read
+        wave_lds_order();
+        x0 = stage[g * nv + (own0 ? v0 : 0)];
+        x1 = stage[g * nv + (own1 ? v1 : 0)];
+        wave_lds_order();
+    };
+    // Staged stores of flat vectors (a routed tile's loads as they came).
+    auto store_flat = [&](const Dst& t, int p, const uint4& f0, const uint4& f1) {
+        const int64_t pass_off = (int64_t)(p * RPP) * out_sh;
+        const int live = pad ? 0 : hrem - p * RPP;
+        if (t.slot_row[0] < live)
+            store_row16<NT>(t.slot_out[0] + pass_off, f0);
+        if (t.slot_row[1] < live)
+            store_row16<NT>(t.slot_out[1] + pass_off, f1);
+    };
     auto store_pass = [&](const Dst& t, int p, const uint4& o0, const uint4& o1) {
         const int64_t pass_off = (int64_t)(p * RPP) * out_sh;           // wave-uniform
         const int live = pad ? 0 : hrem - p * RPP;                       // rows of the pass to store
@@ -249,10 +291,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
                 if (own1) stage[g * nv + v1] = o1;
             }
             wave_lds_order();
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
-                if (t.slot_row[sl] < live)
-                    store_row16<NT>(t.slot_out[sl] + pass_off, stage[sl * 64 + lane]);
+            store_flat(t, p, stage[lane], stage[64 + lane]);
             wave_lds_order();
         } else {
             if (g < live) {
@@ -282,9 +321,14 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
             return;
         const Dst t = dst_of(out_t);
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-            if (p * RPP < hrem)   // wave-uniform: a pass past the tensor has nothing to store
-                store_pass(t, p, d[p][0], d[p][1]);
+        for (int p = 0; p < NP; ++p) {
+            if (p * RPP < hrem) {   // wave-uniform: a pass past the tensor has nothing to store
+                if constexpr (STAGE_LD)
+                    store_flat(t, p, d[p][0], d[p][1]);
+                else
+                    store_pass(t, p, d[p][0], d[p][1]);
+            }
+        }
         return;
     }
 
@@ -411,6 +455,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         // no row to normalise: wave-uniform skip; the load count is unchanged.
         if (p * RPP >= hrem)
             break;
+        if constexpr (STAGE_LD)
+            unstage(d[p][0], d[p][1]);
         const float s0 = E::sumsq(d[p][0], 0.0f);
         const float part = (own0 ? s0 : 0.0f) + (own1 ? E::sumsq(d[p][1], 0.0f) : 0.0f);
         const float rrms = rms_rsqrt(group_sum<LPR>(part) * inv_d + eps, eps_normal);
