@@ -175,6 +175,44 @@ __device__ __forceinline__ void store_row16(char* p, const uint4& v)
     }
 }
 
+// Raw buffer access (stride 0) through a wave-uniform resource over `bytes`
+// bytes at p: the hardware's range check makes a load at an offset >= bytes
+// read zeros and drops a store there, so a slot past the end of a row needs
+// no branch.  The third descriptor word is the gfx9-family data format.
+// NT sets the nontemporal cache policy (as the global forms above).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+template <bool NT>
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool NT>
+__device__ __forceinline__ void buffer_store16(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, NT ? 2 : 0);
+}
+
+template <bool NT>
+__device__ __forceinline__ void buffer_store8(uint32_t lo, uint32_t hi, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t w = {lo, hi};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, NT ? 2 : 0);
+}
+
+template <bool NT>
+__device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, NT ? 2 : 0);
+}
+
 // ---------------------------------------------------------------------------
 // Wavefront reductions without LDS.  DPP moves inside rows of 16 lanes:
 // quad_perm xor 1 and xor 2, then row_half_mirror (lane i <- 7 - i within 8
