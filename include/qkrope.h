@@ -137,8 +137,9 @@ typedef struct {
  *   y[r, i] = round(x[r, i] * rrms_r * weight[i]),
  *   rrms_r = 1 / sqrt(mean_i(x[r, i]^2) + eps), sum of squares in fp32,
  * one rounding to the output type.  x, y: [rows, width] with row strides in
- * elements; weight: [width].  rows == 0 is a no-op.  Below 2048 rows each row
- * runs on a workgroup of four wavefronts, above on one wavefront. */
+ * elements; weight: [width].  rows == 0 is a no-op.  From 2048 to 4096 rows
+ * (and for rows of fewer than 64 16-byte vectors) each row runs on one
+ * wavefront, otherwise on a workgroup of four wavefronts. */
 qkr_status qkr_rms_norm(const void* x_dev, int64_t x_row_stride, void* y_dev, int64_t y_row_stride,
                         const void* weight_dev, int64_t rows, int32_t width, float eps,
                         int32_t dtype, qkr_stream_t stream);

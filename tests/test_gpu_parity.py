@@ -204,7 +204,7 @@ def test_rms_norm_rows(t, variant):
     if variant is not None:
         assert name.startswith(variant + ":"), name
     else:
-        assert name.startswith("rms:wide" if t < 2048 else "rms:rows"), name
+        assert name.startswith("rms:rows" if 2048 <= t <= 4096 else "rms:wide"), name
     ref = oracle.rms_norm(W.as_f32(case.x), W.as_f32(case.weight), case.eps, "bf16")
     assert_bf16_close(host(y), ref, what=f"rms t={t} {name}")
 

@@ -492,14 +492,21 @@ const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, 
     const int vpl_wide = round_vpl((nvec + kThreads - 1) / kThreads);
     int kind = kind_req;
     if (kind < 0) {
-        // A workgroup per row below 2048 rows, a wavefront per row above.
-        // Measured on MI355X, rows of 5120 bf16 (wide / one wave per row /
-        // split): 1 row 2.16 / 3.27 / 2.23 us, 32 rows 2.82 / 4.50 / 3.31,
-        // 128 rows 3.04 / 4.78 / 4.30, 1024 rows 4.95 / 5.97, 2048 rows 7.95
-        // / 8.18, 4096 rows 15.6 / 13.8.  The split variant never wins; it
-        // stays reachable through the variant override.  Rows too long for
+        // A wavefront per row from 2048 to 4096 rows, a workgroup per row
+        // below and above.  Up to 4096 rows (256 compute units x 4 SIMDs x 4
+        // waves) the wave-per-row launch is a single round of waves; past it
+        // the workgroups, four waves each over one row, overlap better.
+        // Measured on MI355X, rows of 5120 bf16, wide / one wave per row, us:
+        // 512 rows 3.44 / 5.28, 1024 5.25 / 5.87, 1536 7.28 / 7.00, 2048
+        // 8.99 / 7.68, 3072 12.4 / 11.0, 4096 15.8 / 14.1, 6144 22.4 / 21.3,
+        // 8192 29.1 / 30.1; with the residual add 1024 8.91 / 7.80, 2048
+        // 15.6 / 14.0, 4096 28.6 / 27.9, 6144 41.5 / 47.1, 8192 54.9 / 60.4.
+        // The split variant (1 row 2.23 us against 2.16 wide, 32 rows 3.31
+        // against 2.82) never wins; it stays reachable through the variant
+        // override.  Rows of fewer than 64 vectors keep a wave each (a
+        // workgroup would leave most of its lanes idle); rows too long for
         // one wavefront go to the workgroup-wide variant.
-        kind = rows < 2048 && nvec >= 64 ? 2 : 0;
+        kind = nvec >= 64 && (rows < 2048 || rows > 4096) ? 2 : 0;
         if (kind == 0 && vpl_wave < 0)
             kind = 2;
     } else {
