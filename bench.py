@@ -46,6 +46,7 @@ CPU_REPS = 5                   # repetitions of each CPU leg (median)
 CPU_MAX_THREADS = 16           # the host share of one GPU
 
 NUMERICS = "contract"          # set from --numerics before any workload is built
+SLOTS = "random"               # set from --slots (cache workload)
 STREAMS = 1                    # set from --streams (imrope)
 
 
@@ -58,6 +59,9 @@ def _parse():
                     choices=["joint", "joint-neox", "imrope", "vit", "vit-fused", "rows1", "rows32", "rows4096",
                              "addrms4096", "addrms4096-fp8", "addrms1", "cache", "tiny", "copy"])
     ap.add_argument("--numerics", default="contract", choices=["contract", "eager"])
+    ap.add_argument("--slots", default="random", choices=["random", "blocks"],
+                    help="cache workload's slot map: random slots (each token's K/V rows land alone), or "
+                         "blocks (16 consecutive tokens fill one block, blocks in random order)")
     ap.add_argument("--streams", type=int, default=1,
                     help="imrope: issue the chunk launches of a step round-robin on this many streams "
                          "(default priority) that fork from and join the main stream, so one chunk's ramp "
@@ -394,8 +398,11 @@ def build_rows(t):
 
 def build_cache():
     """IMROPE QK norm + RoPE of 8192 tokens (16 Q, 8 K/V heads x 128, bf16) with
-    K and V written into a paged cache (2048 blocks x 16 slots) through a
-    random injective slot mapping, one launch."""
+    K and V written into a paged cache (2048 blocks x 16 slots), one launch.
+    Slot map (--slots): random, an injective map of single slots (each
+    token's 2 KB K and V rows land alone: the worst case for the writes), or
+    blocks, the way a paged cache fills: 16 consecutive tokens take the 16
+    slots of one block, the blocks drawn in random order."""
     import torch
 
     import transformer_qk_rmsnorm_amd as qkr
@@ -406,7 +413,12 @@ def build_cache():
     T, H, KV, D = case.q.shape[0], case.q.shape[1], case.k.shape[1], 128
     blocks, bs = 2048, 16
     v_host = W.to_dtype(W.normal((T, KV, D), 0.0, 1.0, 61), "bf16")
-    slots_host = torch.from_numpy(np.random.default_rng(61).permutation(blocks * bs)[:T].astype(np.int64))
+    if SLOTS == "blocks":
+        order = np.random.default_rng(61).permutation(blocks)[:T // bs].astype(np.int64)
+        t_idx = np.arange(T, dtype=np.int64)
+        slots_host = torch.from_numpy(order[t_idx // bs] * bs + t_idx % bs)
+    else:
+        slots_host = torch.from_numpy(np.random.default_rng(61).permutation(blocks * bs)[:T].astype(np.int64))
     pos = torch.from_numpy(case.positions).to(dev)
     inv = torch.from_numpy(case.inv_freq).to(dev)
     rope = qkr.Rope("imrope", D, "neox", inv_freq=inv, positions=pos, sections=case.sections)
@@ -448,7 +460,7 @@ def build_cache():
     w = Workload()
     w.name = "IMROPE QK RMSNorm + RoPE with K/V written into a paged cache by slot mapping"
     w.config = {"workload": w.name, "tokens": T, "q_heads": H, "kv_heads": KV, "head_dim": D,
-                "sections": list(case.sections), "cache_blocks": blocks, "block_size": bs}
+                "sections": list(case.sections), "cache_blocks": blocks, "block_size": bs, "slot_map": SLOTS}
     w.step_bytes = w.launch_bytes = nbytes
     w.launches = 1
     w.make_set, w.step, w.cpu_parts = make_set, step, cpu_parts
@@ -691,7 +703,7 @@ def cpu_baseline(w, seconds):
 
 
 def main():
-    global NUMERICS, STREAMS
+    global NUMERICS, STREAMS, SLOTS
     args = _parse()
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only: every row of the path is per-row "
@@ -702,6 +714,7 @@ def main():
         sys.exit(2)
     NUMERICS = args.numerics
     STREAMS = max(1, args.streams)
+    SLOTS = args.slots
 
     import torch
 
@@ -797,7 +810,9 @@ def main():
                         "us_per_step_min": round(sample_us[0], 3), "us_per_step_max": round(sample_us[-1], 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload) if NUMERICS == "contract" else None,
+                     "traffic": (measured_traffic(args.workload + ("-blocks" if SLOTS == "blocks" and args.workload == "cache"
+                                                                    else ""))
+                                 if NUMERICS == "contract" else None),
                      "bytes_per_launch": w.launch_bytes, "kernel": variant},
     }
     if args.cpu_seconds > 0 and w.cpu_parts is not None:

@@ -974,15 +974,22 @@ def test_cache_write_paged_sparse_slots(dtype):
     assert np.array_equal(host(vc).reshape(num_slots, kvh, d), rv)   # V copied bit for bit
 
 
-def test_cache_write_full_size():
-    """The timed cache-write configuration: 8192 tokens of the IMROPE workload
+@pytest.mark.parametrize("slot_map", ["random", "blocks"])
+def test_cache_write_full_size(slot_map):
+    """The timed cache-write configurations: 8192 tokens of the IMROPE workload
     (16 Q, 8 K/V heads x 128, bf16) into a paged cache of 2048 blocks x 16
-    slots through a random injective slot map, one launch."""
+    slots, one launch, through a random injective map of single slots or a
+    block-ordered one (16 consecutive tokens per block, blocks in random
+    order)."""
     case = W.imrope()
     T, H, KV, D = case.q.shape[0], case.q.shape[1], case.k.shape[1], 128
     blocks, bs = 2048, 16
     v = W.to_dtype(W.normal((T, KV, D), 0.0, 1.0, 61), "bf16")
-    slots = np.random.default_rng(61).permutation(blocks * bs)[:T].astype(np.int64)
+    if slot_map == "blocks":
+        order = np.random.default_rng(61).permutation(blocks)[:T // bs].astype(np.int64)
+        slots = order[np.arange(T) // bs] * bs + np.arange(T) % bs
+    else:
+        slots = np.random.default_rng(61).permutation(blocks * bs)[:T].astype(np.int64)
     kc = torch.zeros((blocks, bs, KV, D), dtype=torch.bfloat16, device=DEV)
     vc = torch.zeros_like(kc)
     rope = qkr.Rope("imrope", D, "neox", inv_freq=gpu(torch.from_numpy(case.inv_freq)),
