@@ -67,32 +67,37 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
     if (row >= a.rows)
         return;   // wave-uniform (workgroup-uniform for KIND 2)
 
-    // Two ways to reach the row, chosen per variant by measurement (rows of
+    // How the row is reached, chosen per variant by measurement (rows of
     // 5120 bf16 on MI355X):
-    //  * BUF (workgroup-per-row and split variants, the few-row launches):
-    //    every access goes through a buffer resource over its row (uniform
-    //    per wave or workgroup).  A slot past the row reads zeros, which add
-    //    nothing to the sum of squares, and its stores are dropped by the
-    //    range check, so no access needs a branch and every load (weights,
-    //    x, residual) is issued before the first store.  Stores count in the
-    //    same vector-memory counter as loads: a load issued after a store
-    //    makes whatever waits for it wait for the store too.  1 / 32 rows:
-    //    1.84 / 2.20 us against 2.13 / 2.50 us in the guarded form; one row
-    //    with the residual add 2.07 against 2.36 us.
-    //  * guarded (wave-per-row variant, 2048 rows and up): per-slot range
-    //    tests, the weight vector read beside each output vector.  The
-    //    launch is a single round of waves, and there the store-by-store
-    //    pacing this gives measured faster than issuing every load first:
-    //    4096 rows 13.95 against 15.3 us, with the residual add 27.4
-    //    against 28.8 us, to FP8 26.5 against 26.4 us.
-    constexpr bool BUF = KIND != 0;
+    //  * EARLY (workgroup-per-row and split variants, the few-row launches,
+    //    and the wave-per-row FP8 output): every load (weights, x, the
+    //    residual) is issued before the first store and no access branches.
+    //    Stores go through a buffer resource over their row, whose range
+    //    check drops a store past the row.  Stores count in the same
+    //    vector-memory counter as loads: a load issued after a store makes
+    //    whatever waits for it wait for the store too.  Rows are read through
+    //    buffer resources as well (a load past the row reads zeros, which add
+    //    nothing to the sum of squares), except in the wave-per-row FP8
+    //    variant, which reads them with global loads clamped into the row and
+    //    zeroed past it (measured 26.15 us for 4096 rows against 26.4 through
+    //    buffers and 26.5 guarded).  1 / 32 rows: 1.84 / 2.20 us against
+    //    2.13 / 2.50 us guarded; one row with the residual add 2.07 against
+    //    2.36 us.
+    //  * guarded (wave-per-row bf16 / fp32 outputs, 2048 to 4096 rows):
+    //    per-slot range tests, the weight vector read beside each output
+    //    vector.  The launch is a single round of waves, and there the
+    //    store-by-store pacing this gives measured faster than issuing every
+    //    load first: 4096 rows 13.95 against 15.3 us, with the residual add
+    //    27.4 against 28.8 us.
+    constexpr bool EARLY = KIND != 0 || FP8;
+    constexpr bool BUF_ROWS = KIND != 0;
     const uint32_t row_bytes = (uint32_t)a.nvec * 16;
     float scale = 1.0f;
     if constexpr (FP8)
         scale = *a.scale;   // wave-uniform
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.w, row_bytes);
-    uint4 wv[BUF ? VPL : 1];
-    if constexpr (BUF) {
+    uint4 wv[EARLY ? VPL : 1];
+    if constexpr (EARLY) {
 #pragma unroll
         for (int k = 0; k < VPL; ++k)
             wv[k] = buffer_load16<false>(wr, (uint32_t)(first + k * step) * 16);
@@ -100,10 +105,16 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
     // Slot k of a row: the lane's vector first + k * step, zero past the row.
     auto load_slot = [&](const char* rowp, const __amdgpu_buffer_rsrc_t& rr, int k) {
         const int v = first + k * step;
-        if constexpr (BUF)
+        if constexpr (BUF_ROWS) {
             return buffer_load16<NT>(rr, (uint32_t)v * 16);
-        else
+        } else if constexpr (EARLY) {
+            uint4 t = load_row16<NT>(rowp + (int64_t)min(v, a.nvec - 1) * 16);
+            if (v >= a.nvec)
+                t = make_uint4(0, 0, 0, 0);
+            return t;
+        } else {
             return v < a.nvec ? load_row16<NT>(rowp + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
+        }
     };
     const char* const xrow = a.x + row * a.x_stride;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(xrow, row_bytes);
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
         for (int k = 0; k < VPL; ++k) {
             const int v = first + k * step;
             d[k] = E::add(d[k], rv[k]);   // zero + zero past the row
-            if constexpr (BUF)
+            if constexpr (EARLY)
                 buffer_store16<NT>(d[k], sr, (uint32_t)v * 16);
             else if (v < a.nvec)
                 store_row16<NT>(srow + (int64_t)v * 16, d[k]);
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
     const float rrms = rms_rsqrt(ss * a.inv_width + a.eps, a.eps >= FLT_MIN);
     const float inv_scale = FP8 ? 1.0f / scale : 1.0f;
 
-    // Output vectors [lo, hi) of the row (the split variant's slice).  BUF:
+    // Output vectors [lo, hi) of the row (the split variant's slice).  EARLY:
     // through a resource over just those vectors, a slot outside them sent to
     // offset `out_bytes`, which the range check drops.
     constexpr uint32_t OUT_VB = FP8 ? VE : 16;   // output bytes per vector
@@ -169,12 +180,12 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
     for (int k = 0; k < VPL; ++k) {
         const int v = first + k * step;
         const bool in_slice = v >= lo && v < hi;
-        if (!BUF && !in_slice)
+        if (!EARLY && !in_slice)
             continue;
         const uint32_t off = in_slice ? (uint32_t)(v - lo) * OUT_VB : out_bytes;
         float xv[VE], wf[VE];
         E::unpack(d[k], xv);
-        if constexpr (BUF)
+        if constexpr (EARLY)
             E::unpack(wv[k], wf);
         else
             E::unpack(load16(a.w + (int64_t)v * 16), wf);
@@ -201,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
                                       div_by_scale(xv[4 * q + 1], scale, inv_scale),
                                       div_by_scale(xv[4 * q + 2], scale, inv_scale),
                                       div_by_scale(xv[4 * q + 3], scale, inv_scale));
-            if constexpr (BUF) {
+            if constexpr (EARLY) {
                 if constexpr (VE == 8)
                     buffer_store8<NT>(c[0], c[1], yr, off);
                 else
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void rms_kernel(const RmsArgs a)
                 }
             }
         } else {
-            if constexpr (BUF)
+            if constexpr (EARLY)
                 buffer_store16<NT>(E::pack(xv), yr, off);
             else
                 store_row16<NT>(yrow + (int64_t)v * 16, E::pack(xv));
