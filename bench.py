@@ -592,19 +592,27 @@ KERNEL_SOURCES = ["transformer_qk_rmsnorm_amd/csrc/" + f for f in
                    "qkr_internal.hpp", "qkr_fastdiv.hpp")]
 
 
-def kernel_source_hash():
-    """Hash of the kernel sources' code with comments removed: the counters
-    depend on the code, so a comment edit keeps them valid."""
+def code_hash(texts):
+    """Hash of C++ sources with comments removed and whitespace runs collapsed:
+    the counters depend on the code, so a comment or layout edit keeps them
+    valid."""
     import hashlib
     import re
     h = hashlib.sha256()
+    for text in texts:
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = re.sub(r"\s+", " ", text).strip()
+        h.update(text.encode("utf-8") + b"\0")
+    return h.hexdigest()
+
+
+def kernel_source_hash():
+    texts = []
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
-            text = f.read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", "", text)
-        h.update(text.encode("utf-8"))
-    return h.hexdigest()
+            texts.append(f.read())
+    return code_hash(texts)
 
 
 def measured_traffic(workload):

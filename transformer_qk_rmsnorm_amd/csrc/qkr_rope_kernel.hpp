@@ -112,8 +112,10 @@ __device__ __forceinline__ T sel3(int i, T v0, T v1, T v2)
 // LDS slice indexed by (row, vector) and leave as vectors lane and 64 + lane
 // of the pass, i.e. contiguous 1 KB runs when a token's heads are adjacent.
 // In the planes mode the rows also arrive that way and reach the lane-local
-// layout through the same slice (8 more VGPRs: a gain where cos/sin come
-// from memory, a loss where the wave computes them, measured both ways).
+// layout through the same slice.  That costs registers (NeoX variants 80 ->
+// 82 VGPRs, 6 -> 5 waves per SIMD): measured a gain where cos/sin come from
+// memory and a loss where the wave computes them, so only the planes mode
+// stages its loads.
 //
 // ROPE: 0 norm only, 1 positions + inv_freq (1D / AXES / IMROPE: the axis
 // table carries the difference), 2 cos/sin planes, 3 ViT positions computed
