@@ -615,11 +615,12 @@ def kernel_source_hash():
     return code_hash(texts)
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, variant):
     """HBM bytes per launch from the committed counter summary of this
     workload (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by
     what the counter reads for a plain copy of known size), or None when no
-    summary exists or the kernels changed since the counters were taken."""
+    summary exists, the kernels changed since the counters were taken, or
+    the call now runs another kernel variant."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -629,7 +630,7 @@ def measured_traffic(workload):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        if kv.get("kernel_source_sha256") != kernel_source_hash():
+        if kv.get("kernel_source_sha256") != kernel_source_hash() or kv.get("variant") != variant:
             return None
         fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
         write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["write_scale"])
@@ -819,7 +820,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (measured_traffic(args.workload + ("-blocks" if SLOTS == "blocks" and args.workload == "cache"
-                                                                    else ""))
+                                                                    else ""), variant)
                                  if NUMERICS == "contract" else None),
                      "bytes_per_launch": w.launch_bytes, "kernel": variant},
     }

@@ -283,6 +283,8 @@ def test_joint_full_size(pairing):
     case = W.joint()
     g, rope = joint_gpu(case, pairing)
     q, k, v = qkr.joint_qk_norm_rope(g["text"], g["image"], case.eps, rope)
+    # 24 heads: three passes of 8 in tiles of two, a quarter of them idle
+    assert qkr.last_variant().startswith("rope:np2:"), qkr.last_variant()
     rq, rk, rv = joint_oracle(case, pairing)
     assert_bf16_close(host(q), rq, 128, pairing, "joint q")
     assert_bf16_close(host(k), rk, 128, pairing, "joint k")
@@ -332,6 +334,8 @@ def test_imrope_full_size_chunked():
     q, k = gpu(case.q), gpu(case.k)
     outs = [imrope_call(case, q[b:b + case.chunk], k[b:b + case.chunk], pos, inv, b)
             for b in range(0, 8192, case.chunk)]
+    # 16 Q heads fill a tile of two passes, 8 K heads half of one
+    assert qkr.last_variant().startswith("rope:np2:"), qkr.last_variant()
     qo = torch.cat([o[0] for o in outs])
     ko = torch.cat([o[1] for o in outs])
     orope = oracle.Rope("imrope", 128, "neox", inv_freq=case.inv_freq, sections=case.sections,
@@ -996,6 +1000,9 @@ def test_cache_write_full_size(slot_map):
                     positions=gpu(torch.from_numpy(case.positions)), sections=case.sections)
     qo = qkr.qk_norm_rope_cache(gpu(case.q), gpu(case.k), gpu(v), gpu(case.q_weight), gpu(case.k_weight), kc, vc,
                                 gpu(torch.from_numpy(slots)), case.eps, rope)
+    # 16 Q heads fill both passes of a tile, 8 K and 8 V heads only one: with
+    # two passes per tile a third of the passes would be idle, so one
+    assert qkr.last_variant().startswith("rope:np1:"), qkr.last_variant()
     orope = oracle.Rope("imrope", D, "neox", inv_freq=case.inv_freq, sections=case.sections,
                         positions=case.positions)
     kc0 = np.zeros((blocks * bs, KV, D), np.float32)

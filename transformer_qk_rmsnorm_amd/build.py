@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 # instantiated once per lanes-per-row value and numerics, in parallel
 # compilations.
 LANES_PER_ROW = (1, 2, 4, 8, 16, 32)
-UNITS = ([("qkr_kernels.hip", [], "qkr_kernels"), ("qkr_api.cpp", [], "qkr_api")] +
+UNITS = ([("qkr_kernels.hip", [], "qkr_kernels"), ("qkr_api.cpp", [], "qkr_api"), ("qkr_plan.cpp", [], "qkr_plan")] +
          [("qkr_rope_part.hip", [f"-DQKR_LPR={n}", f"-DQKR_EAGER={e}"], f"qkr_rope_lpr{n}_eager{e}")
           for n in LANES_PER_ROW for e in (0, 1)])
 # Kernels must not use private (scratch) memory: a stray dynamic index into a

@@ -292,10 +292,8 @@ void fill_out(TensorArgs& t, const qkr_view* v, int esize)
 // cannot run the call is refused, never replaced.
 qkr_status plan_rope(const NormRopeArgs& a, int32_t dtype, RopePlan& plan)
 {
-    int32_t max_heads = 0;
-    for (int i = 0; i < 3; ++i)
-        max_heads = a.t[i].heads > max_heads ? a.t[i].heads : max_heads;
-    const char* why = plan_norm_rope(dtype, a.head_dim, max_heads, g_rope_np.load(), g_rope_lpr.load(),
+    const int32_t heads[3] = {a.t[0].heads, a.t[1].heads, a.t[2].heads};
+    const char* why = plan_norm_rope(dtype, a.head_dim, heads, g_rope_np.load(), g_rope_lpr.load(),
                                      g_rope_stage.load(), g_nt.load(), &plan);
     if (why != nullptr)
         return fail(QKR_ERR_UNSUPPORTED, "forced variant: %s", why);

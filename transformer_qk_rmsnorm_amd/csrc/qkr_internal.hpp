@@ -227,7 +227,7 @@ struct RmsPlan {
 // -1 = automatic, kind -1 = automatic; nt 1 nontemporal, 0 plain.  Returns
 // nullptr, or (static text) why a forced choice cannot run the call: a
 // forced variant is never replaced by another.
-const char* plan_norm_rope(int32_t dtype, int32_t head_dim, int32_t max_heads, int np_req, int lpr_req,
+const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int np_req, int lpr_req,
                            int stage_req, int nt_req, RopePlan* plan);
 const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, int mode, RmsPlan* plan);
 

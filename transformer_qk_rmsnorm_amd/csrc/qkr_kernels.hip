@@ -382,62 +382,9 @@ RmsFn pick_rms_mode(bool nt, bool eager, int mode, int vpl)
     return nt ? pick_rms_nt<E, KIND, true, false>(mode, vpl) : pick_rms_nt<E, KIND, false, false>(mode, vpl);
 }
 
-int round_vpl(int need)
-{
-    static const int sizes[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
-    for (int s : sizes)
-        if (need <= s)
-            return s;
-    return -1;
-}
-
 thread_local char g_variant[96];
 
 }  // namespace
-
-const char* plan_norm_rope(int32_t dtype, int32_t head_dim, int32_t max_heads, int np_req, int lpr_req,
-                           int stage_req, int nt_req, RopePlan* plan)
-{
-    const int ve = dtype == kBF16 ? 8 : 4;
-    const int nv = head_dim / ve;
-    // Lanes per row: the smallest power of two that gives every lane at most
-    // two vectors of the row.
-    int lpr = 1;
-    while (2 * lpr < nv)
-        lpr *= 2;
-    if (lpr_req > 0) {
-        if (2 * lpr_req < nv)
-            return "rope:lpr: too few lanes per row for this head_dim (each lane holds at most two vectors)";
-        lpr = lpr_req;
-    }
-    const int rpp = 64 / lpr;
-    int np = np_req;
-    if (np <= 0) {
-        // Two passes per tile where a tensor has two or more passes of
-        // heads.  Measured on MI355X with two / one / three passes: the joint
-        // op (24 heads of 128) 29.7 / 30.0 / 30.3 us, fused ViT (16 + 16
-        // heads of 80) 19.8 / 24.1 / 21.2 us, a 2048-token IMROPE chunk
-        // (16 + 8 heads of 128) 5.94 / 6.61 / 6.15 us.
-        const int passes = (max_heads + rpp - 1) / rpp;
-        np = passes >= 2 ? 2 : 1;
-    }
-    if (np < 1 || np > 4)
-        return "rope:np: passes per wave must be 1 to 4";
-    // Staged stores where a half row is not a whole number of 128-byte lines;
-    // they exist for 2 to 8 lanes per row (rows of up to 16 vectors).
-    const bool can_stage = lpr >= 2 && lpr <= 8;
-    bool stage = nv % 16 != 0 && can_stage;
-    if (stage_req >= 0) {
-        if (stage_req != 0 && !can_stage)
-            return "rope:stage1: staged stores exist for 2 to 8 lanes per row only";
-        stage = stage_req != 0;
-    }
-    plan->lpr = lpr;
-    plan->np = np;
-    plan->stage = stage;
-    plan->nt = nt_req != 0;
-    return nullptr;
-}
 
 hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, bool eager, const RopePlan& plan,
                             hipStream_t stream, const char** variant)
@@ -494,47 +441,6 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
              pairing == kNeox ? "neox" : "adjacent", (int)plan.stage, eager ? ":eager" : "");
     *variant = g_variant;
     return hipSuccess;
-}
-
-const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, int mode, RmsPlan* plan)
-{
-    const bool add = (mode & 1) != 0;
-    const int vpl_wave = round_vpl((nvec + 63) / 64);              // rows, split
-    const int vpl_wide = round_vpl((nvec + kThreads - 1) / kThreads);
-    int kind = kind_req;
-    if (kind < 0) {
-        // A wavefront per row from 2048 to 4096 rows, a workgroup per row
-        // below and above.  Up to 4096 rows (256 compute units x 4 SIMDs x 4
-        // waves) the wave-per-row launch is a single round of waves; past it
-        // the workgroups, four waves each over one row, overlap better.
-        // Measured on MI355X, rows of 5120 bf16, wide / one wave per row, us:
-        // 512 rows 3.44 / 5.28, 1024 5.25 / 5.87, 1536 7.28 / 7.00, 2048
-        // 8.99 / 7.68, 3072 12.4 / 11.0, 4096 15.8 / 14.1, 6144 22.4 / 21.3,
-        // 8192 29.1 / 30.1; with the residual add 1024 8.91 / 7.80, 2048
-        // 15.6 / 14.0, 4096 28.6 / 27.9, 6144 41.5 / 47.1, 8192 54.9 / 60.4.
-        // The split variant (1 row 2.23 us against 2.16 wide, 32 rows 3.31
-        // against 2.82) never wins; it stays reachable through the variant
-        // override.  Rows of fewer than 64 vectors keep a wave each (a
-        // workgroup would leave most of its lanes idle); rows too long for
-        // one wavefront go to the workgroup-wide variant.
-        kind = nvec >= 64 && (rows < 2048 || rows > 4096) ? 2 : 0;
-        if (kind == 0 && vpl_wave < 0)
-            kind = 2;
-    } else {
-        if (kind == 1 && add)
-            return "rms:split: the split variant cannot take the residual add (its workgroups read the whole "
-                   "row while others write the residual)";
-        if (kind != 2 && vpl_wave < 0)
-            return "rms:rows / rms:split: the row does not fit one wavefront (more than 1024 vectors)";
-    }
-    const int vpl = kind == 2 ? vpl_wide : vpl_wave;
-    if (vpl < 0)
-        return "rms: the row is longer than 4096 vectors";
-    plan->kind = kind;
-    plan->vpl = vpl;
-    plan->nt = nt_req != 0;
-    plan->mode = mode;
-    return nullptr;
 }
 
 hipError_t launch_rms_norm(RmsArgs a, int32_t dtype, bool eager, const RmsPlan& plan, hipStream_t stream,
