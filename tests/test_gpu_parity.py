@@ -1262,3 +1262,34 @@ def test_eager_vit_fused_and_cache_write():
     assert_bf16_close(host(q_out), rq, d, "neox", "eager cache q")
     assert_bf16_close(host(kc)[slots], rk[slots], d, "neox", "eager cache k")
     assert np.array_equal(host(vc), rv)
+
+
+@pytest.mark.parametrize("mode", ["1d", "imrope"])
+@pytest.mark.parametrize("numerics", ["contract", "eager"])
+def test_rounding_points_decide_the_bits(mode, numerics):
+    """On the elements whose bf16 value depends on where the kernel rounds,
+    the GPU takes the oracle's value for its numerics: not the value of a
+    rotation of the unrounded normalised row ([Ovis] kernel review: the
+    normalised value is rounded before the rotation), and not the other
+    preset's value (x * rrms rounded before the weight, cos/sin in the
+    activation type, no fused multiply-add)."""
+    from test_parity_rules import _bf16, _case, _rotate
+    case, x, w, rope, theta = _case(mode)
+    extra = {"sections": case.sections} if mode == "imrope" else {}
+    gr = qkr.Rope(mode, 128, "neox", inv_freq=gpu(torch.from_numpy(case.inv_freq)),
+                  positions=gpu(torch.from_numpy(case.positions if mode == "imrope" else case.positions[:1])),
+                  **extra)
+    q, _ = qkr.qk_norm_rope(gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, gr,
+                            numerics=numerics)
+    got = host(q)
+    ref = oracle.qk_norm_rope(x, w, case.eps, rope, "bf16", numerics=numerics)
+    other = oracle.qk_norm_rope(x, w, case.eps, rope, "bf16",
+                                numerics="eager" if numerics == "contract" else "contract")
+    unrounded = _rotate(oracle.qk_norm_rope(x, w, case.eps, None, "f32"), theta, np.float64)
+    assert_bf16_close(got, ref, 128, "neox", f"{mode} {numerics}")
+    for name, slip in (("unrounded normalised value", unrounded), ("the other numerics", other)):
+        d = ref != slip                                   # elements that tell the two apart
+        assert d.mean() > 0.05, (name, d.mean())          # enough of them to decide
+        took_ref = (got[d] == ref[d]).mean()
+        took_slip = (got[d] == slip[d]).mean()
+        assert took_ref > 0.995 and took_slip < 0.005, (name, d.sum(), took_ref, took_slip)
