@@ -256,7 +256,7 @@ def test_mrope_setup_refusals():
 def test_variant_override_names():
     for name in ("rms:rows", "rms:split", "rms:wide", "rope:np1", "rope:np2", "rope:np3", "rope:np4",
                  "rope:lpr4", "rope:lpr8", "rope:lpr16", "rope:lpr32", "rope:stage0", "rope:stage1", "nt:0",
-                 "nt:1"):
+                 "nt:1", "rope:token", "rope:tile"):
         qkr.set_variant_override(name)
     qkr.set_variant_override(None)
     with pytest.raises(qkr.QkrError):
@@ -271,6 +271,13 @@ def test_variant_override_names():
     ("rope:stage1", lambda: qknr(head_dim=256, q=view(st=16 * 256, sh=256), qo=view(st=16 * 256, sh=256),
                                  k=view(st=8 * 256, sh=256), ko=view(st=8 * 256, sh=256),
                                  rope=rope_c(rotary_dim=256, sections=(48, 40, 40, 0)))),   # 16 lanes per row
+    ("rope:token", lambda: qknr()),                                     # 16 vectors: 8 lanes, a power of two
+    ("rope:token", lambda: qknr(head_dim=80, qh=24, kh=24, q=view(st=24 * 80, sh=80), qo=view(st=24 * 80, sh=80),
+                                k=view(st=24 * 80, sh=80), ko=view(st=24 * 80, sh=80),
+                                rope=rope_c(rotary_dim=80, sections=(14, 13, 13, 0)))),   # 480 vectors > 320
+    ("rope:token,rope:np2", lambda: qknr(head_dim=80, q=view(st=16 * 80, sh=80), qo=view(st=16 * 80, sh=80),
+                                         k=view(st=8 * 80, sh=80), ko=view(st=8 * 80, sh=80),
+                                         rope=rope_c(rotary_dim=80, sections=(14, 13, 13, 0)))),   # a tile knob
 ])
 def test_forced_variant_that_cannot_run_is_refused_before_any_launch(variant, call):
     """A forced variant is never swapped for another: the call returns
@@ -278,7 +285,8 @@ def test_forced_variant_that_cannot_run_is_refused_before_any_launch(variant, ca
     import torch
     if torch.cuda.is_available():
         pytest.skip("stand-in pointers: run where no GPU is visible")
-    qkr.set_variant_override(variant)
+    for name in variant.split(","):
+        qkr.set_variant_override(name)
     try:
         assert call() == UNSUPPORTED, qkr.last_error()
         assert "forced variant" in qkr.last_error()

@@ -691,10 +691,15 @@ def test_odd_vector_counts(dtype, head_dim, rotary_dim, pairing, lpr):
     vector of their own, and an odd count leaves one lane a single vector."""
     case = W.tiny(tokens=29, heads=13, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + rotary_dim)
     pos = np.random.default_rng(head_dim).integers(0, 7000, (1, 29)).astype(np.int32)
-    qo, ko, rq, rk = run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos)
-    assert f":lpr{lpr}:" in qkr.last_variant()
-    check(qo, rq, dtype, rotary_dim, pairing, "q")
-    check(ko, rk, dtype, rotary_dim, pairing, "k")
+    # the tile kernel, forced (some of these rows go to token tiles by
+    # default), then the default choice
+    for variants in (["rope:tile"], []):
+        (qo, ko, rq, rk), name = _with_variants(variants, lambda: run_1d(case, pairing, rotary_dim=rotary_dim,
+                                                                         positions=pos))
+        if variants:
+            assert f":lpr{lpr}:" in name, name
+        check(qo, rq, dtype, rotary_dim, pairing, f"q {name}")
+        check(ko, rk, dtype, rotary_dim, pairing, f"k {name}")
 
 
 # ---------------------------------------------------------------------------
@@ -731,6 +736,34 @@ def test_pass_counts_and_cache_policy_agree_bitwise(dtype, head_dim, pairing):
                 ref = (qo, ko)
             else:
                 assert np.array_equal(qo, ref[0]) and np.array_equal(ko, ref[1]), name
+
+
+@pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing,heads", [
+    ("bf16", 80, 80, "neox", 16), ("bf16", 80, 34, "adjacent", 5), ("bf16", 96, 64, "neox", 13),
+    ("bf16", 48, 48, "adjacent", 26), ("bf16", 112, 112, "neox", 11), ("bf16", 72, 48, "neox", 7),
+    ("f32", 40, 40, "adjacent", 16), ("f32", 24, 16, "neox", 26), ("f32", 48, 48, "neox", 13),
+    ("bf16", 80, 0, "neox", 9),
+])
+def test_token_tiles_and_tile_kernel_match_the_oracle(dtype, head_dim, rotary_dim, pairing, heads):
+    """Rows whose vector pairs take 3, 5, 6 or 7 lanes can run on token
+    tiles (one wave per token, Q and K rows together); by default they do
+    where a row takes 5 to 7 lanes and the angles are computed (here 1-D
+    positions).  Token tiles and the tile kernel, each forced, with
+    nontemporal accesses on and off, against the oracle; ragged passes (13,
+    11, 7, 9 heads), partial rotary and norm only included."""
+    case = W.tiny(tokens=45, heads=heads, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 211)
+    pos = np.random.default_rng(head_dim + 2).integers(0, 8000, (1, 45)).astype(np.int32)
+    (_, _, _, _), name = _with_variants([], lambda: run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos))
+    lanes = (head_dim // (8 if dtype == "bf16" else 4) + 1) // 2
+    assert name.startswith("rope:token:" if lanes >= 5 and rotary_dim > 0 else "rope:np"), name
+    for variant in ("rope:token", "rope:tile"):
+        for nt in ("nt:1", "nt:0"):
+            (qo, ko, rq, rk), name = _with_variants(
+                [variant, nt], lambda: run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos))
+            assert name.startswith("rope:token:" if variant == "rope:token" else "rope:np"), name
+            assert f":nt{nt[-1]}:" in name, name
+            check(qo, rq, dtype, rotary_dim, pairing, f"q {name}")
+            check(ko, rk, dtype, rotary_dim, pairing, f"k {name}")
 
 
 @pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing", [

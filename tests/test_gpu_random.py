@@ -97,27 +97,44 @@ def test_random_case(i):
                             positions=torch.from_numpy(pos).to(DEV), sections=c["sections"],
                             token_base=c["token_base"])
 
-    gbig = big.to(DEV)
-    q = gbig[:, :, q_sl] if hq else None
-    k = gbig[:, :, k_sl] if hk else None
-    kw = {}
-    if c["in_place"]:
-        kw = {"q_out": q, "k_out": k}
-    qo, ko = qkr.qk_norm_rope(q, k, wq.to(DEV) if hq else None, wk.to(DEV) if hk else None, W.EPS, rope, **kw)
-    torch.cuda.synchronize()
+    # Rows whose vector pairs take 3, 5, 6 or 7 lanes, with the token's Q and
+    # K rows within 320 vectors, can run on token tiles; by default they do
+    # where a row takes 5 to 7 lanes and the angles are computed (not planes,
+    # not norm only).  Such cases also run on the other kernel, forced.
+    nv = d // (8 if dtype == "bf16" else 4)
+    lanes = (nv + 1) // 2
+    shape_ok = lanes in (3, 5, 6, 7) and (hq + hk) * nv <= 320
+    token = shape_ok and lanes >= 5 and rot > 0 and c["mode"] != "planes"
+    for variant in [None] + (["rope:tile"] if token else ["rope:token"] if shape_ok else []):
+        gbig = big.to(DEV)
+        q = gbig[:, :, q_sl] if hq else None
+        k = gbig[:, :, k_sl] if hk else None
+        kw = {}
+        if c["in_place"]:
+            kw = {"q_out": q, "k_out": k}
+        qkr.set_variant_override(variant)
+        try:
+            qo, ko = qkr.qk_norm_rope(q, k, wq.to(DEV) if hq else None, wk.to(DEV) if hk else None, W.EPS, rope,
+                                      **kw)
+            chosen = qkr.last_variant()
+        finally:
+            qkr.set_variant_override(None)
+        torch.cuda.synchronize()
+        on_token = variant == "rope:token" or (variant is None and token)
+        assert chosen.startswith("rope:token:" if on_token else "rope:np"), chosen
 
-    for name, out, sl, w, heads in (("q", qo, q_sl, wq, hq), ("k", ko, k_sl, wk, hk)):
-        if not heads:
-            assert out is None
-            continue
-        got = out.detach().float().cpu().numpy()
-        for bi in range(b):
-            ref = oracle.qk_norm_rope(W.as_f32(big[bi, :, sl]), W.as_f32(w), W.EPS, orope, dtype)
-            what = f"case {i} {name} batch {bi}"
-            if dtype == "f32":
-                assert_f32_close(got[bi], ref, what)
-            else:
-                assert_bf16_close(got[bi], ref, rot, c["pairing"], what)
-    # In place, the heads between the two slices stay as they were.
-    if c["pad_heads"] and c["in_place"]:
-        assert torch.equal(gbig[:, :, hq:hq + c["pad_heads"]].cpu(), big[:, :, hq:hq + c["pad_heads"]])
+        for name, out, sl, w, heads in (("q", qo, q_sl, wq, hq), ("k", ko, k_sl, wk, hk)):
+            if not heads:
+                assert out is None
+                continue
+            got = out.detach().float().cpu().numpy()
+            for bi in range(b):
+                ref = oracle.qk_norm_rope(W.as_f32(big[bi, :, sl]), W.as_f32(w), W.EPS, orope, dtype)
+                what = f"case {i} {name} batch {bi} {chosen}"
+                if dtype == "f32":
+                    assert_f32_close(got[bi], ref, what)
+                else:
+                    assert_bf16_close(got[bi], ref, rot, c["pairing"], what)
+        # In place, the heads between the two slices stay as they were.
+        if c["pad_heads"] and c["in_place"]:
+            assert torch.equal(gbig[:, :, hq:hq + c["pad_heads"]].cpu(), big[:, :, hq:hq + c["pad_heads"]])

@@ -36,6 +36,7 @@ std::atomic<int> g_rope_np{0};
 std::atomic<int> g_nt{1};
 std::atomic<int> g_rope_lpr{0};
 std::atomic<int> g_rope_stage{-1};
+std::atomic<int> g_rope_token{-1};
 
 qkr_status fail(qkr_status st, const char* fmt, ...)
 {
@@ -293,8 +294,21 @@ void fill_out(TensorArgs& t, const qkr_view* v, int esize)
 qkr_status plan_rope(const NormRopeArgs& a, int32_t dtype, RopePlan& plan)
 {
     const int32_t heads[3] = {a.t[0].heads, a.t[1].heads, a.t[2].heads};
-    const char* why = plan_norm_rope(dtype, a.head_dim, heads, g_rope_np.load(), g_rope_lpr.load(),
-                                     g_rope_stage.load(), g_nt.load(), &plan);
+    // Token tiles take Q and K of one stream with no slot map, and address a
+    // tensor's rows of one token with 32-bit offsets.
+    bool token_ok = a.t[2].heads == 0 && a.t[0].slots == nullptr && a.t[1].slots == nullptr && a.tokens0 >= a.tokens;
+    const int64_t row_bytes = (int64_t)a.head_dim * (dtype == kBF16 ? 2 : 4);
+    for (int i = 0; i < 2; ++i) {
+        const TensorArgs& t = a.t[i];
+        if (t.heads == 0)
+            continue;
+        for (const int64_t sh : {t.in_sh[0], t.out_sh})
+            token_ok = token_ok && sh >= 0 && (int64_t)(t.heads - 1) * sh + row_bytes <= INT32_MAX;
+    }
+    const bool trig = a.rope.mode != kPosNone && a.rope.mode != kPosPlanes && a.rope.half > 0;
+    const char* why = plan_norm_rope(dtype, a.head_dim, heads, a.rope.mode == kPosNone ? 0 : a.rope.half, trig,
+                                     token_ok, g_rope_np.load(), g_rope_lpr.load(), g_rope_stage.load(),
+                                     g_rope_token.load(), g_nt.load(), &plan);
     if (why != nullptr)
         return fail(QKR_ERR_UNSUPPORTED, "forced variant: %s", why);
     return QKR_OK;
@@ -432,7 +446,12 @@ qkr_status qkr_set_variant_override(const char* name)
         g_rope_np = 0;
         g_rope_lpr = 0;
         g_rope_stage = -1;
+        g_rope_token = -1;
         g_nt = 1;
+        return ok();
+    }
+    if (std::strcmp(name, "rope:tile") == 0 || std::strcmp(name, "rope:token") == 0) {
+        g_rope_token = name[6] == 'o' ? 1 : 0;
         return ok();
     }
     if (std::strcmp(name, "nt:0") == 0 || std::strcmp(name, "nt:1") == 0) {

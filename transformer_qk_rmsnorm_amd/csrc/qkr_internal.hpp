@@ -206,6 +206,13 @@ __host__ __device__ inline void vit_position(const VitArgs& a, uint32_t tok, int
 using NormRopeFn = void (*)(NormRopeArgs);
 template <int LPR, bool EAGER>
 NormRopeFn pick_norm_rope(int32_t dtype, int rope, int32_t pairing, bool nt, bool stage, int np);
+// Token-tile kernel (one wavefront per token, Q and K rows together) for L
+// lanes per row, L in 3, 5, 6, 7; each (L, EAGER) pair is defined in its own
+// build of qkr_token_part.hip.
+template <int L, bool EAGER>
+NormRopeFn pick_norm_rope_token(int32_t dtype, int rope, int32_t pairing, bool nt);
+// Most row vectors of one token the token-tile kernel holds (Q and K rows).
+constexpr int kTokenTileVecs = 320;
 
 // Kernel variant of a QK norm + rotation call.
 struct RopePlan {
@@ -213,6 +220,7 @@ struct RopePlan {
     int np;      // passes (row groups) per wave
     bool stage;  // stores through LDS in contiguous runs
     bool nt;     // nontemporal row accesses
+    int token;   // lanes per row of the token-tile kernel; 0: the tile kernel
 };
 
 // Kernel variant of a row norm call.
@@ -227,8 +235,14 @@ struct RmsPlan {
 // -1 = automatic, kind -1 = automatic; nt 1 nontemporal, 0 plain.  Returns
 // nullptr, or (static text) why a forced choice cannot run the call: a
 // forced variant is never replaced by another.
-const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int np_req, int lpr_req,
-                           int stage_req, int nt_req, RopePlan* plan);
+// trig: the kernel computes the angles (positions or ViT grids, not planes
+// and not norm only); token_ok: the call has no V tensor, no slot map and one
+// stream, and each tensor's rows of one token span less than 2^31 bytes
+// (what the token-tile kernel takes); token_req -1 automatic, 0 the tile
+// kernel, 1 the token-tile kernel.
+const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int32_t half, bool trig,
+                           bool token_ok, int np_req, int lpr_req, int stage_req, int token_req, int nt_req,
+                           RopePlan* plan);
 const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, int mode, RmsPlan* plan);
 
 // Kernel launchers (qkr_kernels.hip).  Each returns the variant name it

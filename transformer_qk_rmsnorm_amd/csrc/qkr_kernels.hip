@@ -386,6 +386,62 @@ thread_local char g_variant[96];
 
 }  // namespace
 
+// One launch per kMaxBlocksPerLaunch workgroups of kWaves tiles, each told
+// its first tile.
+static hipError_t launch_tiles(NormRopeFn fn, NormRopeArgs& a, int64_t tiles, hipStream_t stream)
+{
+    const int64_t blocks = (tiles + kWaves - 1) / kWaves;
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        a.tile_base = (uint32_t)(b0 * kWaves);
+        hipLaunchKernelGGL(fn, dim3((uint32_t)nb), dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+static const char* rope_name(int rope)
+{
+    return rope == 0 ? "none" : (rope == 1 ? "pos" : (rope == 2 ? "planes" : "vit"));
+}
+
+// The token-tile kernel: one tile per (batch, token).
+static hipError_t launch_norm_rope_token(NormRopeArgs a, int32_t dtype, int32_t pairing, bool eager, const RopePlan& plan,
+                                  int rope, hipStream_t stream, const char** variant)
+{
+    const int ve = dtype == kBF16 ? 8 : 4;
+    const int nv = a.head_dim / ve;
+    const int64_t tiles = (int64_t)a.batch * a.tokens;
+    if (tiles == 0)
+        return hipSuccess;
+    if (tiles >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;   // the host layer refuses such calls first
+    a.ntiles = (uint32_t)tiles;
+    a.div_tokens = make_fastdiv((uint32_t)a.tokens);
+    a.nv_recip = (65536u + (uint32_t)nv - 1) / (uint32_t)nv;
+    NormRopeFn fn;
+    switch (plan.token) {
+    case 3: fn = eager ? pick_norm_rope_token<3, true>(dtype, rope, pairing, plan.nt)
+                       : pick_norm_rope_token<3, false>(dtype, rope, pairing, plan.nt); break;
+    case 5: fn = eager ? pick_norm_rope_token<5, true>(dtype, rope, pairing, plan.nt)
+                       : pick_norm_rope_token<5, false>(dtype, rope, pairing, plan.nt); break;
+    case 6: fn = eager ? pick_norm_rope_token<6, true>(dtype, rope, pairing, plan.nt)
+                       : pick_norm_rope_token<6, false>(dtype, rope, pairing, plan.nt); break;
+    default: fn = eager ? pick_norm_rope_token<7, true>(dtype, rope, pairing, plan.nt)
+                        : pick_norm_rope_token<7, false>(dtype, rope, pairing, plan.nt); break;
+    }
+    const hipError_t e = launch_tiles(fn, a, tiles, stream);
+    if (e != hipSuccess)
+        return e;
+    snprintf(g_variant, sizeof(g_variant), "rope:token:nt%d:lanes%d:%s:%s:%s%s", (int)plan.nt, plan.token,
+             dtype == kBF16 ? "bf16" : "f32", rope_name(rope), pairing == kNeox ? "neox" : "adjacent",
+             eager ? ":eager" : "");
+    *variant = g_variant;
+    return hipSuccess;
+}
+
 hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pairing, bool eager, const RopePlan& plan,
                             hipStream_t stream, const char** variant)
 {
@@ -395,6 +451,8 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     const int lpr = plan.lpr, np = plan.np;
     const int rope = a.rope.mode == kPosNone ? 0
                      : (a.rope.mode == kPosPlanes ? 2 : (a.rope.mode == kPosVit ? 3 : 1));
+    if (plan.token > 0)
+        return launch_norm_rope_token(a, dtype, pairing, eager, plan, rope, stream, variant);
     const int rpw = (64 / lpr) * np;
     int32_t tpt = 0;
     for (int i = 0; i < 3; ++i) {
@@ -425,20 +483,12 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     default: fn = eager ? pick_norm_rope<32, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
                         : pick_norm_rope<32, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
     }
-    // One launch per kMaxBlocksPerLaunch workgroups, each told its first tile.
-    const int64_t blocks = (tiles + kWaves - 1) / kWaves;
-    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
-        a.tile_base = (uint32_t)(b0 * kWaves);
-        hipLaunchKernelGGL(fn, dim3((uint32_t)nb), dim3(kThreads), 0, stream, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
+    const hipError_t e = launch_tiles(fn, a, tiles, stream);
+    if (e != hipSuccess)
+        return e;
     snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s:stage%d%s", np, (int)plan.nt, lpr,
-             dtype == kBF16 ? "bf16" : "f32",
-             rope == 0 ? "none" : (rope == 1 ? "pos" : (rope == 2 ? "planes" : "vit")),
-             pairing == kNeox ? "neox" : "adjacent", (int)plan.stage, eager ? ":eager" : "");
+             dtype == kBF16 ? "bf16" : "f32", rope_name(rope), pairing == kNeox ? "neox" : "adjacent",
+             (int)plan.stage, eager ? ":eager" : "");
     *variant = g_variant;
     return hipSuccess;
 }

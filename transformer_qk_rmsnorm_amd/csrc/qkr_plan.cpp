@@ -19,11 +19,49 @@ int round_vpl(int need)
 
 }  // namespace
 
-const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int np_req, int lpr_req,
-                           int stage_req, int nt_req, RopePlan* plan)
+const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int32_t half, bool trig,
+                           bool token_ok, int np_req, int lpr_req, int stage_req, int token_req, int nt_req,
+                           RopePlan* plan)
 {
     const int ve = dtype == kBF16 ? 8 : 4;
     const int nv = head_dim / ve;
+    // Token tiles (one wavefront per token, Q and K rows together, L lanes
+    // per row) where a row's vector pairs need 5, 6 or 7 lanes, so the tile
+    // kernel's row groups of 8 would leave lanes idle, the token's Q and K
+    // rows fit the wave's LDS slice, and the wave computes the angles itself
+    // (positions or ViT grids): the token tile computes them once per token
+    // where the tile kernel computes them once per tensor.  Measured on
+    // MI355X, 8192 tokens, token / tile time: bf16 head_dim 80, 16 + 16 heads,
+    // 1-D positions 0.921 (adjacent pairing 0.935), t/h/w axes 0.975, ViT
+    // grids (7952 tokens) 0.925; head_dim 96 (12 + 12 heads) 0.932, 112
+    // (11 + 11) 0.945; 8 + 8 heads of 80 0.980; fp32 head_dim 40 0.978.  Not
+    // chosen: cos/sin planes 1.002 and norm only 1.026 (no angles to share),
+    // and 3 lanes per row (bf16 head_dim 48, 26 + 26 heads) 1.008.  The tile
+    // kernel's knobs (np, lpr, stage) force the tile kernel.
+    const int token_lanes = (nv + 1) / 2;
+    const bool token_shape = token_lanes == 3 || token_lanes == 5 || token_lanes == 6 || token_lanes == 7;
+    const bool token_fits = (int64_t)(heads[0] + heads[1]) * nv <= kTokenTileVecs && half <= 64;
+    const bool tile_knobs = np_req > 0 || lpr_req > 0 || stage_req >= 0;
+    if (token_req == 1) {
+        if (tile_knobs)
+            return "rope:token: the passes, lanes-per-row and staging choices belong to the tile kernel";
+        if (!token_ok)
+            return "rope:token: token tiles take Q and K only (no V, no slot map, one stream)";
+        if (!token_shape)
+            return "rope:token: token tiles serve rows of 5, 6, 9 to 14 16-byte vectors (3, 5, 6 or 7 lanes)";
+        if (!token_fits)
+            return "rope:token: the token's Q and K rows exceed the 320 vectors of the wave's slice";
+    }
+    const bool token_pays = trig && token_lanes >= 5;
+    if (token_req == 1 || (token_req < 0 && !tile_knobs && token_ok && token_shape && token_fits && token_pays)) {
+        plan->lpr = token_lanes;
+        plan->np = 0;
+        plan->stage = false;
+        plan->nt = nt_req != 0;
+        plan->token = token_lanes;
+        return nullptr;
+    }
+    plan->token = 0;
     // Lanes per row: the smallest power of two that gives every lane at most
     // two vectors of the row.
     int lpr = 1;

@@ -561,5 +561,303 @@ NormRopeFn pick_rope(int rope, int pairing, bool nt, bool stage, int np)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Token tiles: one wavefront takes every Q and K row of one token.
+//
+// Rows of nv vectors need L = ceil(nv / 2) lanes (a lane owns two vectors, as
+// in the tile kernel above).  Where L is not a power of two (3, 5, 6, 7: bf16
+// head_dim 48, 80, 96, 112) the tile kernel's row groups of 4 or 8 lanes leave
+// lanes idle (3 of 8 for head_dim 80); here rows take L lanes each, 64 / L
+// rows per pass, Q rows first, then K rows.  The token's rows (at most
+// kTokenVecs 16-byte vectors) arrive as flat vector loads into the wave's LDS
+// slice: slot s of a tensor is its vectors 64 s + lane (contiguous when the
+// tensor's heads are), Q slots first, so every load has a wave-uniform base
+// and a 32-bit lane offset (the host keeps a tensor's rows of one token
+// within 2^31 bytes).  Each lane reads its two vectors of a row from the
+// slice, and the results leave the same way.  The tensors' weight vectors sit in the slice
+// too.  A row's sum of squares is gathered from its L lanes by ds_bpermute in
+// one fixed order, so every lane of the row gets the same total.  cos/sin are
+// computed once per token instead of once per tensor.
+// ---------------------------------------------------------------------------
+constexpr int kTokenVecs = kTokenTileVecs;   // row vectors of one token held in LDS (5 per lane)
+constexpr int kTokenWeightVecs = 32;   // Q and K weight vectors (two rows of at most 16)
+
+template <class E, int L, int ROPE, int PAIRING, bool NT, bool EAGER>
+__global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRopeArgs a)
+{
+    constexpr int VE = E::VE;
+    constexpr int RP = 64 / L;                         // rows per pass
+    constexpr bool ROT = ROPE != 0;
+    constexpr int kSlots = kTokenVecs / 64 + 1;       // ceil(nq / 64) + ceil(nk / 64) for nq + nk <= kTokenVecs
+    static_assert(L >= 3 && L <= 7 && (L & (L - 1)) != 0, "token tiles serve 3, 5, 6 or 7 lanes per row");
+    __shared__ uint4 lds_all[kWaves * (kTokenVecs + kTokenWeightVecs)];
+
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint4* const st = lds_all + wave * (kTokenVecs + kTokenWeightVecs);
+    uint4* const wst = st + kTokenVecs;
+
+    // Tile = batch * tokens + token.  Padding waves of the last workgroup redo
+    // the last tile and store nothing.
+    const uint32_t tile_raw = a.tile_base + blockIdx.x * kWaves + wave;
+    const bool pad = tile_raw >= a.ntiles;
+    const uint32_t tile = pad ? a.ntiles - 1 : tile_raw;
+    const uint32_t bq = fast_div(tile, a.div_tokens);
+    const int32_t tok = (int32_t)(tile - bq * a.div_tokens.d);
+    const int32_t b = (int32_t)bq;
+
+    const TensorArgs& TQ = a.t[0];
+    const TensorArgs& TK = a.t[1];
+    const int nv = a.head_dim / VE;
+    const int hq = TQ.heads, hk = TK.heads;
+    const int rows = hq + hk;
+    const int nq = hq * nv, nk = hk * nv;              // nq + nk <= kTokenVecs (the planner's condition)
+    const int sq = (nq + 63) >> 6, sk = (nk + 63) >> 6;
+    // Slot s: tensor K from slot sq on (Q again when there is no K: a
+    // re-read, never kept), its slot s - sq.  Wave-uniform.
+    auto slot_is_k = [&](int s) { return s >= sq && hk > 0; };
+    auto slot_in_tensor = [&](int s) { return s >= sq ? s - sq : s; };
+    const char* const qin = TQ.in[0] + (int64_t)b * TQ.in_sb[0] + (int64_t)tok * TQ.in_st[0];
+    const char* const kin = TK.in[0] + (int64_t)b * TK.in_sb[0] + (int64_t)tok * TK.in_st[0];
+
+    // Byte offset within its tensor's token of the tensor's flat vector f.
+    auto flat_off = [&](int f, int32_t sh) {
+        const int fr = (int)(((uint32_t)f * a.nv_recip) >> 16);
+        return (uint32_t)(fr * sh + (f - fr * nv) * 16);
+    };
+
+    // The lane's place in a row: vectors v0 and v1, as in the tile kernel.
+    const int g = lane / L, j = lane - (lane / L) * L;
+    int v0, v1;
+    bool rot_lane = false;
+    if (PAIRING == kNeox && ROT) {
+        const int nr = a.rotary_dim / (2 * VE);
+        if (j < nr) {
+            v0 = j;
+            v1 = j + nr;
+            rot_lane = true;
+        } else {
+            v0 = 2 * nr + 2 * (j - nr);
+            v1 = v0 + 1;
+        }
+    } else {
+        const int hv = (nv + 1) >> 1;
+        v0 = j;
+        v1 = j + hv;
+    }
+    const bool own0 = v0 < nv, own1 = v1 < nv;
+    const int c0i = own0 ? v0 : 0, c1i = own1 ? v1 : 0;
+
+    // 1) Loads: the lane's pair operand, the token's rows as flat vectors
+    //    (past the token's last vector: a re-read of it), the weight vectors.
+    const RopeArgs& rp = a.rope;
+    const int half = (int)uniform((uint32_t)rp.half);
+    const int64_t tabs = rp.token_base + tok;
+    const int p0 = lane < half ? lane : half - 1;
+    float op0 = 0.0f, os0 = 0.0f;
+    int32_t ax0 = 0;
+    if constexpr (ROPE == 1)
+        op0 = load_global(uniform(rp.inv_freq) + p0);
+    if constexpr (ROPE == 2) {
+        ax0 = axis_of(rp.axis_bits, p0);
+        const int64_t i0 = ((int64_t)ax0 * rp.planes_tokens + tabs) * half + p0;
+        op0 = rp.cos_planes[i0];
+        os0 = rp.sin_planes[i0];
+    }
+    if constexpr (ROPE == 3) {
+        ax0 = axis_of(rp.axis_bits, p0);
+        const int32_t o_h = rp.sec[0], o_w = rp.sec[0] + rp.sec[1];
+        const float* const l0 = sel3(ax0, uniform(a.vit.inv[0]), uniform(a.vit.inv[1]), uniform(a.vit.inv[2]));
+        op0 = load_global(l0 + (p0 - sel3(ax0, 0, o_h, o_w)));
+    }
+    uint4 fl[kSlots];
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        const bool isk = slot_is_k(s);
+        const int n = isk ? nk : nq;
+        const int f = 64 * slot_in_tensor(s) + lane;
+        fl[s] = load_row16<NT>((isk ? kin : qin) +
+                               flat_off(f < n ? f : n - 1, (int32_t)(isk ? TK.in_sh[0] : TQ.in_sh[0])));
+    }
+    // Weight vectors: lanes [0, nv) the Q tensor's, [nv, 2 nv) the K tensor's
+    // (an absent tensor's lanes read the other one's: never used).
+    const char* const wq = hq > 0 ? TQ.weight[0] : TK.weight[0];
+    const char* const wk = hk > 0 ? TK.weight[0] : TQ.weight[0];
+    const int wl = lane < nv ? lane : (lane < 2 * nv ? lane - nv : 0);
+    const uint4 wv = load16((lane < nv ? wq : wk) + wl * 16);
+
+    TokenPositions pos{0, 0, 0, 0};
+    if constexpr (ROPE == 1) {
+        pos.t = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[0] + tabs]);
+        pos.h = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[1] + tabs]);
+        pos.w = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[2] + tabs]);
+        pos.e = (int32_t)uniform((uint32_t)rp.positions[rp.plane_off[3] + tabs]);
+    }
+    if constexpr (ROPE == 3)
+        pos = vit_token_positions(a.vit, (uint32_t)tabs);
+
+    // 2) cos/sin of the lane's VE pairs, once for the token.
+    float cs_c[VE], cs_s[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        cs_c[e] = 1.0f;
+        cs_s[e] = 0.0f;
+    }
+    if constexpr (ROT) {
+        float c0, s0;
+        if constexpr (ROPE == 2) {
+            c0 = op0;
+            s0 = os0;
+        } else {
+            if constexpr (ROPE == 1)
+                ax0 = axis_of(rp.axis_bits, p0);
+            pair_cos_sin(ax0, pos, op0, c0, s0);
+        }
+        if constexpr (EAGER)
+            E::round_pair(c0, s0);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            int p;
+            if constexpr (PAIRING == kNeox)
+                p = j * VE + e;
+            else
+                p = (e < VE / 2 ? v0 : v1) * (VE / 2) + (e % (VE / 2));
+            cs_c[e] = bperm(p, c0);
+            cs_s[e] = bperm(p, s0);
+        }
+    }
+
+    // The token's rows (Q rows, then K rows) and the weights into the wave's
+    // slice; re-reads past a tensor's vectors are dropped.
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        const bool isk = slot_is_k(s);
+        const int f = 64 * slot_in_tensor(s) + lane;
+        if (f < (isk ? nk : (s < sq ? nq : 0)))
+            st[(isk ? nq : 0) + f] = fl[s];
+    }
+    if (lane < 2 * nv)
+        wst[lane] = wv;
+    wave_lds_order();
+
+    // 3) Per pass of RP rows: the row's two vectors of this lane, the sum of
+    //    squares over the row's L lanes, normalise, round, rotate, back into
+    //    the slice.
+    const float eps = a.eps, inv_d = a.inv_d;
+    const bool eps_normal = eps >= FLT_MIN;
+    const int base = g * L;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        if (p * RP >= rows)
+            break;   // wave-uniform
+        const int r = p * RP + g;
+        const bool valid = g < RP && r < rows;
+        const int rr = valid ? r : rows - 1;
+        const uint4 d0 = st[rr * nv + c0i], d1 = st[rr * nv + c1i];
+        const float part = (own0 ? E::sumsq(d0, 0.0f) : 0.0f) + (own1 ? E::sumsq(d1, 0.0f) : 0.0f);
+        float tot = bperm(base, part);
+#pragma unroll
+        for (int k = 1; k < L; ++k)
+            tot += bperm(base + k, part);
+        const float rrms = rms_rsqrt(tot * inv_d + eps, eps_normal);
+        const int wb = rr < hq ? 0 : nv;
+        float x0[VE], x1[VE], w0[VE], w1[VE];
+        E::unpack(d0, x0);
+        E::unpack(d1, x1);
+        E::unpack(wst[wb + c0i], w0);
+        E::unpack(wst[wb + c1i], w1);
+        if constexpr (EAGER) {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                x0[e] = x0[e] * rrms;
+                x1[e] = x1[e] * rrms;
+            }
+            E::round_trip(x0);
+            E::round_trip(x1);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                x0[e] = x0[e] * w0[e];
+                x1[e] = x1[e] * w1[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                x0[e] = x0[e] * rrms * w0[e];
+                x1[e] = x1[e] * rrms * w1[e];
+            }
+        }
+        E::round_trip(x0);
+        E::round_trip(x1);
+        auto rot = [](float& xa, float& xb, float c, float sn) {
+            if constexpr (EAGER) {
+                rotate_unfused(xa, xb, c, sn);
+            } else {
+                const float a0 = xa, b0 = xb;
+                xa = a0 * c - b0 * sn;
+                xb = b0 * c + a0 * sn;
+            }
+        };
+        if constexpr (ROT) {
+            if constexpr (PAIRING == kNeox) {
+                if (rot_lane) {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        rot(x0[e], x1[e], cs_c[e], cs_s[e]);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < VE / 2; ++q) {
+                    if (v0 * (VE / 2) + q < half)
+                        rot(x0[2 * q], x0[2 * q + 1], cs_c[q], cs_s[q]);
+                    if (v1 * (VE / 2) + q < half)
+                        rot(x1[2 * q], x1[2 * q + 1], cs_c[VE / 2 + q], cs_s[VE / 2 + q]);
+                }
+            }
+        }
+        if (valid) {
+            if (own0)
+                st[rr * nv + v0] = E::pack(x0);
+            if (own1)
+                st[rr * nv + v1] = E::pack(x1);
+        }
+    }
+    wave_lds_order();
+
+    // 4) The token's results leave as flat vectors.
+    if (pad)
+        return;
+    char* const qout = TQ.out + (int64_t)b * TQ.out_sb + (int64_t)tok * TQ.out_st;
+    char* const kout = TK.out + (int64_t)b * TK.out_sb + (int64_t)tok * TK.out_st;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        const bool isk = slot_is_k(s);
+        const int f = 64 * slot_in_tensor(s) + lane;
+        if (f < (isk ? nk : (s < sq ? nq : 0)))
+            store_row16<NT>((isk ? kout : qout) + flat_off(f, (int32_t)(isk ? TK.out_sh : TQ.out_sh)),
+                            st[(isk ? nq : 0) + f]);
+    }
+}
+
+template <class E, int L, int ROPE, bool EAGER>
+NormRopeFn pick_token_nt(int32_t pairing, bool nt)
+{
+    if (pairing == kNeox)
+        return nt ? norm_rope_token_kernel<E, L, ROPE, kNeox, true, EAGER>
+                  : norm_rope_token_kernel<E, L, ROPE, kNeox, false, EAGER>;
+    return nt ? norm_rope_token_kernel<E, L, ROPE, kAdjacent, true, EAGER>
+              : norm_rope_token_kernel<E, L, ROPE, kAdjacent, false, EAGER>;
+}
+
+template <class E, int L, bool EAGER>
+NormRopeFn pick_token_rope(int rope, int32_t pairing, bool nt)
+{
+    switch (rope) {
+    case 0: return pick_token_nt<E, L, 0, EAGER>(pairing, nt);
+    case 1: return pick_token_nt<E, L, 1, EAGER>(pairing, nt);
+    case 2: return pick_token_nt<E, L, 2, EAGER>(pairing, nt);
+    default: return pick_token_nt<E, L, 3, EAGER>(pairing, nt);
+    }
+}
+
 }  // namespace
 }  // namespace qkr
