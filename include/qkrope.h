@@ -280,13 +280,18 @@ const char* qkr_last_error(void);
  * "rms:split", "rms:wide", "rope:np1", "rope:np2", "rope:np3", "rope:np4"
  * (passes of rows per wavefront), "rope:lpr4", "rope:lpr8", "rope:lpr16",
  * "rope:lpr32" (lanes per row), "rope:stage0" / "rope:stage1" (QK stores
- * straight from registers / through LDS in contiguous runs), "nt:0" / "nt:1"
- * (plain / nontemporal row accesses).  Overrides accumulate until NULL
- * resets all of them.  Unknown names are refused.  A forced variant is
- * never swapped for another: a call it cannot run (a row longer than one
- * wavefront holds under "rms:rows" or "rms:split", the residual add under
- * "rms:split", too few lanes per row for the head_dim, staged stores outside
- * 2 to 8 lanes per row) returns QKR_ERR_UNSUPPORTED before any HIP call. */
+ * straight from registers / through LDS in contiguous runs), "rope:tile" /
+ * "rope:token" (the QK tile kernel / token tiles: one wavefront per token,
+ * Q and K rows together, for rows of 5, 6 or 9 to 14 16-byte vectors),
+ * "nt:0" / "nt:1" (plain / nontemporal row accesses).  Overrides accumulate
+ * until NULL resets all of them.  Unknown names are refused.  A forced
+ * variant is never swapped for another: a call it cannot run (a row longer
+ * than one wavefront holds under "rms:rows" or "rms:split", the residual add
+ * under "rms:split", too few lanes per row for the head_dim, staged stores
+ * outside 2 to 8 lanes per row, token tiles with another row width, with V,
+ * a slot map, two streams, more than 320 Q and K row vectors per token, or
+ * with a tile-kernel choice (passes, lanes per row, staging) forced too)
+ * returns QKR_ERR_UNSUPPORTED before any HIP call. */
 qkr_status qkr_set_variant_override(const char* name);
 
 /* Name of the kernel variant the last successful launch on the calling
