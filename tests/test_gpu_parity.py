@@ -1208,6 +1208,36 @@ def test_eager_qk_norm_rope_1d(dtype, head_dim, pairing):
         assert _differs(host(qo), host(cq)) > 0.05
 
 
+@pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing,heads", [
+    ("bf16", 80, 80, "neox", 16), ("bf16", 48, 48, "adjacent", 26), ("bf16", 112, 112, "neox", 11),
+    ("bf16", 96, 64, "adjacent", 13), ("f32", 24, 16, "neox", 26), ("f32", 48, 48, "adjacent", 9),
+])
+def test_eager_token_tiles_match_the_oracle(dtype, head_dim, rotary_dim, pairing, heads):
+    """Eager numerics on token tiles (3, 5, 6 and 7 lanes per row) and on the
+    tile kernel, each forced, against the eager oracle; for bf16 the result
+    differs visibly from the contracted one, so the eager rounding points
+    are the ones taken."""
+    case = W.tiny(tokens=45, heads=heads, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 613)
+    pos = np.random.default_rng(head_dim + 9).integers(0, 8000, (1, 45)).astype(np.int32)
+    inv = W.inv_freq_ladder(1e4, rotary_dim)
+    rope = qkr.Rope("1d", rotary_dim, pairing, inv_freq=gpu(torch.from_numpy(inv)),
+                    positions=gpu(torch.from_numpy(pos)))
+    orope = oracle.Rope("1d", rotary_dim, pairing, inv_freq=inv, positions=pos)
+    refs = [oracle.qk_norm_rope(W.as_f32(x), W.as_f32(w), case.eps, orope, dtype, numerics="eager")
+            for x, w in ((case.q, case.q_weight), (case.k, case.k_weight))]
+    args = (gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
+    for variant in ("rope:token", "rope:tile"):
+        (qo, ko), name = _with_variants([variant], lambda: qkr.qk_norm_rope(*args, numerics="eager"))
+        assert name.startswith("rope:token:" if variant == "rope:token" else "rope:np"), name
+        assert name.endswith(":eager"), name
+        check(host(qo), refs[0], dtype, rotary_dim, pairing, f"eager q {name}")
+        check(host(ko), refs[1], dtype, rotary_dim, pairing, f"eager k {name}")
+        if dtype == "bf16":
+            (cq, _), cname = _with_variants([variant], lambda: qkr.qk_norm_rope(*args))
+            assert cname.startswith(name.split(":")[0] + ":") and not cname.endswith(":eager"), cname
+            assert _differs(host(qo), host(cq)) > 0.05, name
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_eager_rotation_is_unfused_bitwise(dtype):
     """Rows of +-1 with eps = 0 normalise exactly (rrms = 1), and planes mode
