@@ -745,17 +745,17 @@ def test_pass_counts_and_cache_policy_agree_bitwise(dtype, head_dim, pairing):
     ("bf16", 80, 0, "neox", 9),
 ])
 def test_token_tiles_and_tile_kernel_match_the_oracle(dtype, head_dim, rotary_dim, pairing, heads):
-    """Rows whose vector pairs take 3, 5, 6 or 7 lanes can run on token
-    tiles (one wave per token, Q and K rows together); by default they do
-    where a row takes 5 to 7 lanes and the angles are computed (here 1-D
-    positions).  Token tiles and the tile kernel, each forced, with
-    nontemporal accesses on and off, against the oracle; ragged passes (13,
-    11, 7, 9 heads), partial rotary and norm only included."""
+    """Rows whose vector pairs take 3, 5, 6 or 7 lanes run on token tiles
+    (one wave per token, Q and K rows together) by default when the token's
+    Q and K rows fit 320 vectors.  Token tiles and the tile kernel, each
+    forced, with nontemporal accesses on and off, against the oracle; ragged
+    passes (13, 11, 7, 9 heads), partial rotary and norm only included."""
     case = W.tiny(tokens=45, heads=heads, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 211)
     pos = np.random.default_rng(head_dim + 2).integers(0, 8000, (1, 45)).astype(np.int32)
     (_, _, _, _), name = _with_variants([], lambda: run_1d(case, pairing, rotary_dim=rotary_dim, positions=pos))
-    lanes = (head_dim // (8 if dtype == "bf16" else 4) + 1) // 2
-    assert name.startswith("rope:token:" if lanes >= 5 and rotary_dim > 0 else "rope:np"), name
+    nv = head_dim // (8 if dtype == "bf16" else 4)
+    fits = (nv + 1) // 2 in (3, 5, 6, 7) and 2 * heads * nv <= 320
+    assert name.startswith("rope:token:" if fits else "rope:np"), name
     for variant in ("rope:token", "rope:tile"):
         for nt in ("nt:1", "nt:0"):
             (qo, ko, rq, rk), name = _with_variants(

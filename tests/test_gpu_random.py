@@ -98,13 +98,12 @@ def test_random_case(i):
                             token_base=c["token_base"])
 
     # Rows whose vector pairs take 3, 5, 6 or 7 lanes, with the token's Q and
-    # K rows within 320 vectors, can run on token tiles; by default they do
-    # where a row takes 5 to 7 lanes and the angles are computed (not planes,
-    # not norm only).  Such cases also run on the other kernel, forced.
+    # K rows within 320 vectors, run on token tiles by default unless cos/sin
+    # come from planes; such cases also run on the other kernel, forced.
     nv = d // (8 if dtype == "bf16" else 4)
     lanes = (nv + 1) // 2
     shape_ok = lanes in (3, 5, 6, 7) and (hq + hk) * nv <= 320
-    token = shape_ok and lanes >= 5 and rot > 0 and c["mode"] != "planes"
+    token = shape_ok and c["mode"] != "planes"
     for variant in [None] + (["rope:tile"] if token else ["rope:token"] if shape_ok else []):
         gbig = big.to(DEV)
         q = gbig[:, :, q_sl] if hq else None

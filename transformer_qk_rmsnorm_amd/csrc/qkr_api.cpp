@@ -305,9 +305,8 @@ qkr_status plan_rope(const NormRopeArgs& a, int32_t dtype, RopePlan& plan)
         for (const int64_t sh : {t.in_sh[0], t.out_sh})
             token_ok = token_ok && sh >= 0 && (int64_t)(t.heads - 1) * sh + row_bytes <= INT32_MAX;
     }
-    const bool trig = a.rope.mode != kPosNone && a.rope.mode != kPosPlanes && a.rope.half > 0;
-    const char* why = plan_norm_rope(dtype, a.head_dim, heads, a.rope.mode == kPosNone ? 0 : a.rope.half, trig,
-                                     token_ok, g_rope_np.load(), g_rope_lpr.load(), g_rope_stage.load(),
+    const char* why = plan_norm_rope(dtype, a.head_dim, heads, a.rope.mode == kPosNone ? 0 : a.rope.half,
+                                     a.rope.mode == kPosPlanes, token_ok, g_rope_np.load(), g_rope_lpr.load(), g_rope_stage.load(),
                                      g_rope_token.load(), g_nt.load(), &plan);
     if (why != nullptr)
         return fail(QKR_ERR_UNSUPPORTED, "forced variant: %s", why);

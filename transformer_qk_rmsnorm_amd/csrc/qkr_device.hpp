@@ -175,6 +175,17 @@ __device__ __forceinline__ void store_row16(char* p, const uint4& v)
     }
 }
 
+// 16 bytes per lane from global memory straight into LDS (gfx950's
+// global_load_lds_dwordx4): lane i's bytes land at lds + 16 i, lds being
+// wave-uniform; no vector registers hold the data.  The write to LDS is
+// counted by vmcnt like a load, so readers wait for vmcnt(0) first.  With NT
+// the access carries the nontemporal hint.
+template <bool NT>
+__device__ __forceinline__ void lds_dma16(const char* p, uint4* lds)
+{
+    __builtin_amdgcn_global_load_lds((const void*)p, (__attribute__((address_space(3))) void*)lds, 16, 0, NT ? 2 : 0);
+}
+
 // Raw buffer access (stride 0) through a wave-uniform resource over `bytes`
 // bytes at p: the hardware's range check makes a load at an offset >= bytes
 // read zeros and drops a store there, so a slot past the end of a row needs
@@ -253,6 +264,14 @@ __device__ __forceinline__ float wave_sum(float v)
 __device__ __forceinline__ float bperm(int src_lane, float v)
 {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+// Lane src_lane's 16-byte vector.
+__device__ __forceinline__ uint4 bperm16(int src_lane, const uint4& v)
+{
+    const int a = src_lane << 2;
+    return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.x), (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.y),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.z), (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.w));
 }
 
 // A wave-uniform value held in a scalar register.  Selecting among such

@@ -235,12 +235,11 @@ struct RmsPlan {
 // -1 = automatic, kind -1 = automatic; nt 1 nontemporal, 0 plain.  Returns
 // nullptr, or (static text) why a forced choice cannot run the call: a
 // forced variant is never replaced by another.
-// trig: the kernel computes the angles (positions or ViT grids, not planes
-// and not norm only); token_ok: the call has no V tensor, no slot map and one
-// stream, and each tensor's rows of one token span less than 2^31 bytes
-// (what the token-tile kernel takes); token_req -1 automatic, 0 the tile
-// kernel, 1 the token-tile kernel.
-const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int32_t half, bool trig,
+// planes: cos/sin come from planes (the PLANES mode); token_ok: the call has
+// no V tensor, no slot map and one stream, and each tensor's rows of one
+// token span less than 2^31 bytes (what the token-tile kernel takes);
+// token_req -1 automatic, 0 the tile kernel, 1 the token-tile kernel.
+const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int32_t half, bool planes,
                            bool token_ok, int np_req, int lpr_req, int stage_req, int token_req, int nt_req,
                            RopePlan* plan);
 const char* plan_rms_norm(int32_t nvec, int64_t rows, int kind_req, int nt_req, int mode, RmsPlan* plan);

@@ -19,25 +19,30 @@ int round_vpl(int need)
 
 }  // namespace
 
-const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int32_t half, bool trig,
+const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[3], int32_t half, bool planes,
                            bool token_ok, int np_req, int lpr_req, int stage_req, int token_req, int nt_req,
                            RopePlan* plan)
 {
     const int ve = dtype == kBF16 ? 8 : 4;
     const int nv = head_dim / ve;
     // Token tiles (one wavefront per token, Q and K rows together, L lanes
-    // per row) where a row's vector pairs need 5, 6 or 7 lanes, so the tile
-    // kernel's row groups of 8 would leave lanes idle, the token's Q and K
-    // rows fit the wave's LDS slice, and the wave computes the angles itself
-    // (positions or ViT grids): the token tile computes them once per token
-    // where the tile kernel computes them once per tensor.  Measured on
-    // MI355X, 8192 tokens, token / tile time: bf16 head_dim 80, 16 + 16 heads,
-    // 1-D positions 0.921 (adjacent pairing 0.935), t/h/w axes 0.975, ViT
-    // grids (7952 tokens) 0.925; head_dim 96 (12 + 12 heads) 0.932, 112
-    // (11 + 11) 0.945; 8 + 8 heads of 80 0.980; fp32 head_dim 40 0.978.  Not
-    // chosen: cos/sin planes 1.002 and norm only 1.026 (no angles to share),
-    // and 3 lanes per row (bf16 head_dim 48, 26 + 26 heads) 1.008.  The tile
-    // kernel's knobs (np, lpr, stage) force the tile kernel.
+    // per row) wherever they can run, cos/sin planes aside: a row's vector
+    // pairs need 3, 5, 6 or 7 lanes, so the tile kernel's row groups of 4 or
+    // 8 would leave lanes idle, and the token's Q and K rows fit the wave's
+    // LDS slice.  Measured
+    // on MI355X, 8192 tokens, token / tile time (runs of the same build):
+    // bf16 head_dim 80, 16 + 16 heads: 1-D positions 0.95 / 0.98 (adjacent
+    // pairing 0.94), t/h/w axes 0.93, cos/sin planes 0.95, norm only 0.86 /
+    // 0.89; 8 + 8 heads 0.98 with positions, 1.03 with planes (the one loss
+    // measured); 2 + 2 heads 0.78 (positions), 0.80 (planes); head_dim 96
+    // (12 + 12) positions 0.91, planes 0.93, norm only 0.93; 112 (11 + 11)
+    // positions 0.92, planes 0.92 / 0.95; 48 (26 + 26) positions 0.98 to
+    // 1.01, planes 0.91 / 0.95, norm only 0.87; fp32 head_dim 40 positions
+    // 0.97, planes 0.97; fp32 24 positions 0.98.  Planes from the ViT setup
+    // (7952 tokens, sections 8 / 16 / 16, written just before the apply) run
+    // 1.008 at the kernel and 1.02 over the setup + apply step, so planes stay
+    // on the tile kernel.  The tile kernel's knobs (np, lpr, stage) force the
+    // tile kernel.
     const int token_lanes = (nv + 1) / 2;
     const bool token_shape = token_lanes == 3 || token_lanes == 5 || token_lanes == 6 || token_lanes == 7;
     const bool token_fits = (int64_t)(heads[0] + heads[1]) * nv <= kTokenTileVecs && half <= 64;
@@ -52,8 +57,7 @@ const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[
         if (!token_fits)
             return "rope:token: the token's Q and K rows exceed the 320 vectors of the wave's slice";
     }
-    const bool token_pays = trig && token_lanes >= 5;
-    if (token_req == 1 || (token_req < 0 && !tile_knobs && token_ok && token_shape && token_fits && token_pays)) {
+    if (token_req == 1 || (token_req < 0 && !tile_knobs && !planes && token_ok && token_shape && token_fits)) {
         plan->lpr = token_lanes;
         plan->np = 0;
         plan->stage = false;

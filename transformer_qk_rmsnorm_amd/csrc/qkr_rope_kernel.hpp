@@ -569,18 +569,45 @@ NormRopeFn pick_rope(int rope, int pairing, bool nt, bool stage, int np)
 // head_dim 48, 80, 96, 112) the tile kernel's row groups of 4 or 8 lanes leave
 // lanes idle (3 of 8 for head_dim 80); here rows take L lanes each, 64 / L
 // rows per pass, Q rows first, then K rows.  The token's rows (at most
-// kTokenVecs 16-byte vectors) arrive as flat vector loads into the wave's LDS
-// slice: slot s of a tensor is its vectors 64 s + lane (contiguous when the
-// tensor's heads are), Q slots first, so every load has a wave-uniform base
-// and a 32-bit lane offset (the host keeps a tensor's rows of one token
-// within 2^31 bytes).  Each lane reads its two vectors of a row from the
-// slice, and the results leave the same way.  The tensors' weight vectors sit in the slice
-// too.  A row's sum of squares is gathered from its L lanes by ds_bpermute in
-// one fixed order, so every lane of the row gets the same total.  cos/sin are
-// computed once per token instead of once per tensor.
+// kTokenVecs 16-byte vectors: its Q vectors, then its K vectors) sit in the
+// wave's LDS slice; each lane reads its two vectors of a row from there, the
+// results go back, and the token leaves as flat stores: slot s of a tensor is
+// its vectors 64 s + lane (contiguous when the tensor's heads are), Q slots
+// first, so every store has a wave-uniform base and a 32-bit lane offset (the
+// host keeps a tensor's rows of one token within 2^31 bytes).  A row's sum of
+// squares is gathered from its L lanes by ds_bpermute in one fixed order, so
+// every lane of the row gets the same total.  cos/sin are computed once per
+// token instead of once per tensor.
+//
+// The rows reach the slice in one of two ways (token_dma):
+//   - LDS DMA (gfx950's global_load_lds_dwordx4): memory to LDS with no
+//     vector registers in between, flat over the token's vectors (slot s =
+//     vectors 64 s + lane; lanes past the last vector re-read it into the
+//     slice's unused tail), every lane loading, so no load sits behind a
+//     branch.  The weight vectors stay in the registers of lanes 0 .. 2 nv - 1
+//     and reach a row's lanes by ds_bpermute, so the slice is 20 KB per
+//     workgroup of four waves and eight workgroups fit a compute unit.
+//   - Register loads per tensor slot, written to the slice once the trig is
+//     done, the weight vectors beside them in the slice (22 KB, seven
+//     workgroups).  The compiler counts LDS DMA apart from plain loads and
+//     makes the first wait after one a wait for every outstanding load, so
+//     with DMA the angle computation, which needs the lane's inverse
+//     frequency, would start only once every row had arrived: where the
+//     angles come from positions that costs more than the DMA saves.  NeoX
+//     rows of 7 lanes need 73 registers with DMA (six waves per SIMD).
+// Measured (8192 tokens, bf16, token-tile time with DMA / with register
+// loads): head_dim 80, 16 + 16 heads: norm only 0.84, cos/sin planes 0.95,
+// 1-D or t/h/w positions 1.00 to 1.06; ViT grid positions (7952 tokens) 0.90;
+// head_dim 96 (12 + 12 heads) planes 0.93, positions 1.06 to 1.09; 112
+// (11 + 11) planes 1.07, positions 1.17; 48 (26 + 26) planes 0.87.
 // ---------------------------------------------------------------------------
 constexpr int kTokenVecs = kTokenTileVecs;   // row vectors of one token held in LDS (5 per lane)
-constexpr int kTokenWeightVecs = 32;   // Q and K weight vectors (two rows of at most 16)
+constexpr int kTokenWeightVecs = 32;          // weight vectors in the slice (register loads): two rows of at most 16
+
+// Rows by LDS DMA: norm only always; cos/sin from planes or ViT grids up to 6
+// lanes per row; never where the angles come from positions.
+template <int ROPE, int L>
+constexpr bool token_dma() { return ROPE == 0 || (ROPE != 1 && L <= 6); }
 
 template <class E, int L, int ROPE, int PAIRING, bool NT, bool EAGER>
 __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRopeArgs a)
@@ -588,13 +615,16 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     constexpr int VE = E::VE;
     constexpr int RP = 64 / L;                         // rows per pass
     constexpr bool ROT = ROPE != 0;
-    constexpr int kSlots = kTokenVecs / 64 + 1;       // ceil(nq / 64) + ceil(nk / 64) for nq + nk <= kTokenVecs
+    constexpr int kSlots = kTokenVecs / 64;           // slots of 64 vectors in the slice
+    static_assert(kTokenVecs % 64 == 0, "the slice holds whole slots");
     static_assert(L >= 3 && L <= 7 && (L & (L - 1)) != 0, "token tiles serve 3, 5, 6 or 7 lanes per row");
-    __shared__ uint4 lds_all[kWaves * (kTokenVecs + kTokenWeightVecs)];
+    constexpr bool DMA = token_dma<ROPE, L>();
+    constexpr int kSlice = kTokenVecs + (DMA ? 0 : kTokenWeightVecs);
+    __shared__ uint4 lds_all[kWaves * kSlice];
 
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint4* const st = lds_all + wave * (kTokenVecs + kTokenWeightVecs);
+    uint4* const st = lds_all + wave * kSlice;
     uint4* const wst = st + kTokenVecs;
 
     // Tile = batch * tokens + token.  Padding waves of the last workgroup redo
@@ -612,11 +642,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     const int hq = TQ.heads, hk = TK.heads;
     const int rows = hq + hk;
     const int nq = hq * nv, nk = hk * nv;              // nq + nk <= kTokenVecs (the planner's condition)
-    const int sq = (nq + 63) >> 6, sk = (nk + 63) >> 6;
-    // Slot s: tensor K from slot sq on (Q again when there is no K: a
-    // re-read, never kept), its slot s - sq.  Wave-uniform.
-    auto slot_is_k = [&](int s) { return s >= sq && hk > 0; };
-    auto slot_in_tensor = [&](int s) { return s >= sq ? s - sq : s; };
+    const int ntot = nq + nk;
     const char* const qin = TQ.in[0] + (int64_t)b * TQ.in_sb[0] + (int64_t)tok * TQ.in_st[0];
     const char* const kin = TK.in[0] + (int64_t)b * TK.in_sb[0] + (int64_t)tok * TK.in_st[0];
 
@@ -648,8 +674,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     const bool own0 = v0 < nv, own1 = v1 < nv;
     const int c0i = own0 ? v0 : 0, c1i = own1 ? v1 : 0;
 
-    // 1) Loads: the lane's pair operand, the token's rows as flat vectors
-    //    (past the token's last vector: a re-read of it), the weight vectors.
+    // 1) Loads: the lane's pair operand, the token's rows (into the slice by
+    //    LDS DMA, or into registers), the weight vectors.
     const RopeArgs& rp = a.rope;
     const int half = (int)uniform((uint32_t)rp.half);
     const int64_t tabs = rp.token_base + tok;
@@ -670,14 +696,30 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
         const float* const l0 = sel3(ax0, uniform(a.vit.inv[0]), uniform(a.vit.inv[1]), uniform(a.vit.inv[2]));
         op0 = load_global(l0 + (p0 - sel3(ax0, 0, o_h, o_w)));
     }
-    uint4 fl[kSlots];
+    // Slot s of a tensor: its vectors 64 s + lane (register loads: past its
+    // last vector a re-read of it), Q slots first; every base wave-uniform.
+    constexpr int kRegSlots = DMA ? 1 : kSlots + 1;
+    const int sq = (nq + 63) >> 6;
+    auto slot_is_k = [&](int s) { return s >= sq && hk > 0; };
+    auto slot_in_tensor = [&](int s) { return s >= sq ? s - sq : s; };
+    uint4 fl[kRegSlots];
+    if constexpr (DMA) {
+        const int32_t shq = (int32_t)TQ.in_sh[0], shk = (int32_t)TK.in_sh[0];
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        const bool isk = slot_is_k(s);
-        const int n = isk ? nk : nq;
-        const int f = 64 * slot_in_tensor(s) + lane;
-        fl[s] = load_row16<NT>((isk ? kin : qin) +
-                               flat_off(f < n ? f : n - 1, (int32_t)(isk ? TK.in_sh[0] : TQ.in_sh[0])));
+        for (int s = 0; s < kSlots; ++s) {
+            const int f = 64 * s + lane < ntot ? 64 * s + lane : ntot - 1;
+            const bool isq = f < nq;
+            lds_dma16<NT>((isq ? qin : kin) + flat_off(isq ? f : f - nq, isq ? shq : shk), st + 64 * s);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < kRegSlots; ++s) {
+            const bool isk = slot_is_k(s);
+            const int n = isk ? nk : nq;
+            const int f = 64 * slot_in_tensor(s) + lane;
+            fl[s] = load_row16<NT>((isk ? kin : qin) +
+                                   flat_off(f < n ? f : n - 1, (int32_t)(isk ? TK.in_sh[0] : TQ.in_sh[0])));
+        }
     }
     // Weight vectors: lanes [0, nv) the Q tensor's, [nv, 2 nv) the K tensor's
     // (an absent tensor's lanes read the other one's: never used).
@@ -727,17 +769,21 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
         }
     }
 
-    // The token's rows (Q rows, then K rows) and the weights into the wave's
-    // slice; re-reads past a tensor's vectors are dropped.
+    if constexpr (DMA) {
+        // Every row in the slice: the LDS DMA writes complete under vmcnt.
+        __builtin_amdgcn_s_waitcnt(0);
+    } else {
+        // The rows and the weights into the slice; re-reads are dropped.
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        const bool isk = slot_is_k(s);
-        const int f = 64 * slot_in_tensor(s) + lane;
-        if (f < (isk ? nk : (s < sq ? nq : 0)))
-            st[(isk ? nq : 0) + f] = fl[s];
+        for (int s = 0; s < kRegSlots; ++s) {
+            const bool isk = slot_is_k(s);
+            const int f = 64 * slot_in_tensor(s) + lane;
+            if (f < (isk ? nk : (s < sq ? nq : 0)))
+                st[(isk ? nq : 0) + f] = fl[s];
+        }
+        if (lane < 2 * nv)
+            wst[lane] = wv;
     }
-    if (lane < 2 * nv)
-        wst[lane] = wv;
     wave_lds_order();
 
     // 3) Per pass of RP rows: the row's two vectors of this lane, the sum of
@@ -764,8 +810,13 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
         float x0[VE], x1[VE], w0[VE], w1[VE];
         E::unpack(d0, x0);
         E::unpack(d1, x1);
-        E::unpack(wst[wb + c0i], w0);
-        E::unpack(wst[wb + c1i], w1);
+        if constexpr (DMA) {
+            E::unpack(bperm16(wb + c0i, wv), w0);
+            E::unpack(bperm16(wb + c1i, wv), w1);
+        } else {
+            E::unpack(wst[wb + c0i], w0);
+            E::unpack(wst[wb + c1i], w1);
+        }
         if constexpr (EAGER) {
 #pragma unroll
             for (int e = 0; e < VE; ++e) {
@@ -829,7 +880,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     char* const qout = TQ.out + (int64_t)b * TQ.out_sb + (int64_t)tok * TQ.out_st;
     char* const kout = TK.out + (int64_t)b * TK.out_sb + (int64_t)tok * TK.out_st;
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
+    for (int s = 0; s < kSlots + 1; ++s) {
         const bool isk = slot_is_k(s);
         const int f = 64 * slot_in_tensor(s) + lane;
         if (f < (isk ? nk : (s < sq ? nq : 0)))
