@@ -57,10 +57,12 @@ def _scratch_users(lines):
 
 # The largest LDS a kernel is meant to use per workgroup: the QK tile
 # kernel's staging slice (4 waves x 128 vectors x 16 bytes), and the token-tile
-# kernel's slice (4 waves x 320 row vectors x 16 bytes, so that eight
-# workgroups fit the 160 KB of a compute unit).  More means the compiler has
-# moved a private array into LDS (indexed by the work-item id, which also
-# costs a read of the dispatch packet in every wave).
+# kernel's slice (4 waves x 320 row vectors x 16 bytes where the rows arrive
+# by LDS DMA, so that eight workgroups fit the 160 KB of a compute unit; 4 x
+# (320 + 32 weight vectors) x 16 bytes where they go through registers).
+# More means the compiler has moved a private array into LDS (indexed by the
+# work-item id, which also costs a read of the dispatch packet in every
+# wave).
 LDS_LIMIT = 8192
 LDS_LIMIT_TOKEN = 22528
 
