@@ -620,6 +620,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     static_assert(L >= 3 && L <= 7 && (L & (L - 1)) != 0, "token tiles serve 3, 5, 6 or 7 lanes per row");
     constexpr bool DMA = token_dma<ROPE, L>();
     constexpr int kSlice = kTokenVecs + (DMA ? 0 : kTokenWeightVecs);
+    static_assert(!DMA || kWaves * kSlice * 16 <= 160 * 1024 / 8, "eight DMA workgroups per compute unit");
     __shared__ uint4 lds_all[kWaves * kSlice];
 
     const int lane = threadIdx.x & 63;
