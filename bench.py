@@ -17,6 +17,10 @@ value   = algorithmic bytes per step / time per step (GB/s), whole job, over
           run on (replays of captured graphs, launches back to back).
 gpu_samples: the same K steps cut into at least six samples at graph-replay
           boundaries, each event-timed: median, minimum and maximum per step.
+warm-up: W steps launched one by one, then the whole K-step plan of graph
+          replays once, untimed, so that the GPU's clocks have settled under
+          sustained load before the timed pass (after a short warm-up the first
+          milliseconds of a run read several percent slow).
 roofline.achieved = algorithmic bytes per launch of the dominant kernel /
           its average launch duration over the K steps.
 cpu_baseline: the CPU oracle (plain C, double precision) on the same step,
@@ -588,8 +592,8 @@ def build_copy():
 
 
 KERNEL_SOURCES = ["transformer_qk_rmsnorm_amd/csrc/" + f for f in
-                  ("qkr_kernels.hip", "qkr_rope_part.hip", "qkr_rope_kernel.hpp", "qkr_device.hpp",
-                   "qkr_internal.hpp", "qkr_fastdiv.hpp")]
+                  ("qkr_kernels.hip", "qkr_rope_part.hip", "qkr_token_part.hip", "qkr_rope_kernel.hpp",
+                   "qkr_device.hpp", "qkr_internal.hpp", "qkr_fastdiv.hpp")]
 
 
 def code_hash(texts):
@@ -772,6 +776,10 @@ def main():
             graphs[n] = g
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
+        # The plan once untimed: the clocks settle under the same load.
+        for n in plan:
+            graphs[n].replay()
+        torch.cuda.synchronize()
     # Sample boundaries at replay (or eager step) boundaries: GPU_SAMPLES
     # groups of consecutive replays, as even as the plan allows.
     nsamp = min(GPU_SAMPLES, len(plan))
