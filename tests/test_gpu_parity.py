@@ -1208,21 +1208,38 @@ def test_eager_qk_norm_rope_1d(dtype, head_dim, pairing):
         assert _differs(host(qo), host(cq)) > 0.05
 
 
-@pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing,heads", [
-    ("bf16", 80, 80, "neox", 16), ("bf16", 48, 48, "adjacent", 26), ("bf16", 112, 112, "neox", 11),
-    ("bf16", 96, 64, "adjacent", 13), ("f32", 24, 16, "neox", 26), ("f32", 48, 48, "adjacent", 9),
+@pytest.mark.parametrize("dtype,head_dim,rotary_dim,pairing,heads,mode", [
+    ("bf16", 80, 80, "neox", 16, "1d"), ("bf16", 48, 48, "adjacent", 26, "1d"), ("bf16", 112, 112, "neox", 11, "1d"),
+    ("bf16", 96, 64, "adjacent", 13, "1d"), ("f32", 24, 16, "neox", 26, "1d"), ("f32", 48, 48, "adjacent", 9, "1d"),
+    ("bf16", 80, 0, "neox", 16, "none"), ("f32", 40, 0, "adjacent", 16, "none"),
+    ("bf16", 80, 80, "neox", 16, "planes"), ("bf16", 96, 96, "adjacent", 12, "planes"),
+    ("bf16", 112, 112, "neox", 11, "planes"), ("f32", 40, 40, "neox", 16, "planes"),
 ])
-def test_eager_token_tiles_match_the_oracle(dtype, head_dim, rotary_dim, pairing, heads):
-    """Eager numerics on token tiles (3, 5, 6 and 7 lanes per row) and on the
-    tile kernel, each forced, against the eager oracle; for bf16 the result
-    differs visibly from the contracted one, so the eager rounding points
-    are the ones taken."""
-    case = W.tiny(tokens=45, heads=heads, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 613)
-    pos = np.random.default_rng(head_dim + 9).integers(0, 8000, (1, 45)).astype(np.int32)
-    inv = W.inv_freq_ladder(1e4, rotary_dim)
-    rope = qkr.Rope("1d", rotary_dim, pairing, inv_freq=gpu(torch.from_numpy(inv)),
-                    positions=gpu(torch.from_numpy(pos)))
-    orope = oracle.Rope("1d", rotary_dim, pairing, inv_freq=inv, positions=pos)
+def test_eager_token_tiles_match_the_oracle(dtype, head_dim, rotary_dim, pairing, heads, mode):
+    """Eager numerics on token tiles (3, 5, 6 and 7 lanes per row; rows by
+    LDS DMA for norm only and planes up to 6 lanes, through registers for
+    positions and 7-lane planes) and on the tile kernel, each forced, against
+    the eager oracle; for bf16 the result differs visibly from the contracted
+    one, so the eager rounding points are the ones taken."""
+    tokens = 45
+    case = W.tiny(tokens=tokens, heads=heads, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 613)
+    rng = np.random.default_rng(head_dim + 9)
+    half = rotary_dim // 2
+    if mode == "1d":
+        pos = rng.integers(0, 8000, (1, tokens)).astype(np.int32)
+        inv = W.inv_freq_ladder(1e4, rotary_dim)
+        rope = qkr.Rope("1d", rotary_dim, pairing, inv_freq=gpu(torch.from_numpy(inv)),
+                        positions=gpu(torch.from_numpy(pos)))
+        orope = oracle.Rope("1d", rotary_dim, pairing, inv_freq=inv, positions=pos)
+    elif mode == "planes":
+        ang = rng.uniform(0, 60, (3, tokens, half))
+        cosp, sinp = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+        secs = (half // 4, half // 4, half - 2 * (half // 4), 0)
+        rope = qkr.Rope("planes", rotary_dim, pairing, sections=secs, cos_planes=gpu(torch.from_numpy(cosp)),
+                        sin_planes=gpu(torch.from_numpy(sinp)))
+        orope = oracle.Rope("planes", rotary_dim, pairing, sections=secs, cos_planes=cosp, sin_planes=sinp)
+    else:
+        rope, orope = None, None
     refs = [oracle.qk_norm_rope(W.as_f32(x), W.as_f32(w), case.eps, orope, dtype, numerics="eager")
             for x, w in ((case.q, case.q_weight), (case.k, case.k_weight))]
     args = (gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
@@ -1234,7 +1251,7 @@ def test_eager_token_tiles_match_the_oracle(dtype, head_dim, rotary_dim, pairing
         check(host(ko), refs[1], dtype, rotary_dim, pairing, f"eager k {name}")
         if dtype == "bf16":
             (cq, _), cname = _with_variants([variant], lambda: qkr.qk_norm_rope(*args))
-            assert cname.startswith(name.split(":")[0] + ":") and not cname.endswith(":eager"), cname
+            assert cname + ":eager" == name, (cname, name)
             assert _differs(host(qo), host(cq)) > 0.05, name
 
 
