@@ -626,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint4* const st = lds_all + wave * kSlice;
-    uint4* const wst = st + kTokenVecs;
+    uint4* const wst = st + kTokenVecs;   // weight vectors in the slice: register loads only
 
     // Tile = batch * tokens + token.  Padding waves of the last workgroup redo
     // the last tile and store nothing.
