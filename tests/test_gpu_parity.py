@@ -1212,15 +1212,17 @@ def test_eager_qk_norm_rope_1d(dtype, head_dim, pairing):
     ("bf16", 80, 80, "neox", 16, "1d"), ("bf16", 48, 48, "adjacent", 26, "1d"), ("bf16", 112, 112, "neox", 11, "1d"),
     ("bf16", 96, 64, "adjacent", 13, "1d"), ("f32", 24, 16, "neox", 26, "1d"), ("f32", 48, 48, "adjacent", 9, "1d"),
     ("bf16", 80, 0, "neox", 16, "none"), ("f32", 40, 0, "adjacent", 16, "none"),
+    ("bf16", 96, 0, "adjacent", 13, "none"), ("bf16", 112, 0, "neox", 11, "none"),
     ("bf16", 80, 80, "neox", 16, "planes"), ("bf16", 96, 96, "adjacent", 12, "planes"),
     ("bf16", 112, 112, "neox", 11, "planes"), ("f32", 40, 40, "neox", 16, "planes"),
 ])
-def test_eager_token_tiles_match_the_oracle(dtype, head_dim, rotary_dim, pairing, heads, mode):
-    """Eager numerics on token tiles (3, 5, 6 and 7 lanes per row; rows by
-    LDS DMA for norm only and planes up to 6 lanes, through registers for
-    positions and 7-lane planes) and on the tile kernel, each forced, against
-    the eager oracle; for bf16 the result differs visibly from the contracted
-    one, so the eager rounding points are the ones taken."""
+def test_token_tiles_both_numerics_match_the_oracle(dtype, head_dim, rotary_dim, pairing, heads, mode):
+    """Token tiles (3, 5, 6 and 7 lanes per row; rows by LDS DMA for norm
+    only and for planes up to 6 lanes, through registers for positions and
+    7-lane planes) and the tile kernel, each forced, with the contract and
+    with the eager numerics, against the oracle of each; for bf16 the eager
+    result differs visibly from the contracted one, so the eager rounding
+    points are the ones taken."""
     tokens = 45
     case = W.tiny(tokens=tokens, heads=heads, head_dim=head_dim, dtype=dtype, seed_stream=head_dim + 613)
     rng = np.random.default_rng(head_dim + 9)
@@ -1240,18 +1242,20 @@ def test_eager_token_tiles_match_the_oracle(dtype, head_dim, rotary_dim, pairing
         orope = oracle.Rope("planes", rotary_dim, pairing, sections=secs, cos_planes=cosp, sin_planes=sinp)
     else:
         rope, orope = None, None
-    refs = [oracle.qk_norm_rope(W.as_f32(x), W.as_f32(w), case.eps, orope, dtype, numerics="eager")
-            for x, w in ((case.q, case.q_weight), (case.k, case.k_weight))]
+    refs = {n: [oracle.qk_norm_rope(W.as_f32(x), W.as_f32(w), case.eps, orope, dtype, numerics=n)
+                for x, w in ((case.q, case.q_weight), (case.k, case.k_weight))] for n in ("contract", "eager")}
     args = (gpu(case.q), gpu(case.k), gpu(case.q_weight), gpu(case.k_weight), case.eps, rope)
     for variant in ("rope:token", "rope:tile"):
         (qo, ko), name = _with_variants([variant], lambda: qkr.qk_norm_rope(*args, numerics="eager"))
         assert name.startswith("rope:token:" if variant == "rope:token" else "rope:np"), name
         assert name.endswith(":eager"), name
-        check(host(qo), refs[0], dtype, rotary_dim, pairing, f"eager q {name}")
-        check(host(ko), refs[1], dtype, rotary_dim, pairing, f"eager k {name}")
+        check(host(qo), refs["eager"][0], dtype, rotary_dim, pairing, f"eager q {name}")
+        check(host(ko), refs["eager"][1], dtype, rotary_dim, pairing, f"eager k {name}")
+        (cq, ck), cname = _with_variants([variant], lambda: qkr.qk_norm_rope(*args))
+        assert cname + ":eager" == name, (cname, name)
+        check(host(cq), refs["contract"][0], dtype, rotary_dim, pairing, f"q {cname}")
+        check(host(ck), refs["contract"][1], dtype, rotary_dim, pairing, f"k {cname}")
         if dtype == "bf16":
-            (cq, _), cname = _with_variants([variant], lambda: qkr.qk_norm_rope(*args))
-            assert cname + ":eager" == name, (cname, name)
             assert _differs(host(qo), host(cq)) > 0.05, name
 
 
