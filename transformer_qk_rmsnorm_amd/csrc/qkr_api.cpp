@@ -275,10 +275,10 @@ qkr_status check_rope(const qkr_rope* r, int32_t head_dim, int esize, int64_t to
 
 void fill_in(TensorArgs& t, int s, const qkr_view* v, int esize)
 {
-    t.in[s] = v ? static_cast<const char*>(v->ptr_dev) : nullptr;
-    t.in_sb[s] = v ? v->stride_batch * esize : 0;
-    t.in_st[s] = v ? v->stride_tok * esize : 0;
-    t.in_sh[s] = v ? v->stride_head * esize : 0;
+    t.s[s].in = v ? static_cast<const char*>(v->ptr_dev) : nullptr;
+    t.s[s].sb = v ? v->stride_batch * esize : 0;
+    t.s[s].st = v ? v->stride_tok * esize : 0;
+    t.s[s].sh = v ? v->stride_head * esize : 0;
 }
 
 void fill_out(TensorArgs& t, const qkr_view* v, int esize)
@@ -302,7 +302,7 @@ qkr_status plan_rope(const NormRopeArgs& a, int32_t dtype, RopePlan& plan)
         const TensorArgs& t = a.t[i];
         if (t.heads == 0)
             continue;
-        for (const int64_t sh : {t.in_sh[0], t.out_sh})
+        for (const int64_t sh : {t.s[0].sh, t.out_sh})
             token_ok = token_ok && sh >= 0 && (int64_t)(t.heads - 1) * sh + row_bytes <= INT32_MAX;
     }
     const char* why = plan_norm_rope(dtype, a.head_dim, heads, a.rope.mode == kPosNone ? 0 : a.rope.half,
@@ -716,11 +716,11 @@ qkr_status qkr_qk_norm_rope(int32_t batch, int64_t tokens, int32_t head_dim, int
 
     fill_in(a.t[0], 0, q_heads ? q : nullptr, esize);
     fill_out(a.t[0], q_heads ? q_out : nullptr, esize);
-    a.t[0].weight[0] = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
+    a.t[0].s[0].weight = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
     a.t[0].heads = q_heads;
     fill_in(a.t[1], 0, k_heads ? k : nullptr, esize);
     fill_out(a.t[1], k_heads ? k_out : nullptr, esize);
-    a.t[1].weight[0] = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
+    a.t[1].s[0].weight = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
     a.t[1].heads = k_heads;
     a.t[2].heads = 0;
     a.batch = batch;
@@ -782,14 +782,14 @@ qkr_status qkr_qk_norm_rope_cache(int64_t tokens, int32_t head_dim, int32_t dtyp
 
     fill_in(a.t[0], 0, q_heads ? q : nullptr, esize);
     fill_out(a.t[0], q_heads ? q_out : nullptr, esize);
-    a.t[0].weight[0] = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
+    a.t[0].s[0].weight = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
     a.t[0].heads = q_heads;
     // K and V leave through the caches (num_slots == 0: every slot is
     // outside, nothing is written).
     const int32_t cache_heads = num_slots > 0 ? kv_heads : 0;
     fill_in(a.t[1], 0, cache_heads ? k : nullptr, esize);
     fill_out(a.t[1], cache_heads ? k_cache : nullptr, esize);
-    a.t[1].weight[0] = cache_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
+    a.t[1].s[0].weight = cache_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
     a.t[1].heads = cache_heads;
     a.t[1].slots = slot_mapping_dev;
     a.t[1].nslots = num_slots;
@@ -861,7 +861,7 @@ qkr_status qkr_joint_qk_norm_rope(int32_t batch, int32_t heads, int32_t head_dim
             const qkr_stream* x = streams[s];
             const qkr_view* v = ti == 0 ? &x->q : (ti == 1 ? &x->k : &x->v);
             fill_in(a.t[ti], s, x->tokens > 0 ? v : nullptr, esize);
-            a.t[ti].weight[s] = ti == 2 || x->tokens == 0
+            a.t[ti].s[s].weight = ti == 2 || x->tokens == 0
                                     ? nullptr
                                     : static_cast<const char*>(ti == 0 ? x->q_weight_dev : x->k_weight_dev);
         }
@@ -993,9 +993,9 @@ qkr_status qkr_vit_qk_norm_rope(int64_t tokens, int32_t head_dim, int32_t dtype,
 
     NormRopeArgs base{};
     base.t[0].heads = q_heads;
-    base.t[0].weight[0] = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
+    base.t[0].s[0].weight = q_heads ? static_cast<const char*>(q_weight_dev) : nullptr;
     base.t[1].heads = k_heads;
-    base.t[1].weight[0] = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
+    base.t[1].s[0].weight = k_heads ? static_cast<const char*>(k_weight_dev) : nullptr;
     base.t[2].heads = 0;
     base.batch = 1;
     base.head_dim = head_dim;

@@ -55,10 +55,13 @@ struct VitGridArgs {
 // One of Q, K, V.  Input views exist per stream (stream 1 only for the joint
 // op); strides are in bytes.  weight == nullptr marks a copied tensor (V); a
 // tensor with heads == 0 takes no work.
+struct StreamView {
+    const char* in;
+    int64_t sb, st, sh;         // batch, token and head strides
+    const char* weight;
+};
 struct TensorArgs {
-    const char* in[2];
-    int64_t in_sb[2], in_st[2], in_sh[2];
-    const char* weight[2];
+    StreamView s[2];            // one indexed load fetches a stream's fields
     char* out;
     int64_t out_sb, out_st, out_sh;
     const int64_t* slots;       // non-null: token t's rows go to output row slots[t] (stride out_st)
@@ -181,10 +184,10 @@ __host__ __device__ inline void vit_position(const VitArgs& a, uint32_t tok, int
         start = in_k ? a.cu[k] : start;
         d_frame.d = in_k ? a.div_area[k].d : d_frame.d;
         d_frame.m = in_k ? a.div_area[k].m : d_frame.m;
-        d_frame.l = in_k ? a.div_area[k].l : d_frame.l;
+        d_frame.sh = in_k ? a.div_area[k].sh : d_frame.sh;
         d_bcols.d = in_k ? a.div_bcols[k].d : d_bcols.d;
         d_bcols.m = in_k ? a.div_bcols[k].m : d_bcols.m;
-        d_bcols.l = in_k ? a.div_bcols[k].l : d_bcols.l;
+        d_bcols.sh = in_k ? a.div_bcols[k].sh : d_bcols.sh;
     }
     const uint32_t local = tok - start;
     const uint32_t frame = fast_div(local, d_frame);
@@ -221,6 +224,7 @@ struct RopePlan {
     bool stage;  // stores through LDS in contiguous runs
     bool nt;     // nontemporal row accesses
     int token;   // lanes per row of the token-tile kernel; 0: the tile kernel
+    int waves_cap;   // tile kernel: most waves per SIMD (0: none), held by reserving LDS
 };
 
 // Kernel variant of a row norm call.

@@ -15,6 +15,8 @@
 //            mrope_vit_setup"
 //   [VecRMS] vLLM pull request "Vectorize RMS norm variance using
 //            vectorize_read_with_alignment"
+#include <mutex>
+#include <unordered_map>
 #include "qkr_device.hpp"
 
 namespace qkr {
@@ -386,15 +388,49 @@ thread_local char g_variant[96];
 
 }  // namespace
 
+// LDS a workgroup of the tile kernel reserves so that a compute unit (160 KB
+// of LDS) holds at most `cap` of them, i.e. `cap` waves per SIMD (one wave
+// of each workgroup per SIMD): the dynamic part beyond the kernel's own LDS.
+// Only seven is used: 22 KB per workgroup fits seven (23.4 KB each) and not
+// eight (20 KB each) for every allocation granularity up to 2 KB.
+static hipError_t cap_lds(NormRopeFn fn, int cap, uint32_t* dynamic)
+{
+    *dynamic = 0;
+    if (cap <= 0)
+        return hipSuccess;
+    if (cap != 7)
+        return hipErrorInvalidValue;
+    // The kernel's own LDS, queried once per kernel.
+    static std::mutex mu;
+    static std::unordered_map<const void*, size_t> own;
+    size_t fixed;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = own.find(reinterpret_cast<const void*>(fn));
+        if (it == own.end()) {
+            hipFuncAttributes attr;
+            const hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));
+            if (e != hipSuccess)
+                return e;
+            it = own.emplace(reinterpret_cast<const void*>(fn), attr.sharedSizeBytes).first;
+        }
+        fixed = it->second;
+    }
+    constexpr size_t kCap7 = 22 * 1024;
+    *dynamic = fixed < kCap7 ? (uint32_t)(kCap7 - fixed) : 0;
+    return hipSuccess;
+}
+
 // One launch per kMaxBlocksPerLaunch workgroups of kWaves tiles, each told
 // its first tile.
-static hipError_t launch_tiles(NormRopeFn fn, NormRopeArgs& a, int64_t tiles, hipStream_t stream)
+static hipError_t launch_tiles(NormRopeFn fn, NormRopeArgs& a, int64_t tiles, hipStream_t stream,
+                               uint32_t lds_dynamic = 0)
 {
     const int64_t blocks = (tiles + kWaves - 1) / kWaves;
     for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
         const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
         a.tile_base = (uint32_t)(b0 * kWaves);
-        hipLaunchKernelGGL(fn, dim3((uint32_t)nb), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(fn, dim3((uint32_t)nb), dim3(kThreads), lds_dynamic, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -483,12 +519,16 @@ hipError_t launch_norm_rope(const NormRopeArgs& a_in, int32_t dtype, int32_t pai
     default: fn = eager ? pick_norm_rope<32, true>(dtype, rope, pairing, plan.nt, plan.stage, np)
                         : pick_norm_rope<32, false>(dtype, rope, pairing, plan.nt, plan.stage, np); break;
     }
-    const hipError_t e = launch_tiles(fn, a, tiles, stream);
+    uint32_t lds_dynamic = 0;
+    hipError_t e = cap_lds(fn, plan.waves_cap, &lds_dynamic);
     if (e != hipSuccess)
         return e;
-    snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s:stage%d%s", np, (int)plan.nt, lpr,
+    e = launch_tiles(fn, a, tiles, stream, lds_dynamic);
+    if (e != hipSuccess)
+        return e;
+    snprintf(g_variant, sizeof(g_variant), "rope:np%d:nt%d:lpr%d:%s:%s:%s:stage%d%s%s", np, (int)plan.nt, lpr,
              dtype == kBF16 ? "bf16" : "f32", rope_name(rope), pairing == kNeox ? "neox" : "adjacent",
-             (int)plan.stage, eager ? ":eager" : "");
+             (int)plan.stage, plan.waves_cap > 0 ? ":w7" : "", eager ? ":eager" : "");
     *variant = g_variant;
     return hipSuccess;
 }

@@ -63,6 +63,7 @@ const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[
         plan->stage = false;
         plan->nt = nt_req != 0;
         plan->token = token_lanes;
+        plan->waves_cap = 0;
         return nullptr;
     }
     plan->token = 0;
@@ -112,6 +113,15 @@ const char* plan_norm_rope(int32_t dtype, int32_t head_dim, const int32_t heads[
     plan->np = np;
     plan->stage = stage;
     plan->nt = nt_req != 0;
+    // At most seven waves per SIMD where a wave moves 4 KB or more each way
+    // (its rows in flight at once): an eighth wave adds requests to memory
+    // that is already saturated.  Measured on MI355X (same machine,
+    // alternating runs): the joint op (np 2, eight rows of 256 bytes per
+    // pass, 64 registers) 28.95 us at eight waves, 28.80 us at seven; the
+    // IMROPE chunk, one round of waves, 5.74 us either way; the cache write
+    // (np 1, 2 KB per wave) prefers eight: 24.2 against 25.1 us at seven.
+    const int64_t wave_bytes = (int64_t)rpp * np * head_dim * (dtype == kBF16 ? 2 : 4);
+    plan->waves_cap = wave_bytes >= 4096 ? 7 : 0;
     return nullptr;
 }
 

@@ -30,17 +30,17 @@ __device__ __forceinline__ TokenPositions vit_token_positions(const VitGridArgs&
     // Scalar fields only: selecting whole structs out of the kernel-argument
     // table would make the compiler copy the table to private memory.
     uint32_t start = (uint32_t)v.cu[0];
-    uint32_t a_d = v.div_area[0].d, a_m = v.div_area[0].m, a_l = v.div_area[0].l;
-    uint32_t b_d = v.div_bcols[0].d, b_m = v.div_bcols[0].m, b_l = v.div_bcols[0].l;
+    uint32_t a_d = v.div_area[0].d, a_m = v.div_area[0].m, a_l = v.div_area[0].sh;
+    uint32_t b_d = v.div_bcols[0].d, b_m = v.div_bcols[0].m, b_l = v.div_bcols[0].sh;
     for (int k = 1; k < v.num_grids; ++k) {
         const bool in_k = tok >= (uint32_t)v.cu[k];
         start = in_k ? (uint32_t)v.cu[k] : start;
         a_d = in_k ? v.div_area[k].d : a_d;
         a_m = in_k ? v.div_area[k].m : a_m;
-        a_l = in_k ? v.div_area[k].l : a_l;
+        a_l = in_k ? v.div_area[k].sh : a_l;
         b_d = in_k ? v.div_bcols[k].d : b_d;
         b_m = in_k ? v.div_bcols[k].m : b_m;
-        b_l = in_k ? v.div_bcols[k].l : b_l;
+        b_l = in_k ? v.div_bcols[k].sh : b_l;
     }
     const FastDiv d_frame{a_d, a_m, a_l}, d_bcols{b_d, b_m, b_l};
     const uint32_t local = tok - start;
@@ -136,6 +136,13 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     static_assert((LPR & (LPR - 1)) == 0 && LPR <= 32, "lanes per row: a power of two up to 32");
 
     const int lane = threadIdx.x & 63;
+    // The rotation's scalar parameters depend on no tile coordinate: read
+    // with the first batch of kernel-argument loads.
+    const RopeArgs& rp = a.rope;
+    const int half = (int)uniform((uint32_t)rp.half);
+    const float* const inv_freq = uniform(rp.inv_freq);
+    const int p0 = lane < half ? lane : half - 1;
+    const int p1 = lane + 64 < half ? lane + 64 : half - 1;
     // Tile coordinates are wave-uniform and stay in scalar registers:
     // tile = (batch * tokens + token) * tiles_per_token + k, where tiles
     // [tile_first[i], tile_first[i + 1]) of a token belong to tensor i.
@@ -148,19 +155,24 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     const uint32_t tile = pad ? a.ntiles - 1 : tile_raw;
     const uint32_t bt = fast_div(tile, a.div_tpt);
     const int32_t k = (int32_t)(tile - bt * a.div_tpt.d);
-    const int ti = k >= a.tile_first[2] ? 2 : (k >= a.tile_first[1] ? 1 : 0);
+    // Tensor and stream indices from sign bits (x >= y is the sign of
+    // y - 1 - x for these small non-negative values): plain scalar
+    // arithmetic, where comparisons would be widened to integers through
+    // vector selects, and an index the compiler cannot split into selects,
+    // so a stream's fields come from one computed kernel-argument address.
+    const int ti = (int)(((uint32_t)(a.tile_first[1] - 1 - k) >> 31) + ((uint32_t)(a.tile_first[2] - 1 - k) >> 31));
     const int32_t blk = k - sel3(ti, 0, a.tile_first[1], a.tile_first[2]);
     const uint32_t bq = fast_div(bt, a.div_tokens);
     const int32_t tok = (int32_t)(bt - bq * a.div_tokens.d);
     const int32_t b = (int32_t)bq;
-    const bool s1 = tok >= a.tokens0;              // token of stream 1 (image)
-    const int32_t ltok = s1 ? tok - a.tokens0 : tok;
+    const int si = (int)((uint32_t)(a.tokens0 - 1 - tok) >> 31);   // 1: a token of stream 1 (image)
+    const int32_t ltok = tok - si * a.tokens0;
 
     const TensorArgs& T = a.t[ti];
-    const int si = s1 ? 1 : 0;
-    const char* const in = T.in[si];
-    const int64_t in_sb = T.in_sb[si], in_st = T.in_st[si], in_sh = T.in_sh[si];
-    const char* const wt = T.weight[si];
+    const StreamView& S = T.s[si];
+    const char* const in = S.in;
+    const int64_t in_sb = S.sb, in_st = S.st, in_sh = S.sh;
+    const char* const wt = S.weight;
     char* const out = T.out;
     const int64_t out_sb = T.out_sb, out_st = T.out_st, out_sh = T.out_sh;
     const int32_t heads = T.heads;
@@ -170,15 +182,18 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     // Heads [h0, h0 + hrem) of the tensor are left from this tile on.
     const int32_t h0 = blk * RPP * NP;
     const int32_t hrem = heads - h0;
-    const char* const in_t = in + (int64_t)b * in_sb + (int64_t)ltok * in_st + (int64_t)h0 * in_sh;
+    // b, ltok and h0 are non-negative: zero-extended, each product takes one
+    // multiply fewer than a signed widening.
+    const char* const in_t = in + (int64_t)(uint32_t)b * in_sb + (int64_t)(uint32_t)ltok * in_st +
+                             (int64_t)(uint32_t)h0 * in_sh;
 
     // The two vectors this lane owns in every row.
     const int g = lane / LPR, j = lane % LPR;
-    const int nv = a.head_dim / VE;
+    const int nv = (int)((uint32_t)a.head_dim / VE);
     int v0, v1;
     bool rot_lane = false;
     if (PAIRING == kNeox && ROT) {
-        const int nr = a.rotary_dim / (2 * VE);   // vector pairs that rotate
+        const int nr = (int)((uint32_t)a.rotary_dim / (2 * VE));   // vector pairs that rotate
         if (j < nr) {
             v0 = j;
             v1 = j + nr;
@@ -231,11 +246,14 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
     auto out_base = [&](char*& out_t) {
         int64_t orow = tok;
         if (slots != nullptr) {
-            orow = slots[tok];
+            // A load through the constant address space is a scalar load for
+            // a uniform address: V tiles would otherwise read the slot with a
+            // vector load queued behind their rows.
+            orow = *(const __attribute__((address_space(4))) int64_t*)(slots + tok);
             if (orow < 0 || orow >= nslots)
                 return false;
         }
-        out_t = out + (int64_t)b * out_sb + orow * out_st + (int64_t)h0 * out_sh;
+        out_t = out + (int64_t)(uint32_t)b * out_sb + orow * out_st + (int64_t)(uint32_t)h0 * out_sh;
         return true;
     };
 
@@ -304,14 +322,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_kernel(const NormRopeArgs 
         }
     };
 
-    // The rotation's scalar parameters are read before the V branch, in the
-    // descriptor's batch of kernel-argument loads.
-    const RopeArgs& rp = a.rope;
-    const int half = (int)uniform((uint32_t)rp.half);
     const int64_t tabs = rp.token_base + tok;      // token inside the position planes
-    const float* const inv_freq = uniform(rp.inv_freq);
-    const int p0 = lane < half ? lane : half - 1;
-    const int p1 = lane + 64 < half ? lane + 64 : half - 1;
 
     uint4 d[NP][2];
     if (wt == nullptr) {   // wave-uniform: a routed tensor (V), bit copy
@@ -644,8 +655,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     const int rows = hq + hk;
     const int nq = hq * nv, nk = hk * nv;              // nq + nk <= kTokenVecs (the planner's condition)
     const int ntot = nq + nk;
-    const char* const qin = TQ.in[0] + (int64_t)b * TQ.in_sb[0] + (int64_t)tok * TQ.in_st[0];
-    const char* const kin = TK.in[0] + (int64_t)b * TK.in_sb[0] + (int64_t)tok * TK.in_st[0];
+    const char* const qin = TQ.s[0].in + (int64_t)b * TQ.s[0].sb + (int64_t)tok * TQ.s[0].st;
+    const char* const kin = TK.s[0].in + (int64_t)b * TK.s[0].sb + (int64_t)tok * TK.s[0].st;
 
     // Byte offset within its tensor's token of the tensor's flat vector f.
     auto flat_off = [&](int f, int32_t sh) {
@@ -705,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     auto slot_in_tensor = [&](int s) { return s >= sq ? s - sq : s; };
     uint4 fl[kRegSlots];
     if constexpr (DMA) {
-        const int32_t shq = (int32_t)TQ.in_sh[0], shk = (int32_t)TK.in_sh[0];
+        const int32_t shq = (int32_t)TQ.s[0].sh, shk = (int32_t)TK.s[0].sh;
 #pragma unroll
         for (int s = 0; s < kSlots; ++s) {
             const int f = 64 * s + lane < ntot ? 64 * s + lane : ntot - 1;
@@ -719,13 +730,13 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
             const int n = isk ? nk : nq;
             const int f = 64 * slot_in_tensor(s) + lane;
             fl[s] = load_row16<NT>((isk ? kin : qin) +
-                                   flat_off(f < n ? f : n - 1, (int32_t)(isk ? TK.in_sh[0] : TQ.in_sh[0])));
+                                   flat_off(f < n ? f : n - 1, (int32_t)(isk ? TK.s[0].sh : TQ.s[0].sh)));
         }
     }
     // Weight vectors: lanes [0, nv) the Q tensor's, [nv, 2 nv) the K tensor's
     // (an absent tensor's lanes read the other one's: never used).
-    const char* const wq = hq > 0 ? TQ.weight[0] : TK.weight[0];
-    const char* const wk = hk > 0 ? TK.weight[0] : TQ.weight[0];
+    const char* const wq = hq > 0 ? TQ.s[0].weight : TK.s[0].weight;
+    const char* const wk = hk > 0 ? TK.s[0].weight : TQ.s[0].weight;
     const int wl = lane < nv ? lane : (lane < 2 * nv ? lane - nv : 0);
     const uint4 wv = load16((lane < nv ? wq : wk) + wl * 16);
 
