@@ -80,15 +80,15 @@ struct BF16 {
         return make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
     }
     // Contract rounding: the normalised value is rounded to bf16 before the
-    // rotation ([Ovis] kernel review: one documented rounding contract).
+    // rotation ([Ovis] kernel review: one documented rounding contract).  One
+    // conversion per value with the value in the high half and +0 in the low
+    // half gives the rounded value's fp32 bits directly (a packed conversion
+    // of two values would need two more instructions to unpack them).
     __device__ __forceinline__ static void round_trip(float* x)
     {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w = pack2(x[2 * i], x[2 * i + 1]);
-            x[2 * i] = __uint_as_float(w << 16);
-            x[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
-        }
+        for (int i = 0; i < 8; ++i)
+            x[i] = __uint_as_float(pack2(0.0f, x[i]));
     }
     // Two fp32 values rounded to bf16 (a cos/sin table stored in bf16).
     __device__ __forceinline__ static void round_pair(float& a, float& b)
