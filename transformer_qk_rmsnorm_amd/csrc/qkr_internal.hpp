@@ -180,14 +180,23 @@ __host__ __device__ inline void vit_position(const VitArgs& a, uint32_t tok, int
     uint32_t start = a.cu[0];
     FastDiv d_frame = a.div_area[0], d_bcols = a.div_bcols[0];
     for (int32_t k = 1; k < a.num_grids; ++k) {
-        const bool in_k = tok >= a.cu[k];
-        start = in_k ? a.cu[k] : start;
-        d_frame.d = in_k ? a.div_area[k].d : d_frame.d;
-        d_frame.m = in_k ? a.div_area[k].m : d_frame.m;
-        d_frame.sh = in_k ? a.div_area[k].sh : d_frame.sh;
-        d_bcols.d = in_k ? a.div_bcols[k].d : d_bcols.d;
-        d_bcols.m = in_k ? a.div_bcols[k].m : d_bcols.m;
-        d_bcols.sh = in_k ? a.div_bcols[k].sh : d_bcols.sh;
+        // Every field of grid k is read before the choice: a choice between a
+        // field and the value so far is otherwise compiled into a branch
+        // around that field's load (tokens differ per lane), with a wait of
+        // its own for each field.
+        uint32_t ck = a.cu[k], ad = a.div_area[k].d, am = a.div_area[k].m, as = a.div_area[k].sh;
+        uint32_t bd = a.div_bcols[k].d, bm = a.div_bcols[k].m, bs = a.div_bcols[k].sh;
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm("" : "+s"(ck), "+s"(ad), "+s"(am), "+s"(as), "+s"(bd), "+s"(bm), "+s"(bs));
+#endif
+        const bool in_k = tok >= ck;
+        start = in_k ? ck : start;
+        d_frame.d = in_k ? ad : d_frame.d;
+        d_frame.m = in_k ? am : d_frame.m;
+        d_frame.sh = in_k ? as : d_frame.sh;
+        d_bcols.d = in_k ? bd : d_bcols.d;
+        d_bcols.m = in_k ? bm : d_bcols.m;
+        d_bcols.sh = in_k ? bs : d_bcols.sh;
     }
     const uint32_t local = tok - start;
     const uint32_t frame = fast_div(local, d_frame);

@@ -271,16 +271,19 @@ __global__ __launch_bounds__(kThreads) void debug_fp8_kernel(const float* x, int
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void vit_setup_kernel(const VitArgs a)
 {
-    const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
+    // Threads past the last group compute the last one again and store
+    // nothing: no early exit, so no branch splits the kernel-argument reads.
     const uint32_t groups = a.div_groups.d;
-    if (idx >= (uint32_t)a.tok_count * groups)
-        return;
+    const uint32_t total = (uint32_t)a.tok_count * groups;
+    const uint32_t idx_raw = blockIdx.x * kThreads + threadIdx.x;
+    const bool live = idx_raw < total;
+    const uint32_t idx = live ? idx_raw : total - 1;
     const uint32_t tl = fast_div(idx, a.div_groups);
     const int32_t c0 = 4 * (int32_t)(idx - tl * groups);
     const uint32_t tok = (uint32_t)a.tok_begin + tl;
     int32_t pos[3];
     vit_position(a, tok, &pos[0], &pos[1], &pos[2]);
-    float cv[4], sv[4];
+    float cv[4], sv[4], iv[4];
     int axis[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -288,10 +291,21 @@ __global__ __launch_bounds__(kThreads) void vit_setup_kernel(const VitArgs a)
         const int ax = col < a.off[1] ? 0 : (col < a.off[2] ? 1 : 2);
         const float* inv = ax == 0 ? a.inv[0] : (ax == 1 ? a.inv[1] : a.inv[2]);
         const int32_t off = ax == 0 ? a.off[0] : (ax == 1 ? a.off[1] : a.off[2]);
-        const int32_t p = ax == 0 ? pos[0] : (ax == 1 ? pos[1] : pos[2]);
-        sincosf((float)p * inv[col - off], &sv[e], &cv[e]);
+        iv[e] = inv[col - off];
         axis[e] = ax;
     }
+    // The four inverse frequencies are in hand before the first sincosf:
+    // one wait for the four loads, where the compiler would otherwise place
+    // each load (and a wait for it) just before its sincosf.
+    asm("" : "+v"(iv[0]), "+v"(iv[1]), "+v"(iv[2]), "+v"(iv[3]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int ax = axis[e];
+        const int32_t p = ax == 0 ? pos[0] : (ax == 1 ? pos[1] : pos[2]);
+        sincosf((float)p * iv[e], &sv[e], &cv[e]);
+    }
+    if (!live)
+        return;
     const int64_t row = ((int64_t)axis[0] * a.n_tokens + tok) * a.half_rot + c0;
     if (a.vec_ok) {
         // groups never straddle a section and rows are whole groups
