@@ -33,14 +33,20 @@ __device__ __forceinline__ TokenPositions vit_token_positions(const VitGridArgs&
     uint32_t a_d = v.div_area[0].d, a_m = v.div_area[0].m, a_l = v.div_area[0].sh;
     uint32_t b_d = v.div_bcols[0].d, b_m = v.div_bcols[0].m, b_l = v.div_bcols[0].sh;
     for (int k = 1; k < v.num_grids; ++k) {
-        const bool in_k = tok >= (uint32_t)v.cu[k];
-        start = in_k ? (uint32_t)v.cu[k] : start;
-        a_d = in_k ? v.div_area[k].d : a_d;
-        a_m = in_k ? v.div_area[k].m : a_m;
-        a_l = in_k ? v.div_area[k].sh : a_l;
-        b_d = in_k ? v.div_bcols[k].d : b_d;
-        b_m = in_k ? v.div_bcols[k].m : b_m;
-        b_l = in_k ? v.div_bcols[k].sh : b_l;
+        // Grid k's fields are all read before the choice (an empty asm takes
+        // them): a choice between a field and the value so far would
+        // otherwise become a branch around that field's load, one wait each.
+        uint32_t ck = (uint32_t)v.cu[k], ad = v.div_area[k].d, am = v.div_area[k].m, as = v.div_area[k].sh;
+        uint32_t bd = v.div_bcols[k].d, bm = v.div_bcols[k].m, bs = v.div_bcols[k].sh;
+        asm("" : "+s"(ck), "+s"(ad), "+s"(am), "+s"(as), "+s"(bd), "+s"(bm), "+s"(bs));
+        const bool in_k = tok >= ck;
+        start = in_k ? ck : start;
+        a_d = in_k ? ad : a_d;
+        a_m = in_k ? am : a_m;
+        a_l = in_k ? as : a_l;
+        b_d = in_k ? bd : b_d;
+        b_m = in_k ? bm : b_m;
+        b_l = in_k ? bs : b_l;
     }
     const FastDiv d_frame{a_d, a_m, a_l}, d_bcols{b_d, b_m, b_l};
     const uint32_t local = tok - start;
@@ -639,28 +645,44 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     uint4* const st = lds_all + wave * kSlice;
     uint4* const wst = st + kTokenVecs;   // weight vectors in the slice: register loads only
 
-    // Tile = batch * tokens + token.  Padding waves of the last workgroup redo
-    // the last tile and store nothing.
-    const uint32_t tile_raw = a.tile_base + blockIdx.x * kWaves + wave;
-    const bool pad = tile_raw >= a.ntiles;
-    const uint32_t tile = pad ? a.ntiles - 1 : tile_raw;
-    const uint32_t bq = fast_div(tile, a.div_tokens);
-    const int32_t tok = (int32_t)(tile - bq * a.div_tokens.d);
-    const int32_t b = (int32_t)bq;
-
     const TensorArgs& TQ = a.t[0];
     const TensorArgs& TK = a.t[1];
-    const int nv = a.head_dim / VE;
-    const int hq = TQ.heads, hk = TK.heads;
+    const RopeArgs& rp = a.rope;
+    // Every kernel-argument field that the row loads and the lane's pair
+    // operand depend on, read in one batch: an empty asm takes them all, so
+    // the compiler issues every load before the first wait instead of
+    // spreading them over several scalar round trips.
+    uint32_t tile_base = a.tile_base, ntiles = a.ntiles, td = a.div_tokens.d, tm = a.div_tokens.m,
+             tsh = a.div_tokens.sh, nv_recip = a.nv_recip;
+    int32_t head_dim = a.head_dim, rotary_dim = a.rotary_dim, hq = TQ.heads, hk = TK.heads, half = rp.half;
+    const char* qbase = TQ.s[0].in;
+    const char* kbase = TK.s[0].in;
+    int64_t qsb = TQ.s[0].sb, qst = TQ.s[0].st, ksb = TK.s[0].sb, kst = TK.s[0].st, token_base = rp.token_base;
+    int32_t shq = (int32_t)TQ.s[0].sh, shk = (int32_t)TK.s[0].sh;
+    asm("" : "+s"(tile_base), "+s"(ntiles), "+s"(td), "+s"(tm), "+s"(tsh), "+s"(nv_recip), "+s"(head_dim),
+             "+s"(rotary_dim), "+s"(hq), "+s"(hk), "+s"(half), "+s"(qbase), "+s"(kbase), "+s"(qsb), "+s"(qst),
+             "+s"(ksb), "+s"(kst), "+s"(token_base), "+s"(shq), "+s"(shk));
+
+    // Tile = batch * tokens + token.  Padding waves of the last workgroup redo
+    // the last tile and store nothing.
+    const uint32_t tile_raw = tile_base + blockIdx.x * kWaves + wave;
+    const bool pad = tile_raw >= ntiles;
+    const uint32_t tile = pad ? ntiles - 1 : tile_raw;
+    const FastDiv div_tokens{td, tm, tsh};
+    const uint32_t bq = fast_div(tile, div_tokens);
+    const int32_t tok = (int32_t)(tile - bq * td);
+    const int32_t b = (int32_t)bq;
+
+    const int nv = (int)((uint32_t)head_dim / VE);
     const int rows = hq + hk;
     const int nq = hq * nv, nk = hk * nv;              // nq + nk <= kTokenVecs (the planner's condition)
     const int ntot = nq + nk;
-    const char* const qin = TQ.s[0].in + (int64_t)b * TQ.s[0].sb + (int64_t)tok * TQ.s[0].st;
-    const char* const kin = TK.s[0].in + (int64_t)b * TK.s[0].sb + (int64_t)tok * TK.s[0].st;
+    const char* const qin = qbase + (int64_t)(uint32_t)b * qsb + (int64_t)(uint32_t)tok * qst;
+    const char* const kin = kbase + (int64_t)(uint32_t)b * ksb + (int64_t)(uint32_t)tok * kst;
 
     // Byte offset within its tensor's token of the tensor's flat vector f.
     auto flat_off = [&](int f, int32_t sh) {
-        const int fr = (int)(((uint32_t)f * a.nv_recip) >> 16);
+        const int fr = (int)(((uint32_t)f * nv_recip) >> 16);
         return (uint32_t)(fr * sh + (f - fr * nv) * 16);
     };
 
@@ -669,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     int v0, v1;
     bool rot_lane = false;
     if (PAIRING == kNeox && ROT) {
-        const int nr = a.rotary_dim / (2 * VE);
+        const int nr = (int)((uint32_t)rotary_dim / (2 * VE));
         if (j < nr) {
             v0 = j;
             v1 = j + nr;
@@ -688,9 +710,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
 
     // 1) Loads: the lane's pair operand, the token's rows (into the slice by
     //    LDS DMA, or into registers), the weight vectors.
-    const RopeArgs& rp = a.rope;
-    const int half = (int)uniform((uint32_t)rp.half);
-    const int64_t tabs = rp.token_base + tok;
+    const int64_t tabs = token_base + tok;
     const int p0 = lane < half ? lane : half - 1;
     float op0 = 0.0f, os0 = 0.0f;
     int32_t ax0 = 0;
@@ -716,7 +736,6 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
     auto slot_in_tensor = [&](int s) { return s >= sq ? s - sq : s; };
     uint4 fl[kRegSlots];
     if constexpr (DMA) {
-        const int32_t shq = (int32_t)TQ.s[0].sh, shk = (int32_t)TK.s[0].sh;
 #pragma unroll
         for (int s = 0; s < kSlots; ++s) {
             const int f = 64 * s + lane < ntot ? 64 * s + lane : ntot - 1;
@@ -730,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_token_kernel(const NormRop
             const int n = isk ? nk : nq;
             const int f = 64 * slot_in_tensor(s) + lane;
             fl[s] = load_row16<NT>((isk ? kin : qin) +
-                                   flat_off(f < n ? f : n - 1, (int32_t)(isk ? TK.s[0].sh : TQ.s[0].sh)));
+                                   flat_off(f < n ? f : n - 1, isk ? shk : shq));
         }
     }
     // Weight vectors: lanes [0, nv) the Q tensor's, [nv, 2 nv) the K tensor's
